@@ -1,0 +1,190 @@
+"""Benchmark: batch-invariant token scoring with the 4-layer Llama-8B-shaped decoder.
+
+One step = score one batch of synthetic sequences end to end through the whole hot path:
+embedding gather, per layer RMSNorm -> QKV fixed-order GEMM -> RoPE + KV append ->
+chunked causal attention -> O GEMM + residual -> RMSNorm -> W1||W3 GEMM -> SwiGLU ->
+W2 GEMM + residual; final RMSNorm; LM head (BF16 pass, log-softmax, top-2, margin) with
+selective FP32 recompute of rows whose margin < 0.1.  Inputs (weights, tokens) are
+resident in HBM before the timed region.  value = scored tokens / s = B * (T - 1) / step.
+
+Also printed in the same JSON line:
+  roofline      the dominant kernel (the body projections' register-tiled GEMM), timed
+                with HIP events on its launch stream inside the timed steps;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload (one 64-token
+                sequence at full width), host cores, scaled to tokens / s;
+  bitwise       match rates: repeated steps, prefill vs token-by-token decode at the end of
+                the long context, and the GPU against the oracle on the CPU sample.
+
+Usage: python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--batch 1] [--seq 32768]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector/matrix peak: 256 CU x 2.4 GHz x 256 flop/clk
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--seq", type=int, default=32768)
+    ap.add_argument("--block", type=int, default=4096, help="token rows per prefill block")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows are independent, so N GPUs would each score their own sequences). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from invariant_numerics_amd import binding as inv
+    from invariant_numerics_amd.decoder import Decoder
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = dict(synth.C5)
+    cfg["layers"] = args.layers
+    B, T = args.batch, args.seq
+    t0 = time.time()
+    log("generating synthetic model", cfg)
+    model = synth.decoder_model(cfg, T)
+    toks = synth.tokens(synth.SEEDS["c5_tok"], B, T, cfg["vocab"])
+    log("model ready in %.1fs" % (time.time() - t0))
+    dec = Decoder(model, device=dev, batch=B, tmax=T)
+    td = torch.from_numpy(toks).to(dev)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    def step():
+        return dec.prefill(td, block=args.block)
+
+    for i in range(args.warmup):
+        log("warmup", i)
+        out = step()
+    torch.cuda.synchronize()
+    rec = []
+    dec.gemm_events = rec
+    outs = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        outs.append(step())
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    dec.gemm_events = None
+    ms = elapsed / args.steps * 1e3
+    scored = B * (T - 1)
+    value = scored * args.steps / elapsed
+    log("step %.1f ms, %.0f scored tok/s" % (ms, value))
+
+    # dominant kernel: body projections, HIP events on the launch stream
+    durs = np.array([s.elapsed_time(e) for s, e, _ in rec]) * 1e-3  # seconds
+    flops = np.array([f for _, _, f in rec], np.float64)
+    achieved = float(flops.sum() / durs.sum()) / 1e12
+    gemm_share = float(durs.sum() / elapsed)
+    roof = dict(bound="alu", kernel="gemm_tiled_kernel (body projections)", achieved=round(achieved, 3),
+                peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / FP32_PEAK_TFLOPS, 4),
+                traffic=None, launches=int(len(rec)), avg_launch_us=round(float(durs.mean()) * 1e6, 2),
+                avg_flops_per_launch=float(flops.mean()), share_of_step=round(gemm_share, 3))
+    recomputed = float(outs[-1]["recomputed"].float().mean().item())
+
+    # ---------------------------------------------------------------- bitwise checks
+    bitwise = {}
+    if not args.no_check:
+        keys = ("logprob", "margin", "top1", "top2", "recomputed")
+
+        def rate(a, b):
+            a = a.contiguous().view(torch.int32) if a.dtype == torch.float32 else a
+            b = b.contiguous().view(torch.int32) if b.dtype == torch.float32 else b
+            return (a == b).float().mean().item()
+
+        bitwise["repeat_steps"] = min(rate(outs[0][k], outs[-1][k]) for k in keys)
+        # prefill vs token-by-token decode on the last positions of the long context
+        ndec = min(16, T - 1)
+        p0 = T - 1 - ndec
+        log("decode check: prefill %d tokens, then %d decode steps" % (p0, ndec))
+        dd = Decoder.__new__(Decoder)
+        dd.__dict__.update(dec.__dict__)
+        dd.kc = [torch.zeros_like(k) for k in dec.kc]
+        dd.vc = [torch.zeros_like(v) for v in dec.vc]
+        dd.gemm_events = None
+        if p0 > 0:
+            dd.prefill(td[:, :p0 + 1].contiguous(), block=args.block)
+        agree = []
+        for t in range(p0, T - 1):
+            pos = torch.full((B,), t, dtype=torch.int32, device=dev)
+            r = dd.decode_step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
+            agree.append(min(rate(r[k], outs[-1][k][:, t]) for k in keys))
+        bitwise["prefill_vs_decode"] = float(np.mean(agree))
+        bitwise["prefill_vs_decode_positions"] = [p0, T - 2]
+        del dd
+
+    # ---------------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        from oracle import oracle as orc
+        n = args.cpu_tokens
+        sample = toks[0, :n].copy()
+        orc.lib()
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        log("cpu baseline: oracle on %d tokens at full width, %s threads" % (n, threads))
+        tc = time.perf_counter()
+        want = orc.decoder(sample, model)
+        tcpu = time.perf_counter() - tc
+        cpu = dict(value=round((n - 1) / tcpu, 3), unit="scored tokens/s", cores=threads, kind="oracle",
+                   sample="one %d-token sequence through the same 4-layer full-width decoder and "
+                          "LM head (hidden 4096, vocab 128256, selective recompute); %.1f s" % (n, tcpu))
+        if not args.no_check:
+            g = Decoder(model, device=dev, batch=1, tmax=n).prefill(torch.from_numpy(sample[None]).to(dev))
+            tot = 0
+            same = 0
+            for k, w in want.items():
+                a = g[k][0].cpu().numpy()
+                if a.dtype == np.float32:
+                    a, w = a.view(np.uint32), w.view(np.uint32)
+                same += int((a == w).sum())
+                tot += a.size
+            bitwise["vs_oracle"] = same / tot
+            bitwise["vs_oracle_words"] = tot
+
+    line = dict(
+        metric="scored tokens/s (batch-invariant) + % HBM/FLOP roofline; bitwise-match rate",
+        value=round(value, 2), unit="scored tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 3), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="f32", data="synthetic",
+        config=dict(workload="4-layer Llama-8B-shaped decoder, prefill scoring with selective FP32 "
+                             "LM-head recompute", layers=cfg["layers"], hidden=cfg["hidden"],
+                    q_heads=cfg["hq"], kv_heads=cfg["hkv"], head_dim=cfg["d"], ffn=cfg["ffn"],
+                    vocab=cfg["vocab"], batch=B, seq_len=T, token_block=args.block, tau=0.1,
+                    weights="bf16 storage, fp32 compute", recomputed_fraction=round(recomputed, 4)),
+        roofline=roof, cpu_baseline=cpu, bitwise=bitwise)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

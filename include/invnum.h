@@ -1,0 +1,209 @@
+/*
+ * invnum.h -- C ABI of libinvnum.so: batch-invariant, fixed-reduction-order kernels for
+ * token log-probabilities on AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the pages on invariant numerics:
+ *   - every reduction whose order changes the bits (matmul K-sums, attention score sums,
+ *     the softmax denominator, the logprob accumulation) runs in ONE fixed order that
+ *     prefill and decode share  [Meituan bitwise train/inference alignment page,
+ *     "principles" and "key practices" lists];
+ *   - full-K accumulation, never a split reduce  [same page, "key practices", TP item];
+ *   - LayerCast: weights stored BF16 and upcast to FP32 per layer, all matmul and
+ *     attention arithmetic in FP32  ["Give Me FP32 or Give Me Death?" write-up,
+ *     section 5; Yuan et al. blog, section 4];
+ *   - selective FP32 LM-head recompute when the top-two logit margin falls below a
+ *     threshold  ["Greedy Decoding Is Not Precision-Invariant", abstract].
+ *
+ * The pinned order ("canonical reduction order v0"), used by every entry point:
+ *   dot_KS(x, w, K): contiguous K-slices of 256; per slice c = +0, c = fma(x_k, w_k, c)
+ *     for k ascending; then T = c_0, T = T + c_s for s ascending.
+ *   attention: scores dot_KS(q, k_j, D) * scale; keys in absolute chunks of 256; per
+ *     chunk m_c = max, l_c and o_c summed for j ascending with p = exp_f(s_j - m_c);
+ *     chunks merged left to right from chunk 0; out = o / l.
+ *   LM head: tiles of 1024 vocabulary entries, 64 lanes per tile summing 16 entries each,
+ *     a pairwise lane tree, tiles folded left to right; lp = (z_t - M) - log_f(S).
+ *   exp_f / log_f are the library's own functions (Cody-Waite reduction + degree-7 Taylor;
+ *     atanh series), identical on every device and on the CPU check.
+ * A row's output bits depend only on that row's inputs and these constants: never on the
+ * batch size, the row's position in the batch, the grid, the stream or the CU count.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (e.g. torch tensors' data_ptr()), row-major,
+ *     with the leading dimensions given.  BF16 tensors are passed as uint16_t bit patterns.
+ *     Pointers must be 16-byte aligned and leading dimensions multiples of 4 elements (FP32)
+ *     or 8 elements (BF16); otherwise INV_ERR_ALIGN.
+ *   - The caller owns all memory.  The library never allocates and keeps no pointer after
+ *     the call returns.  Scratch memory comes from a caller-supplied workspace whose size
+ *     is given by the matching *_workspace_bytes() query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     asynchronously; there is no host synchronisation inside any call.  Outputs are valid
+ *     once the stream has completed the enqueued work.
+ *   - Return value: INV_OK (0) or a negative status.  On any validation error nothing is
+ *     enqueued.  A launch failure returns INV_ERR_LAUNCH.  Calls are stateless and
+ *     re-entrant; calls on different streams must not write the same outputs/workspace.
+ */
+#ifndef INVNUM_H
+#define INVNUM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum inv_status {
+    INV_OK = 0,
+    INV_ERR_NULL = -1,        /* a required pointer is NULL */
+    INV_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    INV_ERR_ALIGN = -3,       /* pointer or leading dimension not aligned as required */
+    INV_ERR_DTYPE = -4,       /* unknown dtype code */
+    INV_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the query returned */
+    INV_ERR_UNSUPPORTED = -6, /* valid but unsupported shape (e.g. head dim != 128) */
+    INV_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
+};
+
+enum inv_dtype { INV_BF16 = 0, INV_F32 = 1 };
+
+#define INV_MAX_FLOAT_CONSTS 32
+
+typedef struct inv_constants {
+    int32_t ks;            /* K-slice width of dot_KS: 256 */
+    int32_t chunk;         /* attention KV chunk: 256 */
+    int32_t vocab_tile;    /* LM-head vocabulary tile: 1024 */
+    int32_t lanes;         /* lanes of the vocabulary tree: 64 */
+    int32_t n_float;       /* number of valid entries in float_consts */
+    /* exp_f / log_f constants in a fixed order: log2e, ln2_hi, ln2_lo, exp lower limit,
+     * exp upper limit, 1/k! for k = 0..7, ln2_hi16, ln2_lo16, 2/(2k+1) for k = 1..5 */
+    float float_consts[INV_MAX_FLOAT_CONSTS];
+} inv_constants;
+
+/* Text for a status code (static storage). */
+const char* inv_status_string(int status);
+
+/* The pinned constants of the reduction order.  Host-only; no device is touched. */
+int inv_get_constants(inv_constants* out);
+
+/* ------------------------------------------------------------------------------------ *
+ * inv_fixed_order_gemm -- LayerCast matmul with the fixed K order.
+ *   Y[m, n] = dot_KS(X[m, :], up(W[n, :]), K)        (+ R[m, n] when R != NULL)
+ * X: FP32 [M, K] (row stride ldx).  W: BF16 [N, K] (nn.Linear layout, row stride ldw),
+ * upcast exactly (bits << 16) as it is read.  Y: FP32 [M, N] (row stride ldy).
+ * R: optional FP32 residual [M, N] (row stride ldr) added after the full dot as
+ * Y = R + dot (one rounding; the same bits as a separate inv_add).  R may equal Y.
+ * Sizes: M >= 1, N >= 1, K >= 8 and K % 8 == 0.  X and W follow the 16-byte rule above;
+ * Y and R need only 4-byte alignment (any ldy, ldr >= N).  Each output is owned by one workgroup
+ * (no split-K, no atomics); launch geometry depends on M but the order never does.
+ * Sources: Meituan page, "key practices" (full-K, batch-invariant operators); FP32
+ * write-up section 5 (LayerCast).
+ * ------------------------------------------------------------------------------------ */
+int inv_fixed_order_gemm(const float* X, int64_t M, int64_t K, int64_t ldx,
+                         const uint16_t* W, int64_t N, int64_t ldw,
+                         const float* R, int64_t ldr,
+                         float* Y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * inv_rmsnorm -- ss = dot_KS(x, x, H); r = 1 / sqrt((ss / H) + eps); y_k = (x_k * r) * up(g_k)
+ * X: FP32 [M, H] (ldx); gamma: BF16 [H]; Y: FP32 [M, H] (ldy), may alias X when ldy == ldx.
+ * Division and square root are IEEE correctly rounded.  H >= 8, H % 8 == 0.
+ * ------------------------------------------------------------------------------------ */
+int inv_rmsnorm(const float* X, int64_t M, int64_t H, int64_t ldx, const uint16_t* gamma,
+                float eps, float* Y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * inv_attention_prefill -- causal attention for queries at positions q_start..q_start+Tq-1.
+ * dtype: INV_BF16 (Q, caches BF16, upcast on load) or INV_F32.
+ * Q: [B, Tq, Hq, D]; Kc, Vc: [B, Hkv, Tmax, D] already holding keys/values of positions
+ * 0..q_start+Tq-1; O: FP32 [B, Tq, Hq, D].  Query head h reads kv head h / (Hq / Hkv).
+ * Per row: the chunked order in the header comment, with the merge folded as chunks are
+ * produced -- the same bits as inv_attention_decode for that row.
+ * Constraints: D == 128 (else INV_ERR_UNSUPPORTED), Hq % Hkv == 0, q_start + Tq <= Tmax.
+ * Sources: Meituan page, "principles" (attention score sums, softmax denominator) and
+ * "key practices" (DCP: the forward replays decode's accumulation path).
+ * ------------------------------------------------------------------------------------ */
+int inv_attention_prefill(int dtype, const void* Q, const void* Kc, const void* Vc,
+                          int64_t B, int64_t Tq, int64_t q_start, int64_t Tmax,
+                          int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                          float* O, void* stream);
+
+/* Workspace for inv_attention_decode: B * Hq * ceil(Tmax/256) * (D + 2) floats. */
+size_t inv_attention_decode_workspace_bytes(int64_t B, int64_t Tmax, int64_t Hq, int64_t D);
+
+/* ------------------------------------------------------------------------------------ *
+ * inv_attention_decode -- one query per sequence, at position pos[b] (keys 0..pos[b]).
+ * Q: [B, Hq, D] (dtype as above); caches [B, Hkv, Tmax, D]; pos: INT32 [B] on the device,
+ * 0 <= pos[b] < Tmax (rows may differ; a row with pos outside that range gets NaN and its
+ * cache is not read).  O: FP32 [B, Hq, D].
+ * One workgroup per (b, kv head, chunk) writes the chunk partial (m_c, l_c, o_c) into the
+ * workspace; a second kernel folds them per (b, q head) in ascending chunk order.
+ * ------------------------------------------------------------------------------------ */
+int inv_attention_decode(int dtype, const void* Q, const void* Kc, const void* Vc,
+                         const int32_t* pos, int64_t B, int64_t Tmax,
+                         int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                         float* O, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace for inv_lmhead_logprob_top2. */
+size_t inv_lmhead_workspace_bytes(int64_t B, int64_t K, int64_t V);
+
+/* ------------------------------------------------------------------------------------ *
+ * inv_lmhead_logprob_top2 -- log-softmax at the target, top-2 and margin, with selective
+ * FP32 recompute.
+ *   P pass: a = up(bf(h)) (BF16 operands, FP32 sums); z_v = dot_KS(a, up(W_v), K);
+ *           top1 = lowest index of the maximum, top2 = lowest other index of the maximum
+ *           of the rest; M = z_top1; margin = z_top1 - z_top2; S as in the header comment;
+ *           lp = (z_target - M) - log_f(S).
+ *   Rows with margin_P < tau (strict) are compacted on the device and redone with a = h
+ *   (F pass); their outputs are F's and recomputed[b] = 1.  tau = +inf recomputes every
+ *   row; tau = 0 recomputes none.
+ * Hs: FP32 [B, K] (ldh); W: BF16 [V, K] (row stride K); target: INT32 [B] (device),
+ * 0 <= t < V (a row whose target is outside that range gets logprob NaN).
+ * Outputs (device, [B]): logprob, margin (FP32), top1, top2 (INT32), recomputed (UINT8).
+ * V >= 2, K >= 8, K % 8 == 0.
+ * Sources: "Greedy Decoding Is Not Precision-Invariant", abstract and "key design"
+ * paragraph (margin-triggered FP32 LM-head recompute); Meituan page, "principles"
+ * (logprob accumulation is one of the order-sensitive sums).
+ * ------------------------------------------------------------------------------------ */
+int inv_lmhead_logprob_top2(const float* Hs, int64_t B, int64_t K, int64_t ldh,
+                            const uint16_t* W, int64_t V, const int32_t* target, float tau,
+                            float* logprob, float* margin, int32_t* top1, int32_t* top2,
+                            uint8_t* recomputed, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- decoder helpers --- *
+ * Elementwise steps of a Llama-shaped decoder (no reductions, so no order to pin).
+ * ------------------------------------------------------------------------------------ */
+
+/* X[m, :] = up(table[ids[m], :]).  table BF16 [Vocab, H]; ids INT32 [M] (device).
+ * An id outside [0, Vocab) is not read; its row is filled with NaN. */
+int inv_embed(const int32_t* ids, int64_t M, const uint16_t* table, int64_t vocab, int64_t H,
+              float* X, int64_t ldx, void* stream);
+
+/* Rotate-half RoPE on the q and k parts of a fused projection, and cache append.
+ * QKV: FP32 [M, (Hq + 2 Hkv) D] (ldqkv) laid out [q heads | k heads | v heads].
+ * Row m belongs to sequence seq[m] at position pos[m] (INT32, device).
+ * cos_t, sin_t: FP32 [Tmax, D/2].  For pairs (i, i + D/2):
+ *   y_i = (x_i c_i) - (x_{i+D/2} s_i);  y_{i+D/2} = (x_i s_i) + (x_{i+D/2} c_i)   (no fma)
+ * Qout: FP32 [M, Hq, D]; Kc, Vc: FP32 [Bcache, Hkv, Tmax, D] receive rotated k and v at
+ * [seq[m], g, pos[m], :].  D even.  Rows whose seq/pos fall outside the cache are skipped
+ * (nothing written for them). */
+int inv_rope_kv_append(const float* QKV, int64_t M, int64_t ldqkv, int64_t Hq, int64_t Hkv,
+                       int64_t D, const int32_t* seq, const int32_t* pos,
+                       const float* cos_t, const float* sin_t, int64_t Tmax, int64_t Bcache,
+                       float* Qout, float* Kc, float* Vc, void* stream);
+
+/* Hout[m, f] = silu(G[m, f]) * U[m, f], silu(a) = a / (1 + exp_f(-a)). */
+int inv_swiglu(const float* G, const float* U, int64_t M, int64_t F, int64_t ldg, int64_t ldu,
+               float* Hout, int64_t ldh, void* stream);
+
+/* Y[m, n] = A[m, n] + Bm[m, n]. */
+int inv_add(const float* A, const float* Bm, int64_t M, int64_t N, int64_t lda, int64_t ldb,
+            float* Y, int64_t ldy, void* stream);
+
+/* Diagnostic: y[i] = exp_f(x[i]) (fn 0), log_f(x[i]) (fn 1) or up(bf(x[i])) (fn 2) on the
+ * device, for checking the library's scalar primitives against the CPU check. */
+int inv_eval_numerics(int fn, const float* x, float* y, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INVNUM_H */

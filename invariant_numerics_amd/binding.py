@@ -1,0 +1,276 @@
+"""Thin ctypes binding of libinvnum.so.
+
+Each ``inv_*`` function below has the name of the C entry point it calls and only
+marshals arguments: torch tensors supply device pointers, torch's current stream is
+passed as the HIP stream, and every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing the import of this module
+fails, and a non-zero status raises ``InvError``.
+"""
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libinvnum.so")
+
+INV_BF16 = 0
+INV_F32 = 1
+
+i64 = ctypes.c_int64
+vp = ctypes.c_void_p
+
+
+class InvError(RuntimeError):
+    pass
+
+
+class _Consts(ctypes.Structure):
+    _fields_ = [("ks", ctypes.c_int32), ("chunk", ctypes.c_int32), ("vocab_tile", ctypes.c_int32),
+                ("lanes", ctypes.c_int32), ("n_float", ctypes.c_int32),
+                ("float_consts", ctypes.c_float * 32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libinvnum.so is not built (run __graft_entry__.build() or "
+                          "python invariant_numerics_amd/build.py); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "inv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "inv_get_constants": (ctypes.c_int, [ctypes.POINTER(_Consts)]),
+        "inv_fixed_order_gemm": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp]),
+        "inv_rmsnorm": (ctypes.c_int, [vp, i64, i64, i64, vp, ctypes.c_float, vp, i64, vp]),
+        "inv_attention_prefill": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                                 i64, ctypes.c_float, vp, vp]),
+        "inv_attention_decode_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64, i64]),
+        "inv_attention_decode": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
+        "inv_lmhead_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64]),
+        "inv_lmhead_logprob_top2": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, ctypes.c_float, vp, vp,
+                                                   vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "inv_embed": (ctypes.c_int, [vp, i64, vp, i64, i64, vp, i64, vp]),
+        "inv_rope_kv_append": (ctypes.c_int, [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i64, vp,
+                                              vp, vp, vp]),
+        "inv_swiglu": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
+        "inv_add": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
+        "inv_eval_numerics": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+LIB = _load()
+EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "inv_rmsnorm",
+           "inv_attention_prefill", "inv_attention_decode_workspace_bytes", "inv_attention_decode",
+           "inv_lmhead_workspace_bytes", "inv_lmhead_logprob_top2", "inv_embed", "inv_rope_kv_append",
+           "inv_swiglu", "inv_add", "inv_eval_numerics")
+
+
+def _check(status, what):
+    if status != 0:
+        raise InvError("%s: %s (%d)" % (what, LIB.inv_status_string(status).decode(), status))
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise InvError("tensors must be on the GPU (the library runs HIP kernels only)")
+
+
+def _bf16(t):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise InvError("BF16 operand expected (bfloat16 or its 16-bit pattern), got %s" % t.dtype)
+    return t
+
+
+def _f32(t):
+    if t.dtype != torch.float32:
+        raise InvError("float32 operand expected, got %s" % t.dtype)
+    return t
+
+
+def _row_ld(t):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise InvError("2-D row-major tensor with unit inner stride expected")
+    return t.stride(0)
+
+
+# --------------------------------------------------------------------------- host --
+
+def inv_status_string(status):
+    return LIB.inv_status_string(int(status)).decode()
+
+
+def inv_get_constants():
+    c = _Consts()
+    _check(LIB.inv_get_constants(ctypes.byref(c)), "inv_get_constants")
+    return dict(ks=c.ks, chunk=c.chunk, vocab_tile=c.vocab_tile, lanes=c.lanes,
+                float_consts=[c.float_consts[i] for i in range(c.n_float)])
+
+
+def inv_attention_decode_workspace_bytes(B, Tmax, Hq, D):
+    return int(LIB.inv_attention_decode_workspace_bytes(B, Tmax, Hq, D))
+
+
+def inv_lmhead_workspace_bytes(B, K, V):
+    return int(LIB.inv_lmhead_workspace_bytes(B, K, V))
+
+
+# ------------------------------------------------------------------------- device --
+
+def inv_fixed_order_gemm(X, W, R=None, out=None):
+    """Y = X . up(W)^T (+ R), X fp32 [M, K], W bf16 [N, K]."""
+    _dev(X, W, R, out)
+    _f32(X)
+    _bf16(W)
+    M, K = X.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _check(LIB.inv_fixed_order_gemm(_p(X), M, K, _row_ld(X), _p(W), N, _row_ld(W), _p(R),
+                                    _row_ld(R) if R is not None else 0, _p(out), _row_ld(out),
+                                    _stream(X)), "inv_fixed_order_gemm")
+    return out
+
+
+def inv_rmsnorm(X, gamma, eps=1e-5, out=None):
+    _dev(X, gamma, out)
+    _f32(X)
+    _bf16(gamma)
+    M, H = X.shape
+    if out is None:
+        out = torch.empty_like(X)
+    _check(LIB.inv_rmsnorm(_p(X), M, H, _row_ld(X), _p(gamma), float(eps), _p(out), _row_ld(out),
+                           _stream(X)), "inv_rmsnorm")
+    return out
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return INV_F32
+    _bf16(t)
+    return INV_BF16
+
+
+def _scale(D, scale):
+    if scale is None:
+        scale = float(torch.tensor(1.0, dtype=torch.float32) / torch.sqrt(torch.tensor(float(D),
+                                                                                    dtype=torch.float32)))
+    return float(scale)
+
+
+def inv_attention_prefill(Q, Kc, Vc, q_start=0, scale=None, out=None):
+    """Q [B, Tq, Hq, D]; Kc, Vc [B, Hkv, Tmax, D]; returns fp32 [B, Tq, Hq, D]."""
+    _dev(Q, Kc, Vc, out)
+    B, Tq, Hq, D = Q.shape
+    _, Hkv, Tmax, _ = Kc.shape
+    for t in (Q, Kc, Vc):
+        if not t.is_contiguous():
+            raise InvError("contiguous tensors expected")
+    if out is None:
+        out = torch.empty((B, Tq, Hq, D), dtype=torch.float32, device=Q.device)
+    _check(LIB.inv_attention_prefill(_dtype_code(Q), _p(Q), _p(Kc), _p(Vc), B, Tq, q_start, Tmax, Hq, Hkv,
+                                     D, _scale(D, scale), _p(out), _stream(Q)), "inv_attention_prefill")
+    return out
+
+
+def inv_attention_decode(Q, Kc, Vc, pos, scale=None, out=None, ws=None):
+    """Q [B, Hq, D]; caches [B, Hkv, Tmax, D]; pos int32 [B] (device)."""
+    _dev(Q, Kc, Vc, pos, out, ws)
+    B, Hq, D = Q.shape
+    _, Hkv, Tmax, _ = Kc.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=Q.device)
+    need = inv_attention_decode_workspace_bytes(B, Tmax, Hq, D)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    _check(LIB.inv_attention_decode(_dtype_code(Q), _p(Q), _p(Kc), _p(Vc), _p(pos), B, Tmax, Hq, Hkv, D,
+                                    _scale(D, scale), _p(out), _p(ws), ws.numel() * ws.element_size(),
+                                    _stream(Q)), "inv_attention_decode")
+    return out
+
+
+def inv_lmhead_logprob_top2(Hs, W, target, tau=0.1, ws=None, out=None):
+    """Selective-recompute LM head.  Returns dict of device tensors
+    (logprob, margin, top1, top2, recomputed)."""
+    _dev(Hs, W, target, ws)
+    _f32(Hs)
+    _bf16(W)
+    B, K = Hs.shape
+    V = W.shape[0]
+    dev = Hs.device
+    if out is None:
+        out = dict(logprob=torch.empty(B, dtype=torch.float32, device=dev),
+                   margin=torch.empty(B, dtype=torch.float32, device=dev),
+                   top1=torch.empty(B, dtype=torch.int32, device=dev),
+                   top2=torch.empty(B, dtype=torch.int32, device=dev),
+                   recomputed=torch.empty(B, dtype=torch.uint8, device=dev))
+    need = inv_lmhead_workspace_bytes(B, K, V)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(LIB.inv_lmhead_logprob_top2(_p(Hs), B, K, _row_ld(Hs), _p(W), V, _p(target), float(tau),
+                                       _p(out["logprob"]), _p(out["margin"]), _p(out["top1"]),
+                                       _p(out["top2"]), _p(out["recomputed"]), _p(ws),
+                                       ws.numel() * ws.element_size(), _stream(Hs)),
+           "inv_lmhead_logprob_top2")
+    return out
+
+
+def inv_embed(ids, table, out=None):
+    _dev(ids, table, out)
+    M = ids.numel()
+    V, H = table.shape
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float32, device=ids.device)
+    _check(LIB.inv_embed(_p(ids), M, _p(table), V, H, _p(out), _row_ld(out), _stream(ids)), "inv_embed")
+    return out
+
+
+def inv_rope_kv_append(QKV, Hq, Hkv, D, seq, pos, cos_t, sin_t, Qout, Kc, Vc):
+    _dev(QKV, seq, pos, cos_t, sin_t, Qout, Kc, Vc)
+    M = QKV.shape[0]
+    Bc, _, Tmax, _ = Kc.shape
+    _check(LIB.inv_rope_kv_append(_p(QKV), M, _row_ld(QKV), Hq, Hkv, D, _p(seq), _p(pos), _p(cos_t),
+                                  _p(sin_t), Tmax, Bc, _p(Qout), _p(Kc), _p(Vc), _stream(QKV)),
+           "inv_rope_kv_append")
+    return Qout
+
+
+def inv_swiglu(G, U, out=None):
+    _dev(G, U, out)
+    M, F = G.shape
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.float32, device=G.device)
+    _check(LIB.inv_swiglu(_p(G), _p(U), M, F, _row_ld(G), _row_ld(U), _p(out), _row_ld(out), _stream(G)),
+           "inv_swiglu")
+    return out
+
+
+def inv_add(A, Bm, out=None):
+    _dev(A, Bm, out)
+    M, N = A.shape
+    if out is None:
+        out = torch.empty_like(A)
+    _check(LIB.inv_add(_p(A), _p(Bm), M, N, _row_ld(A), _row_ld(Bm), _p(out), _row_ld(out), _stream(A)),
+           "inv_add")
+    return out
+
+
+def inv_eval_numerics(fn, x, out=None):
+    _dev(x, out)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(LIB.inv_eval_numerics(int(fn), _p(x), _p(out), x.numel(), _stream(x)), "inv_eval_numerics")
+    return out

@@ -1,0 +1,176 @@
+// abi.hip -- extern "C" entry points of libinvnum.so: argument validation, then launches.
+// Every check happens before anything is enqueued, so a rejected call leaves the stream
+// untouched.  Status codes and argument meaning are documented in include/invnum.h.
+#include "invnum.h"
+#include "kernels.h"
+#include "numerics.h"
+
+#include <string.h>
+
+using namespace invnum;
+
+namespace {
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int fin(hipError_t e) { return e == hipSuccess ? INV_OK : INV_ERR_LAUNCH; }
+constexpr int64_t I32MAX = 2147483647;
+
+}  // namespace
+
+extern "C" {
+
+const char* inv_status_string(int status) {
+    switch (status) {
+        case INV_OK: return "ok";
+        case INV_ERR_NULL: return "null pointer argument";
+        case INV_ERR_SHAPE: return "invalid or inconsistent shape";
+        case INV_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+        case INV_ERR_DTYPE: return "unknown dtype code";
+        case INV_ERR_WORKSPACE: return "workspace missing or too small";
+        case INV_ERR_UNSUPPORTED: return "unsupported shape";
+        case INV_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int inv_get_constants(inv_constants* out) {
+    if (!out) return INV_ERR_NULL;
+    memset(out, 0, sizeof(*out));
+    out->ks = KS;
+    out->chunk = CHUNK;
+    out->vocab_tile = TV;
+    out->lanes = LW;
+    const int n = (int)(sizeof(kFloatConsts) / sizeof(kFloatConsts[0]));
+    out->n_float = n;
+    for (int i = 0; i < n; ++i) out->float_consts[i] = kFloatConsts[i];
+    return INV_OK;
+}
+
+int inv_fixed_order_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* W,
+                         int64_t N, int64_t ldw, const float* R, int64_t ldr, float* Y, int64_t ldy,
+                         void* stream) {
+    if (!X || !W || !Y) return INV_ERR_NULL;
+    if (M < 1 || N < 1 || K < 8 || K % 8 != 0 || M > I32MAX || N > I32MAX || K > I32MAX)
+        return INV_ERR_SHAPE;
+    if (ldx < K || ldw < K || ldy < N || (R && ldr < N)) return INV_ERR_SHAPE;
+    if (!al16(X) || !al16(W) || ldx % 4 || ldw % 8) return INV_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(Y) & 3u) || (R && (reinterpret_cast<uintptr_t>(R) & 3u)))
+        return INV_ERR_ALIGN;
+    GemmArgs a{X, (int)M, (int)K, ldx, W, (int)N, ldw, R, ldr, Y, ldy, nullptr};
+    return fin(launch_gemm(a, S(stream)));
+}
+
+int inv_rmsnorm(const float* X, int64_t M, int64_t H, int64_t ldx, const uint16_t* gamma, float eps,
+                float* Y, int64_t ldy, void* stream) {
+    if (!X || !gamma || !Y) return INV_ERR_NULL;
+    if (M < 1 || H < 8 || H % 8 != 0 || ldx < H || ldy < H || M > I32MAX) return INV_ERR_SHAPE;
+    if (H > 16384) return INV_ERR_UNSUPPORTED;
+    if (!al16(X) || !al16(Y) || !al16(gamma) || ldx % 4 || ldy % 4) return INV_ERR_ALIGN;
+    return fin(launch_rmsnorm(X, (int)M, (int)H, ldx, gamma, eps, Y, ldy, S(stream)));
+}
+
+static int check_attn(int dtype, const void* Q, const void* Kc, const void* Vc, const float* O,
+                      int64_t B, int64_t Tq, int64_t q_start, int64_t Tmax, int64_t Hq, int64_t Hkv,
+                      int64_t D) {
+    if (!Q || !Kc || !Vc || !O) return INV_ERR_NULL;
+    if (dtype != INV_BF16 && dtype != INV_F32) return INV_ERR_DTYPE;
+    if (B < 1 || Tq < 1 || q_start < 0 || Tmax < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+        q_start + Tq > Tmax || B > 65535 || Hq > 65535 || Tmax > I32MAX / 2)
+        return INV_ERR_SHAPE;
+    if (D != 128 || Hq / Hkv > 16) return INV_ERR_UNSUPPORTED;
+    if (!al16(Q) || !al16(Kc) || !al16(Vc) || !al16(O)) return INV_ERR_ALIGN;
+    return INV_OK;
+}
+
+int inv_attention_prefill(int dtype, const void* Q, const void* Kc, const void* Vc, int64_t B,
+                          int64_t Tq, int64_t q_start, int64_t Tmax, int64_t Hq, int64_t Hkv,
+                          int64_t D, float scale, float* O, void* stream) {
+    int st = check_attn(dtype, Q, Kc, Vc, O, B, Tq, q_start, Tmax, Hq, Hkv, D);
+    if (st != INV_OK) return st;
+    AttnArgs a{dtype, Q, Kc, Vc, (int)B, (int)Tq, (int)q_start, (int)Tmax, (int)Hq, (int)Hkv, (int)D,
+               scale, O};
+    return fin(launch_attention_prefill(a, S(stream)));
+}
+
+size_t inv_attention_decode_workspace_bytes(int64_t B, int64_t Tmax, int64_t Hq, int64_t D) {
+    if (B < 1 || Tmax < 1 || Hq < 1 || D < 1) return 0;
+    const int64_t nch = (Tmax + CHUNK - 1) / CHUNK;
+    return sizeof(float) * (size_t)(B * Hq * nch * (D + 2));
+}
+
+int inv_attention_decode(int dtype, const void* Q, const void* Kc, const void* Vc, const int32_t* pos,
+                         int64_t B, int64_t Tmax, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                         float* O, void* ws, size_t ws_bytes, void* stream) {
+    if (!pos) return INV_ERR_NULL;
+    int st = check_attn(dtype, Q, Kc, Vc, O, B, 1, 0, Tmax, Hq, Hkv, D);
+    if (st != INV_OK) return st;
+    if (!ws || ws_bytes < inv_attention_decode_workspace_bytes(B, Tmax, Hq, D)) return INV_ERR_WORKSPACE;
+    if (!al16(ws)) return INV_ERR_ALIGN;
+    AttnArgs a{dtype, Q, Kc, Vc, (int)B, 1, 0, (int)Tmax, (int)Hq, (int)Hkv, (int)D, scale, O};
+    return fin(launch_attention_decode(a, pos, reinterpret_cast<float*>(ws), S(stream)));
+}
+
+size_t inv_lmhead_workspace_bytes(int64_t B, int64_t K, int64_t V) {
+    if (B < 1 || K < 1 || V < 1) return 0;
+    return lmhead_ws_bytes(B, K, V);
+}
+
+int inv_lmhead_logprob_top2(const float* Hs, int64_t B, int64_t K, int64_t ldh, const uint16_t* W,
+                            int64_t V, const int32_t* target, float tau, float* logprob, float* margin,
+                            int32_t* top1, int32_t* top2, uint8_t* recomputed, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (!Hs || !W || !target || !logprob || !margin || !top1 || !top2 || !recomputed)
+        return INV_ERR_NULL;
+    if (B < 1 || K < 8 || K % 8 != 0 || V < 2 || ldh < K || B > 65535 || K > I32MAX ||
+        V > (int64_t)1024 * TV)
+        return INV_ERR_SHAPE;
+    if (!ws || ws_bytes < inv_lmhead_workspace_bytes(B, K, V)) return INV_ERR_WORKSPACE;
+    if (!al16(Hs) || !al16(W) || !al16(ws) || ldh % 4) return INV_ERR_ALIGN;
+    LmheadArgs a{Hs, (int)B, (int)K, ldh, W, (int)V, target, tau, logprob, margin, top1, top2,
+                 recomputed, ws};
+    return fin(launch_lmhead(a, S(stream)));
+}
+
+int inv_embed(const int32_t* ids, int64_t M, const uint16_t* table, int64_t vocab, int64_t H, float* X,
+              int64_t ldx, void* stream) {
+    if (!ids || !table || !X) return INV_ERR_NULL;
+    if (M < 1 || vocab < 1 || H < 8 || H % 8 != 0 || ldx < H || M > I32MAX || vocab > I32MAX)
+        return INV_ERR_SHAPE;
+    if (!al16(table) || !al16(X) || ldx % 4) return INV_ERR_ALIGN;
+    return fin(launch_embed(ids, (int)M, table, (int)vocab, (int)H, X, ldx, S(stream)));
+}
+
+int inv_rope_kv_append(const float* QKV, int64_t M, int64_t ldqkv, int64_t Hq, int64_t Hkv, int64_t D,
+                       const int32_t* seq, const int32_t* pos, const float* cos_t, const float* sin_t,
+                       int64_t Tmax, int64_t Bcache, float* Qout, float* Kc, float* Vc, void* stream) {
+    if (!QKV || !seq || !pos || !cos_t || !sin_t || !Qout || !Kc || !Vc) return INV_ERR_NULL;
+    if (M < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 != 0 || Tmax < 1 || Bcache < 1 ||
+        ldqkv < (Hq + 2 * Hkv) * D || M > I32MAX || Tmax > I32MAX || Bcache > I32MAX)
+        return INV_ERR_SHAPE;
+    return fin(launch_rope_kv_append(QKV, (int)M, ldqkv, (int)Hq, (int)Hkv, (int)D, seq, pos, cos_t,
+                                     sin_t, (int)Tmax, (int)Bcache, Qout, Kc, Vc, S(stream)));
+}
+
+int inv_swiglu(const float* G, const float* U, int64_t M, int64_t F, int64_t ldg, int64_t ldu,
+               float* Hout, int64_t ldh, void* stream) {
+    if (!G || !U || !Hout) return INV_ERR_NULL;
+    if (M < 1 || F < 1 || ldg < F || ldu < F || ldh < F || M * F > ((int64_t)1 << 40)) return INV_ERR_SHAPE;
+    return fin(launch_swiglu(G, U, (int)M, (int)F, ldg, ldu, Hout, ldh, S(stream)));
+}
+
+int inv_add(const float* A, const float* Bm, int64_t M, int64_t N, int64_t lda, int64_t ldb, float* Y,
+            int64_t ldy, void* stream) {
+    if (!A || !Bm || !Y) return INV_ERR_NULL;
+    if (M < 1 || N < 1 || lda < N || ldb < N || ldy < N) return INV_ERR_SHAPE;
+    return fin(launch_add(A, Bm, (int)M, (int)N, lda, ldb, Y, ldy, S(stream)));
+}
+
+int inv_eval_numerics(int fn, const float* x, float* y, int64_t n, void* stream) {
+    if (!x || !y) return INV_ERR_NULL;
+    if (fn < 0 || fn > 2) return INV_ERR_DTYPE;
+    if (n < 1) return INV_ERR_SHAPE;
+    return fin(launch_eval_numerics(fn, x, y, n, S(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// elementwise.hip -- RMSNorm (one fixed-order reduction per row) and the decoder's
+// elementwise steps (embedding gather, RoPE + KV-cache append, SwiGLU, residual add).
+#include "numerics.h"
+#include "kernels.h"
+
+namespace invnum {
+
+namespace {
+
+// RMSNorm: one wavefront per row.  The row is staged in LDS with coalesced 16-byte loads;
+// lane s then runs the slice chain ss_s = fma(x_k, x_k, ss_s) over k in slice s (ascending);
+// lane 0 folds the slices in order and evaluates r = 1 / sqrt(ss / H + eps); finally every
+// lane writes y_k = (x_k * r) * up(g_k).
+__global__ __launch_bounds__(64) void rmsnorm_kernel(const float* __restrict__ X, int H, int64_t ldx,
+                                                     const uint16_t* __restrict__ g, float eps,
+                                                     float* __restrict__ Y, int64_t ldy) {
+    extern __shared__ float lds[];  // [H] row, then [S] slice partials, then r
+    const int S = (H + KS - 1) / KS;
+    float* xs = lds;
+    float* part = lds + H;
+    const int row = blockIdx.x;
+    const int lane = threadIdx.x;
+    const float* x = X + (int64_t)row * ldx;
+    for (int i = lane * 4; i < H; i += 256)
+        *reinterpret_cast<float4*>(xs + i) = *reinterpret_cast<const float4*>(x + i);
+    __syncthreads();
+    for (int s = lane; s < S; s += 64) {
+        const int k0 = s * KS, k1 = min(H, k0 + KS);
+        float c = 0.0f;
+        for (int k = k0; k < k1; k += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(xs + k);
+            c = __builtin_fmaf(v.x, v.x, c);
+            c = __builtin_fmaf(v.y, v.y, c);
+            c = __builtin_fmaf(v.z, v.z, c);
+            c = __builtin_fmaf(v.w, v.w, c);
+        }
+        part[s] = c;
+    }
+    __syncthreads();
+    if (lane == 0) {
+        float T = part[0];
+        for (int s = 1; s < S; ++s) T = T + part[s];
+        part[S] = 1.0f / __builtin_sqrtf((T / (float)H) + eps);
+    }
+    __syncthreads();
+    const float r = part[S];
+    float* y = Y + (int64_t)row * ldy;
+    for (int i = lane * 4; i < H; i += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(xs + i);
+        const uint2 gg = *reinterpret_cast<const uint2*>(g + i);
+        float4 o;
+        o.x = (v.x * r) * bf16_lo(gg.x);
+        o.y = (v.y * r) * bf16_hi(gg.x);
+        o.z = (v.z * r) * bf16_lo(gg.y);
+        o.w = (v.w * r) * bf16_hi(gg.y);
+        *reinterpret_cast<float4*>(y + i) = o;
+    }
+}
+
+__global__ void embed_kernel(const int32_t* __restrict__ ids, int M, const uint16_t* __restrict__ table,
+                             int vocab, int H, float* __restrict__ X, int64_t ldx) {
+    const int64_t n4 = (int64_t)M * (H / 4);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int m = (int)(i / (H / 4));
+        const int k = (int)(i % (H / 4)) * 4;
+        const int id = ids[m];
+        float4 o;
+        if (id >= 0 && id < vocab) {
+            const uint2 w = *reinterpret_cast<const uint2*>(table + (int64_t)id * H + k);
+            o = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+        } else {
+            const float nan = __builtin_nanf("");
+            o = make_float4(nan, nan, nan, nan);   // out-of-range id: poisoned row
+        }
+        *reinterpret_cast<float4*>(X + (int64_t)m * ldx + k) = o;
+    }
+}
+
+// One thread per (row, head, pair i < D/2).  Heads 0..Hq-1 are q heads (written to Qout),
+// Hq..Hq+Hkv-1 are k heads (rotated into Kc), the last Hkv are v heads (copied into Vc).
+__global__ void rope_kv_kernel(const float* __restrict__ QKV, int M, int64_t ldqkv, int Hq, int Hkv,
+                               int D, const int32_t* __restrict__ seq, const int32_t* __restrict__ pos,
+                               const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+                               int Tmax, int Bcache, float* __restrict__ Qout, float* __restrict__ Kc,
+                               float* __restrict__ Vc) {
+    const int half = D / 2;
+    const int nh = Hq + 2 * Hkv;
+    const int64_t total = (int64_t)M * nh * half;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int i = (int)(t % half);
+        const int h = (int)((t / half) % nh);
+        const int m = (int)(t / ((int64_t)half * nh));
+        const float* x = QKV + (int64_t)m * ldqkv + (int64_t)h * D;
+        const int p = pos[m];
+        const int sq = seq[m];
+        if (p < 0 || p >= Tmax || sq < 0 || sq >= Bcache) continue;   // row outside the cache
+        if (h < Hq + Hkv) {
+            const float c = cos_t[(int64_t)p * half + i];
+            const float s = sin_t[(int64_t)p * half + i];
+            const float a = x[i], b = x[i + half];
+            const float y0 = (a * c) - (b * s);
+            const float y1 = (a * s) + (b * c);
+            if (h < Hq) {
+                float* q = Qout + ((int64_t)m * Hq + h) * D;
+                q[i] = y0;
+                q[i + half] = y1;
+            } else {
+                const int gk = h - Hq;
+                float* k = Kc + (((int64_t)sq * Hkv + gk) * Tmax + p) * D;
+                k[i] = y0;
+                k[i + half] = y1;
+            }
+        } else {
+            const int gv = h - Hq - Hkv;
+            float* v = Vc + (((int64_t)sq * Hkv + gv) * Tmax + p) * D;
+            v[i] = x[i];
+            v[i + half] = x[i + half];
+        }
+    }
+}
+
+__global__ void swiglu_kernel(const float* __restrict__ G, const float* __restrict__ U, int M, int F,
+                              int64_t ldg, int64_t ldu, float* __restrict__ Hout, int64_t ldh) {
+    const int64_t total = (int64_t)M * F;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int m = (int)(t / F), f = (int)(t % F);
+        const float g = G[(int64_t)m * ldg + f];
+        const float sg = g / (1.0f + exp_f(-g));
+        Hout[(int64_t)m * ldh + f] = sg * U[(int64_t)m * ldu + f];
+    }
+}
+
+__global__ void add_kernel(const float* __restrict__ A, const float* __restrict__ B, int M, int N,
+                           int64_t lda, int64_t ldb, float* __restrict__ Y, int64_t ldy) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int m = (int)(t / N), n = (int)(t % N);
+        Y[(int64_t)m * ldy + n] = A[(int64_t)m * lda + n] + B[(int64_t)m * ldb + n];
+    }
+}
+
+__global__ void eval_numerics_kernel(int fn, const float* __restrict__ x, float* __restrict__ y,
+                                     int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const float v = x[i];
+        y[i] = fn == 0 ? exp_f(v) : fn == 1 ? log_f(v) : bf16_up(bf16_rne(v));
+    }
+}
+
+inline int grid_for(int64_t work, int block) {
+    int64_t g = (work + block - 1) / block;
+    if (g > 65536) g = 65536;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const float* X, int M, int H, int64_t ldx, const uint16_t* g, float eps,
+                          float* Y, int64_t ldy, hipStream_t st) {
+    const int S = (H + KS - 1) / KS;
+    const size_t lds = sizeof(float) * ((size_t)H + S + 1);
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(64), lds, st, X, H, ldx, g, eps, Y, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed(const int32_t* ids, int M, const uint16_t* table, int vocab, int H, float* X,
+                        int64_t ldx, hipStream_t st) {
+    hipLaunchKernelGGL(embed_kernel, dim3(grid_for((int64_t)M * H / 4, 256)), dim3(256), 0, st,
+                       ids, M, table, vocab, H, X, ldx);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_kv_append(const float* QKV, int M, int64_t ldqkv, int Hq, int Hkv, int D,
+                                 const int32_t* seq, const int32_t* pos, const float* cos_t,
+                                 const float* sin_t, int Tmax, int Bcache, float* Qout, float* Kc,
+                                 float* Vc, hipStream_t st) {
+    const int64_t work = (int64_t)M * (Hq + 2 * Hkv) * (D / 2);
+    hipLaunchKernelGGL(rope_kv_kernel, dim3(grid_for(work, 256)), dim3(256), 0, st, QKV, M, ldqkv,
+                       Hq, Hkv, D, seq, pos, cos_t, sin_t, Tmax, Bcache, Qout, Kc, Vc);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const float* G, const float* U, int M, int F, int64_t ldg, int64_t ldu,
+                         float* Hout, int64_t ldh, hipStream_t st) {
+    hipLaunchKernelGGL(swiglu_kernel, dim3(grid_for((int64_t)M * F, 256)), dim3(256), 0, st, G, U,
+                       M, F, ldg, ldu, Hout, ldh);
+    return hipGetLastError();
+}
+
+hipError_t launch_add(const float* A, const float* B, int M, int N, int64_t lda, int64_t ldb,
+                      float* Y, int64_t ldy, hipStream_t st) {
+    hipLaunchKernelGGL(add_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, st, A, B, M,
+                       N, lda, ldb, Y, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_eval_numerics(int fn, const float* x, float* y, int64_t n, hipStream_t st) {
+    hipLaunchKernelGGL(eval_numerics_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, fn, x, y, n);
+    return hipGetLastError();
+}
+
+}  // namespace invnum

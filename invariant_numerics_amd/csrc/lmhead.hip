@@ -1,0 +1,219 @@
+// lmhead.hip -- LM head: logits, log-softmax at the target, top-2 and margin, with
+// selective FP32 recompute of the rows whose top-two logit margin is below tau.
+//
+// Sequence on one stream, no host synchronisation:
+//   1. a_P = up(bf(h))                          (BF16 operands of the primary pass)
+//   2. z = fixed-order GEMM(a_P, W)             (FP32 sums, dot_KS order)
+//   3. row reduce (one workgroup per row): top-2, M = z_top1, S, lp, margin; outputs with
+//      recomputed = (margin < tau)
+//   4. compaction: flagged rows' indices (ascending) and a device-side count; their h
+//      rows are gathered into a dense buffer
+//   5. z = fixed-order GEMM(h_F, W) on the first `count` rows (count read on the device)
+//   6. row reduce of those rows; results overwrite the flagged rows' outputs.
+//
+// Row reduce order (identical for both passes):
+//   top1 = lowest index of the maximum; top2 = lowest index != top1 of the maximum of the
+//   rest (fp compare, so -0 == +0) -- a total order, so any reduction tree finds them;
+//   S: tile u = entries [1024u, 1024u + 1024); lane l sums exp_f(z_v - M) for
+//   v = 1024u + 64j + l, j = 0..15 ascending (v < V), from +0; lanes combine pairwise
+//   a_l = a_l + a_{l+w}, w = 1, 2, ..., 32; S_u = a_0; S = S_0, S = S + S_u ascending;
+//   lp = (z_target - M) - log_f(S).
+#include "numerics.h"
+#include "kernels.h"
+
+namespace invnum {
+
+namespace {
+
+constexpr int RED_THREADS = 256;
+constexpr int MAX_TILES = 1024;  // V <= 2^20
+
+struct Top2 {
+    float v1; int i1; float v2; int i2;
+};
+
+// (value desc, index asc): does (va, ia) come before (vb, ib)?
+__device__ __forceinline__ bool before(float va, int ia, float vb, int ib) {
+    return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void top2_push(Top2& t, float v, int i) {
+    if (before(v, i, t.v1, t.i1)) { t.v2 = t.v1; t.i2 = t.i1; t.v1 = v; t.i1 = i; }
+    else if (before(v, i, t.v2, t.i2)) { t.v2 = v; t.i2 = i; }
+}
+
+__device__ __forceinline__ void top2_merge(Top2& t, const Top2& o) {
+    top2_push(t, o.v1, o.i1);
+    top2_push(t, o.v2, o.i2);
+}
+
+// mode 0: P pass over rows 0..B-1 (output row = row); mode 1: F pass over the first
+// *count rows of the compacted list (output row = idx[row]).
+__global__ __launch_bounds__(RED_THREADS) void lmhead_reduce_kernel(
+    const float* __restrict__ z, int V, const int32_t* __restrict__ target, float tau, int mode,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+    float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
+    int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
+    __shared__ float tileS[MAX_TILES];
+    __shared__ Top2 wtop[RED_THREADS / 64];
+    const int row = blockIdx.x;
+    if (mode == 1 && row >= *count) return;
+    const int orow = mode == 1 ? idx[row] : row;
+    const float* zr = z + (int64_t)row * V;
+    const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+
+    // ---- top-2
+    Top2 t = {-__builtin_inff(), 0x7fffffff, -__builtin_inff(), 0x7fffffff};
+    for (int v = tid; v < V; v += RED_THREADS) top2_push(t, zr[v], v);
+    for (int off = 32; off >= 1; off >>= 1) {
+        Top2 o;
+        o.v1 = __shfl_xor(t.v1, off); o.i1 = __shfl_xor(t.i1, off);
+        o.v2 = __shfl_xor(t.v2, off); o.i2 = __shfl_xor(t.i2, off);
+        top2_merge(t, o);
+    }
+    if (lane == 0) wtop[w] = t;
+    __syncthreads();
+    t = wtop[0];
+    for (int k = 1; k < RED_THREADS / 64; ++k) top2_merge(t, wtop[k]);
+    const float M = zr[t.i1];
+
+    // ---- softmax denominator: wavefront w handles tiles w, w + 4, ...
+    const int ntiles = (V + TV - 1) / TV;
+    for (int u = w; u < ntiles; u += RED_THREADS / 64) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < TV / LW; ++j) {
+            const int v = u * TV + j * LW + lane;
+            if (v < V) acc = acc + exp_f(zr[v] - M);
+        }
+        // pairwise lane tree: a_l + a_{l+w} for w = 1, 2, 4, ..., 32
+#pragma unroll
+        for (int s = 1; s < LW; s <<= 1) acc = acc + __shfl_down(acc, s);
+        if (lane == 0) tileS[u] = acc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float S = tileS[0];
+        for (int u = 1; u < ntiles; ++u) S = S + tileS[u];
+        const int tg = target[orow];
+        const float lp = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
+        const float mg = M - zr[t.i2];
+        logprob[orow] = lp;
+        margin[orow] = mg;
+        top1[orow] = t.i1;
+        top2[orow] = t.i2;
+        recomputed[orow] = (uint8_t)(mode == 1 ? 1 : (mg < tau ? 1 : 0));
+    }
+}
+
+// a_P[b, k] = up(bf(h[b, k]))
+__global__ void round_bf16_kernel(const float* __restrict__ H, int B, int K, int64_t ldh,
+                                  float* __restrict__ A) {
+    const int64_t n4 = (int64_t)B * (K / 4);
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int b = (int)(i / (K / 4)), k = (int)(i % (K / 4)) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(H + (int64_t)b * ldh + k);
+        float4 o;
+        o.x = bf16_up(bf16_rne(v.x)); o.y = bf16_up(bf16_rne(v.y));
+        o.z = bf16_up(bf16_rne(v.z)); o.w = bf16_up(bf16_rne(v.w));
+        *reinterpret_cast<float4*>(A + (int64_t)b * K + k) = o;
+    }
+}
+
+// Single workgroup: ascending list of rows flagged by the P pass, and their count.
+// Every thread keeps its own copy of the running base; the per-wavefront counts are
+// rewritten by each wavefront in every round, between two barriers.
+__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ flag, int B,
+                                                       int32_t* __restrict__ idx,
+                                                       int32_t* __restrict__ count) {
+    __shared__ int32_t wsum[16];
+    const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+    int base = 0;
+    for (int b0 = 0; b0 < B; b0 += 1024) {
+        const int b = b0 + tid;
+        const int f = (b < B && flag[b]) ? 1 : 0;
+        const unsigned long long bal = __ballot(f);
+        const int before_me = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wsum[w] = __popcll(bal);
+        __syncthreads();
+        int off = base, tot = 0;
+        for (int k = 0; k < 16; ++k) {
+            if (k < w) off += wsum[k];
+            tot += wsum[k];
+        }
+        if (f) idx[off + before_me] = b;
+        base += tot;
+        __syncthreads();
+    }
+    if (tid == 0) *count = base;
+}
+
+// Gather the flagged rows of h (fp32) into a dense [count, K] buffer.
+__global__ void gather_rows_kernel(const float* __restrict__ H, int K, int64_t ldh,
+                                   const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+                                   float* __restrict__ A) {
+    const int r = blockIdx.x;
+    if (r >= *count) return;
+    const float* src = H + (int64_t)idx[r] * ldh;
+    float* dst = A + (int64_t)r * K;
+    for (int k = threadIdx.x * 4; k < K; k += blockDim.x * 4)
+        *reinterpret_cast<float4*>(dst + k) = *reinterpret_cast<const float4*>(src + k);
+}
+
+inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t a, z, idx, count, total;
+};
+WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
+    WsLayout L;
+    size_t off = 0;
+    L.a = off; off = align_up(off + sizeof(float) * (size_t)B * K);
+    L.z = off; off = align_up(off + sizeof(float) * (size_t)B * V);
+    L.idx = off; off = align_up(off + sizeof(int32_t) * (size_t)B);
+    L.count = off; off = align_up(off + sizeof(int32_t));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+size_t lmhead_ws_bytes(int64_t B, int64_t K, int64_t V) { return ws_layout(B, K, V).total; }
+
+hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
+    const WsLayout L = ws_layout(a.B, a.K, a.V);
+    char* ws = reinterpret_cast<char*>(a.ws);
+    float* A = reinterpret_cast<float*>(ws + L.a);
+    float* Z = reinterpret_cast<float*>(ws + L.z);
+    int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+    hipError_t e;
+
+    int64_t n4 = (int64_t)a.B * (a.K / 4);
+    int g = (int)((n4 + 255) / 256);
+    if (g > 65536) g = 65536;
+    hipLaunchKernelGGL(round_bf16_kernel, dim3(g), dim3(256), 0, st, a.Hs, a.B, a.K, a.ldh, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    GemmArgs ga{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, nullptr};
+    if ((e = launch_gemm(ga, st, 1)) != hipSuccess) return e;
+
+    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(a.B), dim3(RED_THREADS), 0, st, Z, a.V, a.target,
+                       a.tau, 0, nullptr, nullptr, a.logprob, a.margin, a.top1, a.top2, a.recomputed);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, a.recomputed, a.B, idx, count);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(a.B), dim3(256), 0, st, a.Hs, a.K, a.ldh, idx, count, A);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    GemmArgs gf{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, count};
+    if ((e = launch_gemm(gf, st, 1)) != hipSuccess) return e;
+
+    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(a.B), dim3(RED_THREADS), 0, st, Z, a.V, a.target,
+                       a.tau, 1, idx, count, a.logprob, a.margin, a.top1, a.top2, a.recomputed);
+    return hipGetLastError();
+}
+
+}  // namespace invnum

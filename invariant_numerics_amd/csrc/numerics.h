@@ -1,0 +1,124 @@
+// numerics.h -- device scalar primitives of the fixed-order path (gfx950).
+//
+// Every function here is written so that it produces the same binary32 bits as the
+// definition stated in its comment: IEEE operations with round-to-nearest-even, explicit
+// fused multiply-adds where a single rounding is meant, and nothing else.  The library is
+// compiled with -ffp-contract=off (no implicit fma), without fast-math, with subnormals
+// kept and with correctly rounded division and square root.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace invnum {
+
+// Pinned constants of the reduction order.
+constexpr int KS = 256;       // K-slice width of every dot product
+constexpr int CHUNK = 256;    // attention KV chunk (absolute key positions)
+constexpr int TV = 1024;      // vocabulary tile of the softmax denominator
+constexpr int LW = 64;        // lanes per vocabulary tile (one wavefront)
+
+// exp_f constants: log2(e); ln 2 as a 24-bit head and rounded tail (Cody & Waite 1980);
+// range limits ln(2^-126) and ln(2^128); Taylor coefficients 1/k!.
+#define INV_LOG2E 0x1.715476p+0f
+#define INV_LN2_HI 0x1.62e430p-1f
+#define INV_LN2_LO -0x1.05c610p-29f
+#define INV_EXP_LO -0x1.5d58a0p+6f
+#define INV_EXP_HI 0x1.62e430p+6f
+#define INV_IF0 1.0f
+#define INV_IF1 1.0f
+#define INV_IF2 0x1.000000p-1f
+#define INV_IF3 0x1.555556p-3f
+#define INV_IF4 0x1.555556p-5f
+#define INV_IF5 0x1.111112p-7f
+#define INV_IF6 0x1.6c16c2p-10f
+#define INV_IF7 0x1.a01a02p-13f
+// log_f constants: ln 2 head with 16 significant bits (e * head exact) and its tail;
+// atanh-series coefficients 2/(2k+1), k = 1..5 (Abramowitz & Stegun 4.1.27).
+#define INV_LN2_HI16 0x1.62e400p-1f
+#define INV_LN2_LO16 0x1.7f7d1cp-20f
+#define INV_AT1 0x1.555556p-1f
+#define INV_AT2 0x1.99999ap-2f
+#define INV_AT3 0x1.24924ap-2f
+#define INV_AT4 0x1.c71c72p-3f
+#define INV_AT5 0x1.745d18p-3f
+
+__device__ __forceinline__ float bits2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f2bits(float f) { return __float_as_uint(f); }
+
+// up(): BF16 bits -> FP32, exact.
+__device__ __forceinline__ float bf16_up(uint32_t b16) { return __uint_as_float(b16 << 16); }
+// Low / high BF16 halves of a 32-bit word holding two consecutive elements.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// bf(): FP32 -> BF16 bits, round to nearest even on the dropped 16 bits; NaN stays quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// exp_f(x): n = rint(x log2e); r = fma(-n, ln2_hi, x); r = fma(-n, ln2_lo, r);
+// p = Taylor degree 7 by fma-Horner from the top; result p * 2^n (n = 128 via p*2).
+// x < ln(2^-126) -> +0, x > ln(2^128) -> +inf.
+__device__ __forceinline__ float exp_f(float x) {
+    if (x != x) return x + x;
+    if (x > INV_EXP_HI) return __builtin_inff();
+    if (x < INV_EXP_LO) return 0.0f;
+    float t = x * INV_LOG2E;
+    float n = __builtin_rintf(t);
+    float r = __builtin_fmaf(-n, INV_LN2_HI, x);
+    r = __builtin_fmaf(-n, INV_LN2_LO, r);
+    float p = INV_IF7;
+    p = __builtin_fmaf(p, r, INV_IF6);
+    p = __builtin_fmaf(p, r, INV_IF5);
+    p = __builtin_fmaf(p, r, INV_IF4);
+    p = __builtin_fmaf(p, r, INV_IF3);
+    p = __builtin_fmaf(p, r, INV_IF2);
+    p = __builtin_fmaf(p, r, INV_IF1);
+    p = __builtin_fmaf(p, r, INV_IF0);
+    int ni = (int)n;
+    if (ni > 127) { p = p * 2.0f; ni -= 1; }
+    return p * __uint_as_float((uint32_t)(ni + 127) << 23);
+}
+
+// log_f(x), x > 0: x = 2^e m, m in (sqrt(1/2), sqrt(2)]; f = m - 1; s = f / (2 + f);
+// z = s^2; R = z (2/3 + z (2/5 + z (2/7 + z (2/9 + z 2/11)))); log m = f - s (f - R);
+// result = e ln2_hi16 + (f + fma(e, ln2_lo16, -s (f - R))).
+__device__ __forceinline__ float log_f(float x) {
+    if (x != x) return x + x;
+    if (x < 0.0f) return __builtin_nanf("");
+    if (x == 0.0f) return -__builtin_inff();
+    if (x == __builtin_inff()) return x;
+    int e = 0;
+    uint32_t u = __float_as_uint(x);
+    if (u < 0x00800000u) { x = x * 16777216.0f; u = __float_as_uint(x); e = -24; }
+    e += (int)(u >> 23) - 127;
+    uint32_t frac = u & 0x007fffffu;
+    float m = __uint_as_float(frac | 0x3f800000u);
+    if (frac > 0x003504f3u) { m = m * 0.5f; e += 1; }
+    float f = m - 1.0f;
+    float s = f / (2.0f + f);
+    float z = s * s;
+    float R = INV_AT5;
+    R = __builtin_fmaf(R, z, INV_AT4);
+    R = __builtin_fmaf(R, z, INV_AT3);
+    R = __builtin_fmaf(R, z, INV_AT2);
+    R = __builtin_fmaf(R, z, INV_AT1);
+    R = R * z;
+    float u2 = s * (f - R);
+    float fe = (float)e;
+    float t = __builtin_fmaf(fe, INV_LN2_LO16, -u2);
+    return fe * INV_LN2_HI16 + (f + t);
+}
+
+// Host-side copy of the constant table (same order as the ABI's inv_constants).
+static const float kFloatConsts[] = {
+    INV_LOG2E, INV_LN2_HI, INV_LN2_LO, INV_EXP_LO, INV_EXP_HI,
+    INV_IF0, INV_IF1, INV_IF2, INV_IF3, INV_IF4, INV_IF5, INV_IF6, INV_IF7,
+    INV_LN2_HI16, INV_LN2_LO16, INV_AT1, INV_AT2, INV_AT3, INV_AT4, INV_AT5};
+
+// Status codes mirrored from the public header (kept in one place there).
+}  // namespace invnum

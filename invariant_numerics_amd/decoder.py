@@ -1,0 +1,135 @@
+"""Llama-shaped decoder assembled from the library's C-ABI calls (LayerCast setting:
+BF16 weights, FP32 activations and KV cache, every reduction in the fixed order).
+
+Two ways to score a batch of sequences that must give the same bits at every position:
+  * ``prefill``: token blocks of all sequences at once (rows ordered (sequence, position)),
+    every layer through fixed_order_gemm / rmsnorm / rope_kv_append / attention_prefill;
+  * ``decode_step``: one token per sequence (M = batch), attention_decode over the cache.
+Every op is row-independent and chunk boundaries are absolute key positions, so token
+blocking, batch size and prefill-vs-decode do not change a row's bits.
+
+Weight layouts (nn.Linear): wqkv [(Hq+2Hkv)D, H] = q rows | k rows | v rows; wo [H, Hq D];
+w13 [2F, H] = gate rows | up rows; w2 [H, F]; whead [V, H]; emb [V, H]; RoPE tables
+cos/sin [Tmax, D/2] fp32.
+"""
+import numpy as np
+import torch
+
+from . import binding as inv
+
+
+def _to_dev_bf16(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+class Decoder:
+    def __init__(self, model, device="cuda", batch=1, tmax=None, tau=0.1, eps=1e-5):
+        cfg = model["cfg"]
+        self.cfg = cfg
+        self.H, self.Hq, self.Hkv, self.D = cfg["hidden"], cfg["hq"], cfg["hkv"], cfg["d"]
+        self.F, self.V, self.L = cfg["ffn"], cfg["vocab"], cfg["layers"]
+        self.dev = torch.device(device)
+        self.tau = float(np.float32(tau))
+        self.eps = float(np.float32(eps))
+        self.emb = _to_dev_bf16(model["emb"], self.dev)
+        self.whead = _to_dev_bf16(model["whead"], self.dev)
+        self.gf = _to_dev_bf16(model["gf"], self.dev)
+        self.layers = [{k: _to_dev_bf16(v, self.dev) for k, v in layer.items()} for layer in model["layers"]]
+        self.cos = torch.from_numpy(np.ascontiguousarray(model["cos"])).to(self.dev)
+        self.sin = torch.from_numpy(np.ascontiguousarray(model["sin"])).to(self.dev)
+        self.tmax = int(tmax if tmax is not None else self.cos.shape[0])
+        assert self.cos.shape[0] >= self.tmax
+        self.batch = int(batch)
+        self.kc = [torch.zeros((batch, self.Hkv, self.tmax, self.D), dtype=torch.float32, device=self.dev)
+                   for _ in range(self.L)]
+        self.vc = [torch.zeros_like(k) for k in self.kc]
+        # optional measurement hook: when a list, each body projection appends
+        # (start event, end event, algorithmic flops) recorded on its launch stream
+        self.gemm_events = None
+
+    def _gemm(self, X, W, R=None, out=None):
+        ev = self.gemm_events
+        if ev is None:
+            return inv.inv_fixed_order_gemm(X, W, R=R, out=out)
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        y = inv.inv_fixed_order_gemm(X, W, R=R, out=out)
+        e.record()
+        ev.append((s, e, 2.0 * X.shape[0] * W.shape[0] * X.shape[1]))
+        return y
+
+    # one pass of the decoder body over rows (seq[m], pos[m]); attention via `attend`
+    def _body(self, ids, seq, pos, attend):
+        H, Hq, Hkv, D, F = self.H, self.Hq, self.Hkv, self.D, self.F
+        M = ids.numel()
+        x = inv.inv_embed(ids, self.emb)
+        n = torch.empty_like(x)
+        q = torch.empty((M, Hq, D), dtype=torch.float32, device=self.dev)
+        for li, w in enumerate(self.layers):
+            inv.inv_rmsnorm(x, w["g1"], self.eps, out=n)
+            qkv = self._gemm(n, w["wqkv"])
+            inv.inv_rope_kv_append(qkv, Hq, Hkv, D, seq, pos, self.cos, self.sin, q, self.kc[li], self.vc[li])
+            del qkv
+            att = attend(q, li)
+            self._gemm(att.view(M, Hq * D), w["wo"], R=x, out=x)
+            del att
+            inv.inv_rmsnorm(x, w["g2"], self.eps, out=n)
+            gu = self._gemm(n, w["w13"])
+            h = inv.inv_swiglu(gu[:, :F], gu[:, F:])
+            del gu
+            self._gemm(h, w["w2"], R=x, out=x)
+            del h
+        inv.inv_rmsnorm(x, self.gf, self.eps, out=n)
+        return n
+
+    def prefill(self, tokens, block=2048, lm_rows=None):
+        """Score tokens [B, T] (device int32, B <= batch): returns dict of [B, T-1] device
+        tensors (logprob, margin, top1, top2, recomputed) for positions 0..T-2."""
+        B, T = tokens.shape
+        assert B <= self.batch and T <= self.tmax
+        out = {k: torch.empty((B, T - 1), dtype=dt, device=self.dev) for k, dt in
+               (("logprob", torch.float32), ("margin", torch.float32), ("top1", torch.int32),
+                ("top2", torch.int32), ("recomputed", torch.uint8))}
+        tgt_all = torch.zeros((B, T), dtype=torch.int32, device=self.dev)
+        tgt_all[:, :T - 1] = tokens[:, 1:]
+        for q0 in range(0, T, block):
+            q1 = min(T, q0 + block)
+            nb = q1 - q0
+            ids = tokens[:, q0:q1].contiguous().view(-1)
+            seq = torch.arange(B, dtype=torch.int32, device=self.dev).repeat_interleave(nb)
+            pos = torch.arange(q0, q1, dtype=torch.int32, device=self.dev).repeat(B)
+
+            def attend(q, li, q0=q0, nb=nb):
+                return inv.inv_attention_prefill(q.view(B, nb, self.Hq, self.D), self.kc[li][:B],
+                                                 self.vc[li][:B], q_start=q0)
+
+            hn = self._body(ids, seq, pos, attend)
+            tg = tgt_all[:, q0:q1].contiguous().view(-1)
+            r = self._lmhead(hn, tg, lm_rows)
+            nscore = min(q1, T - 1) - q0
+            if nscore > 0:
+                for k in out:
+                    out[k][:, q0:q0 + nscore] = r[k].view(B, nb)[:, :nscore]
+        return out
+
+    def _lmhead(self, hn, tg, lm_rows=None):
+        M = hn.shape[0]
+        step = M if not lm_rows else int(lm_rows)
+        if step >= M:
+            return inv.inv_lmhead_logprob_top2(hn, self.whead, tg, self.tau)
+        parts = [inv.inv_lmhead_logprob_top2(hn[s:s + step], self.whead, tg[s:s + step], self.tau)
+                 for s in range(0, M, step)]
+        return {k: torch.cat([p[k] for p in parts]) for k in parts[0]}
+
+    def decode_step(self, tok, pos, target):
+        """One token per sequence: tok, pos, target int32 [B] (device).  Writes the cache at
+        pos and returns the LM-head outputs for those positions (dict of [B] tensors)."""
+        B = tok.numel()
+        seq = torch.arange(B, dtype=torch.int32, device=self.dev)
+
+        def attend(q, li):
+            return inv.inv_attention_decode(q, self.kc[li][:B], self.vc[li][:B], pos)
+
+        hn = self._body(tok, seq, pos, attend)
+        return inv.inv_lmhead_logprob_top2(hn, self.whead, target, self.tau)

@@ -132,6 +132,8 @@ def c4_inputs(rows=256, hidden=4096, vocab=128256, stress=False):
 
 C5 = dict(hidden=4096, hq=32, hkv=8, d=128, ffn=14336, vocab=128256, layers=4, theta=500000.0)
 TINY = dict(hidden=64, hq=4, hkv=2, d=16, ffn=160, vocab=512, layers=2, theta=10000.0)
+# smallest shape the GPU path accepts (head dim 128), for fast whole-decoder parity runs
+SMALL = dict(hidden=256, hq=4, hkv=2, d=128, ffn=512, vocab=1000, layers=2, theta=500000.0)
 
 
 def decoder_model(cfg, tmax, seed_base=None, gamma_std=0.0):

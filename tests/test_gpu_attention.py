@@ -1,0 +1,90 @@
+"""attention_prefill / attention_decode on the GPU: bitwise equal to the oracle, and the
+prefill row equals the token-by-token decode row (fixed 256-key chunks, one merge order)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import assert_bitwise, bf16, f32, host, i32, requires_gpu, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+D = 128
+
+
+def inv():
+    import invariant_numerics_amd as m
+    return m
+
+
+def rand_qkv(seed, B, T, Hq, Hkv, bf=False):
+    q = synth.normal(seed, (B, T, Hq, D))
+    k = synth.normal(seed + 1, (B, Hkv, T, D))
+    v = synth.normal(seed + 2, (B, Hkv, T, D))
+    if bf:
+        return synth.to_bf16_bits(q), synth.to_bf16_bits(k), synth.to_bf16_bits(v)
+    return q, k, v
+
+
+def dev(a):
+    return bf16(a) if a.dtype == np.uint16 else f32(a)
+
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,bf", [(1, 1, 1, 1, False), (1, 70, 2, 2, False), (2, 300, 4, 2, False),
+                                           (1, 530, 4, 1, True), (1, 777, 8, 2, False)])
+def test_prefill_matches_oracle(orc, B, T, Hq, Hkv, bf):
+    say("attn prefill", B, T, Hq, Hkv, bf)
+    q, k, v = rand_qkv(8000 + T, B, T, Hq, Hkv, bf)
+    O = host(inv().inv_attention_prefill(dev(q), dev(k), dev(v)))
+    assert_bitwise(O, orc.attention(q, k, v), "prefill")
+
+
+def test_prefill_query_blocks_and_offsets(orc):
+    """Queries at an offset (q_start, not a multiple of 64) give the same rows."""
+    say("attn q_start")
+    q, k, v = rand_qkv(8100, 2, 600, 4, 2)
+    full = host(inv().inv_attention_prefill(f32(q), f32(k), f32(v)))
+    for s in (1, 200, 255, 256, 300, 599):
+        part = host(inv().inv_attention_prefill(f32(q[:, s:].copy()), f32(k), f32(v), q_start=s))
+        assert_bitwise(part, full[:, s:], "q_start=%d" % s)
+
+
+def test_decode_matches_prefill_rows_ragged_positions(orc):
+    say("attn decode ragged")
+    B, T, Hq, Hkv = 3, 700, 8, 2
+    q, k, v = rand_qkv(8200, B, T, Hq, Hkv)
+    full = host(inv().inv_attention_prefill(f32(q), f32(k), f32(v)))
+    kd, vd = f32(k), f32(v)
+    for posv in ([0, 255, 256], [511, 512, 699], [100, 600, 300]):
+        pos = np.array(posv, np.int32)
+        qd = np.stack([q[b, pos[b]] for b in range(B)])
+        O = host(inv().inv_attention_decode(f32(qd), kd, vd, i32(pos)))
+        want = np.stack([full[b, pos[b]] for b in range(B)])
+        assert_bitwise(O, want, "decode pos=%s" % posv)
+
+
+def test_c2_full_prefill_equals_token_by_token_decode_and_oracle(orc):
+    """8 heads x d128, 2048 tokens, bf16 Q/K/V, causal, chunk 256: prefill output equals
+    2048 single-token decode calls bitwise, and the oracle at every row."""
+    say("attn C2 full")
+    d = synth.c2_inputs()
+    q, k, v = d["q"], d["k"], d["v"]
+    qd, kd, vd = bf16(q), bf16(k), bf16(v)
+    pre = host(inv().inv_attention_prefill(qd, kd, vd))
+    import torch
+    outs = torch.empty((2048, 8, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(inv().inv_attention_decode_workspace_bytes(1, 2048, 8, D), dtype=torch.uint8, device="cuda")
+    posd = torch.arange(2048, dtype=torch.int32, device="cuda")
+    for t in range(2048):
+        inv().inv_attention_decode(qd[:, t], kd, vd, posd[t:t + 1], out=outs[t:t + 1], ws=ws)
+    dec = host(outs)
+    assert_bitwise(dec, pre[0], "prefill vs decode")
+    say("attn C2 oracle")
+    assert_bitwise(pre, orc.attention(q, k, v), "oracle")
+
+
+def test_unit_values_exactly_one():
+    say("attn V=1")
+    q, k, _ = rand_qkv(8300, 1, 600, 2, 2)
+    v = np.ones_like(k)
+    O = host(inv().inv_attention_prefill(f32(q), f32(k), f32(v)))
+    assert np.all(O == 1.0)

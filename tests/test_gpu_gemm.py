@@ -1,0 +1,96 @@
+"""fixed_order_gemm on the GPU: bitwise equal to the oracle, and rows bitwise identical
+whatever M (batch size), row position and kernel variant (slice-parallel for M <= 16,
+register-tiled above)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import assert_bitwise, bf16, f32, host, requires_gpu, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def inv():
+    import invariant_numerics_amd as m
+    return m
+
+
+@pytest.mark.parametrize("M,K,N", [
+    (1, 8, 5), (1, 264, 70), (2, 4096, 130), (3, 520, 257), (5, 1000, 64), (16, 4096, 33),
+    (17, 264, 129), (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
+])
+def test_gemm_matches_oracle_small(orc, M, K, N):
+    say("gemm", M, K, N)
+    X = synth.normal(7000 + M, (M, K))
+    W = synth.bf16_normal(7100 + N, (N, K))
+    Y = host(inv().inv_fixed_order_gemm(f32(X), bf16(W)))
+    assert_bitwise(Y, orc.gemm(X, W), "gemm %dx%dx%d" % (M, K, N))
+
+
+def test_gemm_residual_epilogue(orc):
+    say("gemm residual")
+    X = synth.normal(7201, (37, 512))
+    W = synth.bf16_normal(7202, (96, 512))
+    R = synth.normal(7203, (37, 96))
+    want = (R + orc.gemm(X, W)).astype(np.float32)   # float32 add, as in the oracle decoder
+    got = host(inv().inv_fixed_order_gemm(f32(X), bf16(W), R=f32(R)))
+    assert_bitwise(got, want, "residual")
+    Xs = synth.normal(7204, (4, 512))
+    Rs = synth.normal(7205, (4, 96))
+    got = host(inv().inv_fixed_order_gemm(f32(Xs), bf16(W), R=f32(Rs)))
+    assert_bitwise(got, (Rs + orc.gemm(Xs, W)).astype(np.float32), "residual skinny")
+
+
+def test_gemm_worked_example_k3_padded():
+    """0.1 + 0.2 + (-0.1) as a K = 3 dot, padded with exact zeros to K = 8: the left fold."""
+    say("gemm worked example")
+    x = np.zeros((1, 8), np.float32)
+    x[0, :3] = np.array([0.1, 0.2, -0.1], np.float32)
+    W = np.zeros((1, 8), np.uint16)
+    W[0, :3] = 0x3F80
+    y = host(inv().inv_fixed_order_gemm(f32(x), bf16(W)))[0, 0]
+    a, b, c = np.float32(0.1), np.float32(0.2), np.float32(-0.1)
+    assert y.view(np.uint32) == ((a + b) + c).view(np.uint32)
+    assert y != a + (b + c)
+
+
+def test_gemm_special_values(orc):
+    """Identity weights reproduce X exactly; small integers give exact products."""
+    say("gemm special")
+    X = synth.normal(7301, (20, 512))
+    Wi = np.zeros((512, 512), np.uint16)
+    Wi[np.arange(512), np.arange(512)] = 0x3F80
+    assert_bitwise(host(inv().inv_fixed_order_gemm(f32(X), bf16(Wi))), X, "identity")
+    rng = np.random.default_rng(5)
+    Xi = rng.integers(-2, 3, size=(9, 4096)).astype(np.float32)
+    Wf = rng.integers(-2, 3, size=(77, 4096)).astype(np.float32)
+    want = (Xi.astype(np.int64) @ Wf.astype(np.int64).T).astype(np.float32)
+    assert_bitwise(host(inv().inv_fixed_order_gemm(f32(Xi), bf16(synth.to_bf16_bits(Wf)))), want, "ints")
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (14336, 4096), (4096, 14336)])
+def test_gemm_full_size_batch_invariance(orc, n, k):
+    """Full sizes (4096x4096, 4096x14336 and the down projection 14336->4096): rows of
+    every M in {1,3,16,64,257,512} and of a shuffled batch are bitwise the same rows;
+    sampled outputs equal the oracle's."""
+    say("gemm full", n, k)
+    if k == 4096:
+        d = synth.c3_inputs(n=n, k=k)
+    else:
+        d = dict(x=synth.normal(synth.SEEDS["c3_xdown"], (512, k)),
+                 w=synth.bf16_normal(synth.SEEDS["c3_wdown"], (n, k)))
+    X, W = d["x"], d["w"]
+    Xd, Wd = f32(X), bf16(W)
+    full = host(inv().inv_fixed_order_gemm(Xd, Wd))
+    for M in (1, 3, 16, 64, 257):
+        say("gemm full M", M)
+        part = host(inv().inv_fixed_order_gemm(Xd[:M].contiguous(), Wd))
+        assert_bitwise(part, full[:M], "M=%d" % M)
+    perm = synth.permutation(7400, 512)
+    shuf = host(inv().inv_fixed_order_gemm(f32(X[perm]), Wd))
+    assert_bitwise(shuf, full[perm], "shuffled")
+    # oracle on sampled rows and columns (each output is one row's dot product)
+    rows = [0, 1, 2, 63, 64, 256, 511]
+    cols = np.sort(synth.permutation(7401, n)[:192])
+    want = orc.gemm(X[rows], W[cols])
+    assert_bitwise(full[rows][:, cols], want, "oracle sample")

@@ -1,0 +1,100 @@
+"""lmhead_logprob_top2 on the GPU: bitwise equal to the oracle (logprob, margin, top-2,
+recompute flag), per-row bits independent of the batch size, tau limits, ties."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import assert_bitwise, bf16, f32, host, i32, requires_gpu, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+KEYS = ("logprob", "margin", "top1", "top2", "recomputed")
+
+
+def inv():
+    import invariant_numerics_amd as m
+    return m
+
+
+def run(h, W, tgt, tau=0.1, Wd=None):
+    r = inv().inv_lmhead_logprob_top2(f32(h), Wd if Wd is not None else bf16(W), i32(tgt), tau)
+    return {k: host(v) for k, v in r.items()}
+
+
+def check(got, want, what):
+    for k in KEYS:
+        assert_bitwise(got[k], want[k], "%s %s" % (what, k))
+
+
+def test_c1_all_batch_sizes(orc):
+    """hidden 256, vocab 4096, 64 tokens, batch 1/2/4/8: per-row bits equal across batch
+    sizes and equal to the oracle."""
+    say("lmhead C1")
+    d = synth.c1_inputs()
+    want = orc.lmhead(d["h"], d["w"], d["target"])
+    Wd = bf16(d["w"])
+    assert 0 < want["recomputed"].sum() < 64
+    for B in (1, 2, 4, 8):
+        parts = [run(d["h"][s:s + B], None, d["target"][s:s + B], Wd=Wd) for s in range(0, 64, B)]
+        got = {k: np.concatenate([p[k] for p in parts]) for k in KEYS}
+        check(got, want, "B=%d" % B)
+
+
+@pytest.mark.parametrize("B,K,V", [(1, 8, 2), (3, 264, 1025), (17, 256, 3000), (40, 512, 4096)])
+def test_shapes_match_oracle(orc, B, K, V):
+    say("lmhead shape", B, K, V)
+    h = synth.normal(9000 + V, (B, K))
+    W = synth.bf16_normal(9100 + V, (V, K), 0.1)
+    tgt = synth.uniform_int(9200 + V, (B,), V)
+    check(run(h, W, tgt), orc.lmhead(h, W, tgt), "shape")
+
+
+def test_tau_limits_and_ties(orc):
+    say("lmhead tau/ties")
+    d = synth.c1_inputs(rows=16)
+    for tau, mode in ((0.0, 1), (np.inf, 2)):
+        check(run(d["h"], d["w"], d["target"], tau=tau), orc.lmhead(d["h"], d["w"], d["target"], mode=mode),
+              "tau=%s" % tau)
+    W0 = np.zeros((4096, 256), np.uint16)
+    got = run(d["h"], W0, d["target"])
+    assert np.all(got["top1"] == 0) and np.all(got["top2"] == 1) and np.all(got["margin"] == 0)
+    assert np.all(got["recomputed"] == 1)
+    check(got, orc.lmhead(d["h"], W0, d["target"]), "W=0")
+    W = d["w"].copy()
+    W[10] = W[3000] = W[20]
+    check(run(d["h"], W, d["target"]), orc.lmhead(d["h"], W, d["target"]), "duplicate rows")
+
+
+@pytest.fixture(scope="module")
+def c4():
+    return synth.c4_inputs()
+
+
+def test_c4_batch_invariance_and_oracle_sample(orc, c4):
+    """hidden 4096, vocab 128256: batches 1..256 give the same per-row bits; sampled rows
+    equal the oracle (selective recompute, margin < 0.1)."""
+    h, W, tgt = c4["h"], c4["w"], c4["target"]
+    Wd = bf16(W)
+    say("lmhead C4 B=256")
+    full = run(h, None, tgt, Wd=Wd)
+    for B in (1, 2, 3, 4, 8, 16, 32, 64, 128):
+        say("lmhead C4 B", B)
+        got = run(h[:B], None, tgt[:B], Wd=Wd)
+        check(got, {k: v[:B] for k, v in full.items()}, "B=%d" % B)
+    frac = full["recomputed"].mean()
+    assert 0.1 < frac < 0.6, frac
+    rows = [0, 1, 5, 100, 255]
+    say("lmhead C4 oracle rows", rows)
+    want = orc.lmhead(h[rows], W, tgt[rows])
+    check({k: v[rows] for k, v in full.items()}, want, "oracle rows")
+
+
+def test_c4_margin_stress(orc):
+    """Near-tied weight rows (w_b = w_a + N(0, 1e-3)) make small margins common."""
+    d = synth.c4_inputs(rows=16, stress=True)
+    say("lmhead C4 stress")
+    got = run(d["h"], d["w"], d["target"])
+    rows = [0, 7, 15]
+    want = orc.lmhead(d["h"][rows], d["w"], d["target"][rows])
+    check({k: v[rows] for k, v in got.items()}, want, "stress")
+    assert got["recomputed"].mean() > 0.5
