@@ -202,6 +202,15 @@ int inv_add(const float* A, const float* Bm, int64_t M, int64_t N, int64_t lda, 
  * device, for checking the library's scalar primitives against the CPU check. */
 int inv_eval_numerics(int fn, const float* x, float* y, int64_t n, void* stream);
 
+/* Diagnostic: runs one v_mfma_f32_16x16x4_f32 per test.  Test t reads A [16 x 4],
+ * B [4 x 16] and C [16 x 16] (row-major FP32, at A + 64 t, B + 64 t, C + 256 t) and writes
+ * D = C + A B (at D + 256 t) exactly as the instruction rounds it.  The matrix-core paths of
+ * fixed_order_gemm and attention rely on this instruction being the same arithmetic as four
+ * fused multiply-adds in k order (k = 0, 1, 2, 3), i.e. the slice chain of dot_KS; the test
+ * suite checks that property against the CPU reference through this entry point. */
+int inv_mfma_f32_check(const float* A, const float* B, const float* C, float* D, int64_t ntests,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -173,4 +173,11 @@ int inv_eval_numerics(int fn, const float* x, float* y, int64_t n, void* stream)
     return fin(launch_eval_numerics(fn, x, y, n, S(stream)));
 }
 
+int inv_mfma_f32_check(const float* A, const float* B, const float* C, float* D, int64_t ntests,
+                       void* stream) {
+    if (!A || !B || !C || !D) return INV_ERR_NULL;
+    if (ntests < 1) return INV_ERR_SHAPE;
+    return fin(launch_mfma_check(A, B, C, D, ntests, S(stream)));
+}
+
 }  // extern "C"

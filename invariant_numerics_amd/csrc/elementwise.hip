@@ -152,6 +152,25 @@ __global__ void eval_numerics_kernel(int fn, const float* __restrict__ x, float*
     }
 }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// One v_mfma_f32_16x16x4_f32 per test: test t supplies A [16 x 4], B [4 x 16], C [16 x 16]
+// (row-major) and receives D = C + A B as the instruction computes it.
+__global__ __launch_bounds__(64) void mfma_check_kernel(const float* __restrict__ A,
+                                                        const float* __restrict__ B,
+                                                        const float* __restrict__ C,
+                                                        float* __restrict__ D, int64_t ntest) {
+    const int l = threadIdx.x, g = l >> 4, r = l & 15;
+    for (int64_t t = blockIdx.x; t < ntest; t += gridDim.x) {
+        const float a = A[t * 64 + r * 4 + g];      // A[r][g]
+        const float b = B[t * 64 + g * 16 + r];     // B[g][r]
+        f32x4_t c;
+        for (int v = 0; v < 4; ++v) c[v] = C[t * 256 + (4 * g + v) * 16 + r];
+        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+        for (int v = 0; v < 4; ++v) D[t * 256 + (4 * g + v) * 16 + r] = d[v];
+    }
+}
+
 inline int grid_for(int64_t work, int block) {
     int64_t g = (work + block - 1) / block;
     if (g > 65536) g = 65536;
@@ -202,6 +221,13 @@ hipError_t launch_add(const float* A, const float* B, int M, int N, int64_t lda,
 
 hipError_t launch_eval_numerics(int fn, const float* x, float* y, int64_t n, hipStream_t st) {
     hipLaunchKernelGGL(eval_numerics_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, fn, x, y, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
+                             hipStream_t st) {
+    const int grid = (int)(ntest < 4096 ? ntest : 4096);
+    hipLaunchKernelGGL(mfma_check_kernel, dim3(grid), dim3(64), 0, st, A, B, C, D, ntest);
     return hipGetLastError();
 }
 

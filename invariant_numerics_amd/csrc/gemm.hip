@@ -4,9 +4,9 @@
 //   K is cut into contiguous slices of 256; within a slice c = +0 then c = fma(x_k, w_k, c)
 //   for k ascending; the slices are folded T = c_0, T = T + c_s for s ascending.
 // Two kernels implement it:
-//   * gemm_tiled: a workgroup owns a BM x BN output tile; each thread owns TM x TN outputs
-//     and walks K in 32-wide LDS tiles (8 per slice) keeping two registers per output
-//     (the slice accumulator c and the folded total T).  Used when M is large.
+//   * gemm_mfma: a workgroup owns a BM x BN output tile and walks K in 32-wide LDS tiles
+//     (8 per slice) on the FP32 matrix cores, keeping two registers per output (the slice
+//     accumulator and the folded total T).  Used when M > 16.
 //   * gemm_skinny: for M <= 16 the work per output row is too small to fill the chip,
 //     so a workgroup owns 16 weight rows and all M activation rows; each thread owns one
 //     (weight row, slice) pair, keeps one accumulator per activation row, and the slice
@@ -19,33 +19,49 @@ namespace invnum {
 
 namespace {
 
-constexpr int BK = 32;  // K tile of gemm_tiled; divides KS, so slice ends fall on tile ends
+constexpr int BK = 32;  // K tile; divides KS, so slice ends fall on tile ends
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Position of k (0..31) inside a tile row of LDS: lane group g of an MFMA reads
+// k = g, g+4, ..., g+28 (one per 4-wide MFMA step) as 8 contiguous floats.
+__device__ __forceinline__ int kpos(int k) { return (k & 3) * 8 + (k >> 2); }
+
+// Register-tiled GEMM on the FP32 matrix cores.  v_mfma_f32_16x16x4_f32 advances every
+// output of a 16x16 tile by k = 4s, 4s+1, 4s+2, 4s+3 as four fused multiply-adds in that
+// order (each rounded once) -- the same arithmetic as the sequential fma chain of a slice,
+// so issuing the steps s in ascending order reproduces dot_KS bit for bit.  (This is a
+// measured property of the gfx950 instruction, checked by the test suite against the
+// CPU reference through inv_mfma_f32_check.)
+// Workgroup: 256 threads = 4 wavefronts in a 2 x 2 grid over a BM x BN output tile; each
+// wavefront owns (BM/2) x (BN/2) outputs = TI x TJ MFMA tiles.  Per output two registers:
+// the slice accumulator (MFMA C/D) and the folded total T.
 // ROLE only separates instantiations: 0 = activation projections, 1 = the vocabulary
-// projection of the LM head (N up to 128256), so each can carry its own tile choice and
-// profiles attribute their time separately.
-template <int BM, int BN, int TM, int TN, int ROLE>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(
+// projection of the LM head, so each can carry its own tile choice and profiles attribute
+// their time separately.
+template <int BM, int BN, int ROLE>
+__global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
     float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
-    constexpr int NTX = BN / TN;
-    constexpr int NTY = BM / TM;
-    static_assert(NTX * NTY == 256, "256 threads");
-    constexpr int PADA = 4, PADB = 4;
-    constexpr int XV = BM * (BK / 4) / 256;  // float4 loads of X per thread per tile
-    constexpr int WV = BN * (BK / 8) / 256;  // 16-byte loads of W per thread per tile
-    static_assert(XV >= 1 && WV >= 1, "tile too small");
-    __shared__ float As[2][BK][BM + PADA];
-    __shared__ float Bs[2][BK][BN + PADB];
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int TI = WM / 16, TJ = WN / 16;
+    constexpr int LDT = BK + 4;                    // padded LDS row (floats)
+    constexpr int XV = BM * (BK / 4) / 256;        // float4 loads of X per thread per tile
+    constexpr int WV = BN * (BK / 8) / 256;        // 16-byte loads of W per thread per tile
+    static_assert(XV >= 1 && WV >= 1 && TI >= 1 && TJ >= 1, "tile too small");
+    __shared__ float As[2][BM][LDT];
+    __shared__ float Bs[2][BN][LDT];
 
     if (Mdev) M = min(M, *Mdev);
     const int m0 = blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
     if (m0 >= M) return;
     const int tid = threadIdx.x;
-    const int tx = tid % NTX, ty = tid / NTX;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int wm0 = (wv >> 1) * WM, wn0 = (wv & 1) * WN;
 
     float4 xr[XV];
     uint4 wr[WV];
@@ -53,8 +69,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int idx = tid + i * 256;
-            const int r = idx / (BK / 4), q = idx % (BK / 4);
-            const int gm = m0 + r, gk = k0 + 4 * q;
+            const int row = idx / (BK / 4), q = idx % (BK / 4);
+            const int gm = m0 + row, gk = k0 + 4 * q;
             if (gm < M && gk < K)
                 xr[i] = *reinterpret_cast<const float4*>(X + (int64_t)gm * ldx + gk);
             else
@@ -63,8 +79,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
             const int idx = tid + i * 256;
-            const int r = idx / (BK / 8), o = idx % (BK / 8);
-            const int gn = n0 + r, gk = k0 + 8 * o;
+            const int row = idx / (BK / 8), o = idx % (BK / 8);
+            const int gn = n0 + row, gk = k0 + 8 * o;
             if (gn < N && gk < K)
                 wr[i] = *reinterpret_cast<const uint4*>(W + (int64_t)gn * ldw + gk);
             else
@@ -75,44 +91,36 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int idx = tid + i * 256;
-            const int r = idx / (BK / 4), q = idx % (BK / 4);
-            As[buf][4 * q + 0][r] = xr[i].x;
-            As[buf][4 * q + 1][r] = xr[i].y;
-            As[buf][4 * q + 2][r] = xr[i].z;
-            As[buf][4 * q + 3][r] = xr[i].w;
+            const int row = idx / (BK / 4), q = idx % (BK / 4);
+            float* d = As[buf][row];
+            d[kpos(4 * q + 0)] = xr[i].x;
+            d[kpos(4 * q + 1)] = xr[i].y;
+            d[kpos(4 * q + 2)] = xr[i].z;
+            d[kpos(4 * q + 3)] = xr[i].w;
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
             const int idx = tid + i * 256;
-            const int r = idx / (BK / 8), o = idx % (BK / 8);
-            Bs[buf][8 * o + 0][r] = bf16_lo(wr[i].x);
-            Bs[buf][8 * o + 1][r] = bf16_hi(wr[i].x);
-            Bs[buf][8 * o + 2][r] = bf16_lo(wr[i].y);
-            Bs[buf][8 * o + 3][r] = bf16_hi(wr[i].y);
-            Bs[buf][8 * o + 4][r] = bf16_lo(wr[i].z);
-            Bs[buf][8 * o + 5][r] = bf16_hi(wr[i].z);
-            Bs[buf][8 * o + 6][r] = bf16_lo(wr[i].w);
-            Bs[buf][8 * o + 7][r] = bf16_hi(wr[i].w);
+            const int row = idx / (BK / 8), o = idx % (BK / 8);
+            float* d = Bs[buf][row];
+            d[kpos(8 * o + 0)] = bf16_lo(wr[i].x);
+            d[kpos(8 * o + 1)] = bf16_hi(wr[i].x);
+            d[kpos(8 * o + 2)] = bf16_lo(wr[i].y);
+            d[kpos(8 * o + 3)] = bf16_hi(wr[i].y);
+            d[kpos(8 * o + 4)] = bf16_lo(wr[i].z);
+            d[kpos(8 * o + 5)] = bf16_hi(wr[i].z);
+            d[kpos(8 * o + 6)] = bf16_lo(wr[i].w);
+            d[kpos(8 * o + 7)] = bf16_hi(wr[i].w);
         }
     };
 
-    float c[TM][TN], T[TM][TN];
+    f32x4 acc[TI][TJ], T[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) { c[i][j] = 0.0f; T[i][j] = 0.0f; }
-
-    auto step = [&](int buf, int kk) {
-        float a[TM], b[TN];
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = As[buf][kk][ty * TM + i];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = Bs[buf][kk][tx * TN + j];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) c[i][j] = __builtin_fmaf(a[i], b[j], c[i][j]);
-    };
+            for (int v = 0; v < 4; ++v) { acc[i][j][v] = 0.0f; T[i][j][v] = 0.0f; }
 
     const int nt = (K + BK - 1) / BK;
     load_tile(0);
@@ -121,41 +129,76 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     for (int t = 0; t < nt; ++t) {
         const int buf = t & 1;
         if (t + 1 < nt) load_tile((t + 1) * BK);
+        float a[TI][8], b[TJ][8];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+            const float4* src = reinterpret_cast<const float4*>(&As[buf][wm0 + i * 16 + r][g * 8]);
+            const float4 lo = src[0], hi = src[1];
+            a[i][0] = lo.x; a[i][1] = lo.y; a[i][2] = lo.z; a[i][3] = lo.w;
+            a[i][4] = hi.x; a[i][5] = hi.y; a[i][6] = hi.z; a[i][7] = hi.w;
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+            const float4* src = reinterpret_cast<const float4*>(&Bs[buf][wn0 + j * 16 + r][g * 8]);
+            const float4 lo = src[0], hi = src[1];
+            b[j][0] = lo.x; b[j][1] = lo.y; b[j][2] = lo.z; b[j][3] = lo.w;
+            b[j][4] = hi.x; b[j][5] = hi.y; b[j][6] = hi.z; b[j][7] = hi.w;
+        }
         const int kend = min(BK, K - t * BK);
         if (kend == BK) {
 #pragma unroll
-            for (int kk = 0; kk < BK; ++kk) step(buf, kk);
+            for (int s = 0; s < BK / 4; ++s)
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
         } else {
-            for (int kk = 0; kk < kend; ++kk) step(buf, kk);
+            // partial last tile: only the k-steps below K (zero padding is never multiplied in)
+#pragma unroll
+            for (int s = 0; s < BK / 4; ++s) {
+                if (4 * s < kend) {
+#pragma unroll
+                    for (int i = 0; i < TI; ++i)
+#pragma unroll
+                        for (int j = 0; j < TJ; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+                }
+            }
         }
         const int kdone = t * BK + kend;
         if (kdone % KS == 0 || kdone == K) {
             const bool first = kdone <= KS;
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    T[i][j] = first ? c[i][j] : T[i][j] + c[i][j];
-                    c[i][j] = 0.0f;
-                }
+                for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        T[i][j][v] = first ? acc[i][j][v] : T[i][j][v] + acc[i][j][v];
+                        acc[i][j][v] = 0.0f;
+                    }
         }
         if (t + 1 < nt) store_tile(buf ^ 1);
         __syncthreads();
     }
 
+    // lane (g, r) holds rows 4g..4g+3, column r of each 16 x 16 tile
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int gm = m0 + ty * TM + i;
-        if (gm >= M) continue;
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int gn = n0 + tx * TN + j;
-            if (gn >= N) continue;
-            float y = T[i][j];
-            if (R) y = R[(int64_t)gm * ldr + gn] + y;
-            Y[(int64_t)gm * ldy + gn] = y;
+        for (int v = 0; v < 4; ++v) {
+            const int gm = m0 + wm0 + i * 16 + 4 * g + v;
+            if (gm >= M) continue;
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+                const int gn = n0 + wn0 + j * 16 + r;
+                if (gn >= N) continue;
+                float y = T[i][j][v];
+                if (R) y = R[(int64_t)gm * ldr + gn] + y;
+                Y[(int64_t)gm * ldy + gn] = y;
+            }
         }
-    }
 }
 
 // ---------------------------------------------------------------- skinny --
@@ -224,10 +267,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     }
 }
 
-template <int BM, int BN, int TM, int TN, int ROLE>
+template <int BM, int BN, int ROLE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
-    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, TM, TN, ROLE>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, ROLE>), grid, dim3(256), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
 }
@@ -259,8 +302,8 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         if (a.M <= 8) return launch_skinny<8, ROLE>(a, st);
         return launch_skinny<16, ROLE>(a, st);
     }
-    if (a.M <= 64) return launch_tiled<64, 64, 4, 4, ROLE>(a, st);
-    return launch_tiled<128, 128, 8, 8, ROLE>(a, st);
+    if (a.M <= 64) return launch_tiled<64, 64, ROLE>(a, st);
+    return launch_tiled<128, 128, ROLE>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role) {

@@ -53,5 +53,7 @@ hipError_t launch_swiglu(const float* G, const float* U, int M, int F, int64_t l
 hipError_t launch_add(const float* A, const float* B, int M, int N, int64_t lda, int64_t ldb,
                       float* Y, int64_t ldy, hipStream_t st);
 hipError_t launch_eval_numerics(int fn, const float* x, float* y, int64_t n, hipStream_t st);
+hipError_t launch_mfma_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
+                             hipStream_t st);
 
 }  // namespace invnum
