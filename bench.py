@@ -8,7 +8,7 @@ selective FP32 recompute of rows whose margin < 0.1.  Inputs (weights, tokens) a
 resident in HBM before the timed region.  value = scored tokens / s = B * (T - 1) / step.
 
 Also printed in the same JSON line:
-  roofline      the dominant kernel (the body projections' register-tiled GEMM), timed
+  roofline      the dominant kernel (the body projections' FP32-MFMA GEMM), timed
                 with HIP events on its launch stream inside the timed steps;
   cpu_baseline  the CPU oracle on a bounded sample of the same workload (one 64-token
                 sequence at full width), host cores, scaled to tokens / s;
@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector/matrix peak: 256 CU x 2.4 GHz x 256 flop/clk
+FP32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix (MFMA) peak: 256 CU x 2.4 GHz x 256 flop/clk
 
 
 def parse():
@@ -107,7 +107,8 @@ def main():
     flops = np.array([f for _, _, f in rec], np.float64)
     achieved = float(flops.sum() / durs.sum()) / 1e12
     gemm_share = float(durs.sum() / elapsed)
-    roof = dict(bound="alu", kernel="gemm_tiled_kernel (body projections)", achieved=round(achieved, 3),
+    roof = dict(bound="mfma", kernel="gemm_mfma_kernel<128,128,0> (body projections, FP32 matrix cores)",
+                achieved=round(achieved, 3),
                 peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / FP32_PEAK_TFLOPS, 4),
                 traffic=None, launches=int(len(rec)), avg_launch_us=round(float(durs.mean()) * 1e6, 2),
                 avg_flops_per_launch=float(flops.mean()), share_of_step=round(gemm_share, 3))

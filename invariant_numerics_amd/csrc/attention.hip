@@ -21,8 +21,6 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BQ = 64;    // query rows per prefill workgroup
-constexpr int SUB = 32;   // keys staged per LDS sub-block
-constexpr int SPAD = 4;
 
 template <int DT>
 __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* dst) {
@@ -37,154 +35,286 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 }
 
 // ------------------------------------------------------------------ prefill --
-// Workgroup: 256 threads, BQ = 64 query rows of one (b, h).  Thread t works on row t / 4:
-// for scores it owns keys (t % 4) * 8 .. +8 of each 32-key sub-block, for the PV sum it
-// owns head dims (t % 4) * 32 .. +32.
+// Matrix-core prefill.  v_mfma_f32_16x16x4_f32 advances each output of a 16 x 16 tile by
+// four fused multiply-adds in k order, so both contractions keep their sequential order:
+// the scores over d = 0..127 and the PV sums over keys in ascending j.
+// Workgroup: 256 threads = 4 wavefronts over BQ = 64 consecutive query rows of one (b, h);
+// wavefront w owns rows 16w .. 16w + 15.  Per 256-key chunk:
+//   1. scores: K staged through LDS in 64-key sub-blocks; 16 key tiles x 32 MFMA steps, all
+//      256 scores of the chunk kept in registers (lane (g, r) holds rows 4g..4g+3 of key
+//      column r of every key tile);
+//   2. chunk max over the row's keys <= i (16-lane shuffles), p = exp_f(s - m_c);
+//   3. PV: p re-laid out through LDS, V staged row-major; MFMA over keys below the first
+//      multiple-of-4 boundary that every row of the wavefront can see; l_c runs on the same
+//      instruction with an all-ones operand (fma(p, 1, l) = l + p, one rounding); the keys
+//      from there to each row's own i (at most 19) continue on the VALU, ascending, so
+//      masked keys are skipped rather than added as zeros;
+//   4. merge into the running (m, l, o) exactly as the decode merge kernel does.
+constexpr int SB = 64;          // keys per LDS sub-block
+constexpr int KPAD = 4;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float rowmax16(float x) {
+    // maximum over the 16 lanes sharing lane >> 4 (max is order independent)
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        const float y = __shfl_xor(x, off);
+        x = (y > x) ? y : x;
+    }
+    return x;
+}
+
+template <int DT>
+__device__ __forceinline__ void load4(const void* base, int64_t off, float* v) {
+    if (DT == 1) {
+        const float4 t = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+        v[0] = bf16_lo(t.x); v[1] = bf16_hi(t.x); v[2] = bf16_lo(t.y); v[3] = bf16_hi(t.y);
+    }
+}
+
+// Global -> register -> LDS staging of one 64-key sub-block of K or V (fp32 in LDS).
+// Thread t carries 8 groups of 4 consecutive d of rows (e / 32) for e = t + 256 i.
+template <int DT>
+struct Stage {
+    float4 v[8];
+    // rows at or beyond kend are read from row kend - 1 (always valid) and replaced by zeros
+    __device__ __forceinline__ void load(const void* base, int64_t kvbase, int kb, int kend, int tid) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = tid + 256 * i;
+            const int jj = e >> 5, d4 = (e & 31) * 4;
+            const bool in = kb + jj < kend;
+            const int row = in ? kb + jj : kend - 1;
+            float t[4];
+            load4<DT>(base, kvbase + (int64_t)row * D + d4, t);
+            v[i] = in ? make_float4(t[0], t[1], t[2], t[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    // K layout: row jj, d permuted (d % 4) * 32 + d / 4 (a lane's 32 operands contiguous)
+    __device__ __forceinline__ void store_k(float* KV, int tid) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = tid + 256 * i;
+            const int jj = e >> 5, q = e & 31;
+            float* dst = KV + jj * (D + KPAD) + q;
+            dst[0] = v[i].x; dst[32] = v[i].y; dst[64] = v[i].z; dst[96] = v[i].w;
+        }
+    }
+    // V layout: row-major [key][d]
+    __device__ __forceinline__ void store_v(float* KV, int tid) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = tid + 256 * i;
+            const int jj = e >> 5, d4 = (e & 31) * 4;
+            *reinterpret_cast<float4*>(KV + jj * (D + KPAD) + d4) = v[i];
+        }
+    }
+};
+
 template <int DT>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
     int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O) {
-    __shared__ float Qs[BQ][D + SPAD];
-    __shared__ float KVs[SUB][D + SPAD];
-    __shared__ float Ss[BQ][CHUNK + SPAD];
+    // two K/V sub-block buffers; per-wavefront p of the whole chunk
+    // [16 rows][4 sub-blocks x 64 keys, keys permuted (j % 4) * 16 + j / 4 inside each]
+    __shared__ float KV[2][SB * (D + KPAD)];
+    __shared__ float Ps[4][16][CHUNK + KPAD];
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int g = h / (Hq / Hkv);
+    const int kvh = h / (Hq / Hkv);
     const int r0 = qb * BQ;
     const int nrows = min(BQ, Tq - r0);
-    const int imax = q_start + r0 + nrows - 1;          // last absolute query position
-    const int64_t kvbase = ((int64_t)b * Hkv + g) * Tmax * D;
+    const int imax = q_start + r0 + nrows - 1;          // last valid absolute row of the block
+    const int64_t kvbase = ((int64_t)b * Hkv + kvh) * Tmax * D;
+    const int wrow0 = r0 + 16 * w;                      // first row (relative) of this wavefront
+    const int i0 = q_start + wrow0;                     // its absolute position
+    int irow[4];                                        // the lane's output rows, clamped
+#pragma unroll
+    for (int v = 0; v < 4; ++v) irow[v] = min(i0 + 4 * g + v, imax);
 
-    // stage the query rows
-    for (int e = tid; e < BQ * (D / 4); e += 256) {
-        const int r = e / (D / 4), d4 = (e % (D / 4)) * 4;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (r < nrows) load_row4<DT>(Q, (((int64_t)b * Tq + r0 + r) * Hq + h) * D + d4, v);
-        Qs[r][d4 + 0] = v[0]; Qs[r][d4 + 1] = v[1]; Qs[r][d4 + 2] = v[2]; Qs[r][d4 + 3] = v[3];
+    // Q fragments: lane (g, r) supplies Q[row r][d = 4s + g], s = 0..31
+    float qf[32];
+    {
+        const int qrow = min(wrow0 + r, Tq - 1);
+        const int64_t qoff = (((int64_t)b * Tq + qrow) * Hq + h) * D;
+#pragma unroll
+        for (int s = 0; s < 32; ++s) {
+            const int d = 4 * s + g;
+            qf[s] = DT == 1 ? reinterpret_cast<const float*>(Q)[qoff + d]
+                            : bf16_up(reinterpret_cast<const uint16_t*>(Q)[qoff + d]);
+        }
     }
 
-    const int r = tid / 4;            // this thread's row
-    const int q4 = tid % 4;
-    const int i = q_start + r0 + r;   // its absolute position
-    const bool rvalid = r < nrows;
-    float o[32], oc[32];
-    float m = 0.0f, l = 0.0f;
+    f32x4 o[8];
+    float m[4], l[4];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) o[u] = 0.0f;
+    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) { m[v] = 0.0f; l[v] = 0.0f; }
 
     const int clast = imax / CHUNK;
+    Stage<DT> st;
+    int buf = 0;
+    // prologue: chunk 0, K sub-block 0
+    st.load(Kc, kvbase, 0, min(CHUNK, imax + 1), tid);
+    st.store_k(KV[0], tid);
+    __syncthreads();
+
     for (int c = 0; c <= clast; ++c) {
         const int kbase = c * CHUNK;
-        const int kend = min(kbase + CHUNK, imax + 1);   // keys needed by some row
-        // ---- scores for this chunk
-        for (int kb = kbase; kb < kend; kb += SUB) {
-            __syncthreads();
-            for (int e = tid; e < SUB * (D / 4); e += 256) {
-                const int jj = e / (D / 4), d4 = (e % (D / 4)) * 4;
-                float v[4] = {0.f, 0.f, 0.f, 0.f};
-                if (kb + jj < kend) load_row4<DT>(Kc, kvbase + (int64_t)(kb + jj) * D + d4, v);
-                KVs[jj][d4 + 0] = v[0]; KVs[jj][d4 + 1] = v[1];
-                KVs[jj][d4 + 2] = v[2]; KVs[jj][d4 + 3] = v[3];
-            }
-            __syncthreads();
-            float acc[8];
+        const int kend = min(kbase + CHUNK, imax + 1);         // keys some row of the block needs
+        const int nsb = (kend - kbase + SB - 1) / SB;          // active sub-blocks (1..4)
+        const int nkend = min(kbase + 2 * CHUNK, imax + 1);    // next chunk's key bound
+        // ------------------------------------------------------ 1. scores (stages K_0..K_nsb-1)
+        f32x4 S[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[u] = 0.0f;
-            for (int d = 0; d < D; d += 4) {
-                const float4 qv = *reinterpret_cast<const float4*>(&Qs[r][d]);
+        for (int t = 0; t < 16; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float4 kv = *reinterpret_cast<const float4*>(&KVs[q4 * 8 + u][d]);
-                    acc[u] = __builtin_fmaf(qv.x, kv.x, acc[u]);
-                    acc[u] = __builtin_fmaf(qv.y, kv.y, acc[u]);
-                    acc[u] = __builtin_fmaf(qv.z, kv.z, acc[u]);
-                    acc[u] = __builtin_fmaf(qv.w, kv.w, acc[u]);
+        for (int sb = 0; sb < CHUNK / SB; ++sb) {
+            if (sb < nsb) {
+                // prefetch the next stage: K_{sb+1}, or V_0 of this chunk
+                if (sb + 1 < nsb) st.load(Kc, kvbase, kbase + (sb + 1) * SB, kend, tid);
+                else st.load(Vc, kvbase, kbase, kend, tid);
+                const float* kvb = KV[buf];
+                if (kbase + sb * SB <= i0 + 15) {
+                    f32x4 acc[SB / 16];
+#pragma unroll
+                    for (int kt = 0; kt < SB / 16; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s4 = 0; s4 < 8; ++s4) {
+                        float4 kk[SB / 16];
+#pragma unroll
+                        for (int kt = 0; kt < SB / 16; ++kt)
+                            kk[kt] = *reinterpret_cast<const float4*>(kvb + (kt * 16 + r) * (D + KPAD) + g * 32 + 4 * s4);
+#pragma unroll
+                        for (int kt = 0; kt < SB / 16; ++kt)
+                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 0], kk[kt].x, acc[kt], 0, 0, 0);
+#pragma unroll
+                        for (int kt = 0; kt < SB / 16; ++kt)
+                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 1], kk[kt].y, acc[kt], 0, 0, 0);
+#pragma unroll
+                        for (int kt = 0; kt < SB / 16; ++kt)
+                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 2], kk[kt].z, acc[kt], 0, 0, 0);
+#pragma unroll
+                        for (int kt = 0; kt < SB / 16; ++kt)
+                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 3], kk[kt].w, acc[kt], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int kt = 0; kt < SB / 16; ++kt) S[sb * 4 + kt] = acc[kt];
                 }
+                if (sb + 1 < nsb) st.store_k(KV[buf ^ 1], tid);
+                else st.store_v(KV[buf ^ 1], tid);
+                __syncthreads();
+                buf ^= 1;
             }
+        }
+        // ------------------------------------------------------ 2. chunk max and p
+        float mc[4];
+        bool ne[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) Ss[r][kb - kbase + q4 * 8 + u] = acc[u] * scale;
+        for (int v = 0; v < 4; ++v) {
+            ne[v] = irow[v] >= kbase;
+            float x = -__builtin_inff();
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int j = kbase + t * 16 + r;
+                const float sv = S[t][v] * scale;
+                S[t][v] = sv;
+                if (j <= irow[v]) x = (sv > x) ? sv : x;
+            }
+            mc[v] = rowmax16(x);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int jj = (t & 3) * 16 + r;                   // key inside its sub-block
+            const int pj = (t >> 2) * SB + (jj & 3) * 16 + (jj >> 2);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int j = kbase + t * 16 + r;
+                Ps[w][4 * g + v][pj] = (j <= irow[v]) ? exp_f(S[t][v] - mc[v]) : 0.0f;
+            }
         }
         __syncthreads();
-        // ---- chunk max and probabilities for this row (4 threads per row)
-        const int jlast = min(kbase + CHUNK - 1, i);     // last key of this chunk for row i
-        const bool nonempty = rvalid && jlast >= kbase;
-        float mc = -__builtin_inff();
-        if (nonempty) {
-            for (int j = kbase + q4; j <= jlast; j += 4) {
-                const float s = Ss[r][j - kbase];
-                mc = (s > mc) ? s : mc;
-            }
-        }
-        // combine the 4 partial maxima of the row (lanes 4r..4r+3 of the wavefront)
-        {
-            float o1 = __shfl_xor(mc, 1);
-            mc = (o1 > mc) ? o1 : mc;
-            float o2 = __shfl_xor(mc, 2);
-            mc = (o2 > mc) ? o2 : mc;
-        }
-        __syncthreads();
-        if (nonempty) {
-            for (int j = kbase + q4; j <= jlast; j += 4) {
-                const float s = Ss[r][j - kbase];
-                Ss[r][j - kbase] = exp_f(s - mc);
-            }
-        }
-        // ---- PV and l_c, j ascending; this thread owns dims q4*32 .. +32
-        float lc = 0.0f;
+        // ------------------------------------------------------ 3. PV and l (stages V_0..)
+        // keys [kbase, jv) go through the matrix cores for every row of the wavefront
+        const int jspan = min(i0, kend) - kbase;
+        const int jv = kbase + ((jspan > 0 ? jspan : 0) & ~3);
+        f32x4 oc[8];
+        f32x4 lc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 32; ++u) oc[u] = 0.0f;
-        for (int kb = kbase; kb < kend; kb += SUB) {
-            __syncthreads();
-            for (int e = tid; e < SUB * (D / 4); e += 256) {
-                const int jj = e / (D / 4), d4 = (e % (D / 4)) * 4;
-                float v[4] = {0.f, 0.f, 0.f, 0.f};
-                if (kb + jj < kend) load_row4<DT>(Vc, kvbase + (int64_t)(kb + jj) * D + d4, v);
-                KVs[jj][d4 + 0] = v[0]; KVs[jj][d4 + 1] = v[1];
-                KVs[jj][d4 + 2] = v[2]; KVs[jj][d4 + 3] = v[3];
-            }
-            __syncthreads();
-            if (nonempty) {
-                const int jstop = min(kb + SUB - 1, jlast);
-                for (int j = kb; j <= jstop; ++j) {
-                    const float p = Ss[r][j - kbase];
-                    lc = lc + p;
-                    const float* vr = &KVs[j - kb][q4 * 32];
+        for (int t = 0; t < 8; ++t) oc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int u = 0; u < 32; u += 4) {
-                        const float4 vv = *reinterpret_cast<const float4*>(vr + u);
-                        oc[u + 0] = __builtin_fmaf(p, vv.x, oc[u + 0]);
-                        oc[u + 1] = __builtin_fmaf(p, vv.y, oc[u + 1]);
-                        oc[u + 2] = __builtin_fmaf(p, vv.z, oc[u + 2]);
-                        oc[u + 3] = __builtin_fmaf(p, vv.w, oc[u + 3]);
+        for (int sb = 0; sb < CHUNK / SB; ++sb) {
+            if (sb < nsb) {
+                const int kb = kbase + sb * SB;
+                // prefetch: V_{sb+1}, or the next chunk's K_0
+                const bool more = sb + 1 < nsb;
+                if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
+                else if (c < clast) st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
+                const float* kvb = KV[buf];
+                const int nsteps = max(0, min(SB, jv - kb)) >> 2;
+                const float* prow = &Ps[w][r][sb * SB + g * 16];
+                for (int s = 0; s < nsteps; ++s) {
+                    const float a = prow[s];
+                    const float* vr = kvb + (4 * s + g) * (D + KPAD) + r;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        oc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vr[t * 16], oc[t], 0, 0, 0);
+                    lc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, 1.0f, lc, 0, 0, 0);
+                }
+                // VALU continuation for keys [max(kb, jv), row's own i], ascending
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int j1 = min(kb + SB, irow[v] + 1);
+                    for (int j = max(kb, jv); j < j1; ++j) {
+                        const int jj = j - kb;
+                        const float pv = Ps[w][4 * g + v][sb * SB + (jj & 3) * 16 + (jj >> 2)];
+                        lc[v] = lc[v] + pv;
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            oc[t][v] = __builtin_fmaf(pv, kvb[jj * (D + KPAD) + t * 16 + r], oc[t][v]);
                     }
                 }
+                if (more) st.store_v(KV[buf ^ 1], tid);
+                else if (c < clast) st.store_k(KV[buf ^ 1], tid);
+                __syncthreads();
+                buf ^= 1;
             }
         }
-        // ---- merge into the running state
-        if (nonempty) {
+        // ------------------------------------------------------ 4. merge
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            if (!ne[v]) continue;
             if (c == 0) {
-                m = mc; l = lc;
+                m[v] = mc[v];
+                l[v] = lc[v];
 #pragma unroll
-                for (int u = 0; u < 32; ++u) o[u] = oc[u];
+                for (int t = 0; t < 8; ++t) o[t][v] = oc[t][v];
             } else {
-                const float mn = (mc > m) ? mc : m;
-                const float a = exp_f(m - mn), bb = exp_f(mc - mn);
-                l = (l * a) + (lc * bb);
+                const float mn = (mc[v] > m[v]) ? mc[v] : m[v];
+                const float al = exp_f(m[v] - mn), be = exp_f(mc[v] - mn);
+                l[v] = (l[v] * al) + (lc[v] * be);
 #pragma unroll
-                for (int u = 0; u < 32; ++u) o[u] = (o[u] * a) + (oc[u] * bb);
-                m = mn;
+                for (int t = 0; t < 8; ++t) o[t][v] = (o[t][v] * al) + (oc[t][v] * be);
+                m[v] = mn;
             }
         }
     }
-    if (rvalid) {
-        float* out = O + (((int64_t)b * Tq + r0 + r) * Hq + h) * D + q4 * 32;
+    // ------------------------------------------------------------------ output
 #pragma unroll
-        for (int u = 0; u < 32; u += 4) {
-            float4 v;
-            v.x = o[u + 0] / l; v.y = o[u + 1] / l; v.z = o[u + 2] / l; v.w = o[u + 3] / l;
-            *reinterpret_cast<float4*>(out + u) = v;
-        }
+    for (int v = 0; v < 4; ++v) {
+        const int rel = wrow0 + 4 * g + v;
+        if (rel >= r0 + nrows) continue;
+        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) out[t * 16 + r] = o[t][v] / l[v];
     }
 }
 

@@ -71,20 +71,18 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
             const int idx = tid + i * 256;
             const int row = idx / (BK / 4), q = idx % (BK / 4);
             const int gm = m0 + row, gk = k0 + 4 * q;
-            if (gm < M && gk < K)
-                xr[i] = *reinterpret_cast<const float4*>(X + (int64_t)gm * ldx + gk);
-            else
-                xr[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            const bool in = gm < M && gk < K;   // outside: read a valid element, use zeros
+            const float4 t = *reinterpret_cast<const float4*>(X + (int64_t)min(gm, M - 1) * ldx + min(gk, K - 4));
+            xr[i] = in ? t : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
             const int idx = tid + i * 256;
             const int row = idx / (BK / 8), o = idx % (BK / 8);
             const int gn = n0 + row, gk = k0 + 8 * o;
-            if (gn < N && gk < K)
-                wr[i] = *reinterpret_cast<const uint4*>(W + (int64_t)gn * ldw + gk);
-            else
-                wr[i] = make_uint4(0u, 0u, 0u, 0u);
+            const bool in = gn < N && gk < K;
+            const uint4 t = *reinterpret_cast<const uint4*>(W + (int64_t)min(gn, N - 1) * ldw + min(gk, K - 8));
+            wr[i] = in ? t : make_uint4(0u, 0u, 0u, 0u);
         }
     };
     auto store_tile = [&](int buf) {

@@ -62,14 +62,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 
 // exp_f(x): n = rint(x log2e); r = fma(-n, ln2_hi, x); r = fma(-n, ln2_lo, r);
 // p = Taylor degree 7 by fma-Horner from the top; result p * 2^n (n = 128 via p*2).
-// x < ln(2^-126) -> +0, x > ln(2^128) -> +inf.
+// x < ln(2^-126) -> +0, x > ln(2^128) -> +inf, NaN -> NaN.
+// Written without branches: the polynomial runs on x clamped into the finite range (for x
+// inside it the clamp is the identity, so the arithmetic is exactly the steps above) and the
+// pinned results outside the range are selected at the end.
 __device__ __forceinline__ float exp_f(float x) {
-    if (x != x) return x + x;
-    if (x > INV_EXP_HI) return __builtin_inff();
-    if (x < INV_EXP_LO) return 0.0f;
-    float t = x * INV_LOG2E;
-    float n = __builtin_rintf(t);
-    float r = __builtin_fmaf(-n, INV_LN2_HI, x);
+    const float xc = __builtin_fminf(__builtin_fmaxf(x, INV_EXP_LO), INV_EXP_HI);
+    const float t = xc * INV_LOG2E;
+    const float n = __builtin_rintf(t);
+    float r = __builtin_fmaf(-n, INV_LN2_HI, xc);
     r = __builtin_fmaf(-n, INV_LN2_LO, r);
     float p = INV_IF7;
     p = __builtin_fmaf(p, r, INV_IF6);
@@ -79,9 +80,14 @@ __device__ __forceinline__ float exp_f(float x) {
     p = __builtin_fmaf(p, r, INV_IF2);
     p = __builtin_fmaf(p, r, INV_IF1);
     p = __builtin_fmaf(p, r, INV_IF0);
-    int ni = (int)n;
-    if (ni > 127) { p = p * 2.0f; ni -= 1; }
-    return p * __uint_as_float((uint32_t)(ni + 127) << 23);
+    const int ni = (int)n;
+    const bool top = ni > 127;
+    const float pp = top ? p * 2.0f : p;
+    const int ne = top ? ni - 1 : ni;
+    float res = pp * __uint_as_float((uint32_t)(ne + 127) << 23);
+    res = (x < INV_EXP_LO) ? 0.0f : res;
+    res = (x > INV_EXP_HI) ? __builtin_inff() : res;
+    return (x != x) ? x + x : res;
 }
 
 // log_f(x), x > 0: x = 2^e m, m in (sqrt(1/2), sqrt(2)]; f = m - 1; s = f / (2 + f);
