@@ -200,8 +200,21 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 }
 
 // ---------------------------------------------------------------- skinny --
+// M <= 16.  A workgroup owns SK_ROWS = 16 weight rows and every activation row; thread
+// (row nl, slice lane sl) computes the chain of slice s = group + sl for all M rows, keeping
+// one accumulator per activation row.  Slices are processed in groups of 16; within a group
+// the weights stream in 4 phases of 64 elements per slice:
+//   * load: 16 rows x 16 slices x 128 bytes, each 128-byte segment read by 8 consecutive
+//     lanes (coalesced), into registers one phase ahead, then into LDS (segments padded to
+//     144 bytes so the 16-byte LDS reads are bank-conflict free); the activation phase tile
+//     X[m][slice][64] is staged the same way and read as a broadcast;
+//   * compute: each thread runs its slice chain over the phase's 64 elements in order.
+// After each group the 16 new slice partials of every output are folded, in slice order,
+// into that output's running total by the thread that owns it.
 constexpr int SK_ROWS = 16;   // weight rows per workgroup
-constexpr int SK_LANES = 16;  // slice lanes per weight row
+constexpr int SK_LANES = 16;  // slices per group
+constexpr int PH = 64;        // elements per slice per phase
+constexpr int WSEG = PH * 2 + 16;   // padded bytes per (row, slice) segment in LDS
 
 template <int MB, int ROLE>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(
@@ -209,59 +222,125 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
     float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
-    extern __shared__ float part[];  // [S][MB][SK_ROWS]
+    __shared__ __attribute__((aligned(16))) unsigned char Wl[SK_ROWS * SK_LANES * WSEG];
+    __shared__ __attribute__((aligned(16))) float Xl[MB][SK_LANES][PH];
+    __shared__ float part[SK_LANES][MB][SK_ROWS];
     if (Mdev) M = min(M, *Mdev);
     if (M <= 0) return;
     const int S = (K + KS - 1) / KS;
     const int tid = threadIdx.x;
     const int nl = tid % SK_ROWS;
     const int sl = tid / SK_ROWS;
-    const int n = blockIdx.x * SK_ROWS + nl;
-    const bool nvalid = n < N;
-    const uint16_t* wrow = W + (int64_t)(nvalid ? n : 0) * ldw;
+    const int n0 = blockIdx.x * SK_ROWS;
 
-    for (int s = sl; s < S; s += SK_LANES) {
-        float c[MB];
+    // load duty: 8 x 16 bytes of weights and MB x 16 bytes of activations per thread
+    uint4 wpre[8];
+    float4 xpre[MB];
+    auto load = [&](int sg, int p) {
 #pragma unroll
-        for (int m = 0; m < MB; ++m) c[m] = 0.0f;
-        const int k0 = s * KS;
-        const int k1 = min(K, k0 + KS);
-        if (nvalid) {
-            for (int k = k0; k < k1; k += 8) {
-                const uint4 w8 = *reinterpret_cast<const uint4*>(wrow + k);
+        for (int i = 0; i < 8; ++i) {
+            const int q = tid + 256 * i;          // 16-byte unit index in the phase tile
+            const int seg = q >> 3, c8 = q & 7;   // segment (row, slice) and chunk in it
+            const int rn = seg >> 4, ss = seg & 15;
+            const int k = (sg + ss) * KS + p * PH + 8 * c8;
+            const bool in = (n0 + rn < N) && (k < K);
+            const uint4 t = *reinterpret_cast<const uint4*>(W + (int64_t)min(n0 + rn, N - 1) * ldw + min(k, K - 8));
+            wpre[i] = in ? t : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            const int ss = tid >> 4, c4 = tid & 15;          // 16 slices x 16 float4
+            const int k = (sg + ss) * KS + p * PH + 4 * c4;
+            const bool in = (m < M) && (k < K);
+            const float4 t = *reinterpret_cast<const float4*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
+            xpre[m] = in ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = tid + 256 * i;
+            const int seg = q >> 3, c8 = q & 7;
+            *reinterpret_cast<uint4*>(&Wl[seg * WSEG + c8 * 16]) = wpre[i];
+        }
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+            *reinterpret_cast<float4*>(&Xl[m][tid >> 4][(tid & 15) * 4]) = xpre[m];
+    };
+
+    const int ngroups = (S + SK_LANES - 1) / SK_LANES;
+    const int nstages = ngroups * (KS / PH);
+    const bool folder = tid < MB * SK_ROWS;
+    const int fm = tid / SK_ROWS, fr = tid % SK_ROWS;   // output folded by this thread
+    float T = 0.0f;
+    float c[MB];
+    load(0, 0);
+    for (int st = 0; st < nstages; ++st) {
+        const int sg = (st / (KS / PH)) * SK_LANES;
+        const int p = st % (KS / PH);
+        __syncthreads();               // everyone is done with the previous phase's LDS data
+        store();
+        __syncthreads();
+        if (st + 1 < nstages) load(((st + 1) / (KS / PH)) * SK_LANES, (st + 1) % (KS / PH));
+        if (p == 0) {
+#pragma unroll
+            for (int m = 0; m < MB; ++m) c[m] = 0.0f;
+        }
+        const int s = sg + sl;
+        const int kb = s * KS + p * PH;                       // first k of this phase
+        const int nk = min(PH, K - kb);                       // elements of this phase (<= 0: none)
+        const unsigned char* wseg = &Wl[(nl * SK_LANES + sl) * WSEG];
+        if (nk == PH) {
+#pragma unroll
+            for (int j = 0; j < PH / 8; ++j) {
+                const uint4 w8 = *reinterpret_cast<const uint4*>(wseg + 16 * j);
                 const float w[8] = {bf16_lo(w8.x), bf16_hi(w8.x), bf16_lo(w8.y), bf16_hi(w8.y),
                                     bf16_lo(w8.z), bf16_hi(w8.z), bf16_lo(w8.w), bf16_hi(w8.w)};
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
-                    if (m < M) {
-                        const float* xr = X + (int64_t)m * ldx + k;
-                        const float4 xa = *reinterpret_cast<const float4*>(xr);
-                        const float4 xb = *reinterpret_cast<const float4*>(xr + 4);
-                        c[m] = __builtin_fmaf(xa.x, w[0], c[m]);
-                        c[m] = __builtin_fmaf(xa.y, w[1], c[m]);
-                        c[m] = __builtin_fmaf(xa.z, w[2], c[m]);
-                        c[m] = __builtin_fmaf(xa.w, w[3], c[m]);
-                        c[m] = __builtin_fmaf(xb.x, w[4], c[m]);
-                        c[m] = __builtin_fmaf(xb.y, w[5], c[m]);
-                        c[m] = __builtin_fmaf(xb.z, w[6], c[m]);
-                        c[m] = __builtin_fmaf(xb.w, w[7], c[m]);
-                    }
+                    const float4 xa = *reinterpret_cast<const float4*>(&Xl[m][sl][8 * j]);
+                    const float4 xb = *reinterpret_cast<const float4*>(&Xl[m][sl][8 * j + 4]);
+                    c[m] = __builtin_fmaf(xa.x, w[0], c[m]);
+                    c[m] = __builtin_fmaf(xa.y, w[1], c[m]);
+                    c[m] = __builtin_fmaf(xa.z, w[2], c[m]);
+                    c[m] = __builtin_fmaf(xa.w, w[3], c[m]);
+                    c[m] = __builtin_fmaf(xb.x, w[4], c[m]);
+                    c[m] = __builtin_fmaf(xb.y, w[5], c[m]);
+                    c[m] = __builtin_fmaf(xb.z, w[6], c[m]);
+                    c[m] = __builtin_fmaf(xb.w, w[7], c[m]);
+                }
+            }
+        } else {
+            for (int j = 0; j < nk / 8; ++j) {
+                const uint4 w8 = *reinterpret_cast<const uint4*>(wseg + 16 * j);
+                const float w[8] = {bf16_lo(w8.x), bf16_hi(w8.x), bf16_lo(w8.y), bf16_hi(w8.y),
+                                    bf16_lo(w8.z), bf16_hi(w8.z), bf16_lo(w8.w), bf16_hi(w8.w)};
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) c[m] = __builtin_fmaf(Xl[m][sl][8 * j + e], w[e], c[m]);
                 }
             }
         }
+        if (p == KS / PH - 1) {
 #pragma unroll
-        for (int m = 0; m < MB; ++m) part[(s * MB + m) * SK_ROWS + nl] = c[m];
+            for (int m = 0; m < MB; ++m) part[sl][m][nl] = c[m];
+            __syncthreads();
+            if (folder) {
+                for (int j = 0; j < SK_LANES; ++j) {
+                    const int sj = sg + j;
+                    if (sj < S) T = (sj == 0) ? part[j][fm][fr] : T + part[j][fm][fr];
+                }
+            }
+        }
     }
-    __syncthreads();
-    // fold: one thread per (m, weight row), slices ascending
-    for (int o = tid; o < MB * SK_ROWS; o += 256) {
-        const int m = o / SK_ROWS, r = o % SK_ROWS;
-        const int gn = blockIdx.x * SK_ROWS + r;
-        if (m >= M || gn >= N) continue;
-        float T = part[(0 * MB + m) * SK_ROWS + r];
-        for (int s = 1; s < S; ++s) T = T + part[(s * MB + m) * SK_ROWS + r];
-        if (R) T = R[(int64_t)m * ldr + gn] + T;
-        Y[(int64_t)m * ldy + gn] = T;
+    if (folder) {
+        const int gn = n0 + fr;
+        if (fm < M && gn < N) {
+            float y = T;
+            if (R) y = R[(int64_t)fm * ldr + gn] + y;
+            Y[(int64_t)fm * ldy + gn] = y;
+        }
     }
 }
 
@@ -275,10 +354,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
 
 template <int MB, int ROLE>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
-    const int S = (a.K + KS - 1) / KS;
-    const size_t lds = sizeof(float) * (size_t)S * MB * SK_ROWS;
     dim3 grid((a.N + SK_ROWS - 1) / SK_ROWS);
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE>), grid, dim3(256), lds, st,
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE>), grid, dim3(256), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
 }
@@ -286,8 +363,7 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 int64_t gemm_skinny_max_k() {
-    // LDS partials: S * 16 * 16 floats must fit in 64 KiB of dynamic LDS.
-    return (int64_t)KS * (65536 / (int)(sizeof(float) * 16 * SK_ROWS));
+    return (int64_t)1 << 30;   // slices are folded group by group: no K limit
 }
 
 template <int ROLE>
