@@ -38,32 +38,32 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 // Matrix-core prefill.  v_mfma_f32_16x16x4_f32 advances each output of a 16 x 16 tile by
 // four fused multiply-adds in k order, so both contractions keep their sequential order:
 // the scores over d = 0..127 and the PV sums over keys in ascending j.
+//
+// Operands are arranged so that the scores never leave registers:
+//   scores  S^T = K Q^T:  A = K tile (lane (g, r) supplies key 16t + pi(r), d = 4s + g),
+//           B = Q^T (lane (g, r) supplies row r, d = 4s + g); with pi(i) = 4 (i % 4) + i / 4
+//           lane (g, r) receives, in register v, the score of row r with key 16t + 4v + g;
+//   PV      O^T = V^T P^T: step s = 4t + u covers keys 16t + 4u .. 16t + 4u + 3; its B operand
+//           for lane (g, r) is P[row r][key 16t + 4u + g] -- exactly register u of the
+//           score tile t that lane already holds; A = V^T (lane (g, r) supplies key 4s + g,
+//           d = 16 dt + r); lane (g, r) accumulates o[row r][d = 16 dt + 4g + v];
+//   l       the same B with an all-ones A: fma(1, p, l) = l + p, one rounding per key.
 // Workgroup: 256 threads = 4 wavefronts over BQ = 64 consecutive query rows of one (b, h);
 // wavefront w owns rows 16w .. 16w + 15.  Per 256-key chunk:
-//   1. scores: K staged through LDS in 64-key sub-blocks; 16 key tiles x 32 MFMA steps, all
-//      256 scores of the chunk kept in registers (lane (g, r) holds rows 4g..4g+3 of key
-//      column r of every key tile);
-//   2. chunk max over the row's keys <= i (16-lane shuffles), p = exp_f(s - m_c);
-//   3. PV: p re-laid out through LDS, V staged row-major; MFMA over keys below the first
-//      multiple-of-4 boundary that every row of the wavefront can see; l_c runs on the same
-//      instruction with an all-ones operand (fma(p, 1, l) = l + p, one rounding); the keys
-//      from there to each row's own i (at most 19) continue on the VALU, ascending, so
-//      masked keys are skipped rather than added as zeros;
-//   4. merge into the running (m, l, o) exactly as the decode merge kernel does.
+//   1. scores for the chunk (K streamed through double-buffered LDS in 64-key sub-blocks,
+//      one sub-block of register prefetch); 16 key tiles kept in registers;
+//   2. row max over keys <= i (lane-local, then across the 4 lane groups), p = exp_f(s - m_c);
+//   3. PV on the matrix cores for keys below the first multiple-of-4 boundary that every
+//      row of the wavefront can see; the remaining causal triangle (at most 19 keys per row)
+//      continues on the VALU in ascending j from a small LDS copy of its p, so masked keys are
+//      skipped rather than added as zeros;
+//   4. merge into the running (m, l, o) with the same formulas as the decode merge kernel.
 constexpr int SB = 64;          // keys per LDS sub-block
-constexpr int KPAD = 4;
+constexpr int KLD = D + 4;      // K rows in LDS (d permuted: (d % 4) * 32 + d / 4)
+constexpr int VLD = D + 8;      // V rows in LDS (row-major)
+constexpr int TAIL = 32;        // LDS slots per row for the causal tail's p
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float rowmax16(float x) {
-    // maximum over the 16 lanes sharing lane >> 4 (max is order independent)
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        const float y = __shfl_xor(x, off);
-        x = (y > x) ? y : x;
-    }
-    return x;
-}
 
 template <int DT>
 __device__ __forceinline__ void load4(const void* base, int64_t off, float* v) {
@@ -78,11 +78,22 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float* v) {
 
 // Global -> register -> LDS staging of one 64-key sub-block of K or V (fp32 in LDS).
 // Thread t carries 8 groups of 4 consecutive d of rows (e / 32) for e = t + 256 i.
+// Rows at or beyond kend are read from row kend - 1 (always valid) and replaced by zeros.
 template <int DT>
 struct Stage {
     float4 v[8];
-    // rows at or beyond kend are read from row kend - 1 (always valid) and replaced by zeros
     __device__ __forceinline__ void load(const void* base, int64_t kvbase, int kb, int kend, int tid) {
+        if (kb + SB <= kend) {
+            // whole sub-block in range: row (tid >> 5) + 8 i, column 4 (tid & 31)
+            const int64_t off = kvbase + (int64_t)(kb + (tid >> 5)) * D + (tid & 31) * 4;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float t[4];
+                load4<DT>(base, off + (int64_t)(8 * i) * D, t);
+                v[i] = make_float4(t[0], t[1], t[2], t[3]);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = tid + 256 * i;
@@ -94,23 +105,21 @@ struct Stage {
             v[i] = in ? make_float4(t[0], t[1], t[2], t[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
-    // K layout: row jj, d permuted (d % 4) * 32 + d / 4 (a lane's 32 operands contiguous)
     __device__ __forceinline__ void store_k(float* KV, int tid) const {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = tid + 256 * i;
             const int jj = e >> 5, q = e & 31;
-            float* dst = KV + jj * (D + KPAD) + q;
+            float* dst = KV + jj * KLD + q;
             dst[0] = v[i].x; dst[32] = v[i].y; dst[64] = v[i].z; dst[96] = v[i].w;
         }
     }
-    // V layout: row-major [key][d]
     __device__ __forceinline__ void store_v(float* KV, int tid) const {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = tid + 256 * i;
             const int jj = e >> 5, d4 = (e & 31) * 4;
-            *reinterpret_cast<float4*>(KV + jj * (D + KPAD) + d4) = v[i];
+            *reinterpret_cast<float4*>(KV + jj * VLD + d4) = v[i];
         }
     }
 };
@@ -119,14 +128,13 @@ template <int DT>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
     int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O) {
-    // two K/V sub-block buffers; per-wavefront p of the whole chunk
-    // [16 rows][4 sub-blocks x 64 keys, keys permuted (j % 4) * 16 + j / 4 inside each]
-    __shared__ float KV[2][SB * (D + KPAD)];
-    __shared__ float Ps[4][16][CHUNK + KPAD];
+    __shared__ __attribute__((aligned(16))) float KV[2][SB * VLD];
+    __shared__ float Pt[4][16][TAIL];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, r = lane & 15;
+    const int pr = 4 * (r & 3) + (r >> 2);             // pi(r)
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int kvh = h / (Hq / Hkv);
     const int r0 = qb * BQ;
@@ -135,11 +143,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const int64_t kvbase = ((int64_t)b * Hkv + kvh) * Tmax * D;
     const int wrow0 = r0 + 16 * w;                      // first row (relative) of this wavefront
     const int i0 = q_start + wrow0;                     // its absolute position
-    int irow[4];                                        // the lane's output rows, clamped
-#pragma unroll
-    for (int v = 0; v < 4; ++v) irow[v] = min(i0 + 4 * g + v, imax);
+    const int irow = min(i0 + r, imax);                 // the lane's row, clamped
 
-    // Q fragments: lane (g, r) supplies Q[row r][d = 4s + g], s = 0..31
+    // Q^T operand: lane (g, r) supplies Q[row r][d = 4s + g], s = 0..31
     float qf[32];
     {
         const int qrow = min(wrow0 + r, Tq - 1);
@@ -153,16 +159,13 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     }
 
     f32x4 o[8];
-    float m[4], l[4];
+    float m = 0.0f, l = 0.0f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) { m[v] = 0.0f; l[v] = 0.0f; }
 
     const int clast = imax / CHUNK;
     Stage<DT> st;
     int buf = 0;
-    // prologue: chunk 0, K sub-block 0
     st.load(Kc, kvbase, 0, min(CHUNK, imax + 1), tid);
     st.store_k(KV[0], tid);
     __syncthreads();
@@ -172,42 +175,36 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         const int kend = min(kbase + CHUNK, imax + 1);         // keys some row of the block needs
         const int nsb = (kend - kbase + SB - 1) / SB;          // active sub-blocks (1..4)
         const int nkend = min(kbase + 2 * CHUNK, imax + 1);    // next chunk's key bound
-        // ------------------------------------------------------ 1. scores (stages K_0..K_nsb-1)
+        // ------------------------------------------------------ 1. scores
         f32x4 S[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sb = 0; sb < CHUNK / SB; ++sb) {
             if (sb < nsb) {
-                // prefetch the next stage: K_{sb+1}, or V_0 of this chunk
                 if (sb + 1 < nsb) st.load(Kc, kvbase, kbase + (sb + 1) * SB, kend, tid);
                 else st.load(Vc, kvbase, kbase, kend, tid);
                 const float* kvb = KV[buf];
                 if (kbase + sb * SB <= i0 + 15) {
-                    f32x4 acc[SB / 16];
-#pragma unroll
-                    for (int kt = 0; kt < SB / 16; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s4 = 0; s4 < 8; ++s4) {
                         float4 kk[SB / 16];
 #pragma unroll
                         for (int kt = 0; kt < SB / 16; ++kt)
-                            kk[kt] = *reinterpret_cast<const float4*>(kvb + (kt * 16 + r) * (D + KPAD) + g * 32 + 4 * s4);
+                            kk[kt] = *reinterpret_cast<const float4*>(kvb + (kt * 16 + pr) * KLD + g * 32 + 4 * s4);
 #pragma unroll
                         for (int kt = 0; kt < SB / 16; ++kt)
-                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 0], kk[kt].x, acc[kt], 0, 0, 0);
+                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].x, qf[4 * s4 + 0], S[sb * 4 + kt], 0, 0, 0);
 #pragma unroll
                         for (int kt = 0; kt < SB / 16; ++kt)
-                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 1], kk[kt].y, acc[kt], 0, 0, 0);
+                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].y, qf[4 * s4 + 1], S[sb * 4 + kt], 0, 0, 0);
 #pragma unroll
                         for (int kt = 0; kt < SB / 16; ++kt)
-                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 2], kk[kt].z, acc[kt], 0, 0, 0);
+                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].z, qf[4 * s4 + 2], S[sb * 4 + kt], 0, 0, 0);
 #pragma unroll
                         for (int kt = 0; kt < SB / 16; ++kt)
-                            acc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[4 * s4 + 3], kk[kt].w, acc[kt], 0, 0, 0);
+                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].w, qf[4 * s4 + 3], S[sb * 4 + kt], 0, 0, 0);
                     }
-#pragma unroll
-                    for (int kt = 0; kt < SB / 16; ++kt) S[sb * 4 + kt] = acc[kt];
                 }
                 if (sb + 1 < nsb) st.store_k(KV[buf ^ 1], tid);
                 else st.store_v(KV[buf ^ 1], tid);
@@ -216,36 +213,55 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             }
         }
         // ------------------------------------------------------ 2. chunk max and p
-        float mc[4];
-        bool ne[4];
+        // lane (g, r), register v of tile t: row r, key kbase + 16t + 4v + g
+        const bool ne = irow >= kbase;
+        const bool full = kbase + CHUNK <= i0;                 // every row sees the whole chunk
+        float mc = -__builtin_inff();
+        if (full) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            ne[v] = irow[v] >= kbase;
-            float x = -__builtin_inff();
+            for (int t = 0; t < 16; ++t)
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int j = kbase + t * 16 + r;
-                const float sv = S[t][v] * scale;
-                S[t][v] = sv;
-                if (j <= irow[v]) x = (sv > x) ? sv : x;
-            }
-            mc[v] = rowmax16(x);
+                for (int v = 0; v < 4; ++v) {
+                    const float sv = S[t][v] * scale;
+                    S[t][v] = sv;
+                    mc = (sv > mc) ? sv : mc;
+                }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int j = kbase + 16 * t + 4 * v + g;
+                    const float sv = S[t][v] * scale;
+                    S[t][v] = sv;
+                    if (j <= irow) mc = (sv > mc) ? sv : mc;
+                }
         }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int jj = (t & 3) * 16 + r;                   // key inside its sub-block
-            const int pj = (t >> 2) * SB + (jj & 3) * 16 + (jj >> 2);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int j = kbase + t * 16 + r;
-                Ps[w][4 * g + v][pj] = (j <= irow[v]) ? exp_f(S[t][v] - mc[v]) : 0.0f;
-            }
+        {
+            float y = __shfl_xor(mc, 16);
+            mc = (y > mc) ? y : mc;
+            y = __shfl_xor(mc, 32);
+            mc = (y > mc) ? y : mc;
         }
-        __syncthreads();
-        // ------------------------------------------------------ 3. PV and l (stages V_0..)
-        // keys [kbase, jv) go through the matrix cores for every row of the wavefront
         const int jspan = min(i0, kend) - kbase;
-        const int jv = kbase + ((jspan > 0 ? jspan : 0) & ~3);
+        const int jv = kbase + ((jspan > 0 ? jspan : 0) & ~3);   // matrix-core keys: [kbase, jv)
+        if (full) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) S[t][v] = exp_f(S[t][v] - mc);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int j = kbase + 16 * t + 4 * v + g;
+                    const float pv = (j <= irow) ? exp_f(S[t][v] - mc) : 0.0f;
+                    S[t][v] = pv;
+                    if (j >= jv && j < jv + TAIL) Pt[w][r][j - jv] = pv;
+                }
+        }
+        // ------------------------------------------------------ 3. PV and l
         f32x4 oc[8];
         f32x4 lc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -254,33 +270,48 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         for (int sb = 0; sb < CHUNK / SB; ++sb) {
             if (sb < nsb) {
                 const int kb = kbase + sb * SB;
-                // prefetch: V_{sb+1}, or the next chunk's K_0
                 const bool more = sb + 1 < nsb;
                 if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
                 else if (c < clast) st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
                 const float* kvb = KV[buf];
-                const int nsteps = max(0, min(SB, jv - kb)) >> 2;
-                const float* prow = &Ps[w][r][sb * SB + g * 16];
-                for (int s = 0; s < nsteps; ++s) {
-                    const float a = prow[s];
-                    const float* vr = kvb + (4 * s + g) * (D + KPAD) + r;
+                const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
+                if (nmk >= SB) {
 #pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        oc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, vr[t * 16], oc[t], 0, 0, 0);
-                    lc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, 1.0f, lc, 0, 0, 0);
-                }
-                // VALU continuation for keys [max(kb, jv), row's own i], ascending
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int j1 = min(kb + SB, irow[v] + 1);
-                    for (int j = max(kb, jv); j < j1; ++j) {
-                        const int jj = j - kb;
-                        const float pv = Ps[w][4 * g + v][sb * SB + (jj & 3) * 16 + (jj >> 2)];
-                        lc[v] = lc[v] + pv;
+                    for (int s = 0; s < SB / 4; ++s) {
+                        const float bp = S[sb * 4 + (s >> 2)][s & 3];
+                        const float* vr = kvb + (4 * s + g) * VLD + r;
 #pragma unroll
                         for (int t = 0; t < 8; ++t)
-                            oc[t][v] = __builtin_fmaf(pv, kvb[jj * (D + KPAD) + t * 16 + r], oc[t][v]);
+                            oc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * t], bp, oc[t], 0, 0, 0);
+                        lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
                     }
+                } else if (nmk > 0) {
+#pragma unroll
+                    for (int s = 0; s < SB / 4; ++s) {
+                        if (4 * s < nmk) {
+                            const float bp = S[sb * 4 + (s >> 2)][s & 3];
+                            const float* vr = kvb + (4 * s + g) * VLD + r;
+#pragma unroll
+                            for (int t = 0; t < 8; ++t)
+                                oc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * t], bp, oc[t], 0, 0, 0);
+                            lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
+                        }
+                    }
+                }
+                // VALU continuation for keys [max(kb, jv), i], ascending (row r)
+                const int j1 = min(kb + SB, irow + 1);
+                for (int j = max(kb, jv); j < j1; ++j) {
+                    const float pv = Pt[w][r][j - jv];
+                    const float* vr = kvb + (j - kb) * VLD + 4 * g;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        const float4 vv = *reinterpret_cast<const float4*>(vr + 16 * t);
+                        oc[t][0] = __builtin_fmaf(pv, vv.x, oc[t][0]);
+                        oc[t][1] = __builtin_fmaf(pv, vv.y, oc[t][1]);
+                        oc[t][2] = __builtin_fmaf(pv, vv.z, oc[t][2]);
+                        oc[t][3] = __builtin_fmaf(pv, vv.w, oc[t][3]);
+                    }
+                    lc[0] = lc[0] + pv;
                 }
                 if (more) st.store_v(KV[buf ^ 1], tid);
                 else if (c < clast) st.store_k(KV[buf ^ 1], tid);
@@ -289,32 +320,34 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             }
         }
         // ------------------------------------------------------ 4. merge
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            if (!ne[v]) continue;
+        if (ne) {
             if (c == 0) {
-                m[v] = mc[v];
-                l[v] = lc[v];
+                m = mc;
+                l = lc[0];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) o[t][v] = oc[t][v];
+                for (int t = 0; t < 8; ++t) o[t] = oc[t];
             } else {
-                const float mn = (mc[v] > m[v]) ? mc[v] : m[v];
-                const float al = exp_f(m[v] - mn), be = exp_f(mc[v] - mn);
-                l[v] = (l[v] * al) + (lc[v] * be);
+                const float mn = (mc > m) ? mc : m;
+                const float al = exp_f(m - mn), be = exp_f(mc - mn);
+                l = (l * al) + (lc[0] * be);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) o[t][v] = (o[t][v] * al) + (oc[t][v] * be);
-                m[v] = mn;
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[t][v] = (o[t][v] * al) + (oc[t][v] * be);
+                m = mn;
             }
         }
     }
     // ------------------------------------------------------------------ output
+    const int rel = wrow0 + r;
+    if (rel < r0 + nrows) {
+        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D + 4 * g;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int rel = wrow0 + 4 * g + v;
-        if (rel >= r0 + nrows) continue;
-        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) out[t * 16 + r] = o[t][v] / l[v];
+        for (int t = 0; t < 8; ++t) {
+            float4 y;
+            y.x = o[t][0] / l; y.y = o[t][1] / l; y.z = o[t][2] / l; y.w = o[t][3] / l;
+            *reinterpret_cast<float4*>(out + 16 * t) = y;
+        }
     }
 }
 
