@@ -63,25 +63,50 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const int g = lane >> 4, r = lane & 15;
     const int wm0 = (wv >> 1) * WM, wn0 = (wv & 1) * WN;
 
+    // Per-thread source rows (clamped into range, with validity flags) computed once; each
+    // tile advances the pointers by BK.  Elements outside M x K or N x K load as zeros.
     float4 xr[XV];
     uint4 wr[WV];
+    const float* xp[XV];
+    const uint16_t* wp[WV];
+    bool xin[XV], win[WV];
+#pragma unroll
+    for (int i = 0; i < XV; ++i) {
+        const int idx = tid + i * 256;
+        const int row = idx / (BK / 4), q = idx % (BK / 4);
+        xin[i] = m0 + row < M;
+        xp[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + 4 * q;
+    }
+#pragma unroll
+    for (int i = 0; i < WV; ++i) {
+        const int idx = tid + i * 256;
+        const int row = idx / (BK / 8), o = idx % (BK / 8);
+        win[i] = n0 + row < N;
+        wp[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + 8 * o;
+    }
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
     auto load_tile = [&](int k0) {
+        if (interior && k0 + BK <= K) {
+#pragma unroll
+            for (int i = 0; i < XV; ++i) xr[i] = *reinterpret_cast<const float4*>(xp[i] + k0);
+#pragma unroll
+            for (int i = 0; i < WV; ++i) wr[i] = *reinterpret_cast<const uint4*>(wp[i] + k0);
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
-            const int idx = tid + i * 256;
-            const int row = idx / (BK / 4), q = idx % (BK / 4);
-            const int gm = m0 + row, gk = k0 + 4 * q;
-            const bool in = gm < M && gk < K;   // outside: read a valid element, use zeros
-            const float4 t = *reinterpret_cast<const float4*>(X + (int64_t)min(gm, M - 1) * ldx + min(gk, K - 4));
+            const int q = (tid + i * 256) % (BK / 4);
+            const int gk = k0 + 4 * q;
+            const bool in = xin[i] && gk < K;
+            const float4 t = *reinterpret_cast<const float4*>(xp[i] + min(k0, K - 4 - 4 * q));
             xr[i] = in ? t : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
-            const int idx = tid + i * 256;
-            const int row = idx / (BK / 8), o = idx % (BK / 8);
-            const int gn = n0 + row, gk = k0 + 8 * o;
-            const bool in = gn < N && gk < K;
-            const uint4 t = *reinterpret_cast<const uint4*>(W + (int64_t)min(gn, N - 1) * ldw + min(gk, K - 8));
+            const int o = (tid + i * 256) % (BK / 8);
+            const int gk = k0 + 8 * o;
+            const bool in = win[i] && gk < K;
+            const uint4 t = *reinterpret_cast<const uint4*>(wp[i] + min(k0, K - 8 - 8 * o));
             wr[i] = in ? t : make_uint4(0u, 0u, 0u, 0u);
         }
     };
@@ -187,14 +212,15 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int gm = m0 + wm0 + i * 16 + 4 * g + v;
-            if (gm >= M) continue;
+            if (!interior && gm >= M) continue;
+            float* yrow = Y + (int64_t)gm * ldy + n0 + wn0 + r;
+            const float* rrow = R ? R + (int64_t)gm * ldr + n0 + wn0 + r : nullptr;
 #pragma unroll
             for (int j = 0; j < TJ; ++j) {
-                const int gn = n0 + wn0 + j * 16 + r;
-                if (gn >= N) continue;
+                if (!interior && n0 + wn0 + j * 16 + r >= N) continue;
                 float y = T[i][j][v];
-                if (R) y = R[(int64_t)gm * ldr + gn] + y;
-                Y[(int64_t)gm * ldy + gn] = y;
+                if (rrow) y = rrow[j * 16] + y;
+                yrow[j * 16] = y;
             }
         }
 }
