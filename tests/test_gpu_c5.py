@@ -1,0 +1,94 @@
+"""Full-size decoder (4 layers, hidden 4096, 32/8 heads of 128, FFN 14336, vocab 128256,
+random init, BF16 weights, FP32 compute and KV cache): bitwise equal to the oracle where the
+oracle can run, and bitwise self-consistent across batch sizes, token blocks and prefill vs
+token-by-token decode up to a 32k context."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import assert_bitwise, host, i32, requires_gpu, say
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+KEYS = ("logprob", "margin", "top1", "top2", "recomputed")
+TMAX = 32768
+
+
+@pytest.fixture(scope="module")
+def c5():
+    say("c5 model generation")
+    model = synth.decoder_model(synth.C5, TMAX)
+    toks = synth.tokens(synth.SEEDS["c5_tok"], 3, TMAX, synth.C5["vocab"])
+    return model, toks
+
+
+@pytest.fixture(scope="module")
+def dec(c5):
+    from invariant_numerics_amd.decoder import Decoder
+    say("c5 decoder upload")
+    return Decoder(c5[0], batch=3, tmax=TMAX)
+
+
+def reset(d):
+    for k, v in zip(d.kc, d.vc):
+        k.zero_()
+        v.zero_()
+
+
+def test_c5_matches_oracle_short(orc, c5, dec):
+    """Every scored position of a 12-token sequence, bitwise equal to the oracle."""
+    model, toks = c5
+    say("c5 oracle 12 tokens")
+    reset(dec)
+    got = {k: host(v)[0] for k, v in dec.prefill(i32(toks[:1, :12])).items()}
+    want = orc.decoder(toks[0, :12], model)
+    for k in KEYS:
+        assert_bitwise(got[k], want[k], k)
+
+
+def test_c5_prefill_decode_batch_and_blocks(c5, dec):
+    """T = 300 (two KV chunks): 3 sequences prefilled in token blocks of 128 equal
+    (a) one sequence prefilled in one block, (b) token-by-token decode of all three."""
+    import torch
+    _, toks = c5
+    T = 300
+    td = i32(toks[:, :T])
+    say("c5 prefill B=3 block 128")
+    reset(dec)
+    pre = {k: host(v) for k, v in dec.prefill(td, block=128).items()}
+    say("c5 prefill B=1 block 4096")
+    reset(dec)
+    one = {k: host(v) for k, v in dec.prefill(td[2:3].contiguous(), block=4096).items()}
+    for k in KEYS:
+        assert_bitwise(one[k][0], pre[k][2], "batch/block %s" % k)
+    say("c5 token-by-token decode")
+    reset(dec)
+    outs = {k: [] for k in KEYS}
+    for t in range(T - 1):
+        pos = torch.full((3,), t, dtype=torch.int32, device="cuda")
+        r = dec.decode_step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
+        for k in KEYS:
+            outs[k].append(r[k])
+    for k in KEYS:
+        assert_bitwise(host(torch.stack(outs[k], dim=1)), pre[k], "prefill vs decode %s" % k)
+
+
+def test_c5_32k_prefill_equals_decode_tail(c5, dec):
+    """32k context: full prefill vs prefill of the first 32752 tokens followed by 15
+    decode steps, at the last 15 scored positions."""
+    import torch
+    _, toks = c5
+    td = i32(toks[:1])
+    say("c5 32k full prefill")
+    reset(dec)
+    full = {k: host(v)[0] for k, v in dec.prefill(td, block=4096).items()}
+    assert 0.1 < full["recomputed"].mean() < 0.6
+    p0 = TMAX - 16
+    say("c5 32k prefill", p0 + 1, "then decode")
+    reset(dec)
+    dec.prefill(td[:, :p0 + 1].contiguous(), block=4096)
+    for t in range(p0, TMAX - 1):
+        pos = torch.full((1,), t, dtype=torch.int32, device="cuda")
+        r = dec.decode_step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
+        for k in KEYS:
+            assert_bitwise(host(r[k]), full[k][t:t + 1], "position %d %s" % (t, k))
