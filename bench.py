@@ -116,6 +116,7 @@ def main():
 
     # ---------------------------------------------------------------- bitwise checks
     bitwise = {}
+    decode = None
     if not args.no_check:
         keys = ("logprob", "margin", "top1", "top2", "recomputed")
 
@@ -125,7 +126,9 @@ def main():
             return (a == b).float().mean().item()
 
         bitwise["repeat_steps"] = min(rate(outs[0][k], outs[-1][k]) for k in keys)
-        # prefill vs token-by-token decode on the last positions of the long context
+        # prefill vs token-by-token decode on the last positions of the long context; the
+        # decode steps are also timed (HBM-bound path: every weight byte and the whole KV
+        # cache are read once per step)
         ndec = min(16, T - 1)
         p0 = T - 1 - ndec
         log("decode check: prefill %d tokens, then %d decode steps" % (p0, ndec))
@@ -136,13 +139,39 @@ def main():
         dd.gemm_events = None
         if p0 > 0:
             dd.prefill(td[:, :p0 + 1].contiguous(), block=args.block)
+        gstep = dd.decode_graph(B)      # one decode step captured as a HIP graph
         agree = []
+        step_s = []
+        step_bytes = []
+        H, F, V, L = cfg["hidden"], cfg["ffn"], cfg["vocab"], cfg["layers"]
+        QKV = (cfg["hq"] + 2 * cfg["hkv"]) * cfg["d"]
+        body_w = L * 2 * (QKV * H + H * cfg["hq"] * cfg["d"] + 2 * F * H + H * F)
+        head_w = 2 * V * H
         for t in range(p0, T - 1):
             pos = torch.full((B,), t, dtype=torch.int32, device=dev)
-            r = dd.decode_step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
+            tok_t, tgt_t = td[:, t].contiguous(), td[:, t + 1].contiguous()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            r = gstep(tok_t, pos, tgt_t)
+            torch.cuda.synchronize()
+            step_s.append(time.perf_counter() - t1)
+            kv = L * 2 * cfg["hkv"] * (t + 1) * cfg["d"] * 4 * B
+            nrec = int(r["recomputed"].sum().item())
+            step_bytes.append(body_w + head_w * (2 if nrec else 1) + kv)
             agree.append(min(rate(r[k], outs[-1][k][:, t]) for k in keys))
         bitwise["prefill_vs_decode"] = float(np.mean(agree))
         bitwise["prefill_vs_decode_positions"] = [p0, T - 2]
+        # drop the first step (first touch of the decode path)
+        ds = np.array(step_s[1:]) if len(step_s) > 1 else np.array(step_s)
+        db = np.array(step_bytes[1:]) if len(step_bytes) > 1 else np.array(step_bytes)
+        gbs = float(db.sum() / ds.sum()) / 1e9
+        decode = dict(context=p0, batch=B, steps=int(len(ds)), ms_per_step=round(float(ds.mean()) * 1e3, 3),
+                      tokens_per_s=round(B / float(ds.mean()), 2),
+                      algorithmic_bytes_per_step=float(db.mean()),
+                      hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                      note="host-timed whole decode step replayed from a HIP graph (all layers + LM "
+                           "head incl. recompute pass); bytes = BF16 weights + FP32 KV cache read once "
+                           "(+ second vocabulary pass when a row is recomputed)")
         del dd
 
     # ---------------------------------------------------------------- CPU baseline
@@ -183,7 +212,7 @@ def main():
                     q_heads=cfg["hq"], kv_heads=cfg["hkv"], head_dim=cfg["d"], ffn=cfg["ffn"],
                     vocab=cfg["vocab"], batch=B, seq_len=T, token_block=args.block, tau=0.1,
                     weights="bf16 storage, fp32 compute", recomputed_fraction=round(recomputed, 4)),
-        roofline=roof, cpu_baseline=cpu, bitwise=bitwise)
+        roofline=roof, cpu_baseline=cpu, bitwise=bitwise, decode=decode)
     print(json.dumps(line), flush=True)
 
 

@@ -136,6 +136,7 @@ size_t inv_attention_decode_workspace_bytes(int64_t B, int64_t Tmax, int64_t Hq,
  * cache is not read).  O: FP32 [B, Hq, D].
  * One workgroup per (b, kv head, chunk) writes the chunk partial (m_c, l_c, o_c) into the
  * workspace; a second kernel folds them per (b, q head) in ascending chunk order.
+ * Tmax <= 1,048,576 (4096 chunks), else INV_ERR_UNSUPPORTED.
  * ------------------------------------------------------------------------------------ */
 int inv_attention_decode(int dtype, const void* Q, const void* Kc, const void* Vc,
                          const int32_t* pos, int64_t B, int64_t Tmax,

@@ -105,6 +105,7 @@ int inv_attention_decode(int dtype, const void* Q, const void* Kc, const void* V
     if (!pos) return INV_ERR_NULL;
     int st = check_attn(dtype, Q, Kc, Vc, O, B, 1, 0, Tmax, Hq, Hkv, D);
     if (st != INV_OK) return st;
+    if (Tmax > (int64_t)4096 * CHUNK) return INV_ERR_UNSUPPORTED;   // merge keeps <= 4096 chunks
     if (!ws || ws_bytes < inv_attention_decode_workspace_bytes(B, Tmax, Hq, D)) return INV_ERR_WORKSPACE;
     if (!al16(ws)) return INV_ERR_ALIGN;
     AttnArgs a{dtype, Q, Kc, Vc, (int)B, 1, 0, (int)Tmax, (int)Hq, (int)Hkv, (int)D, scale, O};

@@ -352,15 +352,27 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 }
 
 // ------------------------------------------------------------------- decode --
-// Workgroup: one (b, kv head g, chunk c); 256 threads, one key per thread for the scores;
-// the G = Hq / Hkv query heads that share kv head g are done together.
+// attn_decode_partial_kernel: one workgroup per (b, kv head g, chunk c), the G = Hq / Hkv
+// query heads of g together.  The chunk's keys and values stream through LDS in halves of
+// 128 keys with coalesced 16-byte loads (rows padded to 129 floats so a thread's row walk is
+// bank-conflict free).  Per head: s_j = dot_KS(q, k_j) * scale (thread j runs key j's chain
+// over d ascending), m_c = max, p_j = exp_f(s_j - m_c), then thread (head, d) runs
+// o_c[d] = fma(p_j, v_j[d], o_c[d]) and l_c = l_c + p_j for j ascending.
+// attn_decode_merge_kernel: per (b, q head), folds the chunk partials in ascending order,
+// m' = max(m, m_c), a = exp_f(m - m'), b = exp_f(m_c - m'), l = l a + l_c b, o = o a + o_c b.
+// The running maximum is scanned by one thread and every chunk's (a, b) pair is then
+// evaluated in parallel -- the same values the sequential loop computes -- so the 128
+// threads (one per d) only run the fold itself.
 constexpr int GMAX = 16;
+constexpr int DH = 128;              // keys per LDS half-chunk
+constexpr int DLD = D + 1;           // padded LDS row
 
 template <int DT>
 __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
     const int32_t* __restrict__ pos, int Tmax, int Hq, int Hkv, float scale, int nchunks,
     float* __restrict__ ws) {
+    __shared__ float KVs[DH * DLD];
     __shared__ float Qs[GMAX][D];
     __shared__ float Ps[GMAX][CHUNK];
     __shared__ float Ms[GMAX];
@@ -370,46 +382,58 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
     if (p < 0 || p >= Tmax) return;             // invalid position: the merge writes NaN
     const int kbase = c * CHUNK;
     if (kbase > p) return;                      // empty chunk: never folded
-    const int jlast = min(kbase + CHUNK - 1, p);
+    const int nk = min(CHUNK, p + 1 - kbase);   // keys of this chunk for this row
     const int tid = threadIdx.x;
     const int64_t kvbase = ((int64_t)b * Hkv + g) * Tmax * D;
 
     for (int e = tid; e < G * (D / 4); e += 256) {
         const int hh = e / (D / 4), d4 = (e % (D / 4)) * 4;
         float v[4];
-        load_row4<DT>(Q, ((int64_t)b * Hq + g * G + hh) * D + d4, v);
+        load4<DT>(Q, ((int64_t)b * Hq + g * G + hh) * D + d4, v);
         Qs[hh][d4 + 0] = v[0]; Qs[hh][d4 + 1] = v[1]; Qs[hh][d4 + 2] = v[2]; Qs[hh][d4 + 3] = v[3];
     }
-    __syncthreads();
-    const int j = kbase + tid;
-    if (j <= jlast) {
-        float acc[GMAX];
+    // stage rows [h0, h0 + n) of K or V (coalesced 16-byte loads) into KVs
+    // (all 16 loads of a thread are issued before any of its LDS stores)
+    auto stage = [&](const void* base, int h0, int n) {
+        constexpr int NL = DH * (D / 4) / 256;
+        float v[NL][4];
 #pragma unroll
-        for (int hh = 0; hh < GMAX; ++hh) acc[hh] = 0.0f;
-        for (int d = 0; d < D; d += 4) {
-            float kv[4];
-            load_row4<DT>(Kc, kvbase + (int64_t)j * D + d, kv);
-#pragma unroll
-            for (int hh = 0; hh < GMAX; ++hh) {
-                if (hh < G) {
-                    acc[hh] = __builtin_fmaf(Qs[hh][d + 0], kv[0], acc[hh]);
-                    acc[hh] = __builtin_fmaf(Qs[hh][d + 1], kv[1], acc[hh]);
-                    acc[hh] = __builtin_fmaf(Qs[hh][d + 2], kv[2], acc[hh]);
-                    acc[hh] = __builtin_fmaf(Qs[hh][d + 3], kv[3], acc[hh]);
-                }
-            }
+        for (int i = 0; i < NL; ++i) {
+            const int e = tid + 256 * i;
+            const int jj = e >> 5, d4 = (e & 31) * 4;
+            const int row = kbase + h0 + min(jj, n - 1);        // rows past n: any valid row
+            load4<DT>(base, kvbase + (int64_t)row * D + d4, v[i]);
         }
 #pragma unroll
-        for (int hh = 0; hh < GMAX; ++hh)
-            if (hh < G) Ps[hh][tid] = acc[hh] * scale;
+        for (int i = 0; i < NL; ++i) {
+            const int e = tid + 256 * i;
+            const int jj = e >> 5, d4 = (e & 31) * 4;
+            float* dst = KVs + jj * DLD + d4;
+            dst[0] = v[i][0]; dst[1] = v[i][1]; dst[2] = v[i][2]; dst[3] = v[i][3];
+        }
+    };
+    // ---- scores
+    for (int h0 = 0; h0 < nk; h0 += DH) {
+        const int n = min(DH, nk - h0);
+        __syncthreads();
+        stage(Kc, h0, n);
+        __syncthreads();
+        for (int e = tid; e < G * DH; e += 256) {
+            const int hh = e / DH, jj = e % DH;
+            if (jj < n) {
+                const float* kr = KVs + jj * DLD;
+                float acc = 0.0f;
+                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(Qs[hh][d], kr[d], acc);
+                Ps[hh][h0 + jj] = acc * scale;
+            }
+        }
     }
     __syncthreads();
-    // chunk max per head: wavefront w reduces head w, w+4, ...
+    // ---- chunk max per head (wavefront w reduces heads w, w + 4, ...), then p
     const int lane = tid % 64, w = tid / 64;
-    const int nk = jlast - kbase + 1;
     for (int hh = w; hh < G; hh += 4) {
         float mc = -__builtin_inff();
-        for (int jj = lane; jj < nk; jj += 64) { const float s = Ps[hh][jj]; mc = (s > mc) ? s : mc; }
+        for (int jj = lane; jj < nk; jj += 64) { const float sv = Ps[hh][jj]; mc = (sv > mc) ? sv : mc; }
         for (int off = 32; off >= 1; off >>= 1) { const float t = __shfl_xor(mc, off); mc = (t > mc) ? t : mc; }
         if (lane == 0) Ms[hh] = mc;
     }
@@ -418,30 +442,51 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
         const int hh = e / nk, jj = e % nk;
         Ps[hh][jj] = exp_f(Ps[hh][jj] - Ms[hh]);
     }
-    __syncthreads();
-    // o_c[d] and l_c, keys ascending; thread owns (head, d) pairs
-    const int D2 = D + 2;
-    for (int e = tid; e < G * D; e += 256) {
-        const int hh = e / D, d = e % D;
-        float oc = 0.0f, lc = 0.0f;
-        for (int jj = 0; jj < nk; ++jj) {
-            const float pj = Ps[hh][jj];
-            float v;
-            if (DT == 1) v = reinterpret_cast<const float*>(Vc)[kvbase + (int64_t)(kbase + jj) * D + d];
-            else v = bf16_up(reinterpret_cast<const uint16_t*>(Vc)[kvbase + (int64_t)(kbase + jj) * D + d]);
-            oc = __builtin_fmaf(pj, v, oc);
-            lc = lc + pj;
+    // ---- o_c[d] and l_c, keys ascending; thread owns (head, d) pairs
+    float oc[GMAX / 2], lc[GMAX / 2];
+#pragma unroll
+    for (int u = 0; u < GMAX / 2; ++u) { oc[u] = 0.0f; lc[u] = 0.0f; }
+    for (int h0 = 0; h0 < nk; h0 += DH) {
+        const int n = min(DH, nk - h0);
+        __syncthreads();
+        stage(Vc, h0, n);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < GMAX / 2; ++u) {
+            const int e = tid + 256 * u;
+            if (e < G * D) {
+                const int hh = e / D, d = e % D;
+                float o = oc[u], l = lc[u];
+                for (int jj = 0; jj < n; ++jj) {
+                    const float pj = Ps[hh][h0 + jj];
+                    o = __builtin_fmaf(pj, KVs[jj * DLD + d], o);
+                    l = l + pj;
+                }
+                oc[u] = o;
+                lc[u] = l;
+            }
         }
-        float* dst = ws + (((int64_t)b * Hq + g * G + hh) * nchunks + c) * D2;
-        dst[2 + d] = oc;
-        if (d == 0) { dst[0] = Ms[hh]; dst[1] = lc; }
+    }
+    const int D2 = D + 2;
+#pragma unroll
+    for (int u = 0; u < GMAX / 2; ++u) {
+        const int e = tid + 256 * u;
+        if (e < G * D) {
+            const int hh = e / D, d = e % D;
+            float* dst = ws + (((int64_t)b * Hq + g * G + hh) * nchunks + c) * D2;
+            dst[2 + d] = oc[u];
+            if (d == 0) { dst[0] = Ms[hh]; dst[1] = lc[u]; }
+        }
     }
 }
+
+constexpr int MAXCH = 4096;   // chunks per merge workgroup held in LDS (Tmax <= 1M)
 
 __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* __restrict__ pos,
                                                                 int Hq, int Tmax, int nchunks,
                                                                 const float* __restrict__ ws,
                                                                 float* __restrict__ O) {
+    __shared__ float Mc[MAXCH], Lc[MAXCH], Al[MAXCH], Be[MAXCH], Mr[MAXCH];
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int p = pos[b];
     if (p < 0 || p >= Tmax) {
@@ -451,15 +496,36 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
     const int nc = p / CHUNK + 1;
     const int D2 = D + 2;
     const float* src = ws + ((int64_t)b * Hq + h) * nchunks * D2;
-    float m = src[0], l = src[1], o = src[2 + d];
-    for (int c = 1; c < nc; ++c) {
-        const float* s = src + (int64_t)c * D2;
-        const float mc = s[0], lc = s[1], oc = s[2 + d];
-        const float mn = (mc > m) ? mc : m;
-        const float a = exp_f(m - mn), bb = exp_f(mc - mn);
-        l = (l * a) + (lc * bb);
-        o = (o * a) + (oc * bb);
-        m = mn;
+    for (int c = d; c < nc; c += D) { Mc[c] = src[(int64_t)c * D2]; Lc[c] = src[(int64_t)c * D2 + 1]; }
+    __syncthreads();
+    if (d == 0) {                                 // running maximum, exactly as the fold takes it
+        float m = Mc[0];
+        Mr[0] = m;
+        for (int c = 1; c < nc; ++c) { const float mc = Mc[c]; m = (mc > m) ? mc : m; Mr[c] = m; }
+    }
+    __syncthreads();
+    for (int c = 1 + d; c < nc; c += D) {
+        Al[c] = exp_f(Mr[c - 1] - Mr[c]);
+        Be[c] = exp_f(Mc[c] - Mr[c]);
+    }
+    __syncthreads();
+    float l = Lc[0], o = src[2 + d];
+    int c = 1;
+    for (; c + 8 <= nc; c += 8) {
+        float oc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) oc[u] = src[(int64_t)(c + u) * D2 + 2 + d];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float a = Al[c + u], bb = Be[c + u];
+            l = (l * a) + (Lc[c + u] * bb);
+            o = (o * a) + (oc[u] * bb);
+        }
+    }
+    for (; c < nc; ++c) {
+        const float a = Al[c], bb = Be[c];
+        l = (l * a) + (Lc[c] * bb);
+        o = (o * a) + (src[(int64_t)c * D2 + 2 + d] * bb);
     }
     O[((int64_t)b * Hq + h) * D + d] = o / l;
 }

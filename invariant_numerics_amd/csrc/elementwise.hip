@@ -21,8 +21,20 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const float* __restrict__ X
     const int row = blockIdx.x;
     const int lane = threadIdx.x;
     const float* x = X + (int64_t)row * ldx;
-    for (int i = lane * 4; i < H; i += 256)
-        *reinterpret_cast<float4*>(xs + i) = *reinterpret_cast<const float4*>(x + i);
+    // stage the row: loads issued 8 at a time before their LDS stores
+    for (int i0 = lane * 4; i0 < H; i0 += 8 * 256) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * 256;
+            v[u] = *reinterpret_cast<const float4*>(x + (i < H ? i : 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * 256;
+            if (i < H) *reinterpret_cast<float4*>(xs + i) = v[u];
+        }
+    }
     __syncthreads();
     for (int s = lane; s < S; s += 64) {
         const int k0 = s * KS, k1 = min(H, k0 + KS);

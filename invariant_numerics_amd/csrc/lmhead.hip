@@ -4,8 +4,8 @@
 // Sequence on one stream, no host synchronisation:
 //   1. a_P = up(bf(h))                          (BF16 operands of the primary pass)
 //   2. z = fixed-order GEMM(a_P, W)             (FP32 sums, dot_KS order)
-//   3. row reduce (one workgroup per row): top-2, M = z_top1, S, lp, margin; outputs with
-//      recomputed = (margin < tau)
+//   3. row reduce (three kernels spread over rows x vocabulary groups): top-2, M = z_top1,
+//      S, lp, margin; outputs with recomputed = (margin < tau)
 //   4. compaction: flagged rows' indices (ascending) and a device-side count; their h
 //      rows are gathered into a dense buffer
 //   5. z = fixed-order GEMM(h_F, W) on the first `count` rows (count read on the device)
@@ -25,8 +25,7 @@ namespace invnum {
 
 namespace {
 
-constexpr int RED_THREADS = 256;
-constexpr int MAX_TILES = 1024;  // V <= 2^20
+constexpr int RED_THREADS = 256;   // 4 wavefronts: one per vocabulary tile of a group
 
 struct Top2 {
     float v1; int i1; float v2; int i2;
@@ -47,24 +46,29 @@ __device__ __forceinline__ void top2_merge(Top2& t, const Top2& o) {
     top2_push(t, o.v2, o.i2);
 }
 
-// mode 0: P pass over rows 0..B-1 (output row = row); mode 1: F pass over the first
-// *count rows of the compacted list (output row = idx[row]).
-__global__ __launch_bounds__(RED_THREADS) void lmhead_reduce_kernel(
-    const float* __restrict__ z, int V, const int32_t* __restrict__ target, float tau, int mode,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-    float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
-    int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
-    __shared__ float tileS[MAX_TILES];
+// Row reduction in three kernels, so a few rows still spread over the whole chip:
+//   top2_kernel   grid (groups of 4 tiles = 4096 entries, rows): each workgroup's top-2 of
+//                 its entries (order free: a total order on (value desc, index asc));
+//   tiles_kernel  same grid: merges the row's partial top-2 pairs (again order free) to get
+//                 M = z_top1, then one wavefront per tile of its group sums exp_f(z - M) in the
+//                 pinned lane order and combines the 64 lanes pairwise -> S_u;
+//   final_kernel  one thread per row: S = S_0, S = S + S_u ascending; lp; margin; flags.
+// mode 0: P pass over rows 0..B-1 (output row = row); mode 1: F pass over the first *count
+// rows of the compacted list (output row = idx[row]).
+constexpr int GROUP = 4;                 // tiles per workgroup
+constexpr int GV = GROUP * TV;           // vocabulary entries per workgroup
+
+__global__ __launch_bounds__(RED_THREADS) void lmhead_top2_kernel(
+    const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
+    Top2* __restrict__ part) {
     __shared__ Top2 wtop[RED_THREADS / 64];
-    const int row = blockIdx.x;
+    const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
     if (mode == 1 && row >= *count) return;
-    const int orow = mode == 1 ? idx[row] : row;
     const float* zr = z + (int64_t)row * V;
     const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
-
-    // ---- top-2
     Top2 t = {-__builtin_inff(), 0x7fffffff, -__builtin_inff(), 0x7fffffff};
-    for (int v = tid; v < V; v += RED_THREADS) top2_push(t, zr[v], v);
+    const int v0 = grp * GV, v1 = min(V, v0 + GV);
+    for (int v = v0 + tid; v < v1; v += RED_THREADS) top2_push(t, zr[v], v);
     for (int off = 32; off >= 1; off >>= 1) {
         Top2 o;
         o.v1 = __shfl_xor(t.v1, off); o.i1 = __shfl_xor(t.i1, off);
@@ -73,37 +77,73 @@ __global__ __launch_bounds__(RED_THREADS) void lmhead_reduce_kernel(
     }
     if (lane == 0) wtop[w] = t;
     __syncthreads();
-    t = wtop[0];
-    for (int k = 1; k < RED_THREADS / 64; ++k) top2_merge(t, wtop[k]);
-    const float M = zr[t.i1];
-
-    // ---- softmax denominator: wavefront w handles tiles w, w + 4, ...
-    const int ntiles = (V + TV - 1) / TV;
-    for (int u = w; u < ntiles; u += RED_THREADS / 64) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < TV / LW; ++j) {
-            const int v = u * TV + j * LW + lane;
-            if (v < V) acc = acc + exp_f(zr[v] - M);
-        }
-        // pairwise lane tree: a_l + a_{l+w} for w = 1, 2, 4, ..., 32
-#pragma unroll
-        for (int s = 1; s < LW; s <<= 1) acc = acc + __shfl_down(acc, s);
-        if (lane == 0) tileS[u] = acc;
-    }
-    __syncthreads();
     if (tid == 0) {
-        float S = tileS[0];
-        for (int u = 1; u < ntiles; ++u) S = S + tileS[u];
-        const int tg = target[orow];
-        const float lp = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
-        const float mg = M - zr[t.i2];
-        logprob[orow] = lp;
-        margin[orow] = mg;
-        top1[orow] = t.i1;
-        top2[orow] = t.i2;
-        recomputed[orow] = (uint8_t)(mode == 1 ? 1 : (mg < tau ? 1 : 0));
+        t = wtop[0];
+        for (int k = 1; k < RED_THREADS / 64; ++k) top2_merge(t, wtop[k]);
+        part[(int64_t)row * ngrp + grp] = t;
     }
+}
+
+// The row's top-2 from its partials.  Values that compare with nothing (NaN logits) leave
+// the sentinel index in place; such an index is replaced by the scan's starting choice
+// (top1 = 0, top2 = the lowest index != top1), so no index >= V ever reaches a load.
+__device__ __forceinline__ Top2 merged_top2(const Top2* __restrict__ part, int row, int ngrp, int V) {
+    Top2 t = part[(int64_t)row * ngrp];
+    for (int k = 1; k < ngrp; ++k) top2_merge(t, part[(int64_t)row * ngrp + k]);
+    if (t.i1 < 0 || t.i1 >= V) t.i1 = 0;
+    if (t.i2 < 0 || t.i2 >= V || t.i2 == t.i1) t.i2 = (t.i1 == 0) ? 1 : 0;
+    return t;
+}
+
+__global__ __launch_bounds__(RED_THREADS) void lmhead_tiles_kernel(
+    const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
+    const Top2* __restrict__ part, float* __restrict__ tileS) {
+    const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
+    if (mode == 1 && row >= *count) return;
+    const float* zr = z + (int64_t)row * V;
+    const Top2 t = merged_top2(part, row, ngrp, V);
+    const float M = zr[t.i1];
+    const int ntiles = (V + TV - 1) / TV;
+    const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+    const int u = grp * GROUP + w;                       // this wavefront's tile
+    if (u >= ntiles) return;
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < TV / LW; ++j) {
+        const int v = u * TV + j * LW + lane;
+        if (v < V) acc = acc + exp_f(zr[v] - M);
+    }
+    // pairwise lane tree: a_l + a_{l+w} for w = 1, 2, 4, ..., 32
+#pragma unroll
+    for (int s = 1; s < LW; s <<= 1) acc = acc + __shfl_down(acc, s);
+    if (lane == 0) tileS[(int64_t)row * ntiles + u] = acc;
+}
+
+__global__ void lmhead_final_kernel(
+    const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau, int mode,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, const Top2* __restrict__ part,
+    int ngrp, const float* __restrict__ tileS,
+    float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
+    int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= B) return;
+    if (mode == 1 && row >= *count) return;
+    const int orow = mode == 1 ? idx[row] : row;
+    const float* zr = z + (int64_t)row * V;
+    const Top2 t = merged_top2(part, row, ngrp, V);
+    const float M = zr[t.i1];
+    const int ntiles = (V + TV - 1) / TV;
+    const float* ts = tileS + (int64_t)row * ntiles;
+    float S = ts[0];
+    for (int u = 1; u < ntiles; ++u) S = S + ts[u];
+    const int tg = target[orow];
+    const float lp = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
+    const float mg = M - zr[t.i2];
+    logprob[orow] = lp;
+    margin[orow] = mg;
+    top1[orow] = t.i1;
+    top2[orow] = t.i2;
+    recomputed[orow] = (uint8_t)(mode == 1 ? 1 : (mg < tau ? 1 : 0));
 }
 
 // a_P[b, k] = up(bf(h[b, k]))
@@ -164,17 +204,35 @@ __global__ void gather_rows_kernel(const float* __restrict__ H, int K, int64_t l
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t a, z, idx, count, total;
+    size_t a, z, idx, count, part, tiles, total;
 };
 WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
     WsLayout L;
+    const int64_t ngrp = (V + GV - 1) / GV, ntiles = (V + TV - 1) / TV;
     size_t off = 0;
     L.a = off; off = align_up(off + sizeof(float) * (size_t)B * K);
     L.z = off; off = align_up(off + sizeof(float) * (size_t)B * V);
     L.idx = off; off = align_up(off + sizeof(int32_t) * (size_t)B);
     L.count = off; off = align_up(off + sizeof(int32_t));
+    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)B * ngrp);
+    L.tiles = off; off = align_up(off + sizeof(float) * (size_t)B * ntiles);
     L.total = off;
     return L;
+}
+
+hipError_t launch_reduce(const LmheadArgs& a, int mode, const float* Z, const int32_t* idx,
+                         const int32_t* count, Top2* part, float* tiles, hipStream_t st) {
+    const int ngrp = (a.V + GV - 1) / GV;
+    dim3 grid(ngrp, a.B);
+    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, part, tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(lmhead_final_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, Z, a.V, a.B, a.target,
+                       a.tau, mode, idx, count, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
+                       a.recomputed);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -188,6 +246,8 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     float* Z = reinterpret_cast<float*>(ws + L.z);
     int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
     int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+    Top2* part = reinterpret_cast<Top2*>(ws + L.part);
+    float* tiles = reinterpret_cast<float*>(ws + L.tiles);
     hipError_t e;
 
     int64_t n4 = (int64_t)a.B * (a.K / 4);
@@ -199,9 +259,7 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     GemmArgs ga{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, nullptr};
     if ((e = launch_gemm(ga, st, 1)) != hipSuccess) return e;
 
-    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(a.B), dim3(RED_THREADS), 0, st, Z, a.V, a.target,
-                       a.tau, 0, nullptr, nullptr, a.logprob, a.margin, a.top1, a.top2, a.recomputed);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_reduce(a, 0, Z, nullptr, nullptr, part, tiles, st)) != hipSuccess) return e;
 
     hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, a.recomputed, a.B, idx, count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -211,9 +269,7 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     GemmArgs gf{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, count};
     if ((e = launch_gemm(gf, st, 1)) != hipSuccess) return e;
 
-    hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(a.B), dim3(RED_THREADS), 0, st, Z, a.V, a.target,
-                       a.tau, 1, idx, count, a.logprob, a.margin, a.top1, a.top2, a.recomputed);
-    return hipGetLastError();
+    return launch_reduce(a, 1, Z, idx, count, part, tiles, st);
 }
 
 }  // namespace invnum

@@ -133,3 +133,35 @@ class Decoder:
 
         hn = self._body(tok, seq, pos, attend)
         return inv.inv_lmhead_logprob_top2(hn, self.whead, target, self.tau)
+
+    def decode_graph(self, B=None):
+        """Capture one decode step (batch B) in a HIP graph.  Returns step(tok, pos, target)
+        that copies the int32 [B] inputs into the graph's static buffers, replays it and returns
+        the graph's output tensors (valid until the next replay).  Every kernel of the step reads
+        token, position and target from device memory, and none of them issues a memset, so one
+        capture serves every position."""
+        B = self.batch if B is None else int(B)
+        st_tok = torch.zeros(B, dtype=torch.int32, device=self.dev)
+        # position -1 during warm-up: rope_kv_append skips rows outside the cache and decode
+        # attention reads nothing for them, so the warm-up leaves the KV cache untouched
+        st_pos = torch.full((B,), -1, dtype=torch.int32, device=self.dev)
+        st_tgt = torch.zeros(B, dtype=torch.int32, device=self.dev)
+        side = torch.cuda.Stream(device=self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            self.decode_step(st_tok, st_pos, st_tgt)          # warm-up outside the capture
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize(self.dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            st_out = self.decode_step(st_tok, st_pos, st_tgt)
+
+        def step(tok, pos, target):
+            st_tok.copy_(tok)
+            st_pos.copy_(pos)
+            st_tgt.copy_(target)
+            graph.replay()
+            return st_out
+
+        step.graph = graph
+        return step

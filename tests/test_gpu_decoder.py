@@ -96,3 +96,31 @@ def test_small_decoder_prefill_equals_decode_and_batch(orc, small):
             outs[k].append(host(r[k]))
     for k in KEYS:
         assert_bitwise(np.stack(outs[k], axis=1), pre[k], "prefill vs decode %s" % k)
+
+
+def test_small_decoder_graph_replays_equal_eager(small):
+    """One decode step captured in a graph and replayed at every position, with eager work
+    and synchronisations between replays: every replay bitwise equal to eager decode."""
+    from invariant_numerics_amd.decoder import Decoder
+    import torch
+    say("small decoder graph decode")
+    T = 280
+    toks = synth.tokens(9800, 2, T, synth.SMALL["vocab"])
+    td = i32(toks)
+    eager = Decoder(small, batch=2, tmax=320)
+    ref = []
+    for t in range(T - 1):
+        pos = torch.full((2,), t, dtype=torch.int32, device="cuda")
+        r = eager.decode_step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
+        ref.append({k: host(v) for k, v in r.items()})
+    gdec = Decoder(small, batch=2, tmax=320)
+    # capture after a prefill of the first 100 tokens: capturing must not disturb the cache
+    gdec.prefill(td[:, :101].contiguous(), block=64)
+    step = gdec.decode_graph()
+    for t in range(100, T - 1):
+        pos = torch.full((2,), t, dtype=torch.int32, device="cuda")
+        r = step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
+        got = {k: host(v) for k, v in r.items()}
+        _ = torch.randn(1000, device="cuda").sum().item()   # eager work between replays
+        for k in KEYS:
+            assert_bitwise(got[k], ref[t][k], "graph replay %d %s" % (t, k))

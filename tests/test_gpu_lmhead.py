@@ -98,3 +98,19 @@ def test_c4_margin_stress(orc):
     want = orc.lmhead(d["h"][rows], d["w"], d["target"][rows])
     check({k: v[rows] for k, v in got.items()}, want, "stress")
     assert got["recomputed"].mean() > 0.5
+
+
+def test_nan_rows_stay_in_bounds(orc):
+    """Rows whose logits are all NaN (NaN hidden state): no logit is orderable, so the top-2
+    takes the scan's starting choice (0, 1) and logprob is NaN; finite rows beside them are
+    unaffected.  (Regression: the reduction once indexed past the row in this case.)"""
+    say("lmhead NaN rows")
+    d = synth.c1_inputs(rows=4)
+    h = d["h"].copy()
+    h[1, :] = np.nan
+    got = run(h, d["w"], d["target"])
+    assert np.isnan(got["logprob"][1]) and got["top1"][1] == 0 and got["top2"][1] == 1
+    assert got["recomputed"][1] == 0
+    rows = [0, 2, 3]
+    want = orc.lmhead(d["h"][rows], d["w"], d["target"][rows])
+    check({k: v[rows] for k, v in got.items()}, want, "finite rows")
