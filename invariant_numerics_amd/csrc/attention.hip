@@ -353,29 +353,36 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
 
 // ------------------------------------------------------------------- decode --
 // attn_decode_partial_kernel: one workgroup per (b, kv head g, chunk c), the G = Hq / Hkv
-// query heads of g together.  The chunk's keys and values stream through LDS in halves of
-// 128 keys with coalesced 16-byte loads (rows padded to 129 floats so a thread's row walk is
-// bank-conflict free).  Per head: s_j = dot_KS(q, k_j) * scale (thread j runs key j's chain
-// over d ascending), m_c = max, p_j = exp_f(s_j - m_c), then thread (head, d) runs
-// o_c[d] = fma(p_j, v_j[d], o_c[d]) and l_c = l_c + p_j for j ascending.
+// query heads of g together (G <= GT, the template bound).  Thread j owns key j of the chunk
+// for the scores: s_j = dot_KS(q, k_j, 128) * scale runs its chain over d ascending with one
+// accumulator per head.  K streams through LDS in four 32-wide d slices of all 256 keys (row
+// segments of 128 bytes, rows padded to 33 floats so each thread's row walk is bank-conflict
+// free); the chain simply continues from one slice to the next.  Then per head m_c = max,
+// p_j = exp_f(s_j - m_c), and V streams through LDS in 64-key blocks while thread (head, d)
+// runs o_c[d] = fma(p_j, v_j[d], o_c[d]) and l_c = l_c + p_j for j ascending.  Every stage
+// is prefetched into registers one stage ahead; about 40 KB of LDS for G = 4 lets four
+// workgroups share a CU, so loads of one overlap the arithmetic of another.
 // attn_decode_merge_kernel: per (b, q head), folds the chunk partials in ascending order,
 // m' = max(m, m_c), a = exp_f(m - m'), b = exp_f(m_c - m'), l = l a + l_c b, o = o a + o_c b.
 // The running maximum is scanned by one thread and every chunk's (a, b) pair is then
 // evaluated in parallel -- the same values the sequential loop computes -- so the 128
 // threads (one per d) only run the fold itself.
 constexpr int GMAX = 16;
-constexpr int DH = 128;              // keys per LDS half-chunk
-constexpr int DLD = D + 1;           // padded LDS row
+constexpr int KSL = 32;               // d per K stage
+constexpr int KSLD = KSL + 1;         // padded K stage row
+constexpr int NKST = D / KSL;         // K stages
+constexpr int VKEYS = 64;             // keys per V stage
+constexpr int DBUF = CHUNK * KSLD;    // stage buffer (floats); >= VKEYS * D
 
-template <int DT>
+template <int DT, int GT>
 __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
     const int32_t* __restrict__ pos, int Tmax, int Hq, int Hkv, float scale, int nchunks,
     float* __restrict__ ws) {
-    __shared__ float KVs[DH * DLD];
-    __shared__ float Qs[GMAX][D];
-    __shared__ float Ps[GMAX][CHUNK];
-    __shared__ float Ms[GMAX];
+    __shared__ __attribute__((aligned(16))) float Buf[DBUF];
+    __shared__ __attribute__((aligned(16))) float Qs[GT][D];
+    __shared__ __attribute__((aligned(16))) float Ps[GT][CHUNK];
+    __shared__ float Ms[GT];
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int G = Hq / Hkv;
     const int p = pos[b];
@@ -383,6 +390,8 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
     const int kbase = c * CHUNK;
     if (kbase > p) return;                      // empty chunk: never folded
     const int nk = min(CHUNK, p + 1 - kbase);   // keys of this chunk for this row
+    const int nvs = (nk + VKEYS - 1) / VKEYS;   // V stages needed
+    const int nst = NKST + nvs;
     const int tid = threadIdx.x;
     const int64_t kvbase = ((int64_t)b * Hkv + g) * Tmax * D;
 
@@ -390,43 +399,77 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
         const int hh = e / (D / 4), d4 = (e % (D / 4)) * 4;
         float v[4];
         load4<DT>(Q, ((int64_t)b * Hq + g * G + hh) * D + d4, v);
-        Qs[hh][d4 + 0] = v[0]; Qs[hh][d4 + 1] = v[1]; Qs[hh][d4 + 2] = v[2]; Qs[hh][d4 + 3] = v[3];
+        *reinterpret_cast<float4*>(&Qs[hh][d4]) = make_float4(v[0], v[1], v[2], v[3]);
     }
-    // stage rows [h0, h0 + n) of K or V (coalesced 16-byte loads) into KVs
-    // (all 16 loads of a thread are issued before any of its LDS stores)
-    auto stage = [&](const void* base, int h0, int n) {
-        constexpr int NL = DH * (D / 4) / 256;
-        float v[NL][4];
+    // stage st < NKST: d slice [32 st, 32 st + 32) of keys 0..255 (rows past nk repeat row
+    // nk - 1, a valid row whose values are never used); stage NKST + v: keys [64 v, 64 v + 64)
+    float pre[8][4];
+    auto load_stage = [&](int st) {
+        if (st < NKST) {
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int e = tid + 256 * i;
-            const int jj = e >> 5, d4 = (e & 31) * 4;
-            const int row = kbase + h0 + min(jj, n - 1);        // rows past n: any valid row
-            load4<DT>(base, kvbase + (int64_t)row * D + d4, v[i]);
-        }
+            for (int i = 0; i < 8; ++i) {
+                const int q = tid + 256 * i, row = q >> 3, c4 = q & 7;
+                load4<DT>(Kc, kvbase + (int64_t)(kbase + min(row, nk - 1)) * D + st * KSL + 4 * c4, pre[i]);
+            }
+        } else {
+            const int j0 = (st - NKST) * VKEYS;
 #pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const int e = tid + 256 * i;
-            const int jj = e >> 5, d4 = (e & 31) * 4;
-            float* dst = KVs + jj * DLD + d4;
-            dst[0] = v[i][0]; dst[1] = v[i][1]; dst[2] = v[i][2]; dst[3] = v[i][3];
-        }
-    };
-    // ---- scores
-    for (int h0 = 0; h0 < nk; h0 += DH) {
-        const int n = min(DH, nk - h0);
-        __syncthreads();
-        stage(Kc, h0, n);
-        __syncthreads();
-        for (int e = tid; e < G * DH; e += 256) {
-            const int hh = e / DH, jj = e % DH;
-            if (jj < n) {
-                const float* kr = KVs + jj * DLD;
-                float acc = 0.0f;
-                for (int d = 0; d < D; ++d) acc = __builtin_fmaf(Qs[hh][d], kr[d], acc);
-                Ps[hh][h0 + jj] = acc * scale;
+            for (int i = 0; i < 8; ++i) {
+                const int q = tid + 256 * i, row = q >> 5, c4 = q & 31;
+                load4<DT>(Vc, kvbase + (int64_t)(kbase + min(j0 + row, nk - 1)) * D + 4 * c4, pre[i]);
             }
         }
+    };
+    auto store_stage = [&](int st) {
+        if (st < NKST) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = tid + 256 * i, row = q >> 3, c4 = q & 7;
+                float* dst = Buf + row * KSLD + 4 * c4;
+                dst[0] = pre[i][0]; dst[1] = pre[i][1]; dst[2] = pre[i][2]; dst[3] = pre[i][3];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = tid + 256 * i, row = q >> 5, c4 = q & 31;
+                *reinterpret_cast<float4*>(Buf + row * D + 4 * c4) =
+                    make_float4(pre[i][0], pre[i][1], pre[i][2], pre[i][3]);
+            }
+        }
+    };
+
+    // ---- scores: thread tid owns key tid
+    float acc[GT];
+#pragma unroll
+    for (int hh = 0; hh < GT; ++hh) acc[hh] = 0.0f;
+    load_stage(0);
+    for (int st = 0; st < NKST; ++st) {
+        __syncthreads();
+        store_stage(st);
+        __syncthreads();
+        load_stage(st + 1);                     // the next K slice, or the first V block
+        const float* kr = Buf + tid * KSLD;
+#pragma unroll
+        for (int dd = 0; dd < KSL; dd += 4) {
+            const float k0 = kr[dd], k1 = kr[dd + 1], k2 = kr[dd + 2], k3 = kr[dd + 3];
+#pragma unroll
+            for (int hh = 0; hh < GT; ++hh) {
+                if (hh < G) {
+                    const float4 qv = *reinterpret_cast<const float4*>(&Qs[hh][st * KSL + dd]);
+                    float a = acc[hh];
+                    a = __builtin_fmaf(qv.x, k0, a);
+                    a = __builtin_fmaf(qv.y, k1, a);
+                    a = __builtin_fmaf(qv.z, k2, a);
+                    a = __builtin_fmaf(qv.w, k3, a);
+                    acc[hh] = a;
+                }
+            }
+        }
+    }
+    if (tid < nk) {
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh)
+            if (hh < G) Ps[hh][tid] = acc[hh] * scale;
     }
     __syncthreads();
     // ---- chunk max per head (wavefront w reduces heads w, w + 4, ...), then p
@@ -438,41 +481,63 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
         if (lane == 0) Ms[hh] = mc;
     }
     __syncthreads();
-    for (int e = tid; e < G * nk; e += 256) {
-        const int hh = e / nk, jj = e % nk;
-        Ps[hh][jj] = exp_f(Ps[hh][jj] - Ms[hh]);
+    if (tid < nk) {
+#pragma unroll
+        for (int hh = 0; hh < GT; ++hh)
+            if (hh < G) Ps[hh][tid] = exp_f(Ps[hh][tid] - Ms[hh]);
     }
-    // ---- o_c[d] and l_c, keys ascending; thread owns (head, d) pairs
-    float oc[GMAX / 2], lc[GMAX / 2];
+    // ---- o_c[d] and l_c, keys ascending; thread owns d = tid % D of heads tid / D + 2u
+    constexpr int NO = GT >= 2 ? GT / 2 : 1;
+    const int d = tid % D, hb = tid / D;
+    float oc[NO], lc[NO];
 #pragma unroll
-    for (int u = 0; u < GMAX / 2; ++u) { oc[u] = 0.0f; lc[u] = 0.0f; }
-    for (int h0 = 0; h0 < nk; h0 += DH) {
-        const int n = min(DH, nk - h0);
+    for (int u = 0; u < NO; ++u) { oc[u] = 0.0f; lc[u] = 0.0f; }
+    for (int st = NKST; st < nst; ++st) {
         __syncthreads();
-        stage(Vc, h0, n);
+        store_stage(st);
         __syncthreads();
+        if (st + 1 < nst) load_stage(st + 1);
+        const int j0 = (st - NKST) * VKEYS;
+        const int n = min(VKEYS, nk - j0);
+        if (n == VKEYS) {
+#pragma unroll 4
+            for (int jj = 0; jj < VKEYS; jj += 4) {
+                const float v0 = Buf[(jj + 0) * D + d], v1 = Buf[(jj + 1) * D + d];
+                const float v2 = Buf[(jj + 2) * D + d], v3 = Buf[(jj + 3) * D + d];
 #pragma unroll
-        for (int u = 0; u < GMAX / 2; ++u) {
-            const int e = tid + 256 * u;
-            if (e < G * D) {
-                const int hh = e / D, d = e % D;
-                float o = oc[u], l = lc[u];
-                for (int jj = 0; jj < n; ++jj) {
-                    const float pj = Ps[hh][h0 + jj];
-                    o = __builtin_fmaf(pj, KVs[jj * DLD + d], o);
-                    l = l + pj;
+                for (int u = 0; u < NO; ++u) {
+                    const int hh = hb + 2 * u;
+                    if (hh < G) {
+                        const float4 pv = *reinterpret_cast<const float4*>(&Ps[hh][j0 + jj]);
+                        float o = oc[u], l = lc[u];
+                        o = __builtin_fmaf(pv.x, v0, o); l = l + pv.x;
+                        o = __builtin_fmaf(pv.y, v1, o); l = l + pv.y;
+                        o = __builtin_fmaf(pv.z, v2, o); l = l + pv.z;
+                        o = __builtin_fmaf(pv.w, v3, o); l = l + pv.w;
+                        oc[u] = o; lc[u] = l;
+                    }
                 }
-                oc[u] = o;
-                lc[u] = l;
+            }
+        } else {
+            for (int jj = 0; jj < n; ++jj) {
+                const float v = Buf[jj * D + d];
+#pragma unroll
+                for (int u = 0; u < NO; ++u) {
+                    const int hh = hb + 2 * u;
+                    if (hh < G) {
+                        const float pj = Ps[hh][j0 + jj];
+                        oc[u] = __builtin_fmaf(pj, v, oc[u]);
+                        lc[u] = lc[u] + pj;
+                    }
+                }
             }
         }
     }
     const int D2 = D + 2;
 #pragma unroll
-    for (int u = 0; u < GMAX / 2; ++u) {
-        const int e = tid + 256 * u;
-        if (e < G * D) {
-            const int hh = e / D, d = e % D;
+    for (int u = 0; u < NO; ++u) {
+        const int hh = hb + 2 * u;
+        if (hh < G) {
             float* dst = ws + (((int64_t)b * Hq + g * G + hh) * nchunks + c) * D2;
             dst[2 + d] = oc[u];
             if (d == 0) { dst[0] = Ms[hh]; dst[1] = lc[u]; }
@@ -486,7 +551,8 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
                                                                 int Hq, int Tmax, int nchunks,
                                                                 const float* __restrict__ ws,
                                                                 float* __restrict__ O) {
-    __shared__ float Mc[MAXCH], Lc[MAXCH], Al[MAXCH], Be[MAXCH], Mr[MAXCH];
+    __shared__ __attribute__((aligned(16))) float Mc[MAXCH];
+    __shared__ float Lc[MAXCH], Al[MAXCH], Be[MAXCH], Mr[MAXCH];
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int p = pos[b];
     if (p < 0 || p >= Tmax) {
@@ -496,12 +562,31 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
     const int nc = p / CHUNK + 1;
     const int D2 = D + 2;
     const float* src = ws + ((int64_t)b * Hq + h) * nchunks * D2;
+    // chunk partials o_c[d] for c = 1.. stream through two register batches; the first batch
+    // is requested before the maxima are scanned (indices past nc - 1 repeat nc - 1: valid
+    // addresses whose values are never folded)
+    constexpr int MBAT = 32;
+    float cur[MBAT], nxt[MBAT];
+#pragma unroll
+    for (int u = 0; u < MBAT; ++u) {
+        cur[u] = src[(int64_t)min(1 + u, nc - 1) * D2 + 2 + d];
+        nxt[u] = 0.0f;
+    }
     for (int c = d; c < nc; c += D) { Mc[c] = src[(int64_t)c * D2]; Lc[c] = src[(int64_t)c * D2 + 1]; }
     __syncthreads();
     if (d == 0) {                                 // running maximum, exactly as the fold takes it
         float m = Mc[0];
         Mr[0] = m;
-        for (int c = 1; c < nc; ++c) { const float mc = Mc[c]; m = (mc > m) ? mc : m; Mr[c] = m; }
+        int c = 1;
+        for (; c < 4 && c < nc; ++c) { const float mc = Mc[c]; m = (mc > m) ? mc : m; Mr[c] = m; }
+        for (; c + 4 <= nc; c += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(&Mc[c]);
+            m = (q.x > m) ? q.x : m; Mr[c] = m;
+            m = (q.y > m) ? q.y : m; Mr[c + 1] = m;
+            m = (q.z > m) ? q.z : m; Mr[c + 2] = m;
+            m = (q.w > m) ? q.w : m; Mr[c + 3] = m;
+        }
+        for (; c < nc; ++c) { const float mc = Mc[c]; m = (mc > m) ? mc : m; Mr[c] = m; }
     }
     __syncthreads();
     for (int c = 1 + d; c < nc; c += D) {
@@ -510,22 +595,35 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
     }
     __syncthreads();
     float l = Lc[0], o = src[2 + d];
-    int c = 1;
-    for (; c + 8 <= nc; c += 8) {
-        float oc[8];
+    for (int c0 = 1; c0 < nc; c0 += MBAT) {
+        if (c0 + MBAT < nc) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) oc[u] = src[(int64_t)(c + u) * D2 + 2 + d];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float a = Al[c + u], bb = Be[c + u];
-            l = (l * a) + (Lc[c + u] * bb);
-            o = (o * a) + (oc[u] * bb);
+            for (int u = 0; u < MBAT; ++u) nxt[u] = src[(int64_t)min(c0 + MBAT + u, nc - 1) * D2 + 2 + d];
         }
-    }
-    for (; c < nc; ++c) {
-        const float a = Al[c], bb = Be[c];
-        l = (l * a) + (Lc[c] * bb);
-        o = (o * a) + (src[(int64_t)c * D2 + 2 + d] * bb);
+        // this batch's factors, read from LDS ahead of the serial fold
+        float fa[MBAT], fb[MBAT], fl[MBAT];
+#pragma unroll
+        for (int u = 0; u < MBAT; ++u) {
+            const int cc = min(c0 + u, nc - 1);
+            fa[u] = Al[cc]; fb[u] = Be[cc]; fl[u] = Lc[cc];
+        }
+        if (c0 + MBAT <= nc) {
+#pragma unroll
+            for (int u = 0; u < MBAT; ++u) {
+                l = (l * fa[u]) + (fl[u] * fb[u]);
+                o = (o * fa[u]) + (cur[u] * fb[u]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < MBAT; ++u) {
+                if (c0 + u < nc) {
+                    l = (l * fa[u]) + (fl[u] * fb[u]);
+                    o = (o * fa[u]) + (cur[u] * fb[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < MBAT; ++u) cur[u] = nxt[u];
     }
     O[((int64_t)b * Hq + h) * D + d] = o / l;
 }
@@ -543,16 +641,32 @@ hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+namespace {
+
+template <int DT, int GT>
+hipError_t launch_partial(const AttnArgs& a, const int32_t* pos, float* ws, int nchunks, hipStream_t st) {
+    dim3 grid(nchunks, a.Hkv, a.B);
+    hipLaunchKernelGGL((attn_decode_partial_kernel<DT, GT>), grid, dim3(256), 0, st, a.Q, a.Kc, a.Vc,
+                       pos, a.Tmax, a.Hq, a.Hkv, a.scale, nchunks, ws);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_partial_dt(const AttnArgs& a, const int32_t* pos, float* ws, int nchunks, hipStream_t st) {
+    const int G = a.Hq / a.Hkv;
+    if (G <= 1) return launch_partial<DT, 1>(a, pos, ws, nchunks, st);
+    if (G <= 2) return launch_partial<DT, 2>(a, pos, ws, nchunks, st);
+    if (G <= 4) return launch_partial<DT, 4>(a, pos, ws, nchunks, st);
+    if (G <= 8) return launch_partial<DT, 8>(a, pos, ws, nchunks, st);
+    return launch_partial<DT, GMAX>(a, pos, ws, nchunks, st);
+}
+
+}  // namespace
+
 hipError_t launch_attention_decode(const AttnArgs& a, const int32_t* pos, float* ws, hipStream_t st) {
     const int nchunks = (a.Tmax + CHUNK - 1) / CHUNK;
-    dim3 grid(nchunks, a.Hkv, a.B);
-    if (a.dtype == 1)
-        hipLaunchKernelGGL(attn_decode_partial_kernel<1>, grid, dim3(256), 0, st, a.Q, a.Kc, a.Vc,
-                           pos, a.Tmax, a.Hq, a.Hkv, a.scale, nchunks, ws);
-    else
-        hipLaunchKernelGGL(attn_decode_partial_kernel<0>, grid, dim3(256), 0, st, a.Q, a.Kc, a.Vc,
-                           pos, a.Tmax, a.Hq, a.Hkv, a.scale, nchunks, ws);
-    hipError_t e = hipGetLastError();
+    hipError_t e = a.dtype == 1 ? launch_partial_dt<1>(a, pos, ws, nchunks, st)
+                                : launch_partial_dt<0>(a, pos, ws, nchunks, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(a.Hq, a.B), dim3(D), 0, st, pos, a.Hq, a.Tmax,
                        nchunks, ws, a.O);

@@ -7,36 +7,46 @@ namespace invnum {
 
 namespace {
 
-// RMSNorm: one wavefront per row.  The row is staged in LDS with coalesced 16-byte loads;
-// lane s then runs the slice chain ss_s = fma(x_k, x_k, ss_s) over k in slice s (ascending);
-// lane 0 folds the slices in order and evaluates r = 1 / sqrt(ss / H + eps); finally every
-// lane writes y_k = (x_k * r) * up(g_k).
-__global__ __launch_bounds__(64) void rmsnorm_kernel(const float* __restrict__ X, int H, int64_t ldx,
-                                                     const uint16_t* __restrict__ g, float eps,
-                                                     float* __restrict__ Y, int64_t ldy) {
+// RMSNorm: one 256-thread workgroup per row.  The row is staged in LDS with coalesced
+// 16-byte loads (up to 4 per thread in flight, together with the gains they will meet);
+// thread s then runs the slice chain ss_s = fma(x_k, x_k, ss_s) over k in slice s
+// (ascending); thread 0 folds the slices in order and evaluates r = 1 / sqrt(ss / H + eps);
+// finally every thread writes y_k = (x_k * r) * up(g_k).
+constexpr int RN_T = 256;     // threads per row
+constexpr int RN_U = 4;       // float4 per thread per batch
+
+__global__ __launch_bounds__(RN_T) void rmsnorm_kernel(const float* __restrict__ X, int H, int64_t ldx,
+                                                       const uint16_t* __restrict__ g, float eps,
+                                                       float* __restrict__ Y, int64_t ldy) {
     extern __shared__ float lds[];  // [H] row, then [S] slice partials, then r
     const int S = (H + KS - 1) / KS;
     float* xs = lds;
     float* part = lds + H;
     const int row = blockIdx.x;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
     const float* x = X + (int64_t)row * ldx;
-    // stage the row: loads issued 8 at a time before their LDS stores
-    for (int i0 = lane * 4; i0 < H; i0 += 8 * 256) {
-        float4 v[8];
+    for (int i0 = tid * 4; i0 < H; i0 += RN_U * RN_T * 4) {
+        float4 v[RN_U];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * 256;
+        for (int u = 0; u < RN_U; ++u) {
+            const int i = i0 + u * RN_T * 4;
             v[u] = *reinterpret_cast<const float4*>(x + (i < H ? i : 0));
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * 256;
+        for (int u = 0; u < RN_U; ++u) {
+            const int i = i0 + u * RN_T * 4;
             if (i < H) *reinterpret_cast<float4*>(xs + i) = v[u];
         }
     }
+    // the first batch of gains is requested before the reduction and used after it
+    uint2 g0[RN_U];
+#pragma unroll
+    for (int u = 0; u < RN_U; ++u) {
+        const int i = tid * 4 + u * RN_T * 4;
+        g0[u] = *reinterpret_cast<const uint2*>(g + (i < H ? i : 0));
+    }
     __syncthreads();
-    for (int s = lane; s < S; s += 64) {
+    for (int s = tid; s < S; s += RN_T) {
         const int k0 = s * KS, k1 = min(H, k0 + KS);
         float c = 0.0f;
         for (int k = k0; k < k1; k += 4) {
@@ -49,7 +59,7 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const float* __restrict__ X
         part[s] = c;
     }
     __syncthreads();
-    if (lane == 0) {
+    if (tid == 0) {
         float T = part[0];
         for (int s = 1; s < S; ++s) T = T + part[s];
         part[S] = 1.0f / __builtin_sqrtf((T / (float)H) + eps);
@@ -57,15 +67,26 @@ __global__ __launch_bounds__(64) void rmsnorm_kernel(const float* __restrict__ X
     __syncthreads();
     const float r = part[S];
     float* y = Y + (int64_t)row * ldy;
-    for (int i = lane * 4; i < H; i += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(xs + i);
-        const uint2 gg = *reinterpret_cast<const uint2*>(g + i);
-        float4 o;
-        o.x = (v.x * r) * bf16_lo(gg.x);
-        o.y = (v.y * r) * bf16_hi(gg.x);
-        o.z = (v.z * r) * bf16_lo(gg.y);
-        o.w = (v.w * r) * bf16_hi(gg.y);
-        *reinterpret_cast<float4*>(y + i) = o;
+    for (int i0 = tid * 4; i0 < H; i0 += RN_U * RN_T * 4) {
+        uint2 gg[RN_U];
+#pragma unroll
+        for (int u = 0; u < RN_U; ++u) {
+            const int i = i0 + u * RN_T * 4;
+            gg[u] = (i0 == tid * 4) ? g0[u] : *reinterpret_cast<const uint2*>(g + (i < H ? i : 0));
+        }
+#pragma unroll
+        for (int u = 0; u < RN_U; ++u) {
+            const int i = i0 + u * RN_T * 4;
+            if (i < H) {
+                const float4 v = *reinterpret_cast<const float4*>(xs + i);
+                float4 o;
+                o.x = (v.x * r) * bf16_lo(gg[u].x);
+                o.y = (v.y * r) * bf16_hi(gg[u].x);
+                o.z = (v.z * r) * bf16_lo(gg[u].y);
+                o.w = (v.w * r) * bf16_hi(gg[u].y);
+                *reinterpret_cast<float4*>(y + i) = o;
+            }
+        }
     }
 }
 
@@ -196,7 +217,7 @@ hipError_t launch_rmsnorm(const float* X, int M, int H, int64_t ldx, const uint1
                           float* Y, int64_t ldy, hipStream_t st) {
     const int S = (H + KS - 1) / KS;
     const size_t lds = sizeof(float) * ((size_t)H + S + 1);
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(64), lds, st, X, H, ldx, g, eps, Y, ldy);
+    hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(RN_T), lds, st, X, H, ldx, g, eps, Y, ldy);
     return hipGetLastError();
 }
 

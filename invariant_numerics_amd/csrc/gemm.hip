@@ -8,7 +8,7 @@
 //     (8 per slice) on the FP32 matrix cores, keeping two registers per output (the slice
 //     accumulator and the folded total T).  Used when M > 16.
 //   * gemm_skinny: for M <= 16 the work per output row is too small to fill the chip,
-//     so a workgroup owns 16 weight rows and all M activation rows; each thread owns one
+//     so a workgroup owns 16 (or 4) weight rows and all M activation rows; each thread owns one
 //     (weight row, slice) pair, keeps one accumulator per activation row, and the slice
 //     partials are folded in slice order through LDS by one thread per output.
 // BF16 weights are upcast (bits << 16, exact) as they are loaded.
@@ -226,88 +226,102 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 }
 
 // ---------------------------------------------------------------- skinny --
-// M <= 16.  A workgroup owns SK_ROWS = 16 weight rows and every activation row; thread
-// (row nl, slice lane sl) computes the chain of slice s = group + sl for all M rows, keeping
-// one accumulator per activation row.  Slices are processed in groups of 16; within a group
-// the weights stream in 4 phases of 64 elements per slice:
-//   * load: 16 rows x 16 slices x 128 bytes, each 128-byte segment read by 8 consecutive
-//     lanes (coalesced), into registers one phase ahead, then into LDS (segments padded to
-//     144 bytes so the 16-byte LDS reads are bank-conflict free); the activation phase tile
-//     X[m][slice][64] is staged the same way and read as a broadcast;
+// M <= 16.  A workgroup owns ROWS weight rows (16, or 4 when the grid would otherwise be
+// too coarse to balance the CUs) and every activation row; thread (slice lane sl, row nl)
+// computes the chain of slice s = group + sl for all M rows, keeping one accumulator per
+// activation row.  Slices are processed in groups of 16; within a group the weights stream
+// in 4 phases of 64 elements per slice:
+//   * load: ROWS rows x 16 slices x 128 bytes, each 128-byte segment read by 8 consecutive
+//     lanes (coalesced), into registers DEPTH phases ahead, then into LDS; the activation
+//     phase tile X[m][slice][64] is staged the same way and read as a broadcast;
 //   * compute: each thread runs its slice chain over the phase's 64 elements in order.
+//     The 16 lanes of an LDS pass hold 16 consecutive slices of one weight row: weight
+//     segments are 144 bytes apart and activation rows 272 bytes apart, so both 16-byte
+//     reads spread over all banks.
 // After each group the 16 new slice partials of every output are folded, in slice order,
 // into that output's running total by the thread that owns it.
-constexpr int SK_ROWS = 16;   // weight rows per workgroup
 constexpr int SK_LANES = 16;  // slices per group
 constexpr int PH = 64;        // elements per slice per phase
 constexpr int WSEG = PH * 2 + 16;   // padded bytes per (row, slice) segment in LDS
+constexpr int XLD = PH + 4;         // padded floats per (m, slice) activation segment
 
-template <int MB, int ROLE>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(
+template <int MB, int ROLE, int ROWS>
+__global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
     float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
-    __shared__ __attribute__((aligned(16))) unsigned char Wl[SK_ROWS * SK_LANES * WSEG];
-    __shared__ __attribute__((aligned(16))) float Xl[MB][SK_LANES][PH];
-    __shared__ float part[SK_LANES][MB][SK_ROWS];
+    constexpr int NT = ROWS * SK_LANES;          // threads
+    constexpr int XU = SK_LANES * (PH / 4) / NT; // activation float4 per thread, row and phase
+    __shared__ __attribute__((aligned(16))) unsigned char Wl[ROWS * SK_LANES * WSEG];
+    __shared__ __attribute__((aligned(16))) float Xl[MB][SK_LANES][XLD];
+    __shared__ float part[SK_LANES][MB][ROWS];
     if (Mdev) M = min(M, *Mdev);
     if (M <= 0) return;
     const int S = (K + KS - 1) / KS;
     const int tid = threadIdx.x;
-    const int nl = tid % SK_ROWS;
-    const int sl = tid / SK_ROWS;
-    const int n0 = blockIdx.x * SK_ROWS;
+    const int sl = tid % SK_LANES;
+    const int nl = tid / SK_LANES;
+    const int n0 = blockIdx.x * ROWS;
 
-    // load duty: 8 x 16 bytes of weights and MB x 16 bytes of activations per thread
-    uint4 wpre[8];
-    float4 xpre[MB];
-    auto load = [&](int sg, int p) {
+    // load duty: 8 x 16 bytes of weights and MB * XU x 16 bytes of activations per thread and
+    // phase; DEPTH phases are in flight in registers (two when the activation tile is small)
+    constexpr int DEPTH = MB * XU <= 4 ? 2 : 1;
+    uint4 wpre[DEPTH][8];
+    float4 xpre[DEPTH][MB * XU];
+    auto load = [&](int stg, uint4 (&wp)[8], float4 (&xp)[MB * XU]) {
+        const int sg = (stg / (KS / PH)) * SK_LANES;
+        const int p = stg % (KS / PH);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int q = tid + 256 * i;          // 16-byte unit index in the phase tile
+            const int q = tid + NT * i;           // 16-byte unit index in the phase tile
             const int seg = q >> 3, c8 = q & 7;   // segment (row, slice) and chunk in it
             const int rn = seg >> 4, ss = seg & 15;
             const int k = (sg + ss) * KS + p * PH + 8 * c8;
             const bool in = (n0 + rn < N) && (k < K);
             const uint4 t = *reinterpret_cast<const uint4*>(W + (int64_t)min(n0 + rn, N - 1) * ldw + min(k, K - 8));
-            wpre[i] = in ? t : make_uint4(0u, 0u, 0u, 0u);
+            wp[i] = in ? t : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-            const int ss = tid >> 4, c4 = tid & 15;          // 16 slices x 16 float4
-            const int k = (sg + ss) * KS + p * PH + 4 * c4;
-            const bool in = (m < M) && (k < K);
-            const float4 t = *reinterpret_cast<const float4*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
-            xpre[m] = in ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < XU; ++j) {
+                const int u = tid + NT * j;
+                const int ss = u >> 4, c4 = u & 15;          // 16 slices x 16 float4
+                const int k = (sg + ss) * KS + p * PH + 4 * c4;
+                const bool in = (m < M) && (k < K);
+                const float4 t = *reinterpret_cast<const float4*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
+                xp[m * XU + j] = in ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
     };
-    auto store = [&]() {
+    auto store = [&](const uint4 (&wp)[8], const float4 (&xp)[MB * XU]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int q = tid + 256 * i;
+            const int q = tid + NT * i;
             const int seg = q >> 3, c8 = q & 7;
-            *reinterpret_cast<uint4*>(&Wl[seg * WSEG + c8 * 16]) = wpre[i];
+            *reinterpret_cast<uint4*>(&Wl[seg * WSEG + c8 * 16]) = wp[i];
         }
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-            *reinterpret_cast<float4*>(&Xl[m][tid >> 4][(tid & 15) * 4]) = xpre[m];
+        for (int m = 0; m < MB; ++m) {
+#pragma unroll
+            for (int j = 0; j < XU; ++j) {
+                const int u = tid + NT * j;
+                *reinterpret_cast<float4*>(&Xl[m][u >> 4][(u & 15) * 4]) = xp[m * XU + j];
+            }
+        }
     };
 
     const int ngroups = (S + SK_LANES - 1) / SK_LANES;
     const int nstages = ngroups * (KS / PH);
-    const bool folder = tid < MB * SK_ROWS;
-    const int fm = tid / SK_ROWS, fr = tid % SK_ROWS;   // output folded by this thread
+    const bool folder = tid < MB * ROWS;
+    const int fm = tid / ROWS, fr = tid % ROWS;   // output folded by this thread
     float T = 0.0f;
     float c[MB];
-    load(0, 0);
-    for (int st = 0; st < nstages; ++st) {
+    // one phase: its tile is in LDS; every thread advances its slice chain over it
+    auto compute = [&](int st) {
         const int sg = (st / (KS / PH)) * SK_LANES;
         const int p = st % (KS / PH);
-        __syncthreads();               // everyone is done with the previous phase's LDS data
-        store();
-        __syncthreads();
-        if (st + 1 < nstages) load(((st + 1) / (KS / PH)) * SK_LANES, (st + 1) % (KS / PH));
         if (p == 0) {
 #pragma unroll
             for (int m = 0; m < MB; ++m) c[m] = 0.0f;
@@ -359,6 +373,22 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
                 }
             }
         }
+    };
+    // phase st lives in register buffer st % DEPTH from its load until its store
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        if (d < nstages) load(d, wpre[d], xpre[d]);
+    for (int st = 0; st < nstages; st += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            if (st + d < nstages) {
+                __syncthreads();       // everyone is done with the previous phase's LDS data
+                store(wpre[d], xpre[d]);
+                __syncthreads();
+                if (st + d + DEPTH < nstages) load(st + d + DEPTH, wpre[d], xpre[d]);
+                compute(st + d);
+            }
+        }
     }
     if (folder) {
         const int gn = n0 + fr;
@@ -380,9 +410,21 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
 
 template <int MB, int ROLE>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
-    dim3 grid((a.N + SK_ROWS - 1) / SK_ROWS);
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE>), grid, dim3(256), 0, st,
-                       a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
+    // 16-row workgroups once they give >= 4 per CU; else 4-row (one wavefront) workgroups so
+    // the small projections still spread evenly over the CUs
+    if constexpr (MB <= 2) {
+        if (a.N < 16 * 1024) {
+            dim3 grid((a.N + 3) / 4);
+            hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, 4>), grid, dim3(4 * SK_LANES), 0, st,
+                               a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
+            return hipGetLastError();
+        }
+    }
+    {
+        dim3 grid((a.N + 15) / 16);
+        hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, 16>), grid, dim3(16 * SK_LANES), 0, st,
+                           a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
+    }
     return hipGetLastError();
 }
 
