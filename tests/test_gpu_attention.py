@@ -62,6 +62,26 @@ def test_decode_matches_prefill_rows_ragged_positions(orc):
         assert_bitwise(O, want, "decode pos=%s" % posv)
 
 
+def test_decode_cache_length_does_not_change_rows():
+    """A row's output depends only on keys 0..pos: a 140000-slot cache and one cut to pos + 1
+    slots give the same bits (positions 0, 70000, 131071), and a row with an invalid
+    position is NaN while the other row is unaffected."""
+    import torch
+    say("attn decode long cache")
+    Hq, Hkv, Tbig = 4, 2, 140000
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8300)
+    K = torch.randn((2, Hkv, Tbig, D), generator=g, device="cuda")
+    V = torch.randn((2, Hkv, Tbig, D), generator=g, device="cuda")
+    Q = torch.randn((2, Hq, D), generator=g, device="cuda")
+    for p in (0, 70000, 131071):
+        pos = torch.tensor([p, -1], dtype=torch.int32, device="cuda")
+        big = host(inv().inv_attention_decode(Q, K, V, pos))
+        small = host(inv().inv_attention_decode(Q, K[:, :, :p + 1].contiguous(), V[:, :, :p + 1].contiguous(), pos))
+        assert_bitwise(big[0], small[0], "Tmax %d vs %d at pos %d" % (Tbig, p + 1, p))
+        assert np.isnan(big[1]).all() and np.isnan(small[1]).all()
+
+
 def test_c2_full_prefill_equals_token_by_token_decode_and_oracle(orc):
     """8 heads x d128, 2048 tokens, bf16 Q/K/V, causal, chunk 256: prefill output equals
     2048 single-token decode calls bitwise, and the oracle at every row."""
