@@ -145,14 +145,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) { acc[i][j][v] = 0.0f; T[i][j][v] = 0.0f; }
 
-    const int nt = (K + BK - 1) / BK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nt) load_tile((t + 1) * BK);
-        float a[TI][8], b[TJ][8];
+    const int ntf = K / BK;                        // full tiles
+    const int nt = (K + BK - 1) / BK;              // plus a partial last tile when K % BK != 0
+    const int nslices = (K + KS - 1) / KS;
+    float a[TI][8], b[TJ][8];
+    auto read_frags = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
             const float4* src = reinterpret_cast<const float4*>(&As[buf][wm0 + i * 16 + r][g * 8]);
@@ -167,8 +164,19 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
             b[j][0] = lo.x; b[j][1] = lo.y; b[j][2] = lo.z; b[j][3] = lo.w;
             b[j][4] = hi.x; b[j][5] = hi.y; b[j][6] = hi.z; b[j][7] = hi.w;
         }
-        const int kend = min(BK, K - t * BK);
-        if (kend == BK) {
+    };
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    // slice by slice (KS / BK tiles each), so the fold T = T + acc runs once per slice; the
+    // loop body sees full tiles only (a partial tile can only be the very last one)
+    int t = 0;
+    for (int sl = 0; sl < nslices; ++sl) {
+        const int tend = min(ntf, t + KS / BK);
+        for (; t < tend; ++t) {
+            const int buf = t & 1;
+            if (t + 1 < nt) load_tile((t + 1) * BK);
+            read_frags(buf);
 #pragma unroll
             for (int s = 0; s < BK / 4; ++s)
 #pragma unroll
@@ -176,8 +184,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
                     for (int j = 0; j < TJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
-        } else {
+            if (t + 1 < nt) store_tile(buf ^ 1);
+            __syncthreads();
+        }
+        if (t == ntf && ntf < nt && sl == nslices - 1) {
             // partial last tile: only the k-steps below K (zero padding is never multiplied in)
+            const int kend = K - t * BK;
+            read_frags(t & 1);
 #pragma unroll
             for (int s = 0; s < BK / 4; ++s) {
                 if (4 * s < kend) {
@@ -188,22 +201,26 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
                             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
                 }
             }
+            ++t;
         }
-        const int kdone = t * BK + kend;
-        if (kdone % KS == 0 || kdone == K) {
-            const bool first = kdone <= KS;
+        // the slice is complete: fold it into T in slice order, restart the accumulator
+        if (sl == 0) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) T[i][j] = acc[i][j];
+        } else {
 #pragma unroll
             for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int j = 0; j < TJ; ++j)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        T[i][j][v] = first ? acc[i][j][v] : T[i][j][v] + acc[i][j][v];
-                        acc[i][j][v] = 0.0f;
-                    }
+                    for (int v = 0; v < 4; ++v) T[i][j][v] = T[i][j][v] + acc[i][j][v];
         }
-        if (t + 1 < nt) store_tile(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // lane (g, r) holds rows 4g..4g+3, column r of each 16 x 16 tile
