@@ -45,8 +45,9 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 //           lane (g, r) receives, in register v, the score of row r with key 16t + 4v + g;
 //   PV      O^T = V^T P^T: step s = 4t + u covers keys 16t + 4u .. 16t + 4u + 3; its B operand
 //           for lane (g, r) is P[row r][key 16t + 4u + g] -- exactly register u of the
-//           score tile t that lane already holds; A = V^T (lane (g, r) supplies key 4s + g,
-//           d = 16 dt + r); lane (g, r) accumulates o[row r][d = 16 dt + 4g + v];
+//           score tile t that lane already holds; A = V^T, output tile dt = 0..7 taking the
+//           columns d = 8i + dt (i = 0..15): lane (g, r) supplies key 4s + g, d = 8r + dt --
+//           eight contiguous floats per step -- and accumulates o[row r][d = 32g + 8v + dt];
 //   l       the same B with an all-ones A: fma(1, p, l) = l + p, one rounding per key.
 // Workgroup: 256 threads = 4 wavefronts over BQ = 64 consecutive query rows of one (b, h);
 // wavefront w owns rows 16w .. 16w + 15.  Per 256-key chunk:
@@ -60,7 +61,10 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 //   4. merge into the running (m, l, o) with the same formulas as the decode merge kernel.
 constexpr int SB = 64;          // keys per LDS sub-block
 constexpr int KLD = D + 4;      // K rows in LDS (d permuted: (d % 4) * 32 + d / 4)
-constexpr int VLD = D + 8;      // V rows in LDS (row-major)
+constexpr int VLD = D + 8;      // V rows in LDS (row-major, 4 floats of padding after d = 63)
+// LDS column of d in a V row: the padding keeps the two 16-byte operand reads of the 16
+// lanes of a lane group (d = 8r .. 8r + 7, r = 0..15) on distinct banks
+__device__ __forceinline__ int vcol(int d) { return d + (d >= 64 ? 4 : 0); }
 constexpr int TAIL = 32;        // LDS slots per row for the causal tail's p
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -119,7 +123,7 @@ struct Stage {
         for (int i = 0; i < 8; ++i) {
             const int e = tid + 256 * i;
             const int jj = e >> 5, d4 = (e & 31) * 4;
-            *reinterpret_cast<float4*>(KV + jj * VLD + d4) = v[i];
+            *reinterpret_cast<float4*>(KV + jj * VLD + vcol(d4)) = v[i];
         }
     }
 };
@@ -275,25 +279,47 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                 else if (c < clast) st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
                 const float* kvb = KV[buf];
                 const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
+                // A operand of step s: lane (g, r) supplies V[key 4s + g][d = 8r + t] for tile t,
+                // eight contiguous floats read as two 16-byte loads, one step ahead
+                const float* vop = kvb + g * VLD + vcol(8 * r);
                 if (nmk >= SB) {
+                    float4 va0 = *reinterpret_cast<const float4*>(vop);
+                    float4 va1 = *reinterpret_cast<const float4*>(vop + 4);
 #pragma unroll
                     for (int s = 0; s < SB / 4; ++s) {
+                        float4 vb0 = va0, vb1 = va1;
+                        if (s + 1 < SB / 4) {
+                            vb0 = *reinterpret_cast<const float4*>(vop + 4 * (s + 1) * VLD);
+                            vb1 = *reinterpret_cast<const float4*>(vop + 4 * (s + 1) * VLD + 4);
+                        }
                         const float bp = S[sb * 4 + (s >> 2)][s & 3];
-                        const float* vr = kvb + (4 * s + g) * VLD + r;
-#pragma unroll
-                        for (int t = 0; t < 8; ++t)
-                            oc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * t], bp, oc[t], 0, 0, 0);
+                        oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.x, bp, oc[0], 0, 0, 0);
+                        oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.y, bp, oc[1], 0, 0, 0);
+                        oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.z, bp, oc[2], 0, 0, 0);
+                        oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.w, bp, oc[3], 0, 0, 0);
+                        oc[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.x, bp, oc[4], 0, 0, 0);
+                        oc[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.y, bp, oc[5], 0, 0, 0);
+                        oc[6] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.z, bp, oc[6], 0, 0, 0);
+                        oc[7] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.w, bp, oc[7], 0, 0, 0);
                         lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
+                        va0 = vb0;
+                        va1 = vb1;
                     }
                 } else if (nmk > 0) {
 #pragma unroll
                     for (int s = 0; s < SB / 4; ++s) {
                         if (4 * s < nmk) {
                             const float bp = S[sb * 4 + (s >> 2)][s & 3];
-                            const float* vr = kvb + (4 * s + g) * VLD + r;
-#pragma unroll
-                            for (int t = 0; t < 8; ++t)
-                                oc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(vr[16 * t], bp, oc[t], 0, 0, 0);
+                            const float4 va0 = *reinterpret_cast<const float4*>(vop + 4 * s * VLD);
+                            const float4 va1 = *reinterpret_cast<const float4*>(vop + 4 * s * VLD + 4);
+                            oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.x, bp, oc[0], 0, 0, 0);
+                            oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.y, bp, oc[1], 0, 0, 0);
+                            oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.z, bp, oc[2], 0, 0, 0);
+                            oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.w, bp, oc[3], 0, 0, 0);
+                            oc[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.x, bp, oc[4], 0, 0, 0);
+                            oc[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.y, bp, oc[5], 0, 0, 0);
+                            oc[6] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.z, bp, oc[6], 0, 0, 0);
+                            oc[7] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.w, bp, oc[7], 0, 0, 0);
                             lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
                         }
                     }
@@ -302,14 +328,19 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                 const int j1 = min(kb + SB, irow + 1);
                 for (int j = max(kb, jv); j < j1; ++j) {
                     const float pv = Pt[w][r][j - jv];
-                    const float* vr = kvb + (j - kb) * VLD + 4 * g;
+                    const float* vr = kvb + (j - kb) * VLD + vcol(32 * g);   // d = 32g + 8v + t
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const float4 vv = *reinterpret_cast<const float4*>(vr + 16 * t);
-                        oc[t][0] = __builtin_fmaf(pv, vv.x, oc[t][0]);
-                        oc[t][1] = __builtin_fmaf(pv, vv.y, oc[t][1]);
-                        oc[t][2] = __builtin_fmaf(pv, vv.z, oc[t][2]);
-                        oc[t][3] = __builtin_fmaf(pv, vv.w, oc[t][3]);
+                    for (int v = 0; v < 4; ++v) {
+                        const float4 x0 = *reinterpret_cast<const float4*>(vr + 8 * v);
+                        const float4 x1 = *reinterpret_cast<const float4*>(vr + 8 * v + 4);
+                        oc[0][v] = __builtin_fmaf(pv, x0.x, oc[0][v]);
+                        oc[1][v] = __builtin_fmaf(pv, x0.y, oc[1][v]);
+                        oc[2][v] = __builtin_fmaf(pv, x0.z, oc[2][v]);
+                        oc[3][v] = __builtin_fmaf(pv, x0.w, oc[3][v]);
+                        oc[4][v] = __builtin_fmaf(pv, x1.x, oc[4][v]);
+                        oc[5][v] = __builtin_fmaf(pv, x1.y, oc[5][v]);
+                        oc[6][v] = __builtin_fmaf(pv, x1.z, oc[6][v]);
+                        oc[7][v] = __builtin_fmaf(pv, x1.w, oc[7][v]);
                     }
                     lc[0] = lc[0] + pv;
                 }
@@ -341,12 +372,14 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     // ------------------------------------------------------------------ output
     const int rel = wrow0 + r;
     if (rel < r0 + nrows) {
-        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D + 4 * g;
+        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D + 32 * g;   // d = 32g + 8v + t
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            float4 y;
-            y.x = o[t][0] / l; y.y = o[t][1] / l; y.z = o[t][2] / l; y.w = o[t][3] / l;
-            *reinterpret_cast<float4*>(out + 16 * t) = y;
+        for (int v = 0; v < 4; ++v) {
+            float4 y0, y1;
+            y0.x = o[0][v] / l; y0.y = o[1][v] / l; y0.z = o[2][v] / l; y0.w = o[3][v] / l;
+            y1.x = o[4][v] / l; y1.y = o[5][v] / l; y1.z = o[6][v] / l; y1.w = o[7][v] / l;
+            *reinterpret_cast<float4*>(out + 8 * v) = y0;
+            *reinterpret_cast<float4*>(out + 8 * v + 4) = y1;
         }
     }
 }
