@@ -220,6 +220,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         // lane (g, r), register v of tile t: row r, key kbase + 16t + 4v + g
         const bool ne = irow >= kbase;
         const bool full = kbase + CHUNK <= i0;                 // every row sees the whole chunk
+        // m_c = max of the row's visible scores.  NaN scores are passed over (as the
+        // sequential compare-and-keep does); which zero a tie between +0 and -0 keeps cannot
+        // change any result, since every p and merge factor built from a zero difference is
+        // exp_f(+-0) = 1.  So the hardware maximum serves.
         float mc = -__builtin_inff();
         if (full) {
 #pragma unroll
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                 for (int v = 0; v < 4; ++v) {
                     const float sv = S[t][v] * scale;
                     S[t][v] = sv;
-                    mc = (sv > mc) ? sv : mc;
+                    mc = __builtin_fmaxf(mc, sv);
                 }
         } else {
 #pragma unroll
@@ -238,15 +242,11 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
                     const int j = kbase + 16 * t + 4 * v + g;
                     const float sv = S[t][v] * scale;
                     S[t][v] = sv;
-                    if (j <= irow) mc = (sv > mc) ? sv : mc;
+                    if (j <= irow) mc = __builtin_fmaxf(mc, sv);
                 }
         }
-        {
-            float y = __shfl_xor(mc, 16);
-            mc = (y > mc) ? y : mc;
-            y = __shfl_xor(mc, 32);
-            mc = (y > mc) ? y : mc;
-        }
+        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 16));
+        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 32));
         const int jspan = min(i0, kend) - kbase;
         const int jv = kbase + ((jspan > 0 ? jspan : 0) & ~3);   // matrix-core keys: [kbase, jv)
         if (full) {

@@ -61,11 +61,14 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
 }
 
 // exp_f(x): n = rint(x log2e); r = fma(-n, ln2_hi, x); r = fma(-n, ln2_lo, r);
-// p = Taylor degree 7 by fma-Horner from the top; result p * 2^n (n = 128 via p*2).
+// p = Taylor degree 7 by fma-Horner from the top; result p * 2^n rounded once.
 // x < ln(2^-126) -> +0, x > ln(2^128) -> +inf, NaN -> NaN.
-// Written without branches: the polynomial runs on x clamped into the finite range (for x
-// inside it the clamp is the identity, so the arithmetic is exactly the steps above) and the
-// pinned results outside the range are selected at the end.
+// Written without branches: the polynomial runs on x clamped into [ln(2^-126), ln(2^128)]
+// (for x inside it the clamp is the identity, so the arithmetic is exactly the steps above),
+// then n lies in [-126, 128] and ldexp(p, n) is p * 2^n with one rounding -- the same value
+// as (p * 2) * 2^127 for n = 128.  At the upper clamp point 128 ln2_hi equals the limit, r is
+// a tiny positive number, p > 1 and p * 2^128 overflows to +inf: every x at or above the limit
+// (+inf included) lands on +inf without a select.  Below the range +0 is selected.
 __device__ __forceinline__ float exp_f(float x) {
     const float xc = __builtin_fminf(__builtin_fmaxf(x, INV_EXP_LO), INV_EXP_HI);
     const float t = xc * INV_LOG2E;
@@ -80,13 +83,8 @@ __device__ __forceinline__ float exp_f(float x) {
     p = __builtin_fmaf(p, r, INV_IF2);
     p = __builtin_fmaf(p, r, INV_IF1);
     p = __builtin_fmaf(p, r, INV_IF0);
-    const int ni = (int)n;
-    const bool top = ni > 127;
-    const float pp = top ? p * 2.0f : p;
-    const int ne = top ? ni - 1 : ni;
-    float res = pp * __uint_as_float((uint32_t)(ne + 127) << 23);
+    float res = __builtin_ldexpf(p, (int)n);
     res = (x < INV_EXP_LO) ? 0.0f : res;
-    res = (x > INV_EXP_HI) ? __builtin_inff() : res;
     return (x != x) ? x + x : res;
 }
 
