@@ -44,11 +44,33 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="before the timed steps, copy 1 GiB device to device once (untimed): the "
+                         "reference dispatch for scaling HBM byte counters in profiler runs")
     return ap.parse_args()
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_128x128_c5_prefill_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "invariant_numerics_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the body-projection GEMM from the profiler counter runs recorded
+    under profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel
+    source has changed since they were taken."""
+    import hashlib
+    try:
+        vals = dict(line.split(": ", 1) for line in open(TRAFFIC_FILE).read().splitlines() if ": " in line)
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        if vals.get("gemm_source_sha256", "").strip() != sha:
+            return None
+        return int(vals["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def main():
@@ -87,6 +109,14 @@ def main():
         log("warmup", i)
         out = step()
     torch.cuda.synchronize()
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)      # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 1 GiB read + 1 GiB written")
     rec = []
     dec.gemm_events = rec
     outs = []
@@ -103,14 +133,18 @@ def main():
     log("step %.1f ms, %.0f scored tok/s" % (ms, value))
 
     # dominant kernel: body projections, HIP events on the launch stream
-    durs = np.array([s.elapsed_time(e) for s, e, _ in rec]) * 1e-3  # seconds
-    flops = np.array([f for _, _, f in rec], np.float64)
+    durs = np.array([s.elapsed_time(e) for s, e, _, _ in rec]) * 1e-3  # seconds
+    flops = np.array([f for _, _, f, _ in rec], np.float64)
     achieved = float(flops.sum() / durs.sum()) / 1e12
     gemm_share = float(durs.sum() / elapsed)
+    default_workload = (B == 1 and T == 32768 and args.block == 4096 and args.layers == 4)
     roof = dict(bound="mfma", kernel="gemm_mfma_kernel<128,128,0> (body projections, FP32 matrix cores)",
                 achieved=round(achieved, 3),
                 peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / FP32_PEAK_TFLOPS, 4),
-                traffic=None, launches=int(len(rec)), avg_launch_us=round(float(durs.mean()) * 1e6, 2),
+                traffic=measured_traffic() if default_workload else None,
+                traffic_unit="bytes per launch (HBM read + write, counter-measured)",
+                algorithmic_bytes_per_launch=float(np.mean([b for _, _, _, b in rec])) if rec else None,
+                launches=int(len(rec)), avg_launch_us=round(float(durs.mean()) * 1e6, 2),
                 avg_flops_per_launch=float(flops.mean()), share_of_step=round(gemm_share, 3))
     recomputed = float(outs[-1]["recomputed"].float().mean().item())
 

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
     float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
+    const int gridM = M;                           // the row count the grid was sized for
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int TI = WM / 16, TJ = WN / 16;
     constexpr int LDT = BK + 4;                    // padded LDS row (floats)
@@ -55,8 +56,35 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     __shared__ float Bs[2][BN][LDT];
 
     if (Mdev) M = min(M, *Mdev);
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+    int m0, n0;
+    {
+        // 1-D grid over the nMt x nNt output tiles.  The mapping decides only which workgroup
+        // owns a tile, never the order inside a dot.
+        const int nMt = (gridM + BM - 1) / BM, nNt = (N + BN - 1) / BN;
+        const int L = blockIdx.x;
+        if constexpr (ROLE == 0) {
+            // Consecutive workgroup ids go to the 8 XCDs in turn, so id L is given tile u from
+            // a contiguous range per XCD (a bijection of [0, T)); within it tiles are walked in
+            // groups of GM tile rows, column by column, so the ~32 workgroups an XCD runs at
+            // once share GM activation and ~32/GM weight tiles in its L2.
+            constexpr int NXCD = 8, GM = 4;
+            const int T = nMt * nNt;
+            const int xcd = L % NXCD, q = L / NXCD;
+            const int u = xcd * (T / NXCD) + min(xcd, T % NXCD) + q;
+            const int grp = u / (GM * nNt);
+            const int mf = grp * GM;
+            const int gsz = min(nMt - mf, GM);
+            const int within = u - grp * GM * nNt;
+            m0 = (mf + within % gsz) * BM;
+            n0 = (within / gsz) * BN;
+        } else {
+            // vocabulary projection: columns fastest.  Its recompute pass has a device-side
+            // row count (trailing tile rows exit at once), and this order keeps the live tiles
+            // spread over every XCD.
+            m0 = (L / nNt) * BM;
+            n0 = (L % nNt) * BN;
+        }
+    }
     if (m0 >= M) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
@@ -419,7 +447,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
 
 template <int BM, int BN, int ROLE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
-    dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+    dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM));
     hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, ROLE>), grid, dim3(256), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();

@@ -44,7 +44,8 @@ class Decoder:
                    for _ in range(self.L)]
         self.vc = [torch.zeros_like(k) for k in self.kc]
         # optional measurement hook: when a list, each body projection appends
-        # (start event, end event, algorithmic flops) recorded on its launch stream
+        # (start event, end event, algorithmic flops, algorithmic bytes) recorded on its
+        # launch stream
         self.gemm_events = None
 
     def _gemm(self, X, W, R=None, out=None):
@@ -56,7 +57,11 @@ class Decoder:
         s.record()
         y = inv.inv_fixed_order_gemm(X, W, R=R, out=out)
         e.record()
-        ev.append((s, e, 2.0 * X.shape[0] * W.shape[0] * X.shape[1]))
+        M, K = X.shape
+        N = W.shape[0]
+        # algorithmic bytes: X and W read once, Y written once (R read once when given)
+        nbytes = 4 * M * K + 2 * N * K + 4 * M * N * (2 if R is not None else 1)
+        ev.append((s, e, 2.0 * M * N * K, float(nbytes)))
         return y
 
     # one pass of the decoder body over rows (seq[m], pos[m]); attention via `attend`
