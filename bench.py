@@ -220,6 +220,20 @@ def main():
                            "BF16 weights + FP32 KV cache read once (+ second vocabulary pass when a row "
                            "is recomputed)")
         del dd
+        # context for the decode fraction: a plain device copy (1 GiB read + 1 GiB written),
+        # timed the same way
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        for a_, b_ in ce:
+            a_.record()
+            dst.copy_(src)
+            b_.record()
+        torch.cuda.synchronize()
+        copy_s = min(a_.elapsed_time(b_) for a_, b_ in ce) * 1e-3
+        decode["copy_gbs_read_plus_write"] = round(2 * (1 << 30) / copy_s / 1e9, 1)
+        del src, dst
 
     # ---------------------------------------------------------------- CPU baseline
     cpu = None
