@@ -15,6 +15,8 @@
 #include "numerics.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace invnum {
 
 namespace {
@@ -39,33 +41,33 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 // four fused multiply-adds in k order, so both contractions keep their sequential order:
 // the scores over d = 0..127 and the PV sums over keys in ascending j.
 //
-// Operands are arranged so that the scores never leave registers:
-//   scores  S^T = K Q^T:  A = K tile (lane (g, r) supplies key 16t + pi(r), d = 4s + g),
-//           B = Q^T (lane (g, r) supplies row r, d = 4s + g); with pi(i) = 4 (i % 4) + i / 4
-//           lane (g, r) receives, in register v, the score of row r with key 16t + 4v + g;
-//   PV      O^T = V^T P^T: step s = 4t + u covers keys 16t + 4u .. 16t + 4u + 3; its B operand
-//           for lane (g, r) is P[row r][key 16t + 4u + g] -- exactly register u of the
-//           score tile t that lane already holds; A = V^T, output tile dt = 0..7 taking the
-//           columns d = 8i + dt (i = 0..15): lane (g, r) supplies key 4s + g, d = 8r + dt --
-//           eight contiguous floats per step -- and accumulates o[row r][d = 32g + 8v + dt];
-//   l       the same B with an all-ones A: fma(1, p, l) = l + p, one rounding per key.
-// Workgroup: 256 threads = 4 wavefronts over BQ = 64 consecutive query rows of one (b, h);
-// wavefront w owns rows 16w .. 16w + 15.  Per 256-key chunk:
-//   1. scores for the chunk (K streamed through double-buffered LDS in 64-key sub-blocks,
-//      one sub-block of register prefetch); 16 key tiles kept in registers;
-//   2. row max over keys <= i (lane-local, then across the 4 lane groups), p = exp_f(s - m_c);
-//   3. PV on the matrix cores for keys below the first multiple-of-4 boundary that every
-//      row of the wavefront can see; the remaining causal triangle (at most 19 keys per row)
-//      continues on the VALU in ascending j from a small LDS copy of its p, so masked keys are
-//      skipped rather than added as zeros;
-//   4. merge into the running (m, l, o) with the same formulas as the decode merge kernel.
+// Workgroup: 512 threads = 8 wavefronts over BQ = 64 consecutive query rows of one (b, h).
+// Row group rg = w % 4 (rows 16 rg .. 16 rg + 15) is shared by the pair of wavefronts
+// w = rg (half 0) and w = rg + 4 (half 1), so each keeps half the state of a row group and two
+// wavefronts run on every SIMD.  Per 256-key chunk:
+//   1. scores S^T = K Q^T on the matrix cores: A = K tile (lane (g, r) supplies key
+//      16t + pi(r), d = 4s + g, with pi(i) = 4 (i % 4) + i / 4), B = Q^T (lane (g, r) supplies
+//      row r, d = 4s + g, held in registers); lane (g, r) receives in register v the score of
+//      row r with key 16t + 4v + g.  K streams through double-buffered LDS in 64-key
+//      sub-blocks; half hf computes key tiles 4 sb + 2 hf and 4 sb + 2 hf + 1 of sub-block sb;
+//   2. each half takes the maximum of its visible scores; the pair exchanges them through LDS
+//      and both form m_c; p = exp_f(s - m_c) for the half's keys, written also to an LDS row
+//      buffer P so the partner and the causal tail can read every p of the chunk;
+//   3. PV: half hf accumulates d in [64 hf, 64 hf + 64) over all keys of the chunk in
+//      ascending order.  O^T = V^T P^T, output tile t (t = 0..3) taking d = 64 hf + 4i + t:
+//      step s covers keys 4s .. 4s + 3, lane (g, r) supplies V[key 4s + g][64 hf + 4r .. + 3]
+//      (one 16-byte LDS read for the four tiles) and, as B, P[row r][key 4s + g] -- from its own
+//      score registers for its own key tiles, else from P -- and accumulates
+//      o[row r][d = 64 hf + 16g + 4v + t].  Half 0 also sums l with an all-ones A operand,
+//      fma(1, p, l) = l + p, one rounding per key.  The matrix cores take the keys below the
+//      first multiple-of-4 boundary that every row of the group sees; the rest of the causal
+//      triangle (at most 19 keys per row) continues on the VALU in ascending j, so masked keys
+//      are skipped rather than added as zeros;
+//   4. merge into the running (m, l, o) with the formulas of the decode merge kernel.
 constexpr int SB = 64;          // keys per LDS sub-block
-constexpr int KLD = D + 4;      // K rows in LDS (d permuted: (d % 4) * 32 + d / 4)
-constexpr int VLD = D + 8;      // V rows in LDS (row-major, 4 floats of padding after d = 63)
-// LDS column of d in a V row: the padding keeps the two 16-byte operand reads of the 16
-// lanes of a lane group (d = 8r .. 8r + 7, r = 0..15) on distinct banks
-__device__ __forceinline__ int vcol(int d) { return d + (d >= 64 ? 4 : 0); }
-constexpr int TAIL = 32;        // LDS slots per row for the causal tail's p
+constexpr int KLD = D + 4;      // LDS row: K with d permuted ((d % 4) * 32 + d / 4), V row-major
+constexpr int PNT = 512;        // threads per prefill workgroup
+constexpr int PLD = CHUNK + 4;  // LDS row of P (floats)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -81,26 +83,26 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float* v) {
 }
 
 // Global -> register -> LDS staging of one 64-key sub-block of K or V (fp32 in LDS).
-// Thread t carries 8 groups of 4 consecutive d of rows (e / 32) for e = t + 256 i.
+// Thread t carries 4 groups of 4 consecutive d of rows (e / 32) for e = t + 512 i.
 // Rows at or beyond kend are read from row kend - 1 (always valid) and replaced by zeros.
 template <int DT>
 struct Stage {
-    float4 v[8];
+    float4 v[4];
     __device__ __forceinline__ void load(const void* base, int64_t kvbase, int kb, int kend, int tid) {
         if (kb + SB <= kend) {
-            // whole sub-block in range: row (tid >> 5) + 8 i, column 4 (tid & 31)
+            // whole sub-block in range: row (tid >> 5) + 16 i, column 4 (tid & 31)
             const int64_t off = kvbase + (int64_t)(kb + (tid >> 5)) * D + (tid & 31) * 4;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4; ++i) {
                 float t[4];
-                load4<DT>(base, off + (int64_t)(8 * i) * D, t);
+                load4<DT>(base, off + (int64_t)(16 * i) * D, t);
                 v[i] = make_float4(t[0], t[1], t[2], t[3]);
             }
             return;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = tid + 256 * i;
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + PNT * i;
             const int jj = e >> 5, d4 = (e & 31) * 4;
             const bool in = kb + jj < kend;
             const int row = in ? kb + jj : kend - 1;
@@ -111,8 +113,8 @@ struct Stage {
     }
     __device__ __forceinline__ void store_k(float* KV, int tid) const {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = tid + 256 * i;
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + PNT * i;
             const int jj = e >> 5, q = e & 31;
             float* dst = KV + jj * KLD + q;
             dst[0] = v[i].x; dst[32] = v[i].y; dst[64] = v[i].z; dst[96] = v[i].w;
@@ -120,23 +122,28 @@ struct Stage {
     }
     __device__ __forceinline__ void store_v(float* KV, int tid) const {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int e = tid + 256 * i;
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + PNT * i;
             const int jj = e >> 5, d4 = (e & 31) * 4;
-            *reinterpret_cast<float4*>(KV + jj * VLD + vcol(d4)) = v[i];
+            *reinterpret_cast<float4*>(KV + jj * KLD + d4) = v[i];
         }
     }
 };
 
 template <int DT>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(
+__global__ __launch_bounds__(PNT) void attn_prefill_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
     int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O) {
-    __shared__ __attribute__((aligned(16))) float KV[2][SB * VLD];
-    __shared__ float Pt[4][16][TAIL];
+    __shared__ __attribute__((aligned(16))) float KV[2][SB * KLD];
+    __shared__ __attribute__((aligned(16))) float P[4][16][PLD];
+    __shared__ float Mx[4][2][16];
+    __shared__ float Lx[4][16];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    // the wavefront index is uniform in a wavefront: in a scalar register, everything derived
+    // from it (row group, half, causal bounds) takes scalar branches
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = w & 3, hf = w >> 2;
     const int g = lane >> 4, r = lane & 15;
     const int pr = 4 * (r & 3) + (r >> 2);             // pi(r)
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     const int nrows = min(BQ, Tq - r0);
     const int imax = q_start + r0 + nrows - 1;          // last valid absolute row of the block
     const int64_t kvbase = ((int64_t)b * Hkv + kvh) * Tmax * D;
-    const int wrow0 = r0 + 16 * w;                      // first row (relative) of this wavefront
+    const int wrow0 = r0 + 16 * rg;                     // first row (relative) of the row group
     const int i0 = q_start + wrow0;                     // its absolute position
     const int irow = min(i0 + r, imax);                 // the lane's row, clamped
 
@@ -162,10 +169,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
         }
     }
 
-    f32x4 o[8];
+    f32x4 o[4];
     float m = 0.0f, l = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int clast = imax / CHUNK;
     Stage<DT> st;
@@ -174,40 +181,45 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
     st.store_k(KV[0], tid);
     __syncthreads();
 
-    for (int c = 0; c <= clast; ++c) {
+    // One chunk.  FAST: every row of the group sees all 256 keys of the chunk and all four
+    // sub-blocks are in range -- the common case -- so no guard, mask or causal tail is needed
+    // and the body is straight-line; otherwise every step checks its bounds.
+    auto chunk = [&](const int c, auto fast_tag) {
+        constexpr bool FAST = decltype(fast_tag)::value;
         const int kbase = c * CHUNK;
         const int kend = min(kbase + CHUNK, imax + 1);         // keys some row of the block needs
-        const int nsb = (kend - kbase + SB - 1) / SB;          // active sub-blocks (1..4)
+        const int nsb = FAST ? CHUNK / SB : (kend - kbase + SB - 1) / SB;   // active sub-blocks
         const int nkend = min(kbase + 2 * CHUNK, imax + 1);    // next chunk's key bound
-        // ------------------------------------------------------ 1. scores
-        f32x4 S[16];
+        // ------------------------------------------------------ 1. scores (own key tiles)
+        // S[2 sb + e] is key tile 4 sb + 2 hf + e of the chunk
+        f32x4 S[8];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sb = 0; sb < CHUNK / SB; ++sb) {
-            if (sb < nsb) {
+            if (FAST || sb < nsb) {
                 if (sb + 1 < nsb) st.load(Kc, kvbase, kbase + (sb + 1) * SB, kend, tid);
                 else st.load(Vc, kvbase, kbase, kend, tid);
                 const float* kvb = KV[buf];
-                if (kbase + sb * SB <= i0 + 15) {
+                if (FAST || kbase + sb * SB <= i0 + 15) {
 #pragma unroll
                     for (int s4 = 0; s4 < 8; ++s4) {
-                        float4 kk[SB / 16];
+                        float4 kk[2];
 #pragma unroll
-                        for (int kt = 0; kt < SB / 16; ++kt)
-                            kk[kt] = *reinterpret_cast<const float4*>(kvb + (kt * 16 + pr) * KLD + g * 32 + 4 * s4);
+                        for (int e = 0; e < 2; ++e)
+                            kk[e] = *reinterpret_cast<const float4*>(kvb + ((2 * hf + e) * 16 + pr) * KLD + g * 32 + 4 * s4);
 #pragma unroll
-                        for (int kt = 0; kt < SB / 16; ++kt)
-                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].x, qf[4 * s4 + 0], S[sb * 4 + kt], 0, 0, 0);
+                        for (int e = 0; e < 2; ++e)
+                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].x, qf[4 * s4 + 0], S[sb * 2 + e], 0, 0, 0);
 #pragma unroll
-                        for (int kt = 0; kt < SB / 16; ++kt)
-                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].y, qf[4 * s4 + 1], S[sb * 4 + kt], 0, 0, 0);
+                        for (int e = 0; e < 2; ++e)
+                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].y, qf[4 * s4 + 1], S[sb * 2 + e], 0, 0, 0);
 #pragma unroll
-                        for (int kt = 0; kt < SB / 16; ++kt)
-                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].z, qf[4 * s4 + 2], S[sb * 4 + kt], 0, 0, 0);
+                        for (int e = 0; e < 2; ++e)
+                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].z, qf[4 * s4 + 2], S[sb * 2 + e], 0, 0, 0);
 #pragma unroll
-                        for (int kt = 0; kt < SB / 16; ++kt)
-                            S[sb * 4 + kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[kt].w, qf[4 * s4 + 3], S[sb * 4 + kt], 0, 0, 0);
+                        for (int e = 0; e < 2; ++e)
+                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].w, qf[4 * s4 + 3], S[sb * 2 + e], 0, 0, 0);
                     }
                 }
                 if (sb + 1 < nsb) st.store_k(KV[buf ^ 1], tid);
@@ -217,169 +229,137 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(
             }
         }
         // ------------------------------------------------------ 2. chunk max and p
-        // lane (g, r), register v of tile t: row r, key kbase + 16t + 4v + g
-        const bool ne = irow >= kbase;
-        const bool full = kbase + CHUNK <= i0;                 // every row sees the whole chunk
         // m_c = max of the row's visible scores.  NaN scores are passed over (as the
         // sequential compare-and-keep does); which zero a tie between +0 and -0 keeps cannot
         // change any result, since every p and merge factor built from a zero difference is
-        // exp_f(+-0) = 1.  So the hardware maximum serves.
-        float mc = -__builtin_inff();
-        if (full) {
+        // exp_f(+-0) = 1.  So the hardware maximum serves, in any grouping.
+        const bool ne = irow >= kbase;
+        const bool full = FAST || kbase + CHUNK <= i0;         // every row sees the whole chunk
+        float mh = -__builtin_inff();
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
+        for (int x = 0; x < 8; ++x) {
+            const int t = 4 * (x >> 1) + 2 * hf + (x & 1);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float sv = S[t][v] * scale;
-                    S[t][v] = sv;
-                    mc = __builtin_fmaxf(mc, sv);
-                }
-        } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int j = kbase + 16 * t + 4 * v + g;
-                    const float sv = S[t][v] * scale;
-                    S[t][v] = sv;
-                    if (j <= irow) mc = __builtin_fmaxf(mc, sv);
-                }
+            for (int v = 0; v < 4; ++v) {
+                const int j = kbase + 16 * t + 4 * v + g;
+                const float sv = S[x][v] * scale;
+                S[x][v] = sv;
+                if (full || j <= irow) mh = __builtin_fmaxf(mh, sv);
+            }
         }
-        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 16));
-        mc = __builtin_fmaxf(mc, __shfl_xor(mc, 32));
+        mh = __builtin_fmaxf(mh, __shfl_xor(mh, 16));
+        mh = __builtin_fmaxf(mh, __shfl_xor(mh, 32));
+        if (g == 0) Mx[rg][hf][r] = mh;
+        __syncthreads();
+        const float mc = __builtin_fmaxf(Mx[rg][0][r], Mx[rg][1][r]);
+        float* prow = &P[rg][r][0];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            const int t = 4 * (x >> 1) + 2 * hf + (x & 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int j = kbase + 16 * t + 4 * v + g;
+                const float pv = (full || j <= irow) ? exp_f(S[x][v] - mc) : 0.0f;
+                S[x][v] = pv;
+                prow[16 * t + 4 * v + g] = pv;
+            }
+        }
         const int jspan = min(i0, kend) - kbase;
-        const int jv = kbase + ((jspan > 0 ? jspan : 0) & ~3);   // matrix-core keys: [kbase, jv)
-        if (full) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) S[t][v] = exp_f(S[t][v] - mc);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int j = kbase + 16 * t + 4 * v + g;
-                    const float pv = (j <= irow) ? exp_f(S[t][v] - mc) : 0.0f;
-                    S[t][v] = pv;
-                    if (j >= jv && j < jv + TAIL) Pt[w][r][j - jv] = pv;
-                }
-        }
+        const int jv = FAST ? kbase + CHUNK : kbase + ((jspan > 0 ? jspan : 0) & ~3);   // MFMA keys: [kbase, jv)
+        __syncthreads();                                          // P complete for both halves
         // ------------------------------------------------------ 3. PV and l
-        f32x4 oc[8];
+        f32x4 oc[4];
         f32x4 lc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) oc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 4; ++t) oc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sb = 0; sb < CHUNK / SB; ++sb) {
-            if (sb < nsb) {
+            if (FAST || sb < nsb) {
                 const int kb = kbase + sb * SB;
                 const bool more = sb + 1 < nsb;
+                // after the last V sub-block comes the next chunk's first K sub-block (past the
+                // last chunk every row is out of range: the stage clamps and stores zeros)
                 if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
-                else if (c < clast) st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
+                else st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
                 const float* kvb = KV[buf];
+                const float* vop = kvb + g * KLD + 64 * hf + 4 * r;   // + 4 s KLD at step s
                 const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
-                // A operand of step s: lane (g, r) supplies V[key 4s + g][d = 8r + t] for tile t,
-                // eight contiguous floats read as two 16-byte loads, one step ahead
-                const float* vop = kvb + g * VLD + vcol(8 * r);
-                if (nmk >= SB) {
-                    float4 va0 = *reinterpret_cast<const float4*>(vop);
-                    float4 va1 = *reinterpret_cast<const float4*>(vop + 4);
 #pragma unroll
-                    for (int s = 0; s < SB / 4; ++s) {
-                        float4 vb0 = va0, vb1 = va1;
-                        if (s + 1 < SB / 4) {
-                            vb0 = *reinterpret_cast<const float4*>(vop + 4 * (s + 1) * VLD);
-                            vb1 = *reinterpret_cast<const float4*>(vop + 4 * (s + 1) * VLD + 4);
-                        }
-                        const float bp = S[sb * 4 + (s >> 2)][s & 3];
-                        oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.x, bp, oc[0], 0, 0, 0);
-                        oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.y, bp, oc[1], 0, 0, 0);
-                        oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.z, bp, oc[2], 0, 0, 0);
-                        oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.w, bp, oc[3], 0, 0, 0);
-                        oc[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.x, bp, oc[4], 0, 0, 0);
-                        oc[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.y, bp, oc[5], 0, 0, 0);
-                        oc[6] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.z, bp, oc[6], 0, 0, 0);
-                        oc[7] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.w, bp, oc[7], 0, 0, 0);
-                        lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
-                        va0 = vb0;
-                        va1 = vb1;
-                    }
-                } else if (nmk > 0) {
-#pragma unroll
-                    for (int s = 0; s < SB / 4; ++s) {
-                        if (4 * s < nmk) {
-                            const float bp = S[sb * 4 + (s >> 2)][s & 3];
-                            const float4 va0 = *reinterpret_cast<const float4*>(vop + 4 * s * VLD);
-                            const float4 va1 = *reinterpret_cast<const float4*>(vop + 4 * s * VLD + 4);
-                            oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.x, bp, oc[0], 0, 0, 0);
-                            oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.y, bp, oc[1], 0, 0, 0);
-                            oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.z, bp, oc[2], 0, 0, 0);
-                            oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va0.w, bp, oc[3], 0, 0, 0);
-                            oc[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.x, bp, oc[4], 0, 0, 0);
-                            oc[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.y, bp, oc[5], 0, 0, 0);
-                            oc[6] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.z, bp, oc[6], 0, 0, 0);
-                            oc[7] = __builtin_amdgcn_mfma_f32_16x16x4f32(va1.w, bp, oc[7], 0, 0, 0);
-                            lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
-                        }
+                for (int s = 0; s < SB / 4; ++s) {
+                    if (FAST || 4 * s < nmk) {
+                        // key tile 4 sb + s / 4 is this half's own when (s / 8) == hf
+                        const float own = S[sb * 2 + ((s >> 2) & 1)][s & 3];
+                        const float oth = prow[16 * (4 * sb + (s >> 2)) + 4 * (s & 3) + g];
+                        const float bp = ((s >> 3) == hf) ? own : oth;
+                        const float4 va = *reinterpret_cast<const float4*>(vop + 4 * s * KLD);
+                        oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, bp, oc[0], 0, 0, 0);
+                        oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, bp, oc[1], 0, 0, 0);
+                        oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, bp, oc[2], 0, 0, 0);
+                        oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, bp, oc[3], 0, 0, 0);
+                        if (hf == 0) lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
                     }
                 }
-                // VALU continuation for keys [max(kb, jv), i], ascending (row r)
-                const int j1 = min(kb + SB, irow + 1);
-                for (int j = max(kb, jv); j < j1; ++j) {
-                    const float pv = Pt[w][r][j - jv];
-                    const float* vr = kvb + (j - kb) * VLD + vcol(32 * g);   // d = 32g + 8v + t
+                if (!FAST) {
+                    // VALU continuation for keys [max(kb, jv), i], ascending (row r)
+                    const int j1 = min(kb + SB, irow + 1);
+                    for (int j = max(kb, jv); j < j1; ++j) {
+                        const float pv = prow[j - kbase];
+                        const float* vr = kvb + (j - kb) * KLD + 64 * hf + 16 * g;   // d = 64hf + 16g + 4v + t
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const float4 x0 = *reinterpret_cast<const float4*>(vr + 8 * v);
-                        const float4 x1 = *reinterpret_cast<const float4*>(vr + 8 * v + 4);
-                        oc[0][v] = __builtin_fmaf(pv, x0.x, oc[0][v]);
-                        oc[1][v] = __builtin_fmaf(pv, x0.y, oc[1][v]);
-                        oc[2][v] = __builtin_fmaf(pv, x0.z, oc[2][v]);
-                        oc[3][v] = __builtin_fmaf(pv, x0.w, oc[3][v]);
-                        oc[4][v] = __builtin_fmaf(pv, x1.x, oc[4][v]);
-                        oc[5][v] = __builtin_fmaf(pv, x1.y, oc[5][v]);
-                        oc[6][v] = __builtin_fmaf(pv, x1.z, oc[6][v]);
-                        oc[7][v] = __builtin_fmaf(pv, x1.w, oc[7][v]);
+                        for (int v = 0; v < 4; ++v) {
+                            const float4 x4 = *reinterpret_cast<const float4*>(vr + 4 * v);
+                            oc[0][v] = __builtin_fmaf(pv, x4.x, oc[0][v]);
+                            oc[1][v] = __builtin_fmaf(pv, x4.y, oc[1][v]);
+                            oc[2][v] = __builtin_fmaf(pv, x4.z, oc[2][v]);
+                            oc[3][v] = __builtin_fmaf(pv, x4.w, oc[3][v]);
+                        }
+                        lc[0] = lc[0] + pv;
                     }
-                    lc[0] = lc[0] + pv;
                 }
                 if (more) st.store_v(KV[buf ^ 1], tid);
-                else if (c < clast) st.store_k(KV[buf ^ 1], tid);
+                else st.store_k(KV[buf ^ 1], tid);
                 __syncthreads();
                 buf ^= 1;
             }
         }
-        // ------------------------------------------------------ 4. merge
+        // ------------------------------------------------------ 4. merge (l: half 0)
         if (ne) {
             if (c == 0) {
                 m = mc;
                 l = lc[0];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) o[t] = oc[t];
+                for (int t = 0; t < 4; ++t) o[t] = oc[t];
             } else {
                 const float mn = (mc > m) ? mc : m;
                 const float al = exp_f(m - mn), be = exp_f(mc - mn);
                 l = (l * al) + (lc[0] * be);
 #pragma unroll
-                for (int t = 0; t < 8; ++t)
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) o[t][v] = (o[t][v] * al) + (oc[t][v] * be);
                 m = mn;
             }
         }
+    };
+    for (int c = 0; c <= clast; ++c) {
+        // the fast path needs the whole workgroup to agree: its first row group sees the
+        // whole chunk (every later group does too) and the chunk ends inside the block's range
+        const bool wg_fast = (c + 1) * CHUNK <= q_start + r0 && (c + 1) * CHUNK <= imax + 1;
+        if (wg_fast) chunk(c, std::integral_constant<bool, true>());
+        else chunk(c, std::integral_constant<bool, false>());
     }
     // ------------------------------------------------------------------ output
+    if (hf == 0 && g == 0) Lx[rg][r] = l;
+    __syncthreads();
+    const float lr = Lx[rg][r];
     const int rel = wrow0 + r;
     if (rel < r0 + nrows) {
-        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D + 32 * g;   // d = 32g + 8v + t
+        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D + 64 * hf + 16 * g;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            float4 y0, y1;
-            y0.x = o[0][v] / l; y0.y = o[1][v] / l; y0.z = o[2][v] / l; y0.w = o[3][v] / l;
-            y1.x = o[4][v] / l; y1.y = o[5][v] / l; y1.z = o[6][v] / l; y1.w = o[7][v] / l;
-            *reinterpret_cast<float4*>(out + 8 * v) = y0;
-            *reinterpret_cast<float4*>(out + 8 * v + 4) = y1;
+            float4 y;
+            y.x = o[0][v] / lr; y.y = o[1][v] / lr; y.z = o[2][v] / lr; y.w = o[3][v] / lr;
+            *reinterpret_cast<float4*>(out + 4 * v) = y;
         }
     }
 }
@@ -666,10 +646,10 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
 hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
     dim3 grid((a.Tq + BQ - 1) / BQ, a.Hq, a.B);
     if (a.dtype == 1)
-        hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, st, a.Q, a.Kc, a.Vc, a.Tq,
+        hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.Tq,
                            a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
     else
-        hipLaunchKernelGGL(attn_prefill_kernel<0>, grid, dim3(256), 0, st, a.Q, a.Kc, a.Vc, a.Tq,
+        hipLaunchKernelGGL(attn_prefill_kernel<0>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.Tq,
                            a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
     return hipGetLastError();
 }
