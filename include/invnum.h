@@ -103,6 +103,21 @@ int inv_fixed_order_gemm(const float* X, int64_t M, int64_t K, int64_t ldx,
                          float* Y, int64_t ldy, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
+ * inv_gated_gemm -- SwiGLU of a gate/up projection pair in one call:
+ *   H[m, i] = silu(dot_KS(X[m, :], up(W[2i, :]), K)) * dot_KS(X[m, :], up(W[2i+1, :]), K)
+ * with silu(a) = a / (1 + exp_f(-a)): bit for bit inv_fixed_order_gemm(X, W) followed by
+ * inv_swiglu on its even (gate) and odd (up) columns, without the intermediate.
+ * W: BF16 [N2, K] with the gate and up rows interleaved (row 2i = gate i, row 2i+1 = up i);
+ * N2 even.  H: FP32 [M, N2/2] (row stride ldh >= N2/2, 4-byte aligned, must not overlap X).
+ * X, M, K, ldx, ldw as inv_fixed_order_gemm.
+ * Sources: FP32 write-up section 5 (LayerCast); Meituan page, "key practices"
+ * (batch-invariant operators).
+ * ------------------------------------------------------------------------------------ */
+int inv_gated_gemm(const float* X, int64_t M, int64_t K, int64_t ldx,
+                   const uint16_t* W, int64_t N2, int64_t ldw,
+                   float* H, int64_t ldh, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
  * inv_rmsnorm -- ss = dot_KS(x, x, H); r = 1 / sqrt((ss / H) + eps); y_k = (x_k * r) * up(g_k)
  * X: FP32 [M, H] (ldx); gamma: BF16 [H]; Y: FP32 [M, H] (ldy), may alias X when ldy == ldx.
  * Division and square root are IEEE correctly rounded.  H >= 8, H % 8 == 0.

@@ -41,6 +41,7 @@ def _load():
         "inv_get_constants": (ctypes.c_int, [ctypes.POINTER(_Consts)]),
         "inv_fixed_order_gemm": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp]),
         "inv_rmsnorm": (ctypes.c_int, [vp, i64, i64, i64, vp, ctypes.c_float, vp, i64, vp]),
+        "inv_gated_gemm": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, i64, vp, i64, vp]),
         "inv_attention_prefill": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                                  i64, ctypes.c_float, vp, vp]),
         "inv_attention_decode_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64, i64]),
@@ -65,7 +66,7 @@ def _load():
 
 
 LIB = _load()
-EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "inv_rmsnorm",
+EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "inv_gated_gemm", "inv_rmsnorm",
            "inv_attention_prefill", "inv_attention_decode_workspace_bytes", "inv_attention_decode",
            "inv_lmhead_workspace_bytes", "inv_lmhead_logprob_top2", "inv_embed", "inv_rope_kv_append",
            "inv_swiglu", "inv_add", "inv_eval_numerics", "inv_mfma_f32_check")
@@ -143,6 +144,21 @@ def inv_fixed_order_gemm(X, W, R=None, out=None):
     _check(LIB.inv_fixed_order_gemm(_p(X), M, K, _row_ld(X), _p(W), N, _row_ld(W), _p(R),
                                     _row_ld(R) if R is not None else 0, _p(out), _row_ld(out),
                                     _stream(X)), "inv_fixed_order_gemm")
+    return out
+
+
+def inv_gated_gemm(X, W, out=None):
+    """H = silu(X . up(W[0::2])^T) * (X . up(W[1::2])^T): W bf16 [N2, K] with gate/up rows
+    interleaved; H fp32 [M, N2/2]."""
+    _dev(X, W, out)
+    _f32(X)
+    _bf16(W)
+    M, K = X.shape
+    N2 = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N2 // 2), dtype=torch.float32, device=X.device)
+    _check(LIB.inv_gated_gemm(_p(X), M, K, _row_ld(X), _p(W), N2, _row_ld(W), _p(out), _row_ld(out),
+                              _stream(X)), "inv_gated_gemm")
     return out
 
 

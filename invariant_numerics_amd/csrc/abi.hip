@@ -61,6 +61,18 @@ int inv_fixed_order_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, cons
     return fin(launch_gemm(a, S(stream)));
 }
 
+int inv_gated_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* W, int64_t N2,
+                   int64_t ldw, float* H, int64_t ldh, void* stream) {
+    if (!X || !W || !H) return INV_ERR_NULL;
+    if (M < 1 || N2 < 2 || N2 % 2 != 0 || K < 8 || K % 8 != 0 || M > I32MAX || N2 > I32MAX || K > I32MAX)
+        return INV_ERR_SHAPE;
+    if (ldx < K || ldw < K || ldh < N2 / 2) return INV_ERR_SHAPE;
+    if (!al16(X) || !al16(W) || ldx % 4 || ldw % 8) return INV_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(H) & 3u) return INV_ERR_ALIGN;
+    GemmArgs a{X, (int)M, (int)K, ldx, W, (int)N2, ldw, nullptr, 0, H, ldh, nullptr};
+    return fin(launch_gemm(a, S(stream), 2));
+}
+
 int inv_rmsnorm(const float* X, int64_t M, int64_t H, int64_t ldx, const uint16_t* gamma, float eps,
                 float* Y, int64_t ldy, void* stream) {
     if (!X || !gamma || !Y) return INV_ERR_NULL;

@@ -36,9 +36,10 @@ __device__ __forceinline__ int kpos(int k) { return (k & 3) * 8 + (k >> 2); }
 // Workgroup: 256 threads = 4 wavefronts in a 2 x 2 grid over a BM x BN output tile; each
 // wavefront owns (BM/2) x (BN/2) outputs = TI x TJ MFMA tiles.  Per output two registers:
 // the slice accumulator (MFMA C/D) and the folded total T.
-// ROLE only separates instantiations: 0 = activation projections, 1 = the vocabulary
-// projection of the LM head, so each can carry its own tile choice and profiles attribute
-// their time separately.
+// ROLE: 0 = activation projections, 1 = the vocabulary projection of the LM head (separate
+// instantiations, so each carries its own tile order and profiles attribute their time
+// separately), 2 = a gated projection: weight rows interleaved as (gate i, up i) and the
+// epilogue writes silu(gate) * up, the SwiGLU of the two outputs, instead of both.
 template <int BM, int BN, int ROLE>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         // owns a tile, never the order inside a dot.
         const int nMt = (gridM + BM - 1) / BM, nNt = (N + BN - 1) / BN;
         const int L = blockIdx.x;
-        if constexpr (ROLE == 0) {
+        if constexpr (ROLE != 1) {
             // Consecutive workgroup ids go to the 8 XCDs in turn, so id L is given tile u from
             // a contiguous range per XCD (a bijection of [0, T)); within it tiles are walked in
             // groups of GM tile rows, column by column, so the ~32 workgroups an XCD runs at
@@ -252,6 +253,31 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     }
 
     // lane (g, r) holds rows 4g..4g+3, column r of each 16 x 16 tile
+    if constexpr (ROLE == 2) {
+        // gated projection: columns 2i (gate) and 2i + 1 (up) sit in lanes r and r + 1 (r
+        // even).  Of the rows 4g + v' and 4g + v' + 1 (v' = 0, 2) the even lane finishes the
+        // first and the odd lane the second, so each lane evaluates half the
+        // H[m][i] = silu(gate) * up, silu(a) = a / (1 + exp_f(-a))
+        const int odd = r & 1;
+        const int gc = (n0 + wn0 + (r & ~1)) >> 1;          // output column of lane pair, tile 0
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int vp = 0; vp < 4; vp += 2) {
+                const int gm = m0 + wm0 + i * 16 + 4 * g + vp + odd;
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) {
+                    const float a0 = T[i][j][vp], a1 = T[i][j][vp + 1];
+                    const float x0 = __shfl_xor(a0, 1), x1 = __shfl_xor(a1, 1);
+                    const float gate = odd ? x1 : a0;
+                    const float up = odd ? a1 : x0;
+                    const int gn = n0 + wn0 + j * 16 + (r & ~1);
+                    if (interior || (gm < M && gn < N))
+                        Y[(int64_t)gm * ldy + gc + j * 8] = (gate / (1.0f + exp_f(-gate))) * up;
+                }
+            }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -435,6 +461,16 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
             }
         }
     }
+    if constexpr (ROLE == 2) {
+        // gated projection: weight rows 2i (gate) and 2i + 1 (up) are folded by threads fr and
+        // fr + 1 (adjacent lanes; ROWS is even); the even one writes silu(gate) * up
+        const float u = __shfl_down(T, 1);
+        if (folder && (fr & 1) == 0) {
+            const int gn = n0 + fr;
+            if (fm < M && gn < N) Y[(int64_t)fm * ldy + (gn >> 1)] = (T / (1.0f + exp_f(-T))) * u;
+        }
+        return;
+    }
     if (folder) {
         const int gn = n0 + fr;
         if (fm < M && gn < N) {
@@ -490,10 +526,11 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         return launch_skinny<16, ROLE>(a, st);
     }
     if (a.M <= 64) return launch_tiled<64, 64, ROLE>(a, st);
-    return launch_tiled<128, 128, ROLE>(a, st);
+    return launch_tiled<128, 256, ROLE>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role) {
+    if (role == 2) return launch_role<2>(a, st);
     return role == 1 ? launch_role<1>(a, st) : launch_role<0>(a, st);
 }
 

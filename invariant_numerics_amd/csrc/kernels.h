@@ -14,7 +14,8 @@ struct GemmArgs {
     float* Y; int64_t ldy;
     const int* Mdev;  // optional: device-side row count (<= M); rows beyond it are skipped
 };
-// role 0: activation projections; role 1: the LM head's vocabulary projection
+// role 0: activation projections; role 1: the LM head's vocabulary projection; role 2: gated
+// projection (W rows interleaved gate/up, Y[m][i] = silu(gate) * up, N even, R unused)
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role = 0);
 int64_t gemm_skinny_max_k();
 

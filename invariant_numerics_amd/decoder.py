@@ -9,13 +9,24 @@ Every op is row-independent and chunk boundaries are absolute key positions, so 
 blocking, batch size and prefill-vs-decode do not change a row's bits.
 
 Weight layouts (nn.Linear): wqkv [(Hq+2Hkv)D, H] = q rows | k rows | v rows; wo [H, Hq D];
-w13 [2F, H] = gate rows | up rows; w2 [H, F]; whead [V, H]; emb [V, H]; RoPE tables
+w13 [2F, H] = gate rows | up rows (held on the device with gate and up rows interleaved for
+the gated projection); w2 [H, F]; whead [V, H]; emb [V, H]; RoPE tables
 cos/sin [Tmax, D/2] fp32.
 """
 import numpy as np
 import torch
 
 from . import binding as inv
+
+
+def _interleave_gate_up(w13):
+    """[gate rows | up rows] -> rows (gate 0, up 0, gate 1, up 1, ...), the layout the gated
+    projection reads (a row permutation: every output is computed exactly as before)."""
+    F = w13.shape[0] // 2
+    out = np.empty_like(w13)
+    out[0::2] = w13[:F]
+    out[1::2] = w13[F:]
+    return out
 
 
 def _to_dev_bf16(a, dev):
@@ -34,7 +45,8 @@ class Decoder:
         self.emb = _to_dev_bf16(model["emb"], self.dev)
         self.whead = _to_dev_bf16(model["whead"], self.dev)
         self.gf = _to_dev_bf16(model["gf"], self.dev)
-        self.layers = [{k: _to_dev_bf16(v, self.dev) for k, v in layer.items()} for layer in model["layers"]]
+        self.layers = [{k: _to_dev_bf16(_interleave_gate_up(v) if k == "w13" else v, self.dev)
+                        for k, v in layer.items()} for layer in model["layers"]]
         self.cos = torch.from_numpy(np.ascontiguousarray(model["cos"])).to(self.dev)
         self.sin = torch.from_numpy(np.ascontiguousarray(model["sin"])).to(self.dev)
         self.tmax = int(tmax if tmax is not None else self.cos.shape[0])
@@ -48,19 +60,23 @@ class Decoder:
         # launch stream
         self.gemm_events = None
 
-    def _gemm(self, X, W, R=None, out=None):
+    def _gemm(self, X, W, R=None, out=None, gated=False):
+        def call():
+            if gated:
+                return inv.inv_gated_gemm(X, W, out=out)
+            return inv.inv_fixed_order_gemm(X, W, R=R, out=out)
         ev = self.gemm_events
         if ev is None:
-            return inv.inv_fixed_order_gemm(X, W, R=R, out=out)
+            return call()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
-        y = inv.inv_fixed_order_gemm(X, W, R=R, out=out)
+        y = call()
         e.record()
         M, K = X.shape
         N = W.shape[0]
         # algorithmic bytes: X and W read once, Y written once (R read once when given)
-        nbytes = 4 * M * K + 2 * N * K + 4 * M * N * (2 if R is not None else 1)
+        nbytes = 4 * M * K + 2 * N * K + 4 * M * (N // 2 if gated else N) * (2 if R is not None else 1)
         ev.append((s, e, 2.0 * M * N * K, float(nbytes)))
         return y
 
@@ -80,9 +96,7 @@ class Decoder:
             self._gemm(att.view(M, Hq * D), w["wo"], R=x, out=x)
             del att
             inv.inv_rmsnorm(x, w["g2"], self.eps, out=n)
-            gu = self._gemm(n, w["w13"])
-            h = inv.inv_swiglu(gu[:, :F], gu[:, F:])
-            del gu
+            h = self._gemm(n, w["w13"], gated=True)     # silu(gate) * up, [M, F]
             self._gemm(h, w["w2"], R=x, out=x)
             del h
         inv.inv_rmsnorm(x, self.gf, self.eps, out=n)

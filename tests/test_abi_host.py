@@ -61,6 +61,16 @@ def test_gemm_argument_validation(inv):
     assert g(FAKE, 4, 64, 66, FAKE, 8, 64, None, 0, FAKE, 8, None) == -3      # ldx % 4
 
 
+def test_gated_gemm_argument_validation(inv):
+    L = inv.LIB
+    g = L.inv_gated_gemm
+    assert g(None, 1, 64, 64, FAKE, 8, 64, FAKE, 4, None) == -1
+    assert g(FAKE, 1, 64, 64, FAKE, 7, 64, FAKE, 4, None) == -2       # odd N2
+    assert g(FAKE, 1, 64, 64, FAKE, 8, 64, FAKE, 3, None) == -2       # ldh < N2 / 2
+    assert g(FAKE, 1, 60, 64, FAKE, 8, 64, FAKE, 4, None) == -2       # K % 8
+    assert g(MIS, 1, 64, 64, FAKE, 8, 64, FAKE, 4, None) == -3        # misaligned X
+
+
 def test_attention_argument_validation(inv):
     L = inv.LIB
     p = L.inv_attention_prefill

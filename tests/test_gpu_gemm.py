@@ -94,3 +94,27 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
     cols = np.sort(synth.permutation(7401, n)[:192])
     want = orc.gemm(X[rows], W[cols])
     assert_bitwise(full[rows][:, cols], want, "oracle sample")
+
+
+@pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (5, 1000, 64), (16, 4096, 130),
+                                   (17, 264, 129), (64, 768, 64), (65, 4096, 300), (300, 1032, 257)])
+def test_gated_gemm_equals_gemm_then_swiglu(orc, M, K, F):
+    """inv_gated_gemm on gate/up rows interleaved equals inv_fixed_order_gemm followed by
+    inv_swiglu on its even and odd columns, bit for bit, on the one-wavefront GEMV path
+    (M <= 2), the 16-row GEMV path and the matrix-core path; small shapes also match the
+    oracle's gemm + swiglu on the two halves."""
+    say("gated gemm", M, K, F)
+    X = synth.normal(9960 + K, (M, K)) * np.float32(2)
+    W13 = synth.bf16_normal(9961 + F, (2 * F, K), 0.05)
+    Wi = np.empty_like(W13)
+    Wi[0::2] = W13[:F]
+    Wi[1::2] = W13[F:]
+    Xd, Wid = f32(X), bf16(Wi)
+    Y = inv().inv_fixed_order_gemm(Xd, Wid)
+    ref = inv().inv_swiglu(Y[:, 0::2].contiguous(), Y[:, 1::2].contiguous())
+    got = inv().inv_gated_gemm(Xd, Wid)
+    assert tuple(got.shape) == (M, F)
+    assert_bitwise(host(got), host(ref), "gated vs gemm + swiglu")
+    if M * K * F <= 300 * 1032 * 257:
+        want = orc.swiglu(orc.gemm(X, W13[:F]), orc.gemm(X, W13[F:]))
+        assert_bitwise(host(got), want, "oracle")
