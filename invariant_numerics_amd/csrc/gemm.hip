@@ -206,14 +206,23 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
             const int buf = t & 1;
             if (t + 1 < nt) load_tile((t + 1) * BK);
             read_frags(buf);
+            // the next tile goes to the other LDS buffer after the first two k-steps, so its
+            // stores overlap the matrix work instead of waiting at the barrier
 #pragma unroll
-            for (int s = 0; s < BK / 4; ++s)
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int i = 0; i < TI; ++i)
 #pragma unroll
                     for (int j = 0; j < TJ; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
             if (t + 1 < nt) store_tile(buf ^ 1);
+#pragma unroll
+            for (int s = 2; s < BK / 4; ++s)
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
             __syncthreads();
         }
         if (t == ntf && ntf < nt && sl == nslices - 1) {

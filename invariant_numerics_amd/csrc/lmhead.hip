@@ -88,8 +88,17 @@ __global__ __launch_bounds__(RED_THREADS) void lmhead_top2_kernel(
 // the sentinel index in place; such an index is replaced by the scan's starting choice
 // (top1 = 0, top2 = the lowest index != top1), so no index >= V ever reaches a load.
 __device__ __forceinline__ Top2 merged_top2(const Top2* __restrict__ part, int row, int ngrp, int V) {
-    Top2 t = part[(int64_t)row * ngrp];
-    for (int k = 1; k < ngrp; ++k) top2_merge(t, part[(int64_t)row * ngrp + k]);
+    const Top2* pr = part + (int64_t)row * ngrp;
+    Top2 t = pr[0];
+    int k = 1;
+    for (; k + 8 <= ngrp; k += 8) {             // loads issued 8 at a time (the merge is order-free)
+        Top2 q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) q[u] = pr[k + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) top2_merge(t, q[u]);
+    }
+    for (; k < ngrp; ++k) top2_merge(t, pr[k]);
     if (t.i1 < 0 || t.i1 >= V) t.i1 = 0;
     if (t.i2 < 0 || t.i2 >= V || t.i2 == t.i1) t.i2 = (t.i1 == 0) ? 1 : 0;
     return t;
@@ -134,8 +143,17 @@ __global__ void lmhead_final_kernel(
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
     const float* ts = tileS + (int64_t)row * ntiles;
+    // tiles folded in ascending order; their sums are loaded 16 at a time ahead of the adds
     float S = ts[0];
-    for (int u = 1; u < ntiles; ++u) S = S + ts[u];
+    int u = 1;
+    for (; u + 16 <= ntiles; u += 16) {
+        float q[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) q[e] = ts[u + e];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S = S + q[e];
+    }
+    for (; u < ntiles; ++u) S = S + ts[u];
     const int tg = target[orow];
     const float lp = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
     const float mg = M - zr[t.i2];
