@@ -138,7 +138,7 @@ def main():
     achieved = float(flops.sum() / durs.sum()) / 1e12
     gemm_share = float(durs.sum() / elapsed)
     default_workload = (B == 1 and T == 32768 and args.block == 4096 and args.layers == 4)
-    roof = dict(bound="mfma", kernel="gemm_mfma_kernel<128,256,0|2> (the four body projections; W1||W3 with the gated SwiGLU epilogue; FP32 matrix cores)",
+    roof = dict(bound="mfma", kernel="gemm_mfma_kernel<128,256,2,4,0|2> (the four body projections; W1||W3 with the gated SwiGLU epilogue; FP32 matrix cores, 32x32x2)",
                 achieved=round(achieved, 3),
                 peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / FP32_PEAK_TFLOPS, 4),
                 traffic=measured_traffic() if default_workload else None,

@@ -220,12 +220,22 @@ int inv_eval_numerics(int fn, const float* x, float* y, int64_t n, void* stream)
 
 /* Diagnostic: runs one v_mfma_f32_16x16x4_f32 per test.  Test t reads A [16 x 4],
  * B [4 x 16] and C [16 x 16] (row-major FP32, at A + 64 t, B + 64 t, C + 256 t) and writes
- * D = C + A B (at D + 256 t) exactly as the instruction rounds it.  The matrix-core paths of
- * fixed_order_gemm and attention rely on this instruction being the same arithmetic as four
- * fused multiply-adds in k order (k = 0, 1, 2, 3), i.e. the slice chain of dot_KS; the test
- * suite checks that property against the CPU reference through this entry point. */
+ * D = C + A B (at D + 256 t) exactly as the instruction rounds it.  The matrix-core path of
+ * attention relies on this instruction being the same arithmetic as four fused multiply-adds
+ * in k order (k = 0, 1, 2, 3), i.e. a sequential fma chain; the test suite checks that
+ * property against the CPU reference through this entry point. */
 int inv_mfma_f32_check(const float* A, const float* B, const float* C, float* D, int64_t ntests,
                        void* stream);
+
+/* Diagnostic: runs one v_mfma_f32_32x32x2_f32 per test.  Test t reads A [32 x 2], B [2 x 32]
+ * and C [32 x 32] (row-major FP32, at A + 64 t, B + 64 t, C + 1024 t) and writes D = C + A B
+ * (at D + 1024 t) exactly as the instruction rounds it.  The matrix-core path of
+ * fixed_order_gemm (and of the LM head's vocabulary projection) relies on this instruction
+ * being two fused multiply-adds in k order (k = 0, then 1), i.e. the slice chain of dot_KS;
+ * the test suite checks that property against the CPU reference through this entry point.
+ * Status: INV_ERR_NULL for a null pointer, INV_ERR_SHAPE for ntests < 1. */
+int inv_mfma32_f32_check(const float* A, const float* B, const float* C, float* D, int64_t ntests,
+                         void* stream);
 
 #ifdef __cplusplus
 }

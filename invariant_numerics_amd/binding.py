@@ -57,6 +57,7 @@ def _load():
         "inv_add": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
         "inv_eval_numerics": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, vp]),
         "inv_mfma_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
+        "inv_mfma32_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -69,7 +70,8 @@ LIB = _load()
 EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "inv_gated_gemm", "inv_rmsnorm",
            "inv_attention_prefill", "inv_attention_decode_workspace_bytes", "inv_attention_decode",
            "inv_lmhead_workspace_bytes", "inv_lmhead_logprob_top2", "inv_embed", "inv_rope_kv_append",
-           "inv_swiglu", "inv_add", "inv_eval_numerics", "inv_mfma_f32_check")
+           "inv_swiglu", "inv_add", "inv_eval_numerics", "inv_mfma_f32_check",
+           "inv_mfma32_f32_check")
 
 
 def _check(status, what):
@@ -301,4 +303,15 @@ def inv_mfma_f32_check(A, B, C, out=None):
     if out is None:
         out = torch.empty_like(C)
     _check(LIB.inv_mfma_f32_check(_p(A), _p(B), _p(C), _p(out), n, _stream(A)), "inv_mfma_f32_check")
+    return out
+
+
+def inv_mfma32_f32_check(A, B, C, out=None):
+    """A [n, 32, 2], B [n, 2, 32], C [n, 32, 32] fp32 -> D = C + A B per test, as the
+    32x32x2 FP32 matrix instruction computes it."""
+    _dev(A, B, C, out)
+    n = A.shape[0]
+    if out is None:
+        out = torch.empty_like(C)
+    _check(LIB.inv_mfma32_f32_check(_p(A), _p(B), _p(C), _p(out), n, _stream(A)), "inv_mfma32_f32_check")
     return out

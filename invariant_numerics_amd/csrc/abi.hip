@@ -193,4 +193,11 @@ int inv_mfma_f32_check(const float* A, const float* B, const float* C, float* D,
     return fin(launch_mfma_check(A, B, C, D, ntests, S(stream)));
 }
 
+int inv_mfma32_f32_check(const float* A, const float* B, const float* C, float* D, int64_t ntests,
+                         void* stream) {
+    if (!A || !B || !C || !D) return INV_ERR_NULL;
+    if (ntests < 1) return INV_ERR_SHAPE;
+    return fin(launch_mfma32_check(A, B, C, D, ntests, S(stream)));
+}
+
 }  // extern "C"

@@ -253,17 +253,25 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         __syncthreads();
         const float mc = __builtin_fmaxf(Mx[rg][0][r], Mx[rg][1][r]);
         float* prow = &P[rg][r][0];
+        // p of sub-block sb (the half's key tiles 4 sb + 2 hf + e), also into P for the partner
+        // and the causal tail
+        auto p_subblock = [&](const int sb) {
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const int t = 4 * (x >> 1) + 2 * hf + (x & 1);
+            for (int e = 0; e < 2; ++e) {
+                const int x = 2 * sb + e;
+                const int t = 4 * sb + 2 * hf + e;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int j = kbase + 16 * t + 4 * v + g;
-                const float pv = (full || j <= irow) ? exp_f(S[x][v] - mc) : 0.0f;
-                S[x][v] = pv;
-                prow[16 * t + 4 * v + g] = pv;
+                for (int v = 0; v < 4; ++v) {
+                    const int j = kbase + 16 * t + 4 * v + g;
+                    const float pv = (full || j <= irow) ? exp_f(S[x][v] - mc) : 0.0f;
+                    S[x][v] = pv;
+                    prow[16 * t + 4 * v + g] = pv;
+                }
             }
-        }
+        };
+#pragma unroll
+        for (int sb = 0; sb < CHUNK / SB; ++sb)
+            if (FAST || sb < nsb) p_subblock(sb);
         const int jspan = min(i0, kend) - kbase;
         const int jv = FAST ? kbase + CHUNK : kbase + ((jspan > 0 ? jspan : 0) & ~3);   // MFMA keys: [kbase, jv)
         __syncthreads();                                          // P complete for both halves
@@ -272,55 +280,65 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         f32x4 lc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 4; ++t) oc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the half index is a compile-time constant in the fast body, so the l steps (half 0
+        // only) and the choice between own and partner p cost no branch or select per step
+        auto pv_phase = [&](auto hf_tag) {
+            const int H = hf_tag;
 #pragma unroll
-        for (int sb = 0; sb < CHUNK / SB; ++sb) {
-            if (FAST || sb < nsb) {
-                const int kb = kbase + sb * SB;
-                const bool more = sb + 1 < nsb;
-                // after the last V sub-block comes the next chunk's first K sub-block (past the
-                // last chunk every row is out of range: the stage clamps and stores zeros)
-                if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
-                else st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
-                const float* kvb = KV[buf];
-                const float* vop = kvb + g * KLD + 64 * hf + 4 * r;   // + 4 s KLD at step s
-                const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
+            for (int sb = 0; sb < CHUNK / SB; ++sb) {
+                if (FAST || sb < nsb) {
+                    const int kb = kbase + sb * SB;
+                    const bool more = sb + 1 < nsb;
+                    // after the last V sub-block comes the next chunk's first K sub-block (past the
+                    // last chunk every row is out of range: the stage clamps and stores zeros)
+                    if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
+                    else st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
+                    const float* kvb = KV[buf];
+                    const float* vop = kvb + g * KLD + 64 * H + 4 * r;    // + 4 s KLD at step s
+                    const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
 #pragma unroll
-                for (int s = 0; s < SB / 4; ++s) {
-                    if (FAST || 4 * s < nmk) {
-                        // key tile 4 sb + s / 4 is this half's own when (s / 8) == hf
-                        const float own = S[sb * 2 + ((s >> 2) & 1)][s & 3];
-                        const float oth = prow[16 * (4 * sb + (s >> 2)) + 4 * (s & 3) + g];
-                        const float bp = ((s >> 3) == hf) ? own : oth;
-                        const float4 va = *reinterpret_cast<const float4*>(vop + 4 * s * KLD);
-                        oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, bp, oc[0], 0, 0, 0);
-                        oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, bp, oc[1], 0, 0, 0);
-                        oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, bp, oc[2], 0, 0, 0);
-                        oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, bp, oc[3], 0, 0, 0);
-                        if (hf == 0) lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
-                    }
-                }
-                if (!FAST) {
-                    // VALU continuation for keys [max(kb, jv), i], ascending (row r)
-                    const int j1 = min(kb + SB, irow + 1);
-                    for (int j = max(kb, jv); j < j1; ++j) {
-                        const float pv = prow[j - kbase];
-                        const float* vr = kvb + (j - kb) * KLD + 64 * hf + 16 * g;   // d = 64hf + 16g + 4v + t
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const float4 x4 = *reinterpret_cast<const float4*>(vr + 4 * v);
-                            oc[0][v] = __builtin_fmaf(pv, x4.x, oc[0][v]);
-                            oc[1][v] = __builtin_fmaf(pv, x4.y, oc[1][v]);
-                            oc[2][v] = __builtin_fmaf(pv, x4.z, oc[2][v]);
-                            oc[3][v] = __builtin_fmaf(pv, x4.w, oc[3][v]);
+                    for (int s = 0; s < SB / 4; ++s) {
+                        if (FAST || 4 * s < nmk) {
+                            // key tile 4 sb + s / 4 is this half's own when (s / 8) == hf
+                            const float bp = ((s >> 3) == H) ? S[sb * 2 + ((s >> 2) & 1)][s & 3]
+                                                             : prow[16 * (4 * sb + (s >> 2)) + 4 * (s & 3) + g];
+                            const float4 va = *reinterpret_cast<const float4*>(vop + 4 * s * KLD);
+                            oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, bp, oc[0], 0, 0, 0);
+                            oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, bp, oc[1], 0, 0, 0);
+                            oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, bp, oc[2], 0, 0, 0);
+                            oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, bp, oc[3], 0, 0, 0);
+                            if (H == 0) lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
                         }
-                        lc[0] = lc[0] + pv;
                     }
+                    if (!FAST) {
+                        // VALU continuation for keys [max(kb, jv), i], ascending (row r)
+                        const int j1 = min(kb + SB, irow + 1);
+                        for (int j = max(kb, jv); j < j1; ++j) {
+                            const float pv = prow[j - kbase];
+                            const float* vr = kvb + (j - kb) * KLD + 64 * H + 16 * g;    // d = 64hf + 16g + 4v + t
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const float4 x4 = *reinterpret_cast<const float4*>(vr + 4 * v);
+                                oc[0][v] = __builtin_fmaf(pv, x4.x, oc[0][v]);
+                                oc[1][v] = __builtin_fmaf(pv, x4.y, oc[1][v]);
+                                oc[2][v] = __builtin_fmaf(pv, x4.z, oc[2][v]);
+                                oc[3][v] = __builtin_fmaf(pv, x4.w, oc[3][v]);
+                            }
+                            lc[0] = lc[0] + pv;
+                        }
+                    }
+                    if (more) st.store_v(KV[buf ^ 1], tid);
+                    else st.store_k(KV[buf ^ 1], tid);
+                    __syncthreads();
+                    buf ^= 1;
                 }
-                if (more) st.store_v(KV[buf ^ 1], tid);
-                else st.store_k(KV[buf ^ 1], tid);
-                __syncthreads();
-                buf ^= 1;
             }
+        };
+        if constexpr (FAST) {
+            if (hf == 0) pv_phase(std::integral_constant<int, 0>());
+            else pv_phase(std::integral_constant<int, 1>());
+        } else {
+            pv_phase(hf);
         }
         // ------------------------------------------------------ 4. merge (l: half 0)
         if (ne) {

@@ -204,6 +204,27 @@ __global__ __launch_bounds__(64) void mfma_check_kernel(const float* __restrict_
     }
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// One v_mfma_f32_32x32x2_f32 per test: test t supplies A [32 x 2], B [2 x 32], C [32 x 32]
+// (row-major) and receives D = C + A B as the instruction computes it.  Lane l supplies
+// A[l % 32][l / 32] and B[l / 32][l % 32]; register v of lane l is the element at row
+// 8 (v / 4) + 4 (l / 32) + (v % 4), column l % 32.
+__global__ __launch_bounds__(64) void mfma32_check_kernel(const float* __restrict__ A,
+                                                          const float* __restrict__ B,
+                                                          const float* __restrict__ C,
+                                                          float* __restrict__ D, int64_t ntest) {
+    const int l = threadIdx.x, h = l >> 5, c = l & 31;
+    for (int64_t t = blockIdx.x; t < ntest; t += gridDim.x) {
+        const float a = A[t * 64 + c * 2 + h];      // A[c][h]
+        const float b = B[t * 64 + h * 32 + c];     // B[h][c]
+        f32x16_t acc;
+        for (int v = 0; v < 16; ++v) acc[v] = C[t * 1024 + (8 * (v >> 2) + 4 * h + (v & 3)) * 32 + c];
+        const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+        for (int v = 0; v < 16; ++v) D[t * 1024 + (8 * (v >> 2) + 4 * h + (v & 3)) * 32 + c] = d[v];
+    }
+}
+
 inline int grid_for(int64_t work, int block) {
     int64_t g = (work + block - 1) / block;
     if (g > 65536) g = 65536;
@@ -261,6 +282,13 @@ hipError_t launch_mfma_check(const float* A, const float* B, const float* C, flo
                              hipStream_t st) {
     const int grid = (int)(ntest < 4096 ? ntest : 4096);
     hipLaunchKernelGGL(mfma_check_kernel, dim3(grid), dim3(64), 0, st, A, B, C, D, ntest);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma32_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
+                               hipStream_t st) {
+    const int grid = (int)(ntest < 4096 ? ntest : 4096);
+    hipLaunchKernelGGL(mfma32_check_kernel, dim3(grid), dim3(64), 0, st, A, B, C, D, ntest);
     return hipGetLastError();
 }
 

@@ -21,37 +21,45 @@ namespace {
 
 constexpr int BK = 32;  // K tile; divides KS, so slice ends fall on tile ends
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Position of k (0..31) inside a tile row of LDS: lane group g of an MFMA reads
-// k = g, g+4, ..., g+28 (one per 4-wide MFMA step) as 8 contiguous floats.
-__device__ __forceinline__ int kpos(int k) { return (k & 3) * 8 + (k >> 2); }
+// Position of k (0..31) inside a tile row of LDS: the lane half h of an MFMA reads
+// k = h, h+2, ..., h+30 (one per 2-wide MFMA step) as 16 contiguous floats.
+__device__ __forceinline__ int kpos(int k) { return (k & 1) * 16 + (k >> 1); }
 
-// Register-tiled GEMM on the FP32 matrix cores.  v_mfma_f32_16x16x4_f32 advances every
-// output of a 16x16 tile by k = 4s, 4s+1, 4s+2, 4s+3 as four fused multiply-adds in that
-// order (each rounded once) -- the same arithmetic as the sequential fma chain of a slice,
-// so issuing the steps s in ascending order reproduces dot_KS bit for bit.  (This is a
-// measured property of the gfx950 instruction, checked by the test suite against the
-// CPU reference through inv_mfma_f32_check.)
-// Workgroup: 256 threads = 4 wavefronts in a 2 x 2 grid over a BM x BN output tile; each
-// wavefront owns (BM/2) x (BN/2) outputs = TI x TJ MFMA tiles.  Per output two registers:
-// the slice accumulator (MFMA C/D) and the folded total T.
+// Register-tiled GEMM on the FP32 matrix cores.  v_mfma_f32_32x32x2_f32 advances every
+// output of a 32x32 tile by k = 2s, then k = 2s+1, as two fused multiply-adds in that order
+// (each rounded once) -- the same arithmetic as the sequential fma chain of a slice, so
+// issuing the steps s in ascending order reproduces dot_KS bit for bit.  (This is a measured
+// property of the gfx950 instruction, checked by the test suite against the CPU reference
+// through inv_mfma_f32_check.)  The 32x32 form is used rather than the 16x16x4 one because
+// a single wavefront per SIMD keeps the matrix pipe nearly full with it; with the 16x16
+// form it issues a quarter of its cycles idle.
+// Operands: lane l (half h = l / 32, c = l % 32) supplies A[row c][k = 2s + h] and
+// B[k = 2s + h][column c]; result register v of lane l is the output at row
+// 8 (v / 4) + 4 h + (v % 4), column c.
+// Workgroup: WGM x WGN wavefronts over a BM x BN output tile; each wavefront owns
+// (BM/WGM) x (BN/WGN) outputs = TI x TJ MFMA tiles.  Per output two registers: the slice
+// accumulator (MFMA C/D) and the folded total T.  The large tile runs 8 wavefronts of
+// 64 x 64 outputs, two per SIMD, so one wavefront's LDS waits and barrier are covered by
+// the other's matrix work.
 // ROLE: 0 = activation projections, 1 = the vocabulary projection of the LM head (separate
 // instantiations, so each carries its own tile order and profiles attribute their time
 // separately), 2 = a gated projection: weight rows interleaved as (gate i, up i) and the
 // epilogue writes silu(gate) * up, the SwiGLU of the two outputs, instead of both.
-template <int BM, int BN, int ROLE>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(
+template <int BM, int BN, int WGM, int WGN, int ROLE>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
     float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
     const int gridM = M;                           // the row count the grid was sized for
-    constexpr int WM = BM / 2, WN = BN / 2;
-    constexpr int TI = WM / 16, TJ = WN / 16;
+    constexpr int NT = 64 * WGM * WGN;              // threads
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int TI = WM / 32, TJ = WN / 32;
     constexpr int LDT = BK + 4;                    // padded LDS row (floats)
-    constexpr int XV = BM * (BK / 4) / 256;        // float4 loads of X per thread per tile
-    constexpr int WV = BN * (BK / 8) / 256;        // 16-byte loads of W per thread per tile
+    constexpr int XV = BM * (BK / 4) / NT;         // float4 loads of X per thread per tile
+    constexpr int WV = BN * (BK / 8) / NT;         // 16-byte loads of W per thread per tile
     static_assert(XV >= 1 && WV >= 1 && TI >= 1 && TJ >= 1, "tile too small");
     __shared__ float As[2][BM][LDT];
     __shared__ float Bs[2][BN][LDT];
@@ -89,8 +97,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     if (m0 >= M) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
-    const int g = lane >> 4, r = lane & 15;
-    const int wm0 = (wv >> 1) * WM, wn0 = (wv & 1) * WN;
+    const int h = lane >> 5, c = lane & 31;
+    const int wm0 = (wv / WGN) * WM, wn0 = (wv % WGN) * WN;
 
     // Per-thread source rows (clamped into range, with validity flags) computed once; each
     // tile advances the pointers by BK.  Elements outside M x K or N x K load as zeros.
@@ -101,14 +109,14 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     bool xin[XV], win[WV];
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
-        const int idx = tid + i * 256;
+        const int idx = tid + i * NT;
         const int row = idx / (BK / 4), q = idx % (BK / 4);
         xin[i] = m0 + row < M;
         xp[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + 4 * q;
     }
 #pragma unroll
     for (int i = 0; i < WV; ++i) {
-        const int idx = tid + i * 256;
+        const int idx = tid + i * NT;
         const int row = idx / (BK / 8), o = idx % (BK / 8);
         win[i] = n0 + row < N;
         wp[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + 8 * o;
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         }
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
-            const int q = (tid + i * 256) % (BK / 4);
+            const int q = (tid + i * NT) % (BK / 4);
             const int gk = k0 + 4 * q;
             const bool in = xin[i] && gk < K;
             const float4 t = *reinterpret_cast<const float4*>(xp[i] + min(k0, K - 4 - 4 * q));
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
-            const int o = (tid + i * 256) % (BK / 8);
+            const int o = (tid + i * NT) % (BK / 8);
             const int gk = k0 + 8 * o;
             const bool in = win[i] && gk < K;
             const uint4 t = *reinterpret_cast<const uint4*>(wp[i] + min(k0, K - 8 - 8 * o));
@@ -142,57 +150,68 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
-            const int idx = tid + i * 256;
+            const int idx = tid + i * NT;
             const int row = idx / (BK / 4), q = idx % (BK / 4);
+            // k = 4q + {0, 2} and 4q + {1, 3} land on adjacent positions
             float* d = As[buf][row];
-            d[kpos(4 * q + 0)] = xr[i].x;
-            d[kpos(4 * q + 1)] = xr[i].y;
-            d[kpos(4 * q + 2)] = xr[i].z;
-            d[kpos(4 * q + 3)] = xr[i].w;
+            *reinterpret_cast<float2*>(d + kpos(4 * q)) = make_float2(xr[i].x, xr[i].z);
+            *reinterpret_cast<float2*>(d + kpos(4 * q + 1)) = make_float2(xr[i].y, xr[i].w);
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
-            const int idx = tid + i * 256;
+            const int idx = tid + i * NT;
             const int row = idx / (BK / 8), o = idx % (BK / 8);
+            // the even k of the 8 (low halves) and the odd k (high halves) are 4 adjacent
+            // positions each
             float* d = Bs[buf][row];
-            d[kpos(8 * o + 0)] = bf16_lo(wr[i].x);
-            d[kpos(8 * o + 1)] = bf16_hi(wr[i].x);
-            d[kpos(8 * o + 2)] = bf16_lo(wr[i].y);
-            d[kpos(8 * o + 3)] = bf16_hi(wr[i].y);
-            d[kpos(8 * o + 4)] = bf16_lo(wr[i].z);
-            d[kpos(8 * o + 5)] = bf16_hi(wr[i].z);
-            d[kpos(8 * o + 6)] = bf16_lo(wr[i].w);
-            d[kpos(8 * o + 7)] = bf16_hi(wr[i].w);
+            *reinterpret_cast<float4*>(d + kpos(8 * o)) =
+                make_float4(bf16_lo(wr[i].x), bf16_lo(wr[i].y), bf16_lo(wr[i].z), bf16_lo(wr[i].w));
+            *reinterpret_cast<float4*>(d + kpos(8 * o + 1)) =
+                make_float4(bf16_hi(wr[i].x), bf16_hi(wr[i].y), bf16_hi(wr[i].z), bf16_hi(wr[i].w));
         }
     };
 
-    f32x4 acc[TI][TJ], T[TI][TJ];
+    f32x16 acc[TI][TJ], T[TI][TJ];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) { acc[i][j][v] = 0.0f; T[i][j][v] = 0.0f; }
+            for (int v = 0; v < 16; ++v) { acc[i][j][v] = 0.0f; T[i][j][v] = 0.0f; }
 
     const int ntf = K / BK;                        // full tiles
     const int nt = (K + BK - 1) / BK;              // plus a partial last tile when K % BK != 0
     const int nslices = (K + KS - 1) / KS;
-    float a[TI][8], b[TJ][8];
+    constexpr int NS = BK / 2;                     // MFMA k-steps per tile
+    float a[TI][NS], b[TJ][NS];
     auto read_frags = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-            const float4* src = reinterpret_cast<const float4*>(&As[buf][wm0 + i * 16 + r][g * 8]);
-            const float4 lo = src[0], hi = src[1];
-            a[i][0] = lo.x; a[i][1] = lo.y; a[i][2] = lo.z; a[i][3] = lo.w;
-            a[i][4] = hi.x; a[i][5] = hi.y; a[i][6] = hi.z; a[i][7] = hi.w;
+            const float4* src = reinterpret_cast<const float4*>(&As[buf][wm0 + i * 32 + c][h * 16]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = src[q];
+                a[i][4 * q] = v.x; a[i][4 * q + 1] = v.y; a[i][4 * q + 2] = v.z; a[i][4 * q + 3] = v.w;
+            }
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-            const float4* src = reinterpret_cast<const float4*>(&Bs[buf][wn0 + j * 16 + r][g * 8]);
-            const float4 lo = src[0], hi = src[1];
-            b[j][0] = lo.x; b[j][1] = lo.y; b[j][2] = lo.z; b[j][3] = lo.w;
-            b[j][4] = hi.x; b[j][5] = hi.y; b[j][6] = hi.z; b[j][7] = hi.w;
+            const float4* src = reinterpret_cast<const float4*>(&Bs[buf][wn0 + j * 32 + c][h * 16]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = src[q];
+                b[j][4 * q] = v.x; b[j][4 * q + 1] = v.y; b[j][4 * q + 2] = v.z; b[j][4 * q + 3] = v.w;
+            }
         }
+    };
+    auto steps = [&](const int s0, const int s1) {
+#pragma unroll
+        for (int s = s0; s < s1; ++s)
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < TJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
     };
     load_tile(0);
     store_tile(0);
@@ -206,23 +225,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
             const int buf = t & 1;
             if (t + 1 < nt) load_tile((t + 1) * BK);
             read_frags(buf);
-            // the next tile goes to the other LDS buffer after the first two k-steps, so its
-            // stores overlap the matrix work instead of waiting at the barrier
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-#pragma unroll
-                    for (int j = 0; j < TJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+            // the next tile goes to the other LDS buffer halfway through the k-steps: its loads
+            // have had half the tile's matrix work to arrive, and its stores overlap the rest
+            // instead of waiting at the barrier
+            steps(0, NS / 2);
             if (t + 1 < nt) store_tile(buf ^ 1);
-#pragma unroll
-            for (int s = 2; s < BK / 4; ++s)
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-#pragma unroll
-                    for (int j = 0; j < TJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+            steps(NS / 2, NS);
             __syncthreads();
         }
         if (t == ntf && ntf < nt && sl == nslices - 1) {
@@ -230,15 +238,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
             const int kend = K - t * BK;
             read_frags(t & 1);
 #pragma unroll
-            for (int s = 0; s < BK / 4; ++s) {
-                if (4 * s < kend) {
-#pragma unroll
-                    for (int i = 0; i < TI; ++i)
-#pragma unroll
-                        for (int j = 0; j < TJ; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
-                }
-            }
+            for (int s = 0; s < NS; ++s)
+                if (2 * s < kend) steps(s, s + 1);
             ++t;
         }
         // the slice is complete: fold it into T in slice order, restart the accumulator
@@ -253,36 +254,38 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
                 for (int j = 0; j < TJ; ++j)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) T[i][j][v] = T[i][j][v] + acc[i][j][v];
+                    for (int v = 0; v < 16; ++v) T[i][j][v] = T[i][j][v] + acc[i][j][v];
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     }
 
-    // lane (g, r) holds rows 4g..4g+3, column r of each 16 x 16 tile
+    // register v of lane (h, c) holds row 8 (v / 4) + 4 h + (v % 4), column c of each 32 x 32 tile
     if constexpr (ROLE == 2) {
-        // gated projection: columns 2i (gate) and 2i + 1 (up) sit in lanes r and r + 1 (r
-        // even).  Of the rows 4g + v' and 4g + v' + 1 (v' = 0, 2) the even lane finishes the
+        // gated projection: columns 2i (gate) and 2i + 1 (up) sit in lanes c and c + 1 (c
+        // even).  Of the rows of registers v and v + 1 (v even) the even lane finishes the
         // first and the odd lane the second, so each lane evaluates half the
         // H[m][i] = silu(gate) * up, silu(a) = a / (1 + exp_f(-a))
-        const int odd = r & 1;
-        const int gc = (n0 + wn0 + (r & ~1)) >> 1;          // output column of lane pair, tile 0
+        const int odd = c & 1;
+        const int gc = (n0 + wn0 + (c & ~1)) >> 1;          // output column of lane pair, tile 0
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
-            for (int vp = 0; vp < 4; vp += 2) {
-                const int gm = m0 + wm0 + i * 16 + 4 * g + vp + odd;
+            for (int vp = 0; vp < 16; vp += 2) {
+                const int gm = m0 + wm0 + i * 32 + 8 * (vp >> 2) + 4 * h + (vp & 3) + odd;
 #pragma unroll
                 for (int j = 0; j < TJ; ++j) {
                     const float a0 = T[i][j][vp], a1 = T[i][j][vp + 1];
                     const float x0 = __shfl_xor(a0, 1), x1 = __shfl_xor(a1, 1);
                     const float gate = odd ? x1 : a0;
                     const float up = odd ? a1 : x0;
-                    const int gn = n0 + wn0 + j * 16 + (r & ~1);
+                    const int gn = n0 + wn0 + j * 32 + (c & ~1);
                     if (interior || (gm < M && gn < N))
-                        Y[(int64_t)gm * ldy + gc + j * 8] = (gate / (1.0f + exp_f(-gate))) * up;
+                        Y[(int64_t)gm * ldy + gc + j * 16] = (gate / (1.0f + exp_f(-gate))) * up;
                 }
             }
         return;
@@ -290,17 +293,17 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int gm = m0 + wm0 + i * 16 + 4 * g + v;
+        for (int v = 0; v < 16; ++v) {
+            const int gm = m0 + wm0 + i * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
             if (!interior && gm >= M) continue;
-            float* yrow = Y + (int64_t)gm * ldy + n0 + wn0 + r;
-            const float* rrow = R ? R + (int64_t)gm * ldr + n0 + wn0 + r : nullptr;
+            float* yrow = Y + (int64_t)gm * ldy + n0 + wn0 + c;
+            const float* rrow = R ? R + (int64_t)gm * ldr + n0 + wn0 + c : nullptr;
 #pragma unroll
             for (int j = 0; j < TJ; ++j) {
-                if (!interior && n0 + wn0 + j * 16 + r >= N) continue;
+                if (!interior && n0 + wn0 + j * 32 + c >= N) continue;
                 float y = T[i][j][v];
-                if (rrow) y = rrow[j * 16] + y;
-                yrow[j * 16] = y;
+                if (rrow) y = rrow[j * 32] + y;
+                yrow[j * 32] = y;
             }
         }
 }
@@ -490,10 +493,10 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     }
 }
 
-template <int BM, int BN, int ROLE>
+template <int BM, int BN, int WGM, int WGN, int ROLE>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, ROLE>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WGM, WGN, ROLE>), grid, dim3(64 * WGM * WGN), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
 }
@@ -534,8 +537,8 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         if (a.M <= 8) return launch_skinny<8, ROLE>(a, st);
         return launch_skinny<16, ROLE>(a, st);
     }
-    if (a.M <= 64) return launch_tiled<64, 64, ROLE>(a, st);
-    return launch_tiled<128, 256, ROLE>(a, st);
+    if (a.M <= 64) return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
+    return launch_tiled<128, 256, 2, 4, ROLE>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role) {

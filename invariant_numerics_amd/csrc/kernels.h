@@ -56,5 +56,7 @@ hipError_t launch_add(const float* A, const float* B, int M, int N, int64_t lda,
 hipError_t launch_eval_numerics(int fn, const float* x, float* y, int64_t n, hipStream_t st);
 hipError_t launch_mfma_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
                              hipStream_t st);
+hipError_t launch_mfma32_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
+                               hipStream_t st);
 
 }  // namespace invnum
