@@ -22,7 +22,7 @@ namespace invnum {
 namespace {
 
 constexpr int D = 128;
-constexpr int BQ = 64;    // query rows per prefill workgroup
+constexpr int BQ = 128;   // query rows per prefill workgroup
 
 template <int DT>
 __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* dst) {
@@ -41,33 +41,35 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 // four fused multiply-adds in k order, so both contractions keep their sequential order:
 // the scores over d = 0..127 and the PV sums over keys in ascending j.
 //
-// Workgroup: 512 threads = 8 wavefronts over BQ = 64 consecutive query rows of one (b, h).
-// Row group rg = w % 4 (rows 16 rg .. 16 rg + 15) is shared by the pair of wavefronts
-// w = rg (half 0) and w = rg + 4 (half 1), so each keeps half the state of a row group and two
-// wavefronts run on every SIMD.  Per 256-key chunk:
+// Workgroup: 512 threads = 8 wavefronts over BQ = 128 consecutive query rows of one (b, h);
+// wavefront w owns rows 16 w .. 16 w + 15 outright (scores of every key, every d of the
+// output), so no partial state is exchanged between wavefronts and all eight share each K/V
+// sub-block staged in LDS.  Per 256-key chunk:
 //   1. scores S^T = K Q^T on the matrix cores: A = K tile (lane (g, r) supplies key
 //      16t + pi(r), d = 4s + g, with pi(i) = 4 (i % 4) + i / 4), B = Q^T (lane (g, r) supplies
 //      row r, d = 4s + g, held in registers); lane (g, r) receives in register v the score of
 //      row r with key 16t + 4v + g.  K streams through double-buffered LDS in 64-key
-//      sub-blocks; half hf computes key tiles 4 sb + 2 hf and 4 sb + 2 hf + 1 of sub-block sb;
-//   2. each half takes the maximum of its visible scores; the pair exchanges them through LDS
-//      and both form m_c; p = exp_f(s - m_c) for the half's keys, written also to an LDS row
-//      buffer P so the partner and the causal tail can read every p of the chunk;
-//   3. PV: half hf accumulates d in [64 hf, 64 hf + 64) over all keys of the chunk in
-//      ascending order.  O^T = V^T P^T, output tile t (t = 0..3) taking d = 64 hf + 4i + t:
-//      step s covers keys 4s .. 4s + 3, lane (g, r) supplies V[key 4s + g][64 hf + 4r .. + 3]
-//      (one 16-byte LDS read for the four tiles) and, as B, P[row r][key 4s + g] -- from its own
-//      score registers for its own key tiles, else from P -- and accumulates
-//      o[row r][d = 64 hf + 16g + 4v + t].  Half 0 also sums l with an all-ones A operand,
-//      fma(1, p, l) = l + p, one rounding per key.  The matrix cores take the keys below the
-//      first multiple-of-4 boundary that every row of the group sees; the rest of the causal
-//      triangle (at most 19 keys per row) continues on the VALU in ascending j, so masked keys
-//      are skipped rather than added as zeros;
+//      sub-blocks (four key tiles each);
+//   2. m_c = the maximum of the row's visible scores (lanes of a row exchange theirs);
+//      p = exp_f(s - m_c) in place;
+//   3. PV: O^T = V^T P^T over all keys of the chunk in ascending order, output tile t
+//      (t = 0..7) taking d = 8i + t: step s covers keys 4s .. 4s + 3, lane (g, r) supplies
+//      V[key 4s + g][8r .. 8r + 7] (two 16-byte LDS reads for the eight tiles) and, as B, its
+//      own p of key 4s + g, and accumulates o[row r][d = 32g + 8v + t].  The l-sum runs on
+//      the same instruction with an all-ones A operand, fma(1, p, l) = l + p, one rounding per
+//      key.  The matrix cores take the keys below the first multiple-of-4 boundary that every
+//      row of the wavefront sees; the rest of the causal triangle (at most 19 keys per row)
+//      continues on the VALU in ascending j, with those p passed through a small per-wavefront
+//      LDS buffer, so masked keys are skipped rather than added as zeros;
 //   4. merge into the running (m, l, o) with the formulas of the decode merge kernel.
+// Blocks are issued heaviest first (the last rows see the most keys), and consecutive
+// workgroup ids cycle over the kv heads so the workgroups running together on one XCD (ids
+// are dealt to the 8 XCDs in turn) share one kv head's K/V in its L2.
 constexpr int SB = 64;          // keys per LDS sub-block
 constexpr int KLD = D + 4;      // LDS row: K with d permuted ((d % 4) * 32 + d / 4), V row-major
 constexpr int PNT = 512;        // threads per prefill workgroup
-constexpr int PLD = CHUNK + 4;  // LDS row of P (floats)
+constexpr int TW = 20;          // keys of the causal tail buffer (at most 19 are used)
+constexpr int TLD = TW + 1;     // its padded row
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -133,26 +135,34 @@ struct Stage {
 template <int DT>
 __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
-    int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O) {
+    int B, int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O) {
     __shared__ __attribute__((aligned(16))) float KV[2][SB * KLD];
-    __shared__ __attribute__((aligned(16))) float P[4][16][PLD];
-    __shared__ float Mx[4][2][16];
-    __shared__ float Lx[4][16];
+    __shared__ float Tail[PNT / 64][16][TLD];
 
     const int tid = threadIdx.x;
     // the wavefront index is uniform in a wavefront: in a scalar register, everything derived
-    // from it (row group, half, causal bounds) takes scalar branches
+    // from it (rows, causal bounds) takes scalar branches
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rg = w & 3, hf = w >> 2;
     const int g = lane >> 4, r = lane & 15;
     const int pr = 4 * (r & 3) + (r >> 2);             // pi(r)
-    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int qb, h, b;
+    {
+        // workgroup id -> (row block, head, sequence): row blocks from the last (heaviest) down;
+        // within one row block, consecutive ids take q heads h = (u % Hkv) G + u / Hkv, i.e. they
+        // cycle over the kv heads
+        const int nqb = (Tq + BQ - 1) / BQ, HB = Hq * B;
+        const int L = blockIdx.x, u = L % HB, G = Hq / Hkv;
+        qb = nqb - 1 - L / HB;
+        b = u / Hq;
+        const int hh = u % Hq;
+        h = (hh % Hkv) * G + hh / Hkv;
+    }
     const int kvh = h / (Hq / Hkv);
     const int r0 = qb * BQ;
     const int nrows = min(BQ, Tq - r0);
     const int imax = q_start + r0 + nrows - 1;          // last valid absolute row of the block
     const int64_t kvbase = ((int64_t)b * Hkv + kvh) * Tmax * D;
-    const int wrow0 = r0 + 16 * rg;                     // first row (relative) of the row group
+    const int wrow0 = r0 + 16 * w;                      // first row (relative) of the wavefront
     const int i0 = q_start + wrow0;                     // its absolute position
     const int irow = min(i0 + r, imax);                 // the lane's row, clamped
 
@@ -169,10 +179,10 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         }
     }
 
-    f32x4 o[4];
+    f32x4 o[8];
     float m = 0.0f, l = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int clast = imax / CHUNK;
     Stage<DT> st;
@@ -180,8 +190,9 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
     st.load(Kc, kvbase, 0, min(CHUNK, imax + 1), tid);
     st.store_k(KV[0], tid);
     __syncthreads();
+    float* tail = &Tail[w][r][0];
 
-    // One chunk.  FAST: every row of the group sees all 256 keys of the chunk and all four
+    // One chunk.  FAST: every row of the workgroup sees all 256 keys of the chunk and all four
     // sub-blocks are in range -- the common case -- so no guard, mask or causal tail is needed
     // and the body is straight-line; otherwise every step checks its bounds.
     auto chunk = [&](const int c, auto fast_tag) {
@@ -190,11 +201,11 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         const int kend = min(kbase + CHUNK, imax + 1);         // keys some row of the block needs
         const int nsb = FAST ? CHUNK / SB : (kend - kbase + SB - 1) / SB;   // active sub-blocks
         const int nkend = min(kbase + 2 * CHUNK, imax + 1);    // next chunk's key bound
-        // ------------------------------------------------------ 1. scores (own key tiles)
-        // S[2 sb + e] is key tile 4 sb + 2 hf + e of the chunk
-        f32x4 S[8];
+        // ------------------------------------------------------ 1. scores
+        // S[t] is key tile t of the chunk
+        f32x4 S[16];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 16; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sb = 0; sb < CHUNK / SB; ++sb) {
             if (FAST || sb < nsb) {
@@ -204,22 +215,22 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
                 if (FAST || kbase + sb * SB <= i0 + 15) {
 #pragma unroll
                     for (int s4 = 0; s4 < 8; ++s4) {
-                        float4 kk[2];
+                        float4 kk[4];
 #pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            kk[e] = *reinterpret_cast<const float4*>(kvb + ((2 * hf + e) * 16 + pr) * KLD + g * 32 + 4 * s4);
+                        for (int e = 0; e < 4; ++e)
+                            kk[e] = *reinterpret_cast<const float4*>(kvb + (e * 16 + pr) * KLD + g * 32 + 4 * s4);
 #pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].x, qf[4 * s4 + 0], S[sb * 2 + e], 0, 0, 0);
+                        for (int e = 0; e < 4; ++e)
+                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].x, qf[4 * s4 + 0], S[sb * 4 + e], 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].y, qf[4 * s4 + 1], S[sb * 2 + e], 0, 0, 0);
+                        for (int e = 0; e < 4; ++e)
+                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].y, qf[4 * s4 + 1], S[sb * 4 + e], 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].z, qf[4 * s4 + 2], S[sb * 2 + e], 0, 0, 0);
+                        for (int e = 0; e < 4; ++e)
+                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].z, qf[4 * s4 + 2], S[sb * 4 + e], 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 2; ++e)
-                            S[sb * 2 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].w, qf[4 * s4 + 3], S[sb * 2 + e], 0, 0, 0);
+                        for (int e = 0; e < 4; ++e)
+                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].w, qf[4 * s4 + 3], S[sb * 4 + e], 0, 0, 0);
                     }
                 }
                 if (sb + 1 < nsb) st.store_k(KV[buf ^ 1], tid);
@@ -237,122 +248,110 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         const bool full = FAST || kbase + CHUNK <= i0;         // every row sees the whole chunk
         float mh = -__builtin_inff();
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            const int t = 4 * (x >> 1) + 2 * hf + (x & 1);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int j = kbase + 16 * t + 4 * v + g;
-                const float sv = S[x][v] * scale;
-                S[x][v] = sv;
-                if (full || j <= irow) mh = __builtin_fmaxf(mh, sv);
-            }
-        }
-        mh = __builtin_fmaxf(mh, __shfl_xor(mh, 16));
-        mh = __builtin_fmaxf(mh, __shfl_xor(mh, 32));
-        if (g == 0) Mx[rg][hf][r] = mh;
-        __syncthreads();
-        const float mc = __builtin_fmaxf(Mx[rg][0][r], Mx[rg][1][r]);
-        float* prow = &P[rg][r][0];
-        // p of sub-block sb (the half's key tiles 4 sb + 2 hf + e), also into P for the partner
-        // and the causal tail
-        auto p_subblock = [&](const int sb) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int x = 2 * sb + e;
-                const int t = 4 * sb + 2 * hf + e;
+        for (int t = 0; t < 16; ++t) {
+            if (FAST || t < 4 * nsb) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int j = kbase + 16 * t + 4 * v + g;
-                    const float pv = (full || j <= irow) ? exp_f(S[x][v] - mc) : 0.0f;
-                    S[x][v] = pv;
-                    prow[16 * t + 4 * v + g] = pv;
+                    const float sv = S[t][v] * scale;
+                    S[t][v] = sv;
+                    if (full || j <= irow) mh = __builtin_fmaxf(mh, sv);
                 }
             }
-        };
-#pragma unroll
-        for (int sb = 0; sb < CHUNK / SB; ++sb)
-            if (FAST || sb < nsb) p_subblock(sb);
+        }
+        mh = __builtin_fmaxf(mh, __shfl_xor(mh, 16));
+        const float mc = __builtin_fmaxf(mh, __shfl_xor(mh, 32));
         const int jspan = min(i0, kend) - kbase;
         const int jv = FAST ? kbase + CHUNK : kbase + ((jspan > 0 ? jspan : 0) & ~3);   // MFMA keys: [kbase, jv)
-        __syncthreads();                                          // P complete for both halves
-        // ------------------------------------------------------ 3. PV and l
-        f32x4 oc[4];
-        f32x4 lc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) oc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // the half index is a compile-time constant in the fast body, so the l steps (half 0
-        // only) and the choice between own and partner p cost no branch or select per step
-        auto pv_phase = [&](auto hf_tag) {
-            const int H = hf_tag;
+        for (int t = 0; t < 16; ++t) {
+            if (FAST || t < 4 * nsb) {
 #pragma unroll
-            for (int sb = 0; sb < CHUNK / SB; ++sb) {
-                if (FAST || sb < nsb) {
-                    const int kb = kbase + sb * SB;
-                    const bool more = sb + 1 < nsb;
-                    // after the last V sub-block comes the next chunk's first K sub-block (past the
-                    // last chunk every row is out of range: the stage clamps and stores zeros)
-                    if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
-                    else st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
-                    const float* kvb = KV[buf];
-                    const float* vop = kvb + g * KLD + 64 * H + 4 * r;    // + 4 s KLD at step s
-                    const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
-#pragma unroll
-                    for (int s = 0; s < SB / 4; ++s) {
-                        if (FAST || 4 * s < nmk) {
-                            // key tile 4 sb + s / 4 is this half's own when (s / 8) == hf
-                            const float bp = ((s >> 3) == H) ? S[sb * 2 + ((s >> 2) & 1)][s & 3]
-                                                             : prow[16 * (4 * sb + (s >> 2)) + 4 * (s & 3) + g];
-                            const float4 va = *reinterpret_cast<const float4*>(vop + 4 * s * KLD);
-                            oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, bp, oc[0], 0, 0, 0);
-                            oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, bp, oc[1], 0, 0, 0);
-                            oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, bp, oc[2], 0, 0, 0);
-                            oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, bp, oc[3], 0, 0, 0);
-                            if (H == 0) lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
-                        }
-                    }
-                    if (!FAST) {
-                        // VALU continuation for keys [max(kb, jv), i], ascending (row r)
-                        const int j1 = min(kb + SB, irow + 1);
-                        for (int j = max(kb, jv); j < j1; ++j) {
-                            const float pv = prow[j - kbase];
-                            const float* vr = kvb + (j - kb) * KLD + 64 * H + 16 * g;    // d = 64hf + 16g + 4v + t
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const float4 x4 = *reinterpret_cast<const float4*>(vr + 4 * v);
-                                oc[0][v] = __builtin_fmaf(pv, x4.x, oc[0][v]);
-                                oc[1][v] = __builtin_fmaf(pv, x4.y, oc[1][v]);
-                                oc[2][v] = __builtin_fmaf(pv, x4.z, oc[2][v]);
-                                oc[3][v] = __builtin_fmaf(pv, x4.w, oc[3][v]);
-                            }
-                            lc[0] = lc[0] + pv;
-                        }
-                    }
-                    if (more) st.store_v(KV[buf ^ 1], tid);
-                    else st.store_k(KV[buf ^ 1], tid);
-                    __syncthreads();
-                    buf ^= 1;
+                for (int v = 0; v < 4; ++v) {
+                    const int j = kbase + 16 * t + 4 * v + g;
+                    const float pv = (full || j <= irow) ? exp_f(S[t][v] - mc) : 0.0f;
+                    S[t][v] = pv;
+                    // the causal tail's p (keys jv .. jv + 18), read back in key order by the
+                    // lanes of the row; the buffer belongs to this wavefront alone
+                    if (!FAST && j >= jv && j < jv + TW) tail[j - jv] = pv;
                 }
             }
-        };
-        if constexpr (FAST) {
-            if (hf == 0) pv_phase(std::integral_constant<int, 0>());
-            else pv_phase(std::integral_constant<int, 1>());
-        } else {
-            pv_phase(hf);
         }
-        // ------------------------------------------------------ 4. merge (l: half 0)
+        // ------------------------------------------------------ 3. PV and l
+        f32x4 oc[8];
+        f32x4 lc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) oc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sb = 0; sb < CHUNK / SB; ++sb) {
+            if (FAST || sb < nsb) {
+                const int kb = kbase + sb * SB;
+                const bool more = sb + 1 < nsb;
+                // after the last V sub-block comes the next chunk's first K sub-block (past the
+                // last chunk every row is out of range: the stage clamps and stores zeros)
+                if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
+                else st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
+                const float* kvb = KV[buf];
+                const float* vop = kvb + g * KLD + 8 * r;       // + 4 s KLD at step s
+                const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
+#pragma unroll
+                for (int s = 0; s < SB / 4; ++s) {
+                    if (FAST || 4 * s < nmk) {
+                        const float bp = S[sb * 4 + (s >> 2)][s & 3];
+                        const float4 va = *reinterpret_cast<const float4*>(vop + 4 * s * KLD);
+                        const float4 vb = *reinterpret_cast<const float4*>(vop + 4 * s * KLD + 4);
+                        oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, bp, oc[0], 0, 0, 0);
+                        oc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.y, bp, oc[1], 0, 0, 0);
+                        oc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.z, bp, oc[2], 0, 0, 0);
+                        oc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.w, bp, oc[3], 0, 0, 0);
+                        oc[4] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.x, bp, oc[4], 0, 0, 0);
+                        oc[5] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.y, bp, oc[5], 0, 0, 0);
+                        oc[6] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.z, bp, oc[6], 0, 0, 0);
+                        oc[7] = __builtin_amdgcn_mfma_f32_16x16x4f32(vb.w, bp, oc[7], 0, 0, 0);
+                        lc = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, bp, lc, 0, 0, 0);
+                    }
+                }
+                if (!FAST) {
+                    // VALU continuation for keys [max(kb, jv), i], ascending (row r)
+                    const int j1 = min(kb + SB, irow + 1);
+                    for (int j = max(kb, jv); j < j1; ++j) {
+                        const float pv = tail[j - jv];
+                        const float* vr = kvb + (j - kb) * KLD + 32 * g;    // d = 32g + 8v + t
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const float4 x0 = *reinterpret_cast<const float4*>(vr + 8 * v);
+                            const float4 x1 = *reinterpret_cast<const float4*>(vr + 8 * v + 4);
+                            oc[0][v] = __builtin_fmaf(pv, x0.x, oc[0][v]);
+                            oc[1][v] = __builtin_fmaf(pv, x0.y, oc[1][v]);
+                            oc[2][v] = __builtin_fmaf(pv, x0.z, oc[2][v]);
+                            oc[3][v] = __builtin_fmaf(pv, x0.w, oc[3][v]);
+                            oc[4][v] = __builtin_fmaf(pv, x1.x, oc[4][v]);
+                            oc[5][v] = __builtin_fmaf(pv, x1.y, oc[5][v]);
+                            oc[6][v] = __builtin_fmaf(pv, x1.z, oc[6][v]);
+                            oc[7][v] = __builtin_fmaf(pv, x1.w, oc[7][v]);
+                        }
+                        lc[0] = lc[0] + pv;
+                    }
+                }
+                if (more) st.store_v(KV[buf ^ 1], tid);
+                else st.store_k(KV[buf ^ 1], tid);
+                __syncthreads();
+                buf ^= 1;
+            }
+        }
+        // ------------------------------------------------------ 4. merge
         if (ne) {
             if (c == 0) {
                 m = mc;
                 l = lc[0];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = oc[t];
+                for (int t = 0; t < 8; ++t) o[t] = oc[t];
             } else {
                 const float mn = (mc > m) ? mc : m;
                 const float al = exp_f(m - mn), be = exp_f(mc - mn);
                 l = (l * al) + (lc[0] * be);
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < 8; ++t)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) o[t][v] = (o[t][v] * al) + (oc[t][v] * be);
                 m = mn;
@@ -360,24 +359,23 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         }
     };
     for (int c = 0; c <= clast; ++c) {
-        // the fast path needs the whole workgroup to agree: its first row group sees the
-        // whole chunk (every later group does too) and the chunk ends inside the block's range
+        // the fast path needs the whole workgroup to agree: its first rows see the whole chunk
+        // (every later row does too) and the chunk ends inside the block's range
         const bool wg_fast = (c + 1) * CHUNK <= q_start + r0 && (c + 1) * CHUNK <= imax + 1;
         if (wg_fast) chunk(c, std::integral_constant<bool, true>());
         else chunk(c, std::integral_constant<bool, false>());
     }
     // ------------------------------------------------------------------ output
-    if (hf == 0 && g == 0) Lx[rg][r] = l;
-    __syncthreads();
-    const float lr = Lx[rg][r];
     const int rel = wrow0 + r;
     if (rel < r0 + nrows) {
-        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D + 64 * hf + 16 * g;
+        float* out = O + (((int64_t)b * Tq + rel) * Hq + h) * D + 32 * g;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            float4 y;
-            y.x = o[0][v] / lr; y.y = o[1][v] / lr; y.z = o[2][v] / lr; y.w = o[3][v] / lr;
-            *reinterpret_cast<float4*>(out + 4 * v) = y;
+            float4 y0, y1;
+            y0.x = o[0][v] / l; y0.y = o[1][v] / l; y0.z = o[2][v] / l; y0.w = o[3][v] / l;
+            y1.x = o[4][v] / l; y1.y = o[5][v] / l; y1.z = o[6][v] / l; y1.w = o[7][v] / l;
+            *reinterpret_cast<float4*>(out + 8 * v) = y0;
+            *reinterpret_cast<float4*>(out + 8 * v + 4) = y1;
         }
     }
 }
@@ -662,12 +660,12 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
 }  // namespace
 
 hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
-    dim3 grid((a.Tq + BQ - 1) / BQ, a.Hq, a.B);
+    dim3 grid(((a.Tq + BQ - 1) / BQ) * a.Hq * a.B);
     if (a.dtype == 1)
-        hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.Tq,
+        hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.B, a.Tq,
                            a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
     else
-        hipLaunchKernelGGL(attn_prefill_kernel<0>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.Tq,
+        hipLaunchKernelGGL(attn_prefill_kernel<0>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.B, a.Tq,
                            a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
     return hipGetLastError();
 }
