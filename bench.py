@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--seq", type=int, default=32768)
-    ap.add_argument("--block", type=int, default=4096, help="token rows per prefill block")
+    ap.add_argument("--block", type=int, default=16384, help="token rows per prefill block")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--cpu-tokens", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true")
@@ -58,15 +58,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_128x256_c5_prefill_traf
 GEMM_SOURCE = os.path.join(ROOT, "invariant_numerics_amd", "csrc", "gemm.hip")
 
 
-def measured_traffic():
+def measured_traffic(block):
     """HBM bytes per launch of the body-projection GEMM from the profiler counter runs recorded
     under profiles/ (FETCH_SIZE + WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel
-    source has changed since they were taken."""
+    source has changed since they were taken or they were taken at another token block."""
     import hashlib
     try:
         vals = dict(line.split(": ", 1) for line in open(TRAFFIC_FILE).read().splitlines() if ": " in line)
         sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
         if vals.get("gemm_source_sha256", "").strip() != sha:
+            return None
+        if int(vals.get("token_block", "0")) != block:
             return None
         return int(vals["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -137,11 +139,11 @@ def main():
     flops = np.array([f for _, _, f, _ in rec], np.float64)
     achieved = float(flops.sum() / durs.sum()) / 1e12
     gemm_share = float(durs.sum() / elapsed)
-    default_workload = (B == 1 and T == 32768 and args.block == 4096 and args.layers == 4)
+    default_workload = (B == 1 and T == 32768 and args.layers == 4)
     roof = dict(bound="mfma", kernel="gemm_mfma_kernel<128,256,2,4,0|2> (the four body projections; W1||W3 with the gated SwiGLU epilogue; FP32 matrix cores, 32x32x2)",
                 achieved=round(achieved, 3),
                 peak=FP32_PEAK_TFLOPS, unit="TFLOP/s", frac=round(achieved / FP32_PEAK_TFLOPS, 4),
-                traffic=measured_traffic() if default_workload else None,
+                traffic=measured_traffic(args.block) if default_workload else None,
                 traffic_unit="bytes per launch (HBM read + write, counter-measured)",
                 algorithmic_bytes_per_launch=float(np.mean([b for _, _, _, b in rec])) if rec else None,
                 launches=int(len(rec)), avg_launch_us=round(float(durs.mean()) * 1e6, 2),
