@@ -308,6 +308,159 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
         }
 }
 
+// ----------------------------------------------------------------- small --
+// M <= 64 (8 < M <= 16 only for N >= 8192): 32 x 32 tiles, one 16 x 16 tile per wavefront on
+// v_mfma_f32_16x16x4_f32 (four fused multiply-adds in k order per step; the same measured
+// property as the 32x32x2 form, checked through inv_mfma_f32_check), so M = 64, N = 4096
+// gives 256 workgroups of 4 wavefronts instead of 64.  K walks the same 32-wide LDS tiles
+// and 256-slices with one fold per slice; inside a tile row k sits at (k % 4) * 8 + k / 4,
+// so lane group g reads its 8 operands (k = g, g + 4, ..., g + 28) as two 16-byte reads.
+// Tile u of a contiguous range per XCD is (row u % nMt, column u / nMt): the tile rows that
+// share a weight tile run on one XCD.
+__device__ __forceinline__ int kpos16(int k) { return (k & 3) * 8 + (k >> 2); }
+
+template <int ROLE>
+__global__ __launch_bounds__(256) void gemm_small_kernel(
+    const float* __restrict__ X, int M, int K, int64_t ldx,
+    const uint16_t* __restrict__ W, int N, int64_t ldw,
+    const float* __restrict__ R, int64_t ldr,
+    float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int TS = 32, LDT = BK + 4;
+    __shared__ __attribute__((aligned(16))) float As[2][TS][LDT];
+    __shared__ __attribute__((aligned(16))) float Bs[2][TS][LDT];
+    const int gridM = M;
+    if (Mdev) M = min(M, *Mdev);
+    int m0, n0;
+    {
+        const int nMt = (gridM + TS - 1) / TS, nNt = (N + TS - 1) / TS;
+        const int T = nMt * nNt, L = blockIdx.x;
+        constexpr int NXCD = 8;
+        const int xcd = L % NXCD, q = L / NXCD;
+        const int u = xcd * (T / NXCD) + min(xcd, T % NXCD) + q;
+        m0 = (u % nMt) * TS;
+        n0 = (u / nMt) * TS;
+    }
+    if (m0 >= M) return;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int wm0 = (wv >> 1) * 16, wn0 = (wv & 1) * 16;
+    // staging: thread t carries X row t / 8, k = 4 (t % 8) .. + 3 and, for t < 128, W row
+    // t / 4, k = 8 (t % 4) .. + 7; rows past M or N read row M - 1 or N - 1 and k past K reads
+    // inside the row: those values only reach outputs that are never stored or k-steps that
+    // are never issued
+    const int xrow = tid >> 3, xq = tid & 7;
+    const int wrw = (tid >> 2) & 31, wo = tid & 3;
+    const bool wl = tid < 128;
+    const float* xp = X + (int64_t)min(m0 + xrow, M - 1) * ldx + 4 * xq;
+    const uint16_t* wp = W + (int64_t)min(n0 + wrw, N - 1) * ldw + 8 * wo;
+    float4 xr;
+    uint4 wr = make_uint4(0u, 0u, 0u, 0u);
+    auto load_tile = [&](int k0) {
+        xr = *reinterpret_cast<const float4*>(xp + min(k0, K - 4 - 4 * xq));
+        if (wl) wr = *reinterpret_cast<const uint4*>(wp + min(k0, K - 8 - 8 * wo));
+    };
+    auto store_tile = [&](int buf) {
+        float* d = As[buf][xrow];
+        d[kpos16(4 * xq + 0)] = xr.x;
+        d[kpos16(4 * xq + 1)] = xr.y;
+        d[kpos16(4 * xq + 2)] = xr.z;
+        d[kpos16(4 * xq + 3)] = xr.w;
+        if (wl) {
+            float* e = Bs[buf][wrw];
+            e[kpos16(8 * wo + 0)] = bf16_lo(wr.x);
+            e[kpos16(8 * wo + 1)] = bf16_hi(wr.x);
+            e[kpos16(8 * wo + 2)] = bf16_lo(wr.y);
+            e[kpos16(8 * wo + 3)] = bf16_hi(wr.y);
+            e[kpos16(8 * wo + 4)] = bf16_lo(wr.z);
+            e[kpos16(8 * wo + 5)] = bf16_hi(wr.z);
+            e[kpos16(8 * wo + 6)] = bf16_lo(wr.w);
+            e[kpos16(8 * wo + 7)] = bf16_hi(wr.w);
+        }
+    };
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, T = f32x4{0.f, 0.f, 0.f, 0.f};
+    float a[8], b[8];
+    auto read_frags = [&](int buf) {
+        const float4* sa = reinterpret_cast<const float4*>(&As[buf][wm0 + r][g * 8]);
+        const float4* sb = reinterpret_cast<const float4*>(&Bs[buf][wn0 + r][g * 8]);
+        const float4 a0 = sa[0], a1 = sa[1], b0 = sb[0], b1 = sb[1];
+        a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w; a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+        b[0] = b0.x; b[1] = b0.y; b[2] = b0.z; b[3] = b0.w; b[4] = b1.x; b[5] = b1.y; b[6] = b1.z; b[7] = b1.w;
+    };
+    const int ntf = K / BK, nt = (K + BK - 1) / BK, nslices = (K + KS - 1) / KS;
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    int t = 0;
+    for (int sl = 0; sl < nslices; ++sl) {
+        const int tend = min(ntf, t + KS / BK);
+        for (; t < tend; ++t) {
+            const int buf = t & 1;
+            if (t + 1 < nt) load_tile((t + 1) * BK);
+            read_frags(buf);
+#pragma unroll
+            for (int s = 0; s < BK / 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+            if (t + 1 < nt) store_tile(buf ^ 1);
+            __syncthreads();
+        }
+        if (t == ntf && ntf < nt && sl == nslices - 1) {
+            // partial last tile: only the k-steps below K
+            const int kend = K - t * BK;
+            read_frags(t & 1);
+#pragma unroll
+            for (int s = 0; s < BK / 4; ++s)
+                if (4 * s < kend) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], acc, 0, 0, 0);
+            ++t;
+        }
+        if (sl == 0) {
+            T = acc;
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) T[v] = T[v] + acc[v];
+        }
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // lane (g, r) holds rows 4g .. 4g + 3, column r of the wavefront's 16 x 16 tile
+    if constexpr (ROLE == 2) {
+        // gated: columns 2i (gate) and 2i + 1 (up) sit in lanes r and r + 1 (r even); the even
+        // lane finishes rows 4g and 4g + 2, the odd lane rows 4g + 1 and 4g + 3
+        const int odd = r & 1;
+        const int gc = (n0 + wn0 + (r & ~1)) >> 1;
+#pragma unroll
+        for (int vp = 0; vp < 4; vp += 2) {
+            const float a0 = T[vp], a1 = T[vp + 1];
+            const float x0 = __shfl_xor(a0, 1), x1 = __shfl_xor(a1, 1);
+            const float gate = odd ? x1 : a0;
+            const float up = odd ? a1 : x0;
+            const int gm = m0 + wm0 + 4 * g + vp + odd;
+            if (gm < M && n0 + wn0 + (r & ~1) < N) Y[(int64_t)gm * ldy + gc] = (gate / (1.0f + exp_f(-gate))) * up;
+        }
+        return;
+    }
+    const int gn = n0 + wn0 + r;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int gm = m0 + wm0 + 4 * g + v;
+        if (gm < M && gn < N) {
+            float y = T[v];
+            if (R) y = R[(int64_t)gm * ldr + gn] + y;
+            Y[(int64_t)gm * ldy + gn] = y;
+        }
+    }
+}
+
+// 32 x 32 tiles for M <= 32 (a 64-row tile would be half padding) and for M <= 64 when the
+// 64 x 64 grid would have fewer than SMALL_BELOW tiles
+constexpr int64_t SMALL_BELOW = 256;
+
+template <int ROLE>
+hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
+    dim3 grid(((a.M + 31) / 32) * ((a.N + 31) / 32));
+    hipLaunchKernelGGL((gemm_small_kernel<ROLE>), grid, dim3(256), 0, st,
+                       a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- skinny --
 // M <= 16.  A workgroup owns ROWS weight rows (16, or 4 when the grid would otherwise be
 // too coarse to balance the CUs) and every activation row; thread (slice lane sl, row nl)
@@ -530,6 +683,9 @@ int64_t gemm_skinny_max_k() {
 template <int ROLE>
 hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
     // M is an upper bound when Mdev is set (rows beyond *Mdev are skipped on the device).
+    // 8 < M <= 16 over many weight rows: the matrix-core tiles beat the VALU GEMV (whose
+    // 16 accumulators per thread make it compute-bound there)
+    if (a.M > 8 && a.M <= 16 && a.N >= 8192) return launch_small<ROLE>(a, st);
     if (a.M <= 16 && a.K <= gemm_skinny_max_k()) {
         if (a.M <= 1) return launch_skinny<1, ROLE>(a, st);
         if (a.M <= 2) return launch_skinny<2, ROLE>(a, st);
@@ -537,7 +693,12 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         if (a.M <= 8) return launch_skinny<8, ROLE>(a, st);
         return launch_skinny<16, ROLE>(a, st);
     }
-    if (a.M <= 64) return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
+    // the large tile only when it gives at least one workgroup per CU; below that the 64 x 64
+    // tile's 8x larger grid wins (e.g. M = 512, N = 4096: 64 large tiles, 512 small ones)
+    const int64_t big = ((a.M + 127) / 128) * (int64_t)((a.N + 255) / 256);
+    const int64_t mid = ((a.M + 63) / 64) * (int64_t)((a.N + 63) / 64);
+    if (a.M <= 64 && (a.M <= 32 || mid < SMALL_BELOW)) return launch_small<ROLE>(a, st);
+    if (a.M <= 64 || big < 256) return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
     return launch_tiled<128, 256, 2, 4, ROLE>(a, st);
 }
 

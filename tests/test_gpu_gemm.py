@@ -97,12 +97,14 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
 
 
 @pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (5, 1000, 64), (16, 4096, 130),
-                                   (17, 264, 129), (64, 768, 64), (65, 4096, 300), (300, 1032, 257)])
+                                   (12, 520, 4200), (17, 264, 129), (64, 768, 64), (65, 4096, 300),
+                                   (300, 1032, 257)])
 def test_gated_gemm_equals_gemm_then_swiglu(orc, M, K, F):
     """inv_gated_gemm on gate/up rows interleaved equals inv_fixed_order_gemm followed by
     inv_swiglu on its even and odd columns, bit for bit, on the one-wavefront GEMV path
-    (M <= 2), the 16-row GEMV path and the matrix-core path; small shapes also match the
-    oracle's gemm + swiglu on the two halves."""
+    (M <= 2), the 16-row GEMV path, the 32 x 32 matrix-core tiles (M <= 16 with many weight
+    rows, M <= 64) and the large tiles; small shapes also match the oracle's gemm + swiglu on
+    the two halves."""
     say("gated gemm", M, K, F)
     X = synth.normal(9960 + K, (M, K)) * np.float32(2)
     W13 = synth.bf16_normal(9961 + F, (2 * F, K), 0.05)
