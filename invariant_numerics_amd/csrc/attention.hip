@@ -22,7 +22,6 @@ namespace invnum {
 namespace {
 
 constexpr int D = 128;
-constexpr int BQ = 128;   // query rows per prefill workgroup
 
 template <int DT>
 __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* dst) {
@@ -41,15 +40,15 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 // four fused multiply-adds in k order, so both contractions keep their sequential order:
 // the scores over d = 0..127 and the PV sums over keys in ascending j.
 //
-// Workgroup: 512 threads = 8 wavefronts over BQ = 128 consecutive query rows of one (b, h);
-// wavefront w owns rows 16 w .. 16 w + 15 outright (scores of every key, every d of the
-// output), so no partial state is exchanged between wavefronts and all eight share each K/V
-// sub-block staged in LDS.  Per 256-key chunk:
+// Workgroup: NW wavefronts (8, or 4 when the grid would be small) over BQ = 16 NW consecutive
+// query rows of one (b, h); wavefront w owns rows 16 w .. 16 w + 15 outright (scores of every
+// key, every d of the output), so no partial state is exchanged between wavefronts and all of
+// them share each K/V sub-block staged in LDS.  Per 256-key chunk:
 //   1. scores S^T = K Q^T on the matrix cores: A = K tile (lane (g, r) supplies key
 //      16t + pi(r), d = 4s + g, with pi(i) = 4 (i % 4) + i / 4), B = Q^T (lane (g, r) supplies
 //      row r, d = 4s + g, held in registers); lane (g, r) receives in register v the score of
-//      row r with key 16t + 4v + g.  K streams through double-buffered LDS in 64-key
-//      sub-blocks (four key tiles each);
+//      row r with key 16t + 4v + g.  K streams through double-buffered LDS in SB-key
+//      sub-blocks (64 or 32 keys: SB / 16 key tiles each);
 //   2. m_c = the maximum of the row's visible scores (lanes of a row exchange theirs);
 //      p = exp_f(s - m_c) in place;
 //   3. PV: O^T = V^T P^T over all keys of the chunk in ascending order, output tile t
@@ -65,9 +64,7 @@ __device__ __forceinline__ void load_row4(const void* base, int64_t off, float* 
 // Blocks are issued heaviest first (the last rows see the most keys), and consecutive
 // workgroup ids cycle over the kv heads so the workgroups running together on one XCD (ids
 // are dealt to the 8 XCDs in turn) share one kv head's K/V in its L2.
-constexpr int SB = 64;          // keys per LDS sub-block
 constexpr int KLD = D + 4;      // LDS row: K with d permuted ((d % 4) * 32 + d / 4), V row-major
-constexpr int PNT = 512;        // threads per prefill workgroup
 constexpr int TW = 20;          // keys of the causal tail buffer (at most 19 are used)
 constexpr int TLD = TW + 1;     // its padded row
 
@@ -84,27 +81,28 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float* v) {
     }
 }
 
-// Global -> register -> LDS staging of one 64-key sub-block of K or V (fp32 in LDS).
-// Thread t carries 4 groups of 4 consecutive d of rows (e / 32) for e = t + 512 i.
+// Global -> register -> LDS staging of one SBK-key sub-block of K or V (fp32 in LDS) by NT
+// threads.  Thread t carries SV groups of 4 consecutive d of rows (e / 32), e = t + NT i.
 // Rows at or beyond kend are read from row kend - 1 (always valid) and replaced by zeros.
-template <int DT>
+template <int DT, int NT, int SBK>
 struct Stage {
-    float4 v[4];
+    static constexpr int SV = SBK * (D / 4) / NT;
+    float4 v[SV];
     __device__ __forceinline__ void load(const void* base, int64_t kvbase, int kb, int kend, int tid) {
-        if (kb + SB <= kend) {
-            // whole sub-block in range: row (tid >> 5) + 16 i, column 4 (tid & 31)
+        if (kb + SBK <= kend) {
+            // whole sub-block in range: row (tid >> 5) + (NT / 32) i, column 4 (tid & 31)
             const int64_t off = kvbase + (int64_t)(kb + (tid >> 5)) * D + (tid & 31) * 4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < SV; ++i) {
                 float t[4];
-                load4<DT>(base, off + (int64_t)(16 * i) * D, t);
+                load4<DT>(base, off + (int64_t)((NT / 32) * i) * D, t);
                 v[i] = make_float4(t[0], t[1], t[2], t[3]);
             }
             return;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + PNT * i;
+        for (int i = 0; i < SV; ++i) {
+            const int e = tid + NT * i;
             const int jj = e >> 5, d4 = (e & 31) * 4;
             const bool in = kb + jj < kend;
             const int row = in ? kb + jj : kend - 1;
@@ -115,8 +113,8 @@ struct Stage {
     }
     __device__ __forceinline__ void store_k(float* KV, int tid) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + PNT * i;
+        for (int i = 0; i < SV; ++i) {
+            const int e = tid + NT * i;
             const int jj = e >> 5, q = e & 31;
             float* dst = KV + jj * KLD + q;
             dst[0] = v[i].x; dst[32] = v[i].y; dst[64] = v[i].z; dst[96] = v[i].w;
@@ -124,20 +122,22 @@ struct Stage {
     }
     __device__ __forceinline__ void store_v(float* KV, int tid) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = tid + PNT * i;
+        for (int i = 0; i < SV; ++i) {
+            const int e = tid + NT * i;
             const int jj = e >> 5, d4 = (e & 31) * 4;
             *reinterpret_cast<float4*>(KV + jj * KLD + d4) = v[i];
         }
     }
 };
 
-template <int DT>
-__global__ __launch_bounds__(PNT) void attn_prefill_kernel(
+template <int DT, int NW, int SB>
+__global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
     int B, int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O) {
+    constexpr int BQ = 16 * NW;                 // query rows per workgroup
+    constexpr int KT = SB / 16;                 // key tiles per sub-block
     __shared__ __attribute__((aligned(16))) float KV[2][SB * KLD];
-    __shared__ float Tail[PNT / 64][16][TLD];
+    __shared__ float Tail[NW][16][TLD];
 
     const int tid = threadIdx.x;
     // the wavefront index is uniform in a wavefront: in a scalar register, everything derived
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
     for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int clast = imax / CHUNK;
-    Stage<DT> st;
+    Stage<DT, 64 * NW, SB> st;
     int buf = 0;
     st.load(Kc, kvbase, 0, min(CHUNK, imax + 1), tid);
     st.store_k(KV[0], tid);
@@ -215,22 +215,22 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
                 if (FAST || kbase + sb * SB <= i0 + 15) {
 #pragma unroll
                     for (int s4 = 0; s4 < 8; ++s4) {
-                        float4 kk[4];
+                        float4 kk[KT];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
+                        for (int e = 0; e < KT; ++e)
                             kk[e] = *reinterpret_cast<const float4*>(kvb + (e * 16 + pr) * KLD + g * 32 + 4 * s4);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].x, qf[4 * s4 + 0], S[sb * 4 + e], 0, 0, 0);
+                        for (int e = 0; e < KT; ++e)
+                            S[sb * KT + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].x, qf[4 * s4 + 0], S[sb * KT + e], 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].y, qf[4 * s4 + 1], S[sb * 4 + e], 0, 0, 0);
+                        for (int e = 0; e < KT; ++e)
+                            S[sb * KT + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].y, qf[4 * s4 + 1], S[sb * KT + e], 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].z, qf[4 * s4 + 2], S[sb * 4 + e], 0, 0, 0);
+                        for (int e = 0; e < KT; ++e)
+                            S[sb * KT + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].z, qf[4 * s4 + 2], S[sb * KT + e], 0, 0, 0);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            S[sb * 4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].w, qf[4 * s4 + 3], S[sb * 4 + e], 0, 0, 0);
+                        for (int e = 0; e < KT; ++e)
+                            S[sb * KT + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(kk[e].w, qf[4 * s4 + 3], S[sb * KT + e], 0, 0, 0);
                     }
                 }
                 if (sb + 1 < nsb) st.store_k(KV[buf ^ 1], tid);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         float mh = -__builtin_inff();
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            if (FAST || t < 4 * nsb) {
+            if (FAST || t < KT * nsb) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int j = kbase + 16 * t + 4 * v + g;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
         const int jv = FAST ? kbase + CHUNK : kbase + ((jspan > 0 ? jspan : 0) & ~3);   // MFMA keys: [kbase, jv)
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            if (FAST || t < 4 * nsb) {
+            if (FAST || t < KT * nsb) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int j = kbase + 16 * t + 4 * v + g;
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(PNT) void attn_prefill_kernel(
 #pragma unroll
                 for (int s = 0; s < SB / 4; ++s) {
                     if (FAST || 4 * s < nmk) {
-                        const float bp = S[sb * 4 + (s >> 2)][s & 3];
+                        const float bp = S[sb * KT + (s >> 2)][s & 3];
                         const float4 va = *reinterpret_cast<const float4*>(vop + 4 * s * KLD);
                         const float4 vb = *reinterpret_cast<const float4*>(vop + 4 * s * KLD + 4);
                         oc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(va.x, bp, oc[0], 0, 0, 0);
@@ -659,15 +659,25 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
 
 }  // namespace
 
-hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
-    dim3 grid(((a.Tq + BQ - 1) / BQ) * a.Hq * a.B);
+template <int NW, int SBK>
+hipError_t launch_prefill_nw(const AttnArgs& a, hipStream_t st) {
+    dim3 grid(((a.Tq + 16 * NW - 1) / (16 * NW)) * a.Hq * a.B);
     if (a.dtype == 1)
-        hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.B, a.Tq,
-                           a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
+        hipLaunchKernelGGL((attn_prefill_kernel<1, NW, SBK>), grid, dim3(64 * NW), 0, st, a.Q, a.Kc, a.Vc,
+                           a.B, a.Tq, a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
     else
-        hipLaunchKernelGGL(attn_prefill_kernel<0>, grid, dim3(PNT), 0, st, a.Q, a.Kc, a.Vc, a.B, a.Tq,
-                           a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
+        hipLaunchKernelGGL((attn_prefill_kernel<0, NW, SBK>), grid, dim3(64 * NW), 0, st, a.Q, a.Kc, a.Vc,
+                           a.B, a.Tq, a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
     return hipGetLastError();
+}
+
+hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
+    // 128-row workgroups (8 wavefronts, 64-key sub-blocks) when they give at least two per
+    // CU; else 64-row ones (4 wavefronts, 32-key sub-blocks) for twice the grid.  The rows'
+    // bits do not depend on the choice.
+    const int64_t wg128 = (int64_t)((a.Tq + 127) / 128) * a.Hq * a.B;
+    if (wg128 >= 512) return launch_prefill_nw<8, 64>(a, st);
+    return launch_prefill_nw<4, 32>(a, st);
 }
 
 namespace {

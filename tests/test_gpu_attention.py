@@ -62,6 +62,29 @@ def test_decode_matches_prefill_rows_ragged_positions(orc):
         assert_bitwise(O, want, "decode pos=%s" % posv)
 
 
+@pytest.mark.parametrize("bf", [False, True])
+def test_large_grid_prefill_equals_decode_and_small_grid(bf):
+    """A prefill big enough for the 128-row workgroups (32 heads x 2048 rows) equals decode at
+    sampled positions and, row for row, the same queries run as small calls (one 16-row block
+    of 4 heads at a time, 64-row workgroups): the workgroup size never changes a bit."""
+    say("attn large grid", bf)
+    B, T, Hq, Hkv = 1, 2048, 32, 8
+    q, k, v = rand_qkv(8300 + int(bf), B, T, Hq, Hkv, bf)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    full = host(inv().inv_attention_prefill(qd, kd, vd))
+    pos = np.array([0, 15, 255, 256, 1000, 1023, 1024, 1500, 2047], np.int32)
+    for p in pos:
+        O = host(inv().inv_attention_decode(qd[:, p].contiguous(), kd, vd, i32(np.array([p], np.int32))))
+        assert_bitwise(O[0], full[0, p], "decode pos=%d" % p)
+    for s0 in (0, 1024, 2032):
+        for h0 in (0, 12, 28):
+            # heads h0 .. h0 + 3 share kv head h0 / 4: run them with their kv head alone
+            qs = q[:, s0:s0 + 16, h0:h0 + 4].copy()
+            ks, vs = k[:, h0 // 4:h0 // 4 + 1].copy(), v[:, h0 // 4:h0 // 4 + 1].copy()
+            part = host(inv().inv_attention_prefill(dev(qs), dev(ks), dev(vs), q_start=s0))
+            assert_bitwise(part, full[:, s0:s0 + 16, h0:h0 + 4], "rows %d, heads %d" % (s0, h0))
+
+
 def test_decode_cache_length_does_not_change_rows():
     """A row's output depends only on keys 0..pos: a 140000-slot cache and one cut to pos + 1
     slots give the same bits (positions 0, 70000, 131071), and a row with an invalid
