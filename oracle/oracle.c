@@ -64,6 +64,58 @@ uint16_t orc_bf16_rne(float x) {
     return (uint16_t)(u >> 16);
 }
 
+/* FP16 (IEEE binary16) = 1 sign, 5 exponent (bias 15), 10 stored fraction bits: normals
+ * from 2^-14 to 65504, subnormals in steps of 2^-24 (FP precision blog, the note on
+ * mantissa widths: BF16 7 bits, FP16 10, FP32 23).  Used for the FP16-activation setting
+ * of the cross-precision comparison ("Greedy Decoding Is Not Precision-Invariant",
+ * abstract: the same model run with BF16 and with FP16 activations).
+ * f16_up(): exact widening to FP32. */
+float orc_f16_up(uint16_t h) {
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    if (e == 0x1fu) return u2f(sign | 0x7f800000u | (m << 13));     /* inf, NaN */
+    if (e == 0) {                                                   /* zero, subnormal */
+        float v = (float)m * 0x1p-24f;                              /* exact: m < 2^10 */
+        return sign ? -v : v;
+    }
+    return u2f(sign | ((e + 112u) << 23) | (m << 13));
+}
+
+/* f16(): FP32 -> FP16, round to nearest, ties to even.  Magnitudes from 65520 (the midpoint
+ * between 65504 and 2^16, which ties to the even neighbour 2^16) up become infinity; below
+ * 2^-14 the result is the nearest multiple of 2^-24 (possibly 2^-14 itself); NaN becomes a
+ * quiet NaN keeping the sign and the top 9 payload bits. */
+uint16_t orc_f16_rne(float x) {
+    uint32_t u = f2u(x);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u | ((a >> 13) & 0x3ffu));
+    float ax = u2f(a);
+    if (ax >= 65520.0f) return (uint16_t)(sign | 0x7c00u);
+    if (ax < 0x1p-14f) {
+        /* ax * 2^24 < 2^10 is exact; nearbyintf rounds half to even in the default mode */
+        return (uint16_t)(sign | (uint16_t)nearbyintf(ax * 0x1p24f));
+    }
+    uint32_t h = (((a >> 23) - 112u) << 10) | ((a >> 13) & 0x3ffu);
+    uint32_t rest = a & 0x1fffu;                       /* the 13 dropped fraction bits */
+    if (rest > 0x1000u || (rest == 0x1000u && (h & 1u))) h += 1u;   /* carry may reach 2^16 */
+    return (uint16_t)(sign | h);
+}
+
+/* Storage rounding of an activation: fmt 0 keeps FP32, 1 rounds to BF16, 2 to FP16; the
+ * result is the rounded value widened back to FP32 (the arithmetic stays FP32). */
+static float round_act(float x, int fmt) {
+    if (fmt == 1) return orc_bf16_up(orc_bf16_rne(x));
+    if (fmt == 2) return orc_f16_up(orc_f16_rne(x));
+    return x;
+}
+void orc_round_act_array(const float* x, int64_t n, int fmt, float* y) {
+    for (int64_t i = 0; i < n; ++i) y[i] = round_act(x[i], fmt);
+}
+static void round_all(float* x, int64_t n, int fmt) {
+    if (fmt) for (int64_t i = 0; i < n; ++i) x[i] = round_act(x[i], fmt);
+}
+
 /* -------------------------------------------------------- exp_f / log_f -- */
 /* Project-defined transcendental functions.  Hardware/libm expf and logf are never
  * used on the compared path because their last bit differs between implementations.
@@ -480,18 +532,18 @@ void orc_lmhead(const float* Hs, int64_t B, int64_t K, int64_t ldh, const uint16
  *   per layer: n = rmsnorm(x, g1); [q|k|v] = n Wqkv^T; q,k = RoPE at position t;
  *              x = x + attn(q, k, v) Wo^T;
  *              n = rmsnorm(x, g2); [g|u] = n W13^T; x = x + (silu(g) * u) W2^T
- *   n = rmsnorm(x, gf); for t = 0..T-2: LM-head row (selective recompute) with target tok_{t+1}.
+ *   n = rmsnorm(x, gf); for t = 0..T-1: LM-head row (selective recompute) with target tgt_t.
+ * The same decoder with BF16 or FP16 activation storage (act_fmt 1 or 2) is the low-precision
+ * body of the cross-precision comparison ("Greedy Decoding Is Not Precision-Invariant",
+ * abstract); the weights and the LM head are unchanged.
  * Weight layouts: Wqkv [(Hq+2Hkv)D, H] (q rows, then k rows, then v rows);
  * Wo [H, Hq D]; W13 [2F, H] (gate rows, then up rows); W2 [H, F]; Whead [V, H]. */
-typedef struct {
-    const uint16_t *g1, *wqkv, *wo, *g2, *w13, *w2;
-} orc_layer;
-
 void orc_decoder(const int32_t* tok, int64_t T, int64_t H, int64_t Hq, int64_t Hkv, int64_t D,
                  int64_t F, int64_t V, int64_t nlayers,
                  const uint16_t* emb, const uint16_t* const* lw /* nlayers*6 pointers */,
                  const uint16_t* gf, const uint16_t* whead, const float* cos_t, const float* sin_t,
-                 float eps, float scale, float tau,
+                 float eps, float scale, float tau, int act_fmt,
+                 const int32_t* tgt /* [T]: target of every position; all T rows are scored */,
                  float* lp, float* margin, int32_t* top1, int32_t* top2, uint8_t* flag,
                  float* x_out /* optional [T, H]: final normed hidden */) {
     int64_t QD = Hq * D, KD = Hkv * D, NQKV = QD + 2 * KD;
@@ -506,15 +558,24 @@ void orc_decoder(const int32_t* tok, int64_t T, int64_t H, int64_t Hq, int64_t H
     float* hh = (float*)malloc(sizeof(float) * (size_t)(T * F));
     int32_t* pos = (int32_t*)malloc(sizeof(int32_t) * (size_t)T);
     float* ktmp = (float*)malloc(sizeof(float) * (size_t)(T * KD));
+    /* act_fmt != 0: every activation tensor an unfused implementation would store between
+     * operations is rounded to that format (embedding, each norm output, each projection
+     * output, rotated q and k, attention output, the SwiGLU product, each residual sum);
+     * each operation still computes in FP32 from the rounded inputs. */
     for (int64_t t = 0; t < T; ++t) pos[t] = (int32_t)t;
     for (int64_t t = 0; t < T; ++t)
         for (int64_t k = 0; k < H; ++k) x[t * H + k] = orc_bf16_up(emb[(int64_t)tok[t] * H + k]);
+    round_all(x, T * H, act_fmt);
     for (int64_t L = 0; L < nlayers; ++L) {
         const uint16_t* const* w = lw + 6 * L;
         orc_rmsnorm(x, T, H, H, w[0], eps, n, H);
+        round_all(n, T * H, act_fmt);
         orc_gemm(n, T, H, H, w[1], NQKV, H, qkv, NQKV);
+        round_all(qkv, T * NQKV, act_fmt);
         orc_rope(qkv, T, Hq, D, NQKV, pos, cos_t, sin_t, q, QD);
         orc_rope(qkv + QD, T, Hkv, D, NQKV, pos, cos_t, sin_t, ktmp, KD);
+        round_all(q, T * QD, act_fmt);
+        round_all(ktmp, T * KD, act_fmt);
         /* cache layout [Hkv, T, D] for this one sequence */
         for (int64_t t = 0; t < T; ++t)
             for (int64_t g = 0; g < Hkv; ++g)
@@ -523,16 +584,25 @@ void orc_decoder(const int32_t* tok, int64_t T, int64_t H, int64_t Hq, int64_t H
                     vc[(g * T + t) * D + d] = qkv[t * NQKV + QD + KD + g * D + d];
                 }
         orc_attention(1, q, kc, vc, 1, T, 0, T, Hq, Hkv, D, scale, att);
+        round_all(att, T * QD, act_fmt);
         orc_gemm(att, T, QD, QD, w[2], H, QD, y, H);
+        round_all(y, T * H, act_fmt);
         for (int64_t i = 0; i < T * H; ++i) x[i] = x[i] + y[i];
+        round_all(x, T * H, act_fmt);
         orc_rmsnorm(x, T, H, H, w[3], eps, n, H);
+        round_all(n, T * H, act_fmt);
         orc_gemm(n, T, H, H, w[4], 2 * F, H, y, 2 * F);
+        round_all(y, T * 2 * F, act_fmt);
         orc_swiglu(y, y + F, T, F, 2 * F, 2 * F, hh, F);
+        round_all(hh, T * F, act_fmt);
         orc_gemm(hh, T, F, F, w[5], H, F, y, H);
+        round_all(y, T * H, act_fmt);
         for (int64_t i = 0; i < T * H; ++i) x[i] = x[i] + y[i];
+        round_all(x, T * H, act_fmt);
     }
     orc_rmsnorm(x, T, H, H, gf, eps, n, H);
+    round_all(n, T * H, act_fmt);
     if (x_out) memcpy(x_out, n, sizeof(float) * (size_t)(T * H));
-    if (T > 1) orc_lmhead(n, T - 1, H, H, whead, V, tok + 1, tau, 0, lp, margin, top1, top2, flag);
+    orc_lmhead(n, T, H, H, whead, V, tgt, tau, 0, lp, margin, top1, top2, flag);
     free(x); free(n); free(qkv); free(q); free(kc); free(vc); free(att); free(y); free(hh); free(pos); free(ktmp);
 }

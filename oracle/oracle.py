@@ -50,6 +50,11 @@ def lib():
         L.orc_exp_f_array.argtypes = [f32p, f32p, i64]
         L.orc_log_f_array.argtypes = [f32p, f32p, i64]
         L.orc_bf16_rne_array.argtypes = [f32p, u16p, i64]
+        L.orc_f16_rne.restype = ctypes.c_uint16
+        L.orc_f16_rne.argtypes = [ctypes.c_float]
+        L.orc_f16_up.restype = ctypes.c_float
+        L.orc_f16_up.argtypes = [ctypes.c_uint16]
+        L.orc_round_act_array.argtypes = [f32p, i64, ctypes.c_int, f32p]
         L.orc_gemm.argtypes = [f32p, i64, i64, i64, u16p, i64, i64, f32p, i64]
         L.orc_rmsnorm.argtypes = [f32p, i64, i64, i64, u16p, ctypes.c_float, f32p, i64]
         L.orc_rope.argtypes = [f32p, i64, i64, i64, i64, i32p, f32p, f32p, f32p, i64]
@@ -60,7 +65,7 @@ def lib():
                                  f32p, f32p, i32p, i32p, u8p]
         L.orc_decoder.argtypes = [i32p, i64, i64, i64, i64, i64, i64, i64, i64,
                                   u16p, ctypes.POINTER(u16p), u16p, u16p, f32p, f32p,
-                                  ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int, i32p,
                                   f32p, f32p, i32p, i32p, u8p, f32p]
         _lib = L
     return _lib
@@ -101,6 +106,19 @@ def bf16_rne(x):
 def bf16_up(b):
     """BF16 bits -> FP32 (the 16 bits become the top half of the word)."""
     return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# activation storage formats of the decoder: FP32 (LayerCast), BF16, FP16
+ACT_FORMATS = {"fp32": 0, "bf16": 1, "fp16": 2}
+
+
+def round_act(x, fmt):
+    """Round FP32 values to the storage format ``fmt`` ("fp32", "bf16", "fp16") and widen the
+    result back to FP32."""
+    x = _c(x, np.float32)
+    y = np.empty_like(x)
+    lib().orc_round_act_array(_p(x, f32p), x.size, ACT_FORMATS[fmt], _p(y, f32p))
+    return y
 
 
 def add_f32(a, b):
@@ -211,9 +229,12 @@ def lmhead(Hs, W, target, tau=np.float32(0.1), mode=0):
     return dict(logprob=lp, margin=mg, top1=t1, top2=t2, recomputed=fl)
 
 
-def decoder(tokens, model, eps=1e-5, tau=np.float32(0.1), return_hidden=False):
+def decoder(tokens, model, eps=1e-5, tau=np.float32(0.1), return_hidden=False, act="fp32",
+            targets=None):
     """Score one sequence with the Llama-shaped decoder.  ``model`` is the dict built by
-    ``synth.decoder_model`` (BF16 weights as uint16 bits, RoPE tables fp32)."""
+    ``synth.decoder_model`` (BF16 weights as uint16 bits, RoPE tables fp32).  ``act`` is the
+    activation storage format.  By default positions 0..T-2 are scored against the next
+    token; with ``targets`` (int32 [T]) all T positions are scored against those."""
     cfg = model["cfg"]
     H, Hq, Hkv, D, F, V, L = (cfg[k] for k in ("hidden", "hq", "hkv", "d", "ffn", "vocab", "layers"))
     tokens = _c(tokens, np.int32)
@@ -231,21 +252,45 @@ def decoder(tokens, model, eps=1e-5, tau=np.float32(0.1), return_hidden=False):
     cos_t = _c(model["cos"], np.float32)
     sin_t = _c(model["sin"], np.float32)
     assert cos_t.shape[0] >= T
-    n = max(T - 1, 1)
-    lp = np.empty(n, np.float32)
-    mg = np.empty(n, np.float32)
-    t1 = np.empty(n, np.int32)
-    t2 = np.empty(n, np.int32)
-    fl = np.empty(n, np.uint8)
+    if targets is None:
+        tgt = np.zeros(T, np.int32)
+        tgt[:T - 1] = tokens[1:]
+        nout = T - 1
+    else:
+        tgt = _c(targets, np.int32)
+        assert tgt.shape == (T,)
+        nout = T
+    lp = np.empty(T, np.float32)
+    mg = np.empty(T, np.float32)
+    t1 = np.empty(T, np.int32)
+    t2 = np.empty(T, np.int32)
+    fl = np.empty(T, np.uint8)
     hid = np.empty((T, H), np.float32) if return_hidden else None
     scale = np.float32(1.0) / np.sqrt(np.float32(D))
     lib().orc_decoder(_p(tokens, i32p), T, H, Hq, Hkv, D, F, V, L, _p(emb, u16p), ptrs, _p(gf, u16p),
                       _p(wh, u16p), _p(cos_t, f32p), _p(sin_t, f32p), float(np.float32(eps)),
-                      float(scale), float(np.float32(tau)),
+                      float(scale), float(np.float32(tau)), ACT_FORMATS[act], _p(tgt, i32p),
                       _p(lp, f32p), _p(mg, f32p), _p(t1, i32p), _p(t2, i32p), _p(fl, u8p),
                       _p(hid, f32p) if hid is not None else None)
-    out = dict(logprob=lp[:T - 1], margin=mg[:T - 1], top1=t1[:T - 1], top2=t2[:T - 1],
-               recomputed=fl[:T - 1])
+    out = dict(logprob=lp[:nout], margin=mg[:nout], top1=t1[:nout], top2=t2[:nout],
+               recomputed=fl[:nout])
     if return_hidden:
         out["hidden"] = hid
+    return out
+
+
+def greedy(prompt, model, steps, act="fp32", tau=np.float32(0.1), eps=1e-5):
+    """Greedy continuation of one prompt: each new token is the top-1 of the LM head at the
+    last position, recomputed from scratch over the whole sequence at every step.  Returns
+    int32 tokens [steps] and the per-step LM-head outputs (margin, top1, top2, recomputed)."""
+    seq = [int(t) for t in np.asarray(prompt)]
+    rec = {k: [] for k in ("margin", "top1", "top2", "recomputed")}
+    for _ in range(steps):
+        r = decoder(np.asarray(seq, np.int32), model, eps=eps, tau=tau, act=act,
+                    targets=np.zeros(len(seq), np.int32))
+        for k in rec:
+            rec[k].append(r[k][-1])
+        seq.append(int(r["top1"][-1]))
+    out = {k: np.asarray(v) for k, v in rec.items()}
+    out["tokens"] = np.asarray(seq[len(prompt):], np.int32)
     return out

@@ -84,22 +84,40 @@ def lmhead_pass(A, W16, target):
     return dict(logprob=lp, margin=margin, top1=t1, top2=t2, logits=Z)
 
 
-def decoder(tokens, model, eps=1e-5):
-    """Float64 forward of the same decoder; returns the final normed hidden [T, H]."""
+def store(x, fmt):
+    """Storage rounding of an activation: "fp32" keeps the float64 value, "fp16" rounds it to
+    the nearest binary16 (NumPy's conversion), "bf16" to the nearest bfloat16 (through the
+    nearest binary32, then the top 16 bits with ties to even)."""
+    x = np.asarray(x, np.float64)
+    if fmt == "fp16":
+        return x.astype(np.float16).astype(np.float64)
+    if fmt == "bf16":
+        u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+        u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        return (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x
+
+
+def decoder(tokens, model, eps=1e-5, act="fp32"):
+    """Float64 forward of the same decoder; returns the final normed hidden [T, H].  With
+    ``act`` "bf16" or "fp16" every activation an unfused implementation stores between
+    operations (embedding, norm outputs, projection outputs, rotated q and k, attention
+    output, the SwiGLU product, residual sums) is rounded to that format."""
     cfg = model["cfg"]
     H, Hq, Hkv, D, F = (cfg[k] for k in ("hidden", "hq", "hkv", "d", "ffn"))
     T = len(tokens)
-    x = up(model["emb"])[np.asarray(tokens)]
+    R = lambda a: store(a, act)  # noqa: E731
+    x = R(up(model["emb"])[np.asarray(tokens)])
     pos = np.arange(T)
     for layer in model["layers"]:
-        n = rmsnorm(x, layer["g1"], eps)
-        qkv = gemm(n, layer["wqkv"])
-        q = rope(qkv[:, :Hq * D].reshape(T, Hq, D), pos, model["cos"], model["sin"])
-        k = rope(qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D), pos, model["cos"], model["sin"])
+        n = R(rmsnorm(x, layer["g1"], eps))
+        qkv = R(gemm(n, layer["wqkv"]))
+        q = R(rope(qkv[:, :Hq * D].reshape(T, Hq, D), pos, model["cos"], model["sin"]))
+        k = R(rope(qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D), pos, model["cos"], model["sin"]))
         v = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
-        att = attention(q[None], k.transpose(1, 0, 2)[None], v.transpose(1, 0, 2)[None])[0]
-        x = x + gemm(att.reshape(T, Hq * D), layer["wo"])
-        n = rmsnorm(x, layer["g2"], eps)
-        gu = gemm(n, layer["w13"])
-        x = x + gemm(swiglu(gu[:, :F], gu[:, F:]), layer["w2"])
-    return rmsnorm(x, model["gf"], eps)
+        att = R(attention(q[None], k.transpose(1, 0, 2)[None], v.transpose(1, 0, 2)[None])[0])
+        x = R(x + R(gemm(att.reshape(T, Hq * D), layer["wo"])))
+        n = R(rmsnorm(x, layer["g2"], eps))
+        gu = R(gemm(n, layer["w13"]))
+        x = R(x + R(gemm(R(swiglu(gu[:, :F], gu[:, F:])), layer["w2"])))
+    return R(rmsnorm(x, model["gf"], eps))

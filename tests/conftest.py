@@ -39,4 +39,8 @@ def numcheck(tmp_path_factory, orc):
                               ctypes.POINTER(ctypes.c_uint32)]
     L.check_bf16_range.restype = ctypes.c_uint64
     L.check_bf16_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    L.check_f16_range.restype = ctypes.c_uint64
+    L.check_f16_range.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    L.check_f16_up.restype = ctypes.c_uint64
+    L.check_f16_up.argtypes = []
     return L

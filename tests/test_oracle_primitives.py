@@ -77,6 +77,50 @@ def test_bf16_rne_special_cases(orc):
         assert int(orc.bf16_rne(x)[0]) == want, hex(fb)
 
 
+def test_f16_rne_exhaustive(numcheck):
+    """All 2^32 binary32 patterns: oracle FP16 rounding == nearer FP16 grid point in double."""
+    assert numcheck.check_f16_range(0, 1 << 32) == 0
+    assert numcheck.check_f16_up() == 0
+
+
+def test_f16_rne_special_cases(orc):
+    lib = orc.lib()
+    cases = {65504.0: 0x7BFF,                  # largest finite
+             65519.99609375: 0x7BFF,           # just below the midpoint to 2^16
+             65520.0: 0x7C00,                  # midpoint ties to the even neighbour, 2^16 = inf
+             2.0 ** -24: 0x0001,               # smallest subnormal
+             2.0 ** -25: 0x0000,               # half of it: tie to even (zero)
+             3 * 2.0 ** -25: 0x0002,           # 1.5 quanta: tie to even (2)
+             2.0 ** -14 - 2.0 ** -25: 0x0400,  # rounds up into the smallest normal
+             1.0 + 2.0 ** -11: 0x3C00,         # tie, even stays
+             1.0 + 3 * 2.0 ** -11: 0x3C02,     # tie, odd rounds up
+             -0.0: 0x8000}
+    for v, want in cases.items():
+        assert int(lib.orc_f16_rne(float(np.float32(v)))) == want, v
+    assert float(lib.orc_f16_up(0x7BFF)) == 65504.0 and float(lib.orc_f16_up(0x0001)) == 2.0 ** -24
+
+
+def test_round_act_matches_library_conversions(orc):
+    """The decoder's storage rounding: FP16 against NumPy's float16 conversion and BF16
+    against the nearest-BF16 definition in exact rationals, on wide random patterns and the
+    FP16 edge region; FP32 is the identity."""
+    rng = np.random.default_rng(77)
+    u = rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    edge = (np.arange(0x33000000, 0x33000000 + (1 << 20), 7, dtype=np.uint32),      # ~2^-25
+            np.arange(0x387fc000, 0x38804000, dtype=np.uint32),                      # ~2^-14
+            np.arange(0x477fe000, 0x47800010, dtype=np.uint32))                      # ~65504..2^16
+    x = np.concatenate([u] + list(edge)).view(np.float32)
+    x = x[np.isfinite(x)]
+    with np.errstate(over="ignore"):
+        want16 = x.astype(np.float16).astype(np.float32)
+    assert np.array_equal(orc.round_act(x, "fp16").view(np.uint32), want16.view(np.uint32))
+    assert np.array_equal(orc.round_act(x, "fp32").view(np.uint32), x.view(np.uint32))
+    few = x[:2000]
+    want_bf = [exact.rnbf16(Fraction(float(v))) for v in few]
+    got_bf = orc.round_act(few, "bf16")
+    assert all(float(g) == w for g, w in zip(got_bf, want_bf) if np.isfinite(g))
+
+
 def test_exp_f_within_one_ulp_everywhere(numcheck):
     """Whole finite domain of exp_f against libm exp in double (error bound: 2 ulp)."""
     w = ctypes.c_uint32()
