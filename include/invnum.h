@@ -63,7 +63,7 @@ enum inv_status {
     INV_ERR_LAUNCH = -7       /* the HIP runtime rejected a launch */
 };
 
-enum inv_dtype { INV_BF16 = 0, INV_F32 = 1 };
+enum inv_dtype { INV_BF16 = 0, INV_F32 = 1, INV_F16 = 2 };
 
 #define INV_MAX_FLOAT_CONSTS 32
 
@@ -200,11 +200,13 @@ int inv_embed(const int32_t* ids, int64_t M, const uint16_t* table, int64_t voca
  *   y_i = (x_i c_i) - (x_{i+D/2} s_i);  y_{i+D/2} = (x_i s_i) + (x_{i+D/2} c_i)   (no fma)
  * Qout: FP32 [M, Hq, D]; Kc, Vc: FP32 [Bcache, Hkv, Tmax, D] receive rotated k and v at
  * [seq[m], g, pos[m], :].  D even.  Rows whose seq/pos fall outside the cache are skipped
- * (nothing written for them). */
+ * (nothing written for them).  out_fmt: INV_F32 stores the values as computed; INV_BF16 or
+ * INV_F16 stores every written value (q, k, v) rounded to that format, exactly as
+ * inv_round_activations would (low-precision activation storage). */
 int inv_rope_kv_append(const float* QKV, int64_t M, int64_t ldqkv, int64_t Hq, int64_t Hkv,
                        int64_t D, const int32_t* seq, const int32_t* pos,
                        const float* cos_t, const float* sin_t, int64_t Tmax, int64_t Bcache,
-                       float* Qout, float* Kc, float* Vc, void* stream);
+                       float* Qout, float* Kc, float* Vc, int out_fmt, void* stream);
 
 /* Hout[m, f] = silu(G[m, f]) * U[m, f], silu(a) = a / (1 + exp_f(-a)). */
 int inv_swiglu(const float* G, const float* U, int64_t M, int64_t F, int64_t ldg, int64_t ldu,
@@ -213,6 +215,25 @@ int inv_swiglu(const float* G, const float* U, int64_t M, int64_t F, int64_t ldg
 /* Y[m, n] = A[m, n] + Bm[m, n]. */
 int inv_add(const float* A, const float* Bm, int64_t M, int64_t N, int64_t lda, int64_t ldb,
             float* Y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
+ * inv_round_activations -- storage rounding of FP32 activations:
+ *   Y[r, c] = widen(round_fmt(X[r, c]))  for r < rows, c < cols,
+ * fmt INV_BF16: the nearest BF16 value (ties to even, overflow to inf, NaN kept quiet);
+ * fmt INV_F16: the nearest IEEE binary16 value (ties to even; 10 fraction bits from 2^-14 to
+ * 65504, multiples of 2^-24 below, inf from 65520 up, NaN kept quiet with its sign and top 9
+ * payload bits); fmt INV_F32: a copy.  The rounded value is returned widened to FP32, so the
+ * following operation keeps computing in FP32 on the stored (rounded) value.
+ * This is the low-precision activation storage of the cross-precision comparison: the same
+ * model with BF16 or with FP16 activations ("Greedy Decoding Is Not Precision-Invariant",
+ * abstract); the format widths follow the Yuan et al. blog, section 2 (mantissa bits).
+ * X, Y: FP32 device pointers, 4-byte aligned, row strides ldx, ldy >= cols (elements).
+ * Y == X with ldy == ldx rounds in place; any other overlap is not allowed.
+ * rows == 0 or cols == 0 enqueues nothing and returns INV_OK.  Errors: INV_ERR_NULL,
+ * INV_ERR_SHAPE (negative size, stride < cols), INV_ERR_ALIGN, INV_ERR_DTYPE (other fmt).
+ * ------------------------------------------------------------------------------------ */
+int inv_round_activations(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                          float* Y, int64_t ldy, void* stream);
 
 /* Diagnostic: y[i] = exp_f(x[i]) (fn 0), log_f(x[i]) (fn 1) or up(bf(x[i])) (fn 2) on the
  * device, for checking the library's scalar primitives against the CPU check. */

@@ -12,5 +12,5 @@ from .binding import (  # noqa: F401
     inv_attention_prefill, inv_embed, inv_eval_numerics, inv_fixed_order_gemm, inv_gated_gemm,
     inv_get_constants,
     inv_lmhead_logprob_top2, inv_lmhead_workspace_bytes, inv_mfma_f32_check, inv_mfma32_f32_check, inv_rmsnorm, inv_rope_kv_append,
-    inv_status_string, inv_swiglu,
+    inv_round_activations, inv_status_string, inv_swiglu,
 )

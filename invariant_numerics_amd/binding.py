@@ -52,9 +52,10 @@ def _load():
                                                    vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "inv_embed": (ctypes.c_int, [vp, i64, vp, i64, i64, vp, i64, vp]),
         "inv_rope_kv_append": (ctypes.c_int, [vp, i64, i64, i64, i64, i64, vp, vp, vp, vp, i64, i64, vp,
-                                              vp, vp, vp]),
+                                              vp, vp, ctypes.c_int, vp]),
         "inv_swiglu": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
         "inv_add": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
+        "inv_round_activations": (ctypes.c_int, [vp, i64, i64, i64, ctypes.c_int, vp, i64, vp]),
         "inv_eval_numerics": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, vp]),
         "inv_mfma_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
         "inv_mfma32_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
@@ -70,7 +71,7 @@ LIB = _load()
 EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "inv_gated_gemm", "inv_rmsnorm",
            "inv_attention_prefill", "inv_attention_decode_workspace_bytes", "inv_attention_decode",
            "inv_lmhead_workspace_bytes", "inv_lmhead_logprob_top2", "inv_embed", "inv_rope_kv_append",
-           "inv_swiglu", "inv_add", "inv_eval_numerics", "inv_mfma_f32_check",
+           "inv_swiglu", "inv_add", "inv_round_activations", "inv_eval_numerics", "inv_mfma_f32_check",
            "inv_mfma32_f32_check")
 
 
@@ -257,12 +258,15 @@ def inv_embed(ids, table, out=None):
     return out
 
 
-def inv_rope_kv_append(QKV, Hq, Hkv, D, seq, pos, cos_t, sin_t, Qout, Kc, Vc):
+def inv_rope_kv_append(QKV, Hq, Hkv, D, seq, pos, cos_t, sin_t, Qout, Kc, Vc, fmt="fp32"):
     _dev(QKV, seq, pos, cos_t, sin_t, Qout, Kc, Vc)
+    if fmt not in ACT_FORMATS:
+        raise InvError("unknown activation format %r" % (fmt,))
     M = QKV.shape[0]
     Bc, _, Tmax, _ = Kc.shape
     _check(LIB.inv_rope_kv_append(_p(QKV), M, _row_ld(QKV), Hq, Hkv, D, _p(seq), _p(pos), _p(cos_t),
-                                  _p(sin_t), Tmax, Bc, _p(Qout), _p(Kc), _p(Vc), _stream(QKV)),
+                                  _p(sin_t), Tmax, Bc, _p(Qout), _p(Kc), _p(Vc), ACT_FORMATS[fmt],
+                                  _stream(QKV)),
            "inv_rope_kv_append")
     return Qout
 
@@ -284,6 +288,27 @@ def inv_add(A, Bm, out=None):
         out = torch.empty_like(A)
     _check(LIB.inv_add(_p(A), _p(Bm), M, N, _row_ld(A), _row_ld(Bm), _p(out), _row_ld(out), _stream(A)),
            "inv_add")
+    return out
+
+
+# activation storage formats: name -> dtype code of the C ABI
+ACT_FORMATS = {"bf16": 0, "fp32": 1, "fp16": 2}
+
+
+def inv_round_activations(X, fmt, out=None):
+    """Round the FP32 2-D tensor X (unit inner stride) to ``fmt`` ("bf16", "fp16", "fp32")
+    and store the widened values in ``out`` (default: a new tensor; ``out=X`` rounds in
+    place)."""
+    _dev(X, out)
+    if X.dtype != torch.float32:
+        raise InvError("FP32 activations expected")
+    if fmt not in ACT_FORMATS:
+        raise InvError("unknown activation format %r" % (fmt,))
+    if out is None:
+        out = torch.empty(X.shape, dtype=torch.float32, device=X.device)
+    rows, cols = X.shape
+    _check(LIB.inv_round_activations(_p(X), rows, cols, _row_ld(X), ACT_FORMATS[fmt], _p(out), _row_ld(out),
+                                     _stream(X)), "inv_round_activations")
     return out
 
 

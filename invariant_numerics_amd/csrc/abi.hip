@@ -156,13 +156,15 @@ int inv_embed(const int32_t* ids, int64_t M, const uint16_t* table, int64_t voca
 
 int inv_rope_kv_append(const float* QKV, int64_t M, int64_t ldqkv, int64_t Hq, int64_t Hkv, int64_t D,
                        const int32_t* seq, const int32_t* pos, const float* cos_t, const float* sin_t,
-                       int64_t Tmax, int64_t Bcache, float* Qout, float* Kc, float* Vc, void* stream) {
+                       int64_t Tmax, int64_t Bcache, float* Qout, float* Kc, float* Vc, int out_fmt,
+                       void* stream) {
     if (!QKV || !seq || !pos || !cos_t || !sin_t || !Qout || !Kc || !Vc) return INV_ERR_NULL;
+    if (out_fmt != INV_BF16 && out_fmt != INV_F16 && out_fmt != INV_F32) return INV_ERR_DTYPE;
     if (M < 1 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 != 0 || Tmax < 1 || Bcache < 1 ||
         ldqkv < (Hq + 2 * Hkv) * D || M > I32MAX || Tmax > I32MAX || Bcache > I32MAX)
         return INV_ERR_SHAPE;
     return fin(launch_rope_kv_append(QKV, (int)M, ldqkv, (int)Hq, (int)Hkv, (int)D, seq, pos, cos_t,
-                                     sin_t, (int)Tmax, (int)Bcache, Qout, Kc, Vc, S(stream)));
+                                     sin_t, (int)Tmax, (int)Bcache, Qout, Kc, Vc, out_fmt, S(stream)));
 }
 
 int inv_swiglu(const float* G, const float* U, int64_t M, int64_t F, int64_t ldg, int64_t ldu,
@@ -177,6 +179,17 @@ int inv_add(const float* A, const float* Bm, int64_t M, int64_t N, int64_t lda, 
     if (!A || !Bm || !Y) return INV_ERR_NULL;
     if (M < 1 || N < 1 || lda < N || ldb < N || ldy < N) return INV_ERR_SHAPE;
     return fin(launch_add(A, Bm, (int)M, (int)N, lda, ldb, Y, ldy, S(stream)));
+}
+
+int inv_round_activations(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt, float* Y,
+                          int64_t ldy, void* stream) {
+    if (!X || !Y) return INV_ERR_NULL;
+    if (fmt != INV_BF16 && fmt != INV_F16 && fmt != INV_F32) return INV_ERR_DTYPE;
+    if (rows < 0 || cols < 0) return INV_ERR_SHAPE;
+    if (((uintptr_t)X & 3) || ((uintptr_t)Y & 3)) return INV_ERR_ALIGN;
+    if (rows == 0 || cols == 0) return INV_OK;
+    if (ldx < cols || ldy < cols) return INV_ERR_SHAPE;
+    return fin(launch_round_activations(X, rows, cols, ldx, fmt, Y, ldy, S(stream)));
 }
 
 int inv_eval_numerics(int fn, const float* x, float* y, int64_t n, void* stream) {

@@ -1,5 +1,7 @@
 // elementwise.hip -- RMSNorm (one fixed-order reduction per row) and the decoder's
-// elementwise steps (embedding gather, RoPE + KV-cache append, SwiGLU, residual add).
+// elementwise steps (embedding gather, RoPE + KV-cache append, SwiGLU, residual add, storage
+// rounding of activations to BF16 / FP16).
+#include "invnum.h"
 #include "numerics.h"
 #include "kernels.h"
 
@@ -110,8 +112,18 @@ __global__ void embed_kernel(const int32_t* __restrict__ ids, int M, const uint1
     }
 }
 
+// Storage rounding of one value to the activation format FMT (INV_F32: unchanged).
+template <int FMT>
+__device__ __forceinline__ float store_round(float v) {
+    if (FMT == INV_BF16) return bf16_up(bf16_rne(v));
+    if (FMT == INV_F16) return f16_round(v);
+    return v;
+}
+
 // One thread per (row, head, pair i < D/2).  Heads 0..Hq-1 are q heads (written to Qout),
 // Hq..Hq+Hkv-1 are k heads (rotated into Kc), the last Hkv are v heads (copied into Vc).
+// Every value written is rounded to the activation format FMT.
+template <int FMT>
 __global__ void rope_kv_kernel(const float* __restrict__ QKV, int M, int64_t ldqkv, int Hq, int Hkv,
                                int D, const int32_t* __restrict__ seq, const int32_t* __restrict__ pos,
                                const float* __restrict__ cos_t, const float* __restrict__ sin_t,
@@ -133,8 +145,8 @@ __global__ void rope_kv_kernel(const float* __restrict__ QKV, int M, int64_t ldq
             const float c = cos_t[(int64_t)p * half + i];
             const float s = sin_t[(int64_t)p * half + i];
             const float a = x[i], b = x[i + half];
-            const float y0 = (a * c) - (b * s);
-            const float y1 = (a * s) + (b * c);
+            const float y0 = store_round<FMT>((a * c) - (b * s));
+            const float y1 = store_round<FMT>((a * s) + (b * c));
             if (h < Hq) {
                 float* q = Qout + ((int64_t)m * Hq + h) * D;
                 q[i] = y0;
@@ -148,8 +160,8 @@ __global__ void rope_kv_kernel(const float* __restrict__ QKV, int M, int64_t ldq
         } else {
             const int gv = h - Hq - Hkv;
             float* v = Vc + (((int64_t)sq * Hkv + gv) * Tmax + p) * D;
-            v[i] = x[i];
-            v[i + half] = x[i + half];
+            v[i] = store_round<FMT>(x[i]);
+            v[i + half] = store_round<FMT>(x[i + half]);
         }
     }
 }
@@ -173,6 +185,30 @@ __global__ void add_kernel(const float* __restrict__ A, const float* __restrict_
          t += (int64_t)gridDim.x * blockDim.x) {
         const int m = (int)(t / N), n = (int)(t % N);
         Y[(int64_t)m * ldy + n] = A[(int64_t)m * lda + n] + B[(int64_t)m * ldb + n];
+    }
+}
+
+// Storage rounding of FP32 activations (fmt INV_BF16, INV_F16, or INV_F32 = copy), 2-D with
+// row strides.  In place when Y == X (each element is read before its own write).  VEC: rows
+// of whole float4s with 16-byte aligned base pointers and strides.
+template <int FMT, bool VEC>
+__global__ void round_act_kernel(const float* X, int64_t rows, int64_t cols, int64_t ldx, float* Y,
+                                 int64_t ldy) {
+    const int64_t cw = VEC ? cols / 4 : cols;
+    const int64_t total = rows * cw;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = t / cw, c = t % cw;
+        if (VEC) {
+            float4 v = *(const float4*)(X + m * ldx + 4 * c);
+            v.x = store_round<FMT>(v.x);
+            v.y = store_round<FMT>(v.y);
+            v.z = store_round<FMT>(v.z);
+            v.w = store_round<FMT>(v.w);
+            *(float4*)(Y + m * ldy + 4 * c) = v;
+        } else {
+            Y[m * ldy + c] = store_round<FMT>(X[m * ldx + c]);
+        }
     }
 }
 
@@ -252,10 +288,18 @@ hipError_t launch_embed(const int32_t* ids, int M, const uint16_t* table, int vo
 hipError_t launch_rope_kv_append(const float* QKV, int M, int64_t ldqkv, int Hq, int Hkv, int D,
                                  const int32_t* seq, const int32_t* pos, const float* cos_t,
                                  const float* sin_t, int Tmax, int Bcache, float* Qout, float* Kc,
-                                 float* Vc, hipStream_t st) {
+                                 float* Vc, int out_fmt, hipStream_t st) {
     const int64_t work = (int64_t)M * (Hq + 2 * Hkv) * (D / 2);
-    hipLaunchKernelGGL(rope_kv_kernel, dim3(grid_for(work, 256)), dim3(256), 0, st, QKV, M, ldqkv,
-                       Hq, Hkv, D, seq, pos, cos_t, sin_t, Tmax, Bcache, Qout, Kc, Vc);
+    const dim3 grid(grid_for(work, 256)), block(256);
+    if (out_fmt == INV_BF16)
+        hipLaunchKernelGGL(rope_kv_kernel<INV_BF16>, grid, block, 0, st, QKV, M, ldqkv, Hq, Hkv, D, seq,
+                           pos, cos_t, sin_t, Tmax, Bcache, Qout, Kc, Vc);
+    else if (out_fmt == INV_F16)
+        hipLaunchKernelGGL(rope_kv_kernel<INV_F16>, grid, block, 0, st, QKV, M, ldqkv, Hq, Hkv, D, seq,
+                           pos, cos_t, sin_t, Tmax, Bcache, Qout, Kc, Vc);
+    else
+        hipLaunchKernelGGL(rope_kv_kernel<INV_F32>, grid, block, 0, st, QKV, M, ldqkv, Hq, Hkv, D, seq,
+                           pos, cos_t, sin_t, Tmax, Bcache, Qout, Kc, Vc);
     return hipGetLastError();
 }
 
@@ -271,6 +315,27 @@ hipError_t launch_add(const float* A, const float* B, int M, int N, int64_t lda,
     hipLaunchKernelGGL(add_kernel, dim3(grid_for((int64_t)M * N, 256)), dim3(256), 0, st, A, B, M,
                        N, lda, ldb, Y, ldy);
     return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_round_fmt(const float* X, int64_t rows, int64_t cols, int64_t ldx, float* Y,
+                                   int64_t ldy, hipStream_t st) {
+    const bool vec = cols % 4 == 0 && ldx % 4 == 0 && ldy % 4 == 0 &&
+                     ((uintptr_t)X & 15) == 0 && ((uintptr_t)Y & 15) == 0;
+    if (vec)
+        hipLaunchKernelGGL((round_act_kernel<FMT, true>), dim3(grid_for(rows * (cols / 4), 256)),
+                           dim3(256), 0, st, X, rows, cols, ldx, Y, ldy);
+    else
+        hipLaunchKernelGGL((round_act_kernel<FMT, false>), dim3(grid_for(rows * cols, 256)), dim3(256),
+                           0, st, X, rows, cols, ldx, Y, ldy);
+    return hipGetLastError();
+}
+
+hipError_t launch_round_activations(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                    float* Y, int64_t ldy, hipStream_t st) {
+    if (fmt == INV_BF16) return launch_round_fmt<INV_BF16>(X, rows, cols, ldx, Y, ldy, st);
+    if (fmt == INV_F16) return launch_round_fmt<INV_F16>(X, rows, cols, ldx, Y, ldy, st);
+    return launch_round_fmt<INV_F32>(X, rows, cols, ldx, Y, ldy, st);
 }
 
 hipError_t launch_eval_numerics(int fn, const float* x, float* y, int64_t n, hipStream_t st) {

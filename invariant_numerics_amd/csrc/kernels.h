@@ -48,11 +48,13 @@ hipError_t launch_embed(const int32_t* ids, int M, const uint16_t* table, int vo
 hipError_t launch_rope_kv_append(const float* QKV, int M, int64_t ldqkv, int Hq, int Hkv, int D,
                                  const int32_t* seq, const int32_t* pos, const float* cos_t,
                                  const float* sin_t, int Tmax, int Bcache, float* Qout, float* Kc,
-                                 float* Vc, hipStream_t st);
+                                 float* Vc, int out_fmt, hipStream_t st);
 hipError_t launch_swiglu(const float* G, const float* U, int M, int F, int64_t ldg, int64_t ldu,
                          float* Hout, int64_t ldh, hipStream_t st);
 hipError_t launch_add(const float* A, const float* B, int M, int N, int64_t lda, int64_t ldb,
                       float* Y, int64_t ldy, hipStream_t st);
+hipError_t launch_round_activations(const float* X, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                                    float* Y, int64_t ldy, hipStream_t st);
 hipError_t launch_eval_numerics(int fn, const float* x, float* y, int64_t n, hipStream_t st);
 hipError_t launch_mfma_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
                              hipStream_t st);

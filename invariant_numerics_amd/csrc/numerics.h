@@ -60,6 +60,26 @@ __device__ __forceinline__ uint32_t bf16_rne(float x) {
     return u >> 16;
 }
 
+// FP16 storage rounding: the binary16 value nearest to x (ties to even), returned widened to
+// FP32.  binary16 keeps 10 fraction bits between 2^-14 and 65504 and steps of 2^-24 below;
+// from 65520 (the tie between 65504 and 2^16, whose even side is 2^16) up the result is inf;
+// NaN stays a quiet NaN with its sign and the top 9 payload bits.
+__device__ __forceinline__ float f16_round(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t s = u & 0x80000000u, a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return __uint_as_float(s | 0x7fc00000u | (a & 0x007fe000u));
+    if (a >= 0x477ff000u) return __uint_as_float(s | 0x7f800000u);      // |x| >= 65520
+    if (a < 0x38800000u) {                                               // |x| < 2^-14
+        // |x| * 2^24 < 2^10 is exact, rint rounds half to even, * 2^-24 is exact
+        const float r = __builtin_rintf(__uint_as_float(a) * 0x1p24f) * 0x1p-24f;
+        return __uint_as_float(s | __float_as_uint(r));
+    }
+    // normal range: round the 13 dropped fraction bits half to even in the FP32 encoding
+    // (a carry out of the fraction steps the exponent, which is the next binade's value)
+    const uint32_t r = (a + 0x0fffu + ((a >> 13) & 1u)) & ~0x1fffu;
+    return __uint_as_float(s | r);
+}
+
 // exp_f(x): n = rint(x log2e); r = fma(-n, ln2_hi, x); r = fma(-n, ln2_lo, r);
 // p = Taylor degree 7 by fma-Horner from the top; result p * 2^n rounded once.
 // x < ln(2^-126) -> +0, x > ln(2^128) -> +inf, NaN -> NaN.

@@ -8,6 +8,14 @@ Two ways to score a batch of sequences that must give the same bits at every pos
 Every op is row-independent and chunk boundaries are absolute key positions, so token
 blocking, batch size and prefill-vs-decode do not change a row's bits.
 
+Activation storage policy ``act``: "fp32" (LayerCast: every activation and the KV cache in
+FP32, fused residual and gated epilogues) or "bf16" / "fp16": every activation tensor an
+unfused implementation stores between operations (embedding, norm outputs, projection outputs,
+rotated q and k and the cache, attention output, the SwiGLU product, residual sums) is rounded
+to that format; each operation still computes in FP32 from the rounded values.  These are the
+low-precision bodies of the cross-precision comparison ("Greedy Decoding Is Not
+Precision-Invariant", abstract).  Weights and the LM head are the same under every policy.
+
 Weight layouts (nn.Linear): wqkv [(Hq+2Hkv)D, H] = q rows | k rows | v rows; wo [H, Hq D];
 w13 [2F, H] = gate rows | up rows (held on the device with gate and up rows interleaved for
 the gated projection); w2 [H, F]; whead [V, H]; emb [V, H]; RoPE tables
@@ -34,7 +42,10 @@ def _to_dev_bf16(a, dev):
 
 
 class Decoder:
-    def __init__(self, model, device="cuda", batch=1, tmax=None, tau=0.1, eps=1e-5):
+    def __init__(self, model, device="cuda", batch=1, tmax=None, tau=0.1, eps=1e-5, act="fp32"):
+        if act not in inv.ACT_FORMATS:
+            raise inv.InvError("unknown activation format %r" % (act,))
+        self.act = act
         cfg = model["cfg"]
         self.cfg = cfg
         self.H, self.Hq, self.Hkv, self.D = cfg["hidden"], cfg["hq"], cfg["hkv"], cfg["d"]
@@ -45,7 +56,10 @@ class Decoder:
         self.emb = _to_dev_bf16(model["emb"], self.dev)
         self.whead = _to_dev_bf16(model["whead"], self.dev)
         self.gf = _to_dev_bf16(model["gf"], self.dev)
-        self.layers = [{k: _to_dev_bf16(_interleave_gate_up(v) if k == "w13" else v, self.dev)
+        # the fused gated projection (FP32 policy) reads gate and up rows interleaved; the
+        # rounded policies store gate and up outputs, so they keep the [gate | up] layout
+        inter = act == "fp32"
+        self.layers = [{k: _to_dev_bf16(_interleave_gate_up(v) if (k == "w13" and inter) else v, self.dev)
                         for k, v in layer.items()} for layer in model["layers"]]
         self.cos = torch.from_numpy(np.ascontiguousarray(model["cos"])).to(self.dev)
         self.sin = torch.from_numpy(np.ascontiguousarray(model["sin"])).to(self.dev)
@@ -82,6 +96,8 @@ class Decoder:
 
     # one pass of the decoder body over rows (seq[m], pos[m]); attention via `attend`
     def _body(self, ids, seq, pos, attend):
+        if self.act != "fp32":
+            return self._body_rounded(ids, seq, pos, attend)
         H, Hq, Hkv, D, F = self.H, self.Hq, self.Hkv, self.D, self.F
         M = ids.numel()
         x = inv.inv_embed(ids, self.emb)
@@ -100,6 +116,41 @@ class Decoder:
             self._gemm(h, w["w2"], R=x, out=x)
             del h
         inv.inv_rmsnorm(x, self.gf, self.eps, out=n)
+        return n
+
+    # the same body with every stored activation rounded to self.act (unfused epilogues:
+    # projection outputs are stored, then added to the residual)
+    def _body_rounded(self, ids, seq, pos, attend):
+        H, Hq, Hkv, D, F = self.H, self.Hq, self.Hkv, self.D, self.F
+        fmt = self.act
+
+        def R(t):
+            return inv.inv_round_activations(t, fmt, out=t)
+
+        M = ids.numel()
+        x = R(inv.inv_embed(ids, self.emb))
+        n = torch.empty_like(x)
+        q = torch.empty((M, Hq, D), dtype=torch.float32, device=self.dev)
+        for li, w in enumerate(self.layers):
+            R(inv.inv_rmsnorm(x, w["g1"], self.eps, out=n))
+            qkv = R(self._gemm(n, w["wqkv"]))
+            inv.inv_rope_kv_append(qkv, Hq, Hkv, D, seq, pos, self.cos, self.sin, q, self.kc[li], self.vc[li],
+                                   fmt=fmt)
+            del qkv
+            att = R(attend(q, li).view(M, Hq * D))
+            o = R(self._gemm(att, w["wo"]))
+            del att
+            R(inv.inv_add(x, o, out=x))
+            del o
+            R(inv.inv_rmsnorm(x, w["g2"], self.eps, out=n))
+            gu = R(self._gemm(n, w["w13"]))             # [gate | up], [M, 2F]
+            h = R(inv.inv_swiglu(gu[:, :F], gu[:, F:]))
+            del gu
+            y = R(self._gemm(h, w["w2"]))
+            del h
+            R(inv.inv_add(x, y, out=x))
+            del y
+        R(inv.inv_rmsnorm(x, self.gf, self.eps, out=n))
         return n
 
     def prefill(self, tokens, block=2048, lm_rows=None):

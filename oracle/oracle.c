@@ -65,10 +65,10 @@ uint16_t orc_bf16_rne(float x) {
 }
 
 /* FP16 (IEEE binary16) = 1 sign, 5 exponent (bias 15), 10 stored fraction bits: normals
- * from 2^-14 to 65504, subnormals in steps of 2^-24 (FP precision blog, the note on
+ * from 2^-14 to 65504, subnormals in steps of 2^-24 (Yuan et al. blog, section 2, the note on
  * mantissa widths: BF16 7 bits, FP16 10, FP32 23).  Used for the FP16-activation setting
  * of the cross-precision comparison ("Greedy Decoding Is Not Precision-Invariant",
- * abstract: the same model run with BF16 and with FP16 activations).
+ * abstract: one model run in BF16 and in FP16, read here as the activation storage format).
  * f16_up(): exact widening to FP32. */
 float orc_f16_up(uint16_t h) {
     uint32_t sign = (uint32_t)(h & 0x8000u) << 16;

@@ -46,6 +46,25 @@ def test_c5_matches_oracle_short(orc, c5, dec):
         assert_bitwise(got[k], want[k], k)
 
 
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_c5_greedy_rounded_storage_matches_oracle(orc, c5, act):
+    """Full-size model with BF16 / FP16 activation storage: a greedy continuation (prompt of
+    8 tokens prefilled, then 3 decode steps with selective recompute) bitwise equal to the
+    oracle's from-scratch loop: tokens, margins, top-2 and recompute flags."""
+    from invariant_numerics_amd import agreement
+    from invariant_numerics_amd.decoder import Decoder
+    import torch
+    model, toks = c5
+    say("c5 greedy", act)
+    d = Decoder(model, batch=1, tmax=64, act=act, tau=0.1)
+    got = agreement.greedy(d, i32(toks[:1, :8]), 3)
+    del d
+    torch.cuda.empty_cache()
+    want = orc.greedy(toks[0, :8], model, 3, act=act, tau=np.float32(0.1))
+    for k in ("tokens", "margin", "top1", "top2", "recomputed"):
+        assert_bitwise(got[k][0], want[k], "%s %s" % (act, k))
+
+
 def test_c5_prefill_decode_batch_and_blocks(c5, dec):
     """T = 300 (two KV chunks): 3 sequences prefilled in token blocks of 128 equal
     (a) one sequence prefilled in one block, (b) token-by-token decode of all three."""
