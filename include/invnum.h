@@ -170,7 +170,9 @@ size_t inv_lmhead_workspace_bytes(int64_t B, int64_t K, int64_t V);
  *           lp = (z_target - M) - log_f(S).
  *   Rows with margin_P < tau (strict) are compacted on the device and redone with a = h
  *   (F pass); their outputs are F's and recomputed[b] = 1.  tau = +inf recomputes every
- *   row; tau = 0 recomputes none.
+ *   row; tau = 0 recomputes none.  For B <= 16 the F-pass logits of every row are computed
+ *   in the same sweep over W as the P ones (the weights are read once), and only the flagged
+ *   rows' are used; the results are the same bits either way.
  * Hs: FP32 [B, K] (ldh); W: BF16 [V, K] (row stride K); target: INT32 [B] (device),
  * 0 <= t < V (a row whose target is outside that range gets logprob NaN).
  * Outputs (device, [B]): logprob, margin (FP32), top1, top2 (INT32), recomputed (UINT8).

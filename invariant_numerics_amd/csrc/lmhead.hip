@@ -10,6 +10,12 @@
 //      rows are gathered into a dense buffer
 //   5. z = fixed-order GEMM(h_F, W) on the first `count` rows (count read on the device)
 //   6. row reduce of those rows; results overwrite the flagged rows' outputs.
+// Up to LM_FUSED_MAX_B rows, the FP32 logits of every row are computed by the same GEMM as
+// the primary ones (operand rows a_P | h, so the weights stream from memory once); step 5
+// disappears and step 6 reads the flagged rows' FP32 logits from the second half of z.  A
+// GEMM row depends on nothing but its own operand row, so these are the same bits as the
+// separate pass.  With tau <= 0 no row can be flagged (margins are >= 0 or NaN), and steps
+// 4-6 are skipped.
 //
 // Row reduce order (identical for both passes):
 //   top1 = lowest index of the maximum; top2 = lowest index != top1 of the maximum of the
@@ -54,17 +60,27 @@ __device__ __forceinline__ void top2_merge(Top2& t, const Top2& o) {
 //                 pinned lane order and combines the 64 lanes pairwise -> S_u;
 //   final_kernel  one thread per row: S = S_0, S = S + S_u ascending; lp; margin; flags.
 // mode 0: P pass over rows 0..B-1 (output row = row); mode 1: F pass over the first *count
-// rows of the compacted list (output row = idx[row]).
+// rows of the compacted list (output row = idx[row]); mode 2: the same rows, whose FP32
+// logits sit at z row B + idx[row] (computed beside the P ones).
 constexpr int GROUP = 4;                 // tiles per workgroup
+constexpr int LM_FUSED_MAX_B = 16;       // batch sizes whose FP32 logits share the primary GEMM
+
+// z row read by reduce row `row`: mode 0 (P pass) the row itself; mode 1 (separate F pass)
+// the compacted row; mode 2 (F logits computed beside the P ones) row zoff + idx[row].
+__device__ __forceinline__ const float* zrow(const float* z, int V, int mode, int row, int zoff,
+                                             const int32_t* idx) {
+    const int r = mode == 2 ? zoff + idx[row] : row;
+    return z + (int64_t)r * V;
+}
 constexpr int GV = GROUP * TV;           // vocabulary entries per workgroup
 
 __global__ __launch_bounds__(RED_THREADS) void lmhead_top2_kernel(
     const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
-    Top2* __restrict__ part) {
+    const int32_t* __restrict__ idx, int zoff, Top2* __restrict__ part) {
     __shared__ Top2 wtop[RED_THREADS / 64];
     const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
-    if (mode == 1 && row >= *count) return;
-    const float* zr = z + (int64_t)row * V;
+    if (mode != 0 && row >= *count) return;
+    const float* zr = zrow(z, V, mode, row, zoff, idx);
     const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
     Top2 t = {-__builtin_inff(), 0x7fffffff, -__builtin_inff(), 0x7fffffff};
     const int v0 = grp * GV, v1 = min(V, v0 + GV);
@@ -106,10 +122,10 @@ __device__ __forceinline__ Top2 merged_top2(const Top2* __restrict__ part, int r
 
 __global__ __launch_bounds__(RED_THREADS) void lmhead_tiles_kernel(
     const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
-    const Top2* __restrict__ part, float* __restrict__ tileS) {
+    const int32_t* __restrict__ idx, int zoff, const Top2* __restrict__ part, float* __restrict__ tileS) {
     const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
-    if (mode == 1 && row >= *count) return;
-    const float* zr = z + (int64_t)row * V;
+    if (mode != 0 && row >= *count) return;
+    const float* zr = zrow(z, V, mode, row, zoff, idx);
     const Top2 t = merged_top2(part, row, ngrp, V);
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
@@ -130,15 +146,15 @@ __global__ __launch_bounds__(RED_THREADS) void lmhead_tiles_kernel(
 
 __global__ void lmhead_final_kernel(
     const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau, int mode,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, const Top2* __restrict__ part,
-    int ngrp, const float* __restrict__ tileS,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int zoff,
+    const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
     float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
     int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= B) return;
-    if (mode == 1 && row >= *count) return;
-    const int orow = mode == 1 ? idx[row] : row;
-    const float* zr = z + (int64_t)row * V;
+    if (mode != 0 && row >= *count) return;
+    const int orow = mode != 0 ? idx[row] : row;
+    const float* zr = zrow(z, V, mode, row, zoff, idx);
     const Top2 t = merged_top2(part, row, ngrp, V);
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
@@ -161,11 +177,11 @@ __global__ void lmhead_final_kernel(
     margin[orow] = mg;
     top1[orow] = t.i1;
     top2[orow] = t.i2;
-    recomputed[orow] = (uint8_t)(mode == 1 ? 1 : (mg < tau ? 1 : 0));
+    recomputed[orow] = (uint8_t)(mode != 0 ? 1 : (mg < tau ? 1 : 0));
 }
 
-// a_P[b, k] = up(bf(h[b, k]))
-__global__ void round_bf16_kernel(const float* __restrict__ H, int B, int K, int64_t ldh,
+// a_P[b, k] = up(bf(h[b, k])); with `both`, also A[B + b, k] = h[b, k] (the FP32 operands)
+__global__ void round_bf16_kernel(const float* __restrict__ H, int B, int K, int64_t ldh, int both,
                                   float* __restrict__ A) {
     const int64_t n4 = (int64_t)B * (K / 4);
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
@@ -176,6 +192,7 @@ __global__ void round_bf16_kernel(const float* __restrict__ H, int B, int K, int
         o.x = bf16_up(bf16_rne(v.x)); o.y = bf16_up(bf16_rne(v.y));
         o.z = bf16_up(bf16_rne(v.z)); o.w = bf16_up(bf16_rne(v.w));
         *reinterpret_cast<float4*>(A + (int64_t)b * K + k) = o;
+        if (both) *reinterpret_cast<float4*>(A + (int64_t)(B + b) * K + k) = v;
     }
 }
 
@@ -227,9 +244,10 @@ struct WsLayout {
 WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
     WsLayout L;
     const int64_t ngrp = (V + GV - 1) / GV, ntiles = (V + TV - 1) / TV;
+    const int64_t zrows = B <= LM_FUSED_MAX_B ? 2 * B : B;     // P rows, then F rows when fused
     size_t off = 0;
-    L.a = off; off = align_up(off + sizeof(float) * (size_t)B * K);
-    L.z = off; off = align_up(off + sizeof(float) * (size_t)B * V);
+    L.a = off; off = align_up(off + sizeof(float) * (size_t)zrows * K);
+    L.z = off; off = align_up(off + sizeof(float) * (size_t)zrows * V);
     L.idx = off; off = align_up(off + sizeof(int32_t) * (size_t)B);
     L.count = off; off = align_up(off + sizeof(int32_t));
     L.part = off; off = align_up(off + sizeof(Top2) * (size_t)B * ngrp);
@@ -241,14 +259,17 @@ WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
 hipError_t launch_reduce(const LmheadArgs& a, int mode, const float* Z, const int32_t* idx,
                          const int32_t* count, Top2* part, float* tiles, hipStream_t st) {
     const int ngrp = (a.V + GV - 1) / GV;
+    const int zoff = a.B;                       // mode 2: the F rows follow the B primary rows
     dim3 grid(ngrp, a.B);
-    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, part);
+    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, idx, zoff,
+                       part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, part, tiles);
+    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, idx, zoff,
+                       part, tiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_final_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, Z, a.V, a.B, a.target,
-                       a.tau, mode, idx, count, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
+                       a.tau, mode, idx, count, zoff, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
                        a.recomputed);
     return hipGetLastError();
 }
@@ -268,19 +289,25 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     float* tiles = reinterpret_cast<float*>(ws + L.tiles);
     hipError_t e;
 
+    // margins are >= 0 (or NaN), so tau <= 0 (or NaN) flags no row: no recompute machinery
+    const bool recompute = a.tau > 0.0f;
+    const bool fused = recompute && a.B <= LM_FUSED_MAX_B;
     int64_t n4 = (int64_t)a.B * (a.K / 4);
     int g = (int)((n4 + 255) / 256);
     if (g > 65536) g = 65536;
-    hipLaunchKernelGGL(round_bf16_kernel, dim3(g), dim3(256), 0, st, a.Hs, a.B, a.K, a.ldh, A);
+    hipLaunchKernelGGL(round_bf16_kernel, dim3(g), dim3(256), 0, st, a.Hs, a.B, a.K, a.ldh, fused ? 1 : 0, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    GemmArgs ga{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, nullptr};
+    const int rows = fused ? 2 * a.B : a.B;
+    GemmArgs ga{A, rows, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, nullptr};
     if ((e = launch_gemm(ga, st, 1)) != hipSuccess) return e;
 
     if ((e = launch_reduce(a, 0, Z, nullptr, nullptr, part, tiles, st)) != hipSuccess) return e;
+    if (!recompute) return hipSuccess;
 
     hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, a.recomputed, a.B, idx, count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (fused) return launch_reduce(a, 2, Z, idx, count, part, tiles, st);
     hipLaunchKernelGGL(gather_rows_kernel, dim3(a.B), dim3(256), 0, st, a.Hs, a.K, a.ldh, idx, count, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 

@@ -49,6 +49,21 @@ def test_shapes_match_oracle(orc, B, K, V):
     check(run(h, W, tgt), orc.lmhead(h, W, tgt), "shape")
 
 
+def test_fused_and_separate_recompute_paths_agree(orc):
+    """Up to 16 rows the FP32 logits share the primary sweep over W; above, flagged rows get
+    their own pass.  Both give the oracle's bits, for tau 0.1, +inf and 0."""
+    d = synth.c1_inputs(rows=40)
+    Wd = bf16(d["w"])
+    for tau, mode in ((0.1, 0), (np.inf, 2), (0.0, 1)):
+        say("lmhead paths tau", tau)
+        want = orc.lmhead(d["h"], d["w"], d["target"], tau=np.float32(tau), mode=mode)
+        sep = run(d["h"], None, d["target"], tau=tau, Wd=Wd)
+        check(sep, want, "B=40 tau=%s" % tau)
+        for B in (16, 5, 1):
+            parts = [run(d["h"][s:s + B], None, d["target"][s:s + B], tau=tau, Wd=Wd) for s in range(0, 40, B)]
+            check({k: np.concatenate([p[k] for p in parts]) for k in KEYS}, want, "B=%d tau=%s" % (B, tau))
+
+
 def test_tau_limits_and_ties(orc):
     say("lmhead tau/ties")
     d = synth.c1_inputs(rows=16)
