@@ -29,6 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# up to this many rows the LM head computes the FP32 (recompute) logits in the same sweep over
+# the vocabulary weights as the primary ones, so a recomputed row adds no weight read
+LM_SHARED_SWEEP_MAX_B = 16
 FP32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix (MFMA) peak: 256 CU x 2.4 GHz x 256 flop/clk
 
 
@@ -203,7 +206,8 @@ def main():
         for i, t in enumerate(steps_t):
             kv = L * 2 * cfg["hkv"] * (t + 1) * cfg["d"] * 4 * B
             nrec = int(res[i]["recomputed"].sum().item())
-            step_bytes.append(body_w + head_w * (2 if nrec else 1) + kv)
+            head_sweeps = 2 if (nrec and B > LM_SHARED_SWEEP_MAX_B) else 1
+            step_bytes.append(body_w + head_w * head_sweeps + kv)
             agree.append(min(rate(res[i][k], outs[-1][k][:, t]) for k in keys))
         bitwise["prefill_vs_decode"] = float(np.mean(agree))
         bitwise["prefill_vs_decode_positions"] = [p0, T - 2]
@@ -219,8 +223,8 @@ def main():
                       note="whole decode step replayed from a HIP graph (all layers + LM head incl. "
                            "recompute pass), steps enqueued back to back and timed with HIP events on "
                            "the stream; host_ms_per_step is the host clock over the same loop; bytes = "
-                           "BF16 weights + FP32 KV cache read once (+ second vocabulary pass when a row "
-                           "is recomputed)")
+                           "BF16 weights + FP32 KV cache read once (+ a second vocabulary sweep when a "
+                           "row is recomputed and the batch exceeds 16 rows)")
         del dd
         # context for the decode fraction: a plain device copy (1 GiB read + 1 GiB written),
         # timed the same way
