@@ -309,7 +309,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
 }
 
 // ----------------------------------------------------------------- small --
-// M <= 64 (8 < M <= 16 only for N >= 8192): 32 x 32 tiles, one 16 x 16 tile per wavefront on
+// 16 < M <= 64: 32 x 32 tiles, one 16 x 16 tile per wavefront on
 // v_mfma_f32_16x16x4_f32 (four fused multiply-adds in k order per step; the same measured
 // property as the 32x32x2 form, checked through inv_mfma_f32_check), so M = 64, N = 4096
 // gives 256 workgroups of 4 wavefronts instead of 64.  K walks the same 32-wide LDS tiles
@@ -461,8 +461,219 @@ hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ gemv16 --
+// 5 <= M <= 16 (one 16-row MFMA tile; rows past M are zero operands, never stored).  Matrix
+// cores (v_mfma_f32_16x16x4_f32, four in-order fused multiply-adds per step) with the
+// activation rows as the A operand and 16 weight rows per wavefront as B, so every weight
+// element is read from LDS once per use and the activation chunk once per wavefront.
+// Workgroup: 4 wavefronts = WN along the weight rows x WK = 4 / WN along K: with WK > 1 the
+// wavefronts of a round take consecutive slices (round r, wavefront wk: slice r * WK + wk)
+// and their slice partials meet in LDS, where one wavefront folds them in ascending slice
+// order into the running total -- the same fold as everywhere else.  Each slice walks four
+// 64-wide chunks staged through LDS (double buffered): the weight tile as BF16 in the order
+// lane group g reads it (k = 4 s + g for s = 0..15: 32 contiguous bytes), the activation
+// tile as FP32 in the same order (64 contiguous bytes).
+constexpr int GV_CH = 64;                 // k per chunk (a quarter slice)
+constexpr int GV_WSEG = 144;              // bytes per (weight row, slice) chunk segment (128 + pad)
+constexpr int GV_XSEG = 68;               // floats per (activation row, slice) chunk segment (64 + pad)
+
+template <int WN, int PD, int ROLE>
+__global__ __launch_bounds__(256) void gemm_gemv16_kernel(
+    const float* __restrict__ X, int M, int K, int64_t ldx,
+    const uint16_t* __restrict__ W, int N, int64_t ldw,
+    const float* __restrict__ R, int64_t ldr,
+    float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    constexpr int WK = 4 / WN;
+    constexpr int BN = 16 * WN;
+    constexpr int XU = WK;                 // activation float4 per thread and chunk
+    __shared__ __attribute__((aligned(16))) unsigned char Wl[2][BN * WK * GV_WSEG];
+    __shared__ __attribute__((aligned(16))) float Xl[2][16 * WK * GV_XSEG];
+    __shared__ __attribute__((aligned(16))) float part[WK > 1 ? WK * WN * 64 * 4 : 4];
+    if (Mdev) M = min(M, *Mdev);
+    if (M <= 0) return;
+    const int n0 = blockIdx.x * BN;
+    const int S = (K + KS - 1) / KS;
+    const int nrounds = (S + WK - 1) / WK;
+    const int nit = nrounds * (KS / GV_CH);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, r = lane & 15;
+    const int wn = wv % WN, wk = wv / WN;
+
+    // PD chunks in flight in registers
+    uint4 wr[PD][2];
+    float4 xr[PD][XU];
+    // global -> registers for chunk `it` (round it / 4, chunk it % 4 of each of its slices);
+    // units past N, K or M are zeros and are not read
+    auto load = [&](int it, uint4 (&wq)[2], float4 (&xq)[XU]) {
+        const int rd = it / (KS / GV_CH), c = it % (KS / GV_CH);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + 256 * i;
+            const int c8 = q & 7, rest = q >> 3;
+            const int sk = rest % WK, rr = rest / WK;
+            const int sl = rd * WK + sk;
+            const int k = sl * KS + c * GV_CH + 8 * c8;
+            wq[i] = make_uint4(0u, 0u, 0u, 0u);
+            if ((sl < S) && (k < K) && (n0 + rr < N))
+                wq[i] = *reinterpret_cast<const uint4*>(W + (int64_t)(n0 + rr) * ldw + k);
+        }
+#pragma unroll
+        for (int j = 0; j < XU; ++j) {
+            const int u = tid + 256 * j;
+            const int q4 = u & 15, rest = u >> 4;
+            const int sk = rest % WK, m = rest / WK;
+            const int sl = rd * WK + sk;
+            const int k = sl * KS + c * GV_CH + 4 * q4;
+            xq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if ((sl < S) && (k < K) && (m < M))
+                xq[j] = *reinterpret_cast<const float4*>(X + (int64_t)m * ldx + k);
+        }
+    };
+    // registers -> LDS in the read order: element k = 8 c8 + e of a weight chunk goes to
+    // lane group g = e % 4, step s = 2 c8 + e / 4; element k = 4 q4 + e of an activation chunk
+    // to g = e, s = q4
+    auto store = [&](int buf, const uint4 (&wq)[2], const float4 (&xq)[XU]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = tid + 256 * i;
+            const int c8 = q & 7, rest = q >> 3;
+            unsigned char* seg = &Wl[buf][rest * GV_WSEG + c8 * 4];
+            const uint4 v = wq[i];
+            *reinterpret_cast<uint32_t*>(seg + 0 * 32) = (v.x & 0xffffu) | (v.z << 16);
+            *reinterpret_cast<uint32_t*>(seg + 1 * 32) = (v.x >> 16) | (v.z & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(seg + 2 * 32) = (v.y & 0xffffu) | (v.w << 16);
+            *reinterpret_cast<uint32_t*>(seg + 3 * 32) = (v.y >> 16) | (v.w & 0xffff0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < XU; ++j) {
+            const int u = tid + 256 * j;
+            const int q4 = u & 15, rest = u >> 4;
+            float* seg = &Xl[buf][rest * GV_XSEG + q4];
+            seg[0] = xq[j].x;
+            seg[16] = xq[j].y;
+            seg[32] = xq[j].z;
+            seg[48] = xq[j].w;
+        }
+    };
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, T = f32x4{0.f, 0.f, 0.f, 0.f};
+    const unsigned char* wseg0 = &Wl[0][((wn * 16 + r) * WK + wk) * GV_WSEG + g * 32];
+    const float* xseg0 = &Xl[0][(r * WK + wk) * GV_XSEG + g * 16];
+    auto compute = [&](int it) {
+        const int buf = it & 1;
+        const int rd = it / (KS / GV_CH), c = it % (KS / GV_CH);
+        const int sl = rd * WK + wk;
+        const int kvalid = sl < S ? min(GV_CH, K - (sl * KS + c * GV_CH)) : 0;
+        const uint4* wp = reinterpret_cast<const uint4*>(wseg0 + buf * (BN * WK * GV_WSEG));
+        const float4* xp = reinterpret_cast<const float4*>(xseg0 + buf * (16 * WK * GV_XSEG));
+        const uint4 w0 = wp[0], w1 = wp[1];
+        const float4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+        const uint32_t wv8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        const float a[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                             x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+        if (kvalid == GV_CH) {
+#pragma unroll
+            for (int st = 0; st < 16; ++st) {
+                const float b = (st & 1) ? bf16_hi(wv8[st >> 1]) : bf16_lo(wv8[st >> 1]);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b, acc, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 16; ++st) {
+                const float b = (st & 1) ? bf16_hi(wv8[st >> 1]) : bf16_lo(wv8[st >> 1]);
+                if (4 * st < kvalid) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b, acc, 0, 0, 0);
+            }
+        }
+        if (c == KS / GV_CH - 1) {
+            // end of a round: every wavefront holds the slice sum of slice rd * WK + wk
+            if constexpr (WK == 1) {
+                if (sl < S) {
+                    if (sl == 0) {
+                        T = acc;
+                    } else {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) T[v] = T[v] + acc[v];
+                    }
+                }
+            } else {
+                *reinterpret_cast<f32x4*>(&part[((wk * WN + wn) * 64 + lane) * 4]) = acc;
+                __syncthreads();
+                if (wk == 0) {
+                    for (int j = 0; j < WK; ++j) {
+                        const int sj = rd * WK + j;
+                        if (sj >= S) break;
+                        const f32x4 pj = *reinterpret_cast<const f32x4*>(&part[((j * WN + wn) * 64 + lane) * 4]);
+                        if (sj == 0) {
+                            T = pj;
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) T[v] = T[v] + pj[v];
+                        }
+                    }
+                }
+            }
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    // chunk it sits in register slot it % PD from its load until its store into LDS buffer
+    // it % 2; chunk it + PD is requested as soon as slot it % PD has been stored
+#pragma unroll
+    for (int d = 0; d < PD; ++d)
+        if (d < nit) load(d, wr[d], xr[d]);
+    store(0, wr[0], xr[0]);
+    __syncthreads();
+    for (int it0 = 0; it0 < nit; it0 += PD) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int it = it0 + d;
+            if (it < nit) {
+                if (it + PD < nit) load(it + PD, wr[d], xr[d]);
+                compute(it);
+                if (it + 1 < nit) store((it + 1) & 1, wr[(d + 1) % PD], xr[(d + 1) % PD]);
+                __syncthreads();
+            }
+        }
+    }
+    if (wk != 0) return;
+    // lane (g, r) holds rows 4g .. 4g + 3, column r of the wavefront's 16 weight rows
+    if constexpr (ROLE == 2) {
+        const int odd = r & 1;
+        const int gc = (n0 + wn * 16 + (r & ~1)) >> 1;
+#pragma unroll
+        for (int vp = 0; vp < 4; vp += 2) {
+            const float a0 = T[vp], a1 = T[vp + 1];
+            const float x0 = __shfl_xor(a0, 1), x1 = __shfl_xor(a1, 1);
+            const float gate = odd ? x1 : a0;
+            const float up = odd ? a1 : x0;
+            const int gm = 4 * g + vp + odd;
+            if (gm < M && n0 + wn * 16 + (r & ~1) < N) Y[(int64_t)gm * ldy + gc] = (gate / (1.0f + exp_f(-gate))) * up;
+        }
+        return;
+    }
+    const int gn = n0 + wn * 16 + r;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int gm = 4 * g + v;
+        if (gm < M && gn < N) {
+            float y = T[v];
+            if (R) y = R[(int64_t)gm * ldr + gn] + y;
+            Y[(int64_t)gm * ldy + gn] = y;
+        }
+    }
+}
+
+template <int WN, int PD, int ROLE>
+hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st) {
+    dim3 grid((a.N + 16 * WN - 1) / (16 * WN));
+    hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, ROLE>), grid, dim3(256), 0, st,
+                       a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- skinny --
-// M <= 16.  A workgroup owns ROWS weight rows (16, or 4 when the grid would otherwise be
+// M <= 4.  A workgroup owns ROWS weight rows (16, or 4 when the grid would otherwise be
 // too coarse to balance the CUs) and every activation row; thread (slice lane sl, row nl)
 // computes the chain of slice s = group + sl for all M rows, keeping one accumulator per
 // activation row.  Slices are processed in groups of 16; within a group the weights stream
@@ -683,15 +894,18 @@ int64_t gemm_skinny_max_k() {
 template <int ROLE>
 hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
     // M is an upper bound when Mdev is set (rows beyond *Mdev are skipped on the device).
-    // 8 < M <= 16 over many weight rows: the matrix-core tiles beat the VALU GEMV (whose
-    // 16 accumulators per thread make it compute-bound there)
-    if (a.M > 8 && a.M <= 16 && a.N >= 8192) return launch_small<ROLE>(a, st);
-    if (a.M <= 16 && a.K <= gemm_skinny_max_k()) {
+    // 5 <= M <= 16: the matrix-core GEMV (the VALU GEMV's per-row accumulators and LDS reads
+    // make it slower from 5 rows on).  At least 12288 weight rows: 32 per workgroup (two
+    // wavefronts along the rows, two along K); fewer: 16 per workgroup with the slices split
+    // over four wavefronts, so the grid still covers the chip.
+    if (a.M >= 5 && a.M <= 16) {
+        if (a.N >= 12288) return launch_gemv16<2, 2, ROLE>(a, st);
+        return launch_gemv16<1, 2, ROLE>(a, st);
+    }
+    if (a.M <= 4 && a.K <= gemm_skinny_max_k()) {
         if (a.M <= 1) return launch_skinny<1, ROLE>(a, st);
         if (a.M <= 2) return launch_skinny<2, ROLE>(a, st);
-        if (a.M <= 4) return launch_skinny<4, ROLE>(a, st);
-        if (a.M <= 8) return launch_skinny<8, ROLE>(a, st);
-        return launch_skinny<16, ROLE>(a, st);
+        return launch_skinny<4, ROLE>(a, st);
     }
     // the large tile only when it gives at least one workgroup per CU; below that the 64 x 64
     // tile's 8x larger grid wins (e.g. M = 512, N = 4096: 64 large tiles, 512 small ones)

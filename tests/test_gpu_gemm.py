@@ -17,6 +17,7 @@ def inv():
 
 @pytest.mark.parametrize("M,K,N", [
     (1, 8, 5), (1, 264, 70), (2, 4096, 130), (3, 520, 257), (5, 1000, 64), (16, 4096, 33),
+    (8, 8, 5), (8, 1000, 12300), (11, 520, 257), (16, 264, 12289), (13, 4104, 70),
     (17, 264, 129), (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
 ])
 def test_gemm_matches_oracle_small(orc, M, K, N):
@@ -35,10 +36,11 @@ def test_gemm_residual_epilogue(orc):
     want = (R + orc.gemm(X, W)).astype(np.float32)   # float32 add, as in the oracle decoder
     got = host(inv().inv_fixed_order_gemm(f32(X), bf16(W), R=f32(R)))
     assert_bitwise(got, want, "residual")
-    Xs = synth.normal(7204, (4, 512))
-    Rs = synth.normal(7205, (4, 96))
-    got = host(inv().inv_fixed_order_gemm(f32(Xs), bf16(W), R=f32(Rs)))
-    assert_bitwise(got, (Rs + orc.gemm(Xs, W)).astype(np.float32), "residual skinny")
+    for rows in (4, 10):
+        Xs = synth.normal(7204 + rows, (rows, 512))
+        Rs = synth.normal(7205 + rows, (rows, 96))
+        got = host(inv().inv_fixed_order_gemm(f32(Xs), bf16(W), R=f32(Rs)))
+        assert_bitwise(got, (Rs + orc.gemm(Xs, W)).astype(np.float32), "residual %d rows" % rows)
 
 
 def test_gemm_worked_example_k3_padded():
@@ -82,7 +84,7 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
     X, W = d["x"], d["w"]
     Xd, Wd = f32(X), bf16(W)
     full = host(inv().inv_fixed_order_gemm(Xd, Wd))
-    for M in (1, 3, 16, 64, 257):
+    for M in (1, 3, 8, 12, 16, 64, 257):
         say("gemm full M", M)
         part = host(inv().inv_fixed_order_gemm(Xd[:M].contiguous(), Wd))
         assert_bitwise(part, full[:M], "M=%d" % M)
@@ -97,7 +99,7 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
 
 
 @pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (5, 1000, 64), (16, 4096, 130),
-                                   (12, 520, 4200), (17, 264, 129), (64, 768, 64), (65, 4096, 300),
+                                   (12, 520, 4200), (9, 264, 6500), (8, 4096, 14336), (17, 264, 129), (64, 768, 64), (65, 4096, 300),
                                    (300, 1032, 257)])
 def test_gated_gemm_equals_gemm_then_swiglu(orc, M, K, F):
     """inv_gated_gemm on gate/up rows interleaved equals inv_fixed_order_gemm followed by
