@@ -293,6 +293,73 @@ void orc_gemm(const float* X, int64_t M, int64_t K, int64_t ldx,
             Y[m * ldy + n] = dot_ks_w16(X + m * ldx, W + n * ldw, K);
 }
 
+/* -------------------------------------------------------- GEMM backward -- */
+/* Backward of the LayerCast matmul Y = X up(W)^T for an output gradient dY:
+ *   dX[m, k] = dot_KS over n of (dY[m, n], up(W[n, k]))   (reduction over the N outputs)
+ *   dW[n, k] = dot_KS over m of (dY[m, n], X[m, k])       (reduction over the M tokens)
+ * Each is the same slice-then-fold order as the forward, taken along the reduced index, so
+ * a gradient's bits do not depend on how the work is split (the Meituan page's principles
+ * list: training and inference share one fixed order for every order-sensitive sum).  dW
+ * is FP32 (the weights are stored BF16; the optimizer's master copy is not part of this).
+ * dY fp32 [M, N] (lddy); X fp32 [M, K] (ldx); W bf16 [N, K] (ldw).  dX or dW may be NULL. */
+static float dx_at(const float* dY, int64_t N, int64_t lddy, const uint16_t* W, int64_t ldw,
+                   int64_t m, int64_t k, float* a, float* b) {
+    for (int64_t n = 0; n < N; ++n) {
+        a[n] = dY[m * lddy + n];
+        b[n] = orc_bf16_up(W[n * ldw + k]);
+    }
+    return dot_ks_f32(a, b, N);
+}
+static float dw_at(const float* dY, int64_t M, int64_t lddy, const float* X, int64_t ldx,
+                   int64_t n, int64_t k, float* a, float* b) {
+    for (int64_t m = 0; m < M; ++m) {
+        a[m] = dY[m * lddy + n];
+        b[m] = X[m * ldx + k];
+    }
+    return dot_ks_f32(a, b, M);
+}
+void orc_gemm_backward(const float* dY, int64_t M, int64_t N, int64_t lddy,
+                       const float* X, int64_t K, int64_t ldx, const uint16_t* W, int64_t ldw,
+                       float* dX, int64_t lddx, float* dW, int64_t lddw) {
+    int64_t L = M > N ? M : N;
+#pragma omp parallel
+    {
+        float* a = (float*)malloc(sizeof(float) * (size_t)L);
+        float* b = (float*)malloc(sizeof(float) * (size_t)L);
+        if (dX) {
+#pragma omp for collapse(2) schedule(static)
+            for (int64_t m = 0; m < M; ++m)
+                for (int64_t k = 0; k < K; ++k) dX[m * lddx + k] = dx_at(dY, N, lddy, W, ldw, m, k, a, b);
+        }
+        if (dW) {
+#pragma omp for collapse(2) schedule(static)
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t k = 0; k < K; ++k) dW[n * lddw + k] = dw_at(dY, M, lddy, X, ldx, n, k, a, b);
+        }
+        free(a);
+        free(b);
+    }
+}
+/* Sampled outputs of the same definitions: out[i] = dX[rows[i], cols[i]] (which 0) or
+ * dW[rows[i], cols[i]] (which 1), for checking full-size results one output at a time. */
+void orc_gemm_backward_at(int which, const float* dY, int64_t M, int64_t N, int64_t lddy,
+                          const float* X, int64_t K, int64_t ldx, const uint16_t* W, int64_t ldw,
+                          const int64_t* rows, const int64_t* cols, int64_t cnt, float* out) {
+    (void)K;
+    int64_t L = M > N ? M : N;
+#pragma omp parallel
+    {
+        float* a = (float*)malloc(sizeof(float) * (size_t)L);
+        float* b = (float*)malloc(sizeof(float) * (size_t)L);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < cnt; ++i)
+            out[i] = which == 0 ? dx_at(dY, N, lddy, W, ldw, rows[i], cols[i], a, b)
+                                : dw_at(dY, M, lddy, X, ldx, rows[i], cols[i], a, b);
+        free(a);
+        free(b);
+    }
+}
+
 /* -------------------------------------------------------------- RMSNorm -- */
 /* ss = dot_KS(x, x, H); r = 1 / sqrt((ss / H) + eps); y_k = (x_k * r) * up(gamma_k). */
 void orc_rmsnorm(const float* X, int64_t M, int64_t H, int64_t ldx,

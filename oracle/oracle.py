@@ -55,6 +55,11 @@ def lib():
         L.orc_f16_up.restype = ctypes.c_float
         L.orc_f16_up.argtypes = [ctypes.c_uint16]
         L.orc_round_act_array.argtypes = [f32p, i64, ctypes.c_int, f32p]
+        L.orc_gemm_backward.argtypes = [f32p, i64, i64, i64, f32p, i64, i64, u16p, i64,
+                                        f32p, i64, f32p, i64]
+        L.orc_gemm_backward_at.argtypes = [ctypes.c_int, f32p, i64, i64, i64, f32p, i64, i64, u16p, i64,
+                                           ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                           i64, f32p]
         L.orc_gemm.argtypes = [f32p, i64, i64, i64, u16p, i64, i64, f32p, i64]
         L.orc_rmsnorm.argtypes = [f32p, i64, i64, i64, u16p, ctypes.c_float, f32p, i64]
         L.orc_rope.argtypes = [f32p, i64, i64, i64, i64, i32p, f32p, f32p, f32p, i64]
@@ -157,6 +162,40 @@ def gemm(X, W):
     Y = np.empty((M, N), np.float32)
     lib().orc_gemm(_p(X, f32p), M, K, K, _p(W, u16p), N, K, _p(Y, f32p), N)
     return Y
+
+
+def gemm_backward(dY, X, W, dx=True, dw=True):
+    """Backward of Y = X up(W)^T: dX = dY up(W) (sum over the N outputs) and dW = dY^T X
+    (sum over the M tokens), each in the dot_KS order along the reduced index.
+    dY fp32 [M, N], X fp32 [M, K], W bf16 bits [N, K].  Returns (dX or None, dW or None)."""
+    dY = _c(dY, np.float32)
+    X = _c(X, np.float32)
+    W = _c(W, np.uint16)
+    M, N = dY.shape
+    M2, K = X.shape
+    assert M == M2 and W.shape == (N, K)
+    gx = np.empty((M, K), np.float32) if dx else None
+    gw = np.empty((N, K), np.float32) if dw else None
+    lib().orc_gemm_backward(_p(dY, f32p), M, N, N, _p(X, f32p), K, K, _p(W, u16p), K,
+                            _p(gx, f32p) if dx else None, K, _p(gw, f32p) if dw else None, K)
+    return gx, gw
+
+
+def gemm_backward_at(which, dY, X, W, rows, cols):
+    """Single outputs of the same definitions: dX[rows[i], cols[i]] (which "dx") or
+    dW[rows[i], cols[i]] (which "dw")."""
+    dY = _c(dY, np.float32)
+    X = _c(X, np.float32)
+    W = _c(W, np.uint16)
+    M, N = dY.shape
+    K = X.shape[1]
+    rows = _c(rows, np.int64)
+    cols = _c(cols, np.int64)
+    out = np.empty(rows.shape[0], np.float32)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib().orc_gemm_backward_at(0 if which == "dx" else 1, _p(dY, f32p), M, N, N, _p(X, f32p), K, K,
+                               _p(W, u16p), K, _p(rows, i64p), _p(cols, i64p), rows.shape[0], _p(out, f32p))
+    return out
 
 
 def rmsnorm(X, gamma, eps=1e-5):

@@ -117,6 +117,79 @@ def test_gemm_rows_independent_of_batch(orc):
         assert np.array_equal(bits(orc.gemm(X[m:m + 1], W)[0]), bits(Y[m]))
 
 
+# ------------------------------------------------------------ GEMM backward --
+
+def test_gemm_backward_small_integers_exact(orc):
+    """Integer operands with all partial sums below 2^24: dX = dY W and dW = dY^T X exactly."""
+    rng = np.random.default_rng(31)
+    M, N, K = 300, 260, 40
+    dY = rng.integers(-2, 3, size=(M, N)).astype(np.float32)
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    Wf = rng.integers(-2, 3, size=(N, K)).astype(np.float32)
+    dX, dW = orc.gemm_backward(dY, X, bf16_of(Wf))
+    i64 = lambda a: a.astype(np.int64)  # noqa: E731
+    assert np.array_equal(dX, (i64(dY) @ i64(Wf)).astype(np.float32))
+    assert np.array_equal(dW, (i64(dY).T @ i64(X)).astype(np.float32))
+
+
+def test_gemm_backward_one_hot_gradients(orc):
+    """dY = e_(m, n): dX row m is up(W[n]) exactly and dW row n is X[m] exactly; every other
+    output is +0."""
+    X = synth.normal(301, (70, 96))
+    W = synth.bf16_normal(302, (33, 96))
+    for m, n in ((0, 0), (69, 32), (17, 5)):
+        dY = np.zeros((70, 33), np.float32)
+        dY[m, n] = 1.0
+        dX, dW = orc.gemm_backward(dY, X, W)
+        want_x = np.zeros_like(dX)
+        want_x[m] = ref64.up(W[n]).astype(np.float32)
+        want_w = np.zeros_like(dW)
+        want_w[n] = X[m]
+        assert np.array_equal(bits(dX), bits(want_x)) and np.array_equal(bits(dW), bits(want_w))
+
+
+def test_gemm_backward_reduces_in_slices_along_the_reduced_index(orc):
+    """The token sum of dW runs in 256-token slices folded left to right (closed forms that a
+    single running sum would not give), and so does the output sum of dX."""
+    M = 768
+    dY = np.ones((M, 1), np.float32)
+    X = np.zeros((M, 2), np.float32)
+    X[0, 0] = 2.0 ** 25
+    X[256:260, 0] = 1.0          # slices 2^25 | 4 | 0 -> 2^25 + 4
+    X[0, 1], X[256, 1], X[512, 1] = 1.0, 2.0 ** 25, -(2.0 ** 25)   # fold ((1 + 2^25) - 2^25) = 0
+    W = bf16_of(np.ones((1, 2), np.float32))
+    _, dW = orc.gemm_backward(dY, X, W, dx=False)
+    assert dW[0, 0] == 2.0 ** 25 + 4 and dW[0, 1] == 0.0
+    N = 768
+    dY = np.zeros((1, N), np.float32)
+    dY[0, 0] = 2.0 ** 25
+    dY[0, 256:260] = 1.0
+    Wo = bf16_of(np.ones((N, 1), np.float32))
+    dX, _ = orc.gemm_backward(dY, np.zeros((1, 1), np.float32), Wo, dw=False)
+    assert dX[0, 0] == 2.0 ** 25 + 4
+
+
+def test_gemm_backward_within_bound_and_sampled_outputs(orc):
+    """Random operands: within the slice-then-fold error bound of the float64 products, and the
+    single-output entry point gives the same bits as the full computation."""
+    dY = synth.normal(303, (600, 520))
+    X = synth.normal(304, (600, 72))
+    W = synth.bf16_normal(305, (520, 72))
+    dX, dW = orc.gemm_backward(dY, X, W)
+    u = 2.0 ** -24
+    Wf = ref64.up(W)
+    d64 = dY.astype(np.float64)
+    for got, want, absum, depth in (
+            (dX, d64 @ Wf, np.abs(d64) @ np.abs(Wf), 256 + 3),
+            (dW, d64.T @ X.astype(np.float64), np.abs(d64).T @ np.abs(X.astype(np.float64)), 256 + 3)):
+        g = depth * u / (1 - depth * u)
+        assert np.all(np.abs(got.astype(np.float64) - want) <= g * absum)
+    rows = np.array([0, 599, 311]); cols = np.array([0, 71, 40])
+    assert np.array_equal(bits(orc.gemm_backward_at("dx", dY, X, W, rows, cols)), bits(dX[rows, cols]))
+    rows = np.array([0, 519, 260])
+    assert np.array_equal(bits(orc.gemm_backward_at("dw", dY, X, W, rows, cols)), bits(dW[rows, cols]))
+
+
 # ------------------------------------------------------------------ RMSNorm --
 
 def test_rmsnorm_constant_row_closed_form(orc):
