@@ -186,6 +186,32 @@ int inv_lmhead_logprob_top2(const float* Hs, int64_t B, int64_t K, int64_t ldh,
                             float* logprob, float* margin, int32_t* top1, int32_t* top2,
                             uint8_t* recomputed, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------ *
+ * inv_gemm_backward -- fixed-order backward of Y = X up(W)^T (inv_fixed_order_gemm) for an
+ * output gradient dY:
+ *   dX[m, k] = dot_KS over n of (dY[m, n], up(W[n, k]))   (sum over the N outputs)
+ *   dW[n, k] = dot_KS over m of (dY[m, n], X[m, k])       (sum over the M tokens)
+ * each in the forward's order along the reduced index (256-wide slices of in-order fused
+ * multiply-adds from +0, folded left to right), so a gradient's bits do not depend on the
+ * batch or on how the work is launched.  dW is FP32.
+ * dY: FP32 [M, N] (lddy); X: FP32 [M, K] (ldx); W: BF16 [N, K] (ldw); dX: FP32 [M, K] (lddx);
+ * dW: FP32 [N, K] (lddw).  dX or dW may be NULL to skip it (X is not read when dW is NULL,
+ * W and the workspace are not used when dX is NULL).
+ * Sizes: M >= 1, N >= 8 with N % 8 == 0, K >= 4 with K % 4 == 0; dY and X 16-byte aligned
+ * with lddy, ldx multiples of 4; W 2-byte aligned (any ldw >= K); dX and dW 4-byte aligned.
+ * Errors: INV_ERR_NULL, INV_ERR_SHAPE, INV_ERR_ALIGN, INV_ERR_WORKSPACE.  ws: at least
+ * inv_gemm_backward_workspace_bytes(M, N, K) bytes, 256-byte aligned (holds W transposed).
+ * Sources: Meituan page, "principles" (training and inference share one fixed order for the
+ * order-sensitive sums; the matmul reduce is one of them) and "key practices" (full-K
+ * accumulation, batch-invariant operators).
+ * ------------------------------------------------------------------------------------ */
+size_t inv_gemm_backward_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int inv_gemm_backward(const float* dY, int64_t M, int64_t N, int64_t lddy,
+                      const float* X, int64_t K, int64_t ldx,
+                      const uint16_t* W, int64_t ldw,
+                      float* dX, int64_t lddx, float* dW, int64_t lddw,
+                      void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- decoder helpers --- *
  * Elementwise steps of a Llama-shaped decoder (no reductions, so no order to pin).
  * ------------------------------------------------------------------------------------ */

@@ -56,6 +56,9 @@ def _load():
         "inv_swiglu": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
         "inv_add": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
         "inv_round_activations": (ctypes.c_int, [vp, i64, i64, i64, ctypes.c_int, vp, i64, vp]),
+        "inv_gemm_backward_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64]),
+        "inv_gemm_backward": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64,
+                                             vp, ctypes.c_size_t, vp]),
         "inv_eval_numerics": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, vp]),
         "inv_mfma_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
         "inv_mfma32_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
@@ -71,8 +74,8 @@ LIB = _load()
 EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "inv_gated_gemm", "inv_rmsnorm",
            "inv_attention_prefill", "inv_attention_decode_workspace_bytes", "inv_attention_decode",
            "inv_lmhead_workspace_bytes", "inv_lmhead_logprob_top2", "inv_embed", "inv_rope_kv_append",
-           "inv_swiglu", "inv_add", "inv_round_activations", "inv_eval_numerics", "inv_mfma_f32_check",
-           "inv_mfma32_f32_check")
+           "inv_swiglu", "inv_add", "inv_round_activations", "inv_gemm_backward_workspace_bytes",
+           "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check")
 
 
 def _check(status, what):
@@ -289,6 +292,34 @@ def inv_add(A, Bm, out=None):
     _check(LIB.inv_add(_p(A), _p(Bm), M, N, _row_ld(A), _row_ld(Bm), _p(out), _row_ld(out), _stream(A)),
            "inv_add")
     return out
+
+
+def inv_gemm_backward_workspace_bytes(M, N, K):
+    return int(LIB.inv_gemm_backward_workspace_bytes(M, N, K))
+
+
+def inv_gemm_backward(dY, X, W, dx=True, dw=True, out_dx=None, out_dw=None, ws=None):
+    """Gradients of Y = inv_fixed_order_gemm(X, W) for the output gradient dY (FP32 [M, N]):
+    dX = dY up(W) (FP32 [M, K]) and dW = dY^T X (FP32 [N, K]), each summed in the fixed
+    order along its reduced index.  Returns (dX or None, dW or None)."""
+    _dev(dY, X, W, out_dx, out_dw, ws)
+    M, N = dY.shape
+    Nw, K = W.shape
+    if Nw != N or (X is not None and tuple(X.shape) != (M, K)):
+        raise InvError("shapes: dY [M, N], X [M, K], W [N, K]")
+    if dx and out_dx is None:
+        out_dx = torch.empty((M, K), dtype=torch.float32, device=dY.device)
+    if dw and out_dw is None:
+        out_dw = torch.empty((N, K), dtype=torch.float32, device=dY.device)
+    if dx and ws is None:
+        ws = torch.empty(max(1, inv_gemm_backward_workspace_bytes(M, N, K)), dtype=torch.uint8, device=dY.device)
+    _check(LIB.inv_gemm_backward(_p(dY), M, N, _row_ld(dY), _p(X) if dw else None, K,
+                                 _row_ld(X) if dw else K, _p(W), _row_ld(W),
+                                 _p(out_dx) if dx else None, _row_ld(out_dx) if dx else K,
+                                 _p(out_dw) if dw else None, _row_ld(out_dw) if dw else K,
+                                 _p(ws) if dx else None, ws.numel() if dx else 0, _stream(dY)),
+           "inv_gemm_backward")
+    return (out_dx if dx else None), (out_dw if dw else None)
 
 
 # activation storage formats: name -> dtype code of the C ABI

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libinvnum.so")
-SOURCES = ["abi.hip", "gemm.hip", "attention.hip", "lmhead.hip", "elementwise.hip"]
+SOURCES = ["abi.hip", "gemm.hip", "attention.hip", "lmhead.hip", "elementwise.hip", "backward.hip"]
 ARCH = os.environ.get("INVNUM_ARCH", "gfx950")
 
 FLAGS = [

@@ -145,6 +145,33 @@ int inv_lmhead_logprob_top2(const float* Hs, int64_t B, int64_t K, int64_t ldh, 
     return fin(launch_lmhead(a, S(stream)));
 }
 
+size_t inv_gemm_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || N < 1 || K < 1) return 0;
+    return gemm_backward_ws_bytes(M, N, K);
+}
+
+int inv_gemm_backward(const float* dY, int64_t M, int64_t N, int64_t lddy, const float* X, int64_t K,
+                      int64_t ldx, const uint16_t* W, int64_t ldw, float* dX, int64_t lddx, float* dW,
+                      int64_t lddw, void* ws, size_t ws_bytes, void* stream) {
+    if (!dY || (dX && !W) || (dW && !X)) return INV_ERR_NULL;
+    if (M < 1 || N < 8 || N % 8 != 0 || K < 4 || K % 4 != 0 || lddy < N || M > I32MAX || N > I32MAX ||
+        K > I32MAX)
+        return INV_ERR_SHAPE;
+    if (dX && (ldw < K || lddx < K)) return INV_ERR_SHAPE;
+    if (dW && (ldx < K || lddw < K)) return INV_ERR_SHAPE;
+    if (!al16(dY) || lddy % 4) return INV_ERR_ALIGN;
+    if (dX) {
+        if (!ws || ws_bytes < inv_gemm_backward_workspace_bytes(M, N, K)) return INV_ERR_WORKSPACE;
+        if ((reinterpret_cast<uintptr_t>(W) & 1u) || (reinterpret_cast<uintptr_t>(ws) & 255u) ||
+            (reinterpret_cast<uintptr_t>(dX) & 3u))
+            return INV_ERR_ALIGN;
+    }
+    if (dW && (!al16(X) || ldx % 4 || (reinterpret_cast<uintptr_t>(dW) & 3u))) return INV_ERR_ALIGN;
+    if (!dX && !dW) return INV_OK;
+    return fin(launch_gemm_backward(dY, (int)M, (int)N, lddy, X, (int)K, ldx, W, ldw, dX, lddx, dW, lddw, ws,
+                                    S(stream)));
+}
+
 int inv_embed(const int32_t* ids, int64_t M, const uint16_t* table, int64_t vocab, int64_t H, float* X,
               int64_t ldx, void* stream) {
     if (!ids || !table || !X) return INV_ERR_NULL;

@@ -41,6 +41,10 @@ struct LmheadArgs {
     void* ws;
 };
 size_t lmhead_ws_bytes(int64_t B, int64_t K, int64_t V);
+size_t gemm_backward_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_backward(const float* dY, int M, int N, int64_t lddy, const float* X, int K, int64_t ldx,
+                                const uint16_t* W, int64_t ldw, float* dX, int64_t lddx, float* dW,
+                                int64_t lddw, void* ws, hipStream_t st);
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st);
 
 hipError_t launch_embed(const int32_t* ids, int M, const uint16_t* table, int vocab, int H, float* X,
