@@ -502,10 +502,10 @@ void orc_swiglu(const float* G, const float* U, int64_t M, int64_t F, int64_t ld
  *      then lanes combine pairwise, a_l = a_l + a_{l+w} for l = 0 mod 2w, w = 1,2,...,32;
  *      S_u = a_0; S = S_0, then S = S + S_u for u ascending
  *   lp = (z_target - M) - log_f(S)                                                    */
-static void lmhead_pass(const float* a, int64_t K, const uint16_t* W, int64_t ldw, int64_t V,
-                        int32_t target, float* z, float* lp, float* margin, int32_t* t1, int32_t* t2) {
-#pragma omp parallel for schedule(static) if (!omp_in_parallel())
-    for (int64_t v = 0; v < V; ++v) z[v] = dot_ks_w16(a, W + v * ldw, K);
+/* Row statistics of logits z[0..V): top-2 (lowest index first on ties), M = z_top1 and S, the
+ * fixed tree of exp_f(z_v - M) (tiles of 1024, 64 lanes, pairwise lane tree, tiles folded in
+ * ascending order). */
+static void lmhead_stats(const float* z, int64_t V, float* Mout, float* Sout, int64_t* t1, int64_t* t2) {
     int64_t b1 = 0;
     for (int64_t v = 1; v < V; ++v) if (z[v] > z[b1]) b1 = v;
     int64_t b2 = (b1 == 0) ? 1 : 0;
@@ -527,6 +527,19 @@ static void lmhead_pass(const float* a, int64_t K, const uint16_t* W, int64_t ld
             for (int l = 0; l < ORC_LW; l += 2 * w) lane[l] = lane[l] + lane[l + w];
         S = (u == 0) ? lane[0] : S + lane[0];
     }
+    *Mout = M;
+    *Sout = S;
+    *t1 = b1;
+    *t2 = b2;
+}
+
+static void lmhead_pass(const float* a, int64_t K, const uint16_t* W, int64_t ldw, int64_t V,
+                        int32_t target, float* z, float* lp, float* margin, int32_t* t1, int32_t* t2) {
+#pragma omp parallel for schedule(static) if (!omp_in_parallel())
+    for (int64_t v = 0; v < V; ++v) z[v] = dot_ks_w16(a, W + v * ldw, K);
+    float M, S;
+    int64_t b1, b2;
+    lmhead_stats(z, V, &M, &S, &b1, &b2);
     *lp = (z[target] - M) - orc_log_f(S);
     *margin = M - z[b2];
     *t1 = (int32_t)b1;
@@ -589,6 +602,36 @@ void orc_lmhead(const float* Hs, int64_t B, int64_t K, int64_t ldh, const uint16
                        lp + b, margin + b, top1 + b, top2 + b, flag + b);
         free(z);
         free(aP);
+    }
+}
+
+/* ------------------------------------------------------ logit gradient -- */
+/* Gradient, with respect to the FP32 logits z = dot_KS(h, up(W_v)), of coef * lp, where lp is
+ * the log-probability of the target under the FP32 pass (the pass every row takes with
+ * tau = +inf: a trainer's policy-gradient term for one token):
+ *   p_v = exp_f(z_v - M) / S        (M and S exactly as the forward computes them)
+ *   g_v = coef * ((v == target ? 1 : 0) - p_v)
+ * d lp / d z_v = [v == target] - softmax_v, the softmax in the forward's fixed order (Meituan
+ * page, "principles": the logprob accumulation is one of the order-sensitive sums, in
+ * training as in inference).  Hs fp32 [B, K] (ldh); W bf16 [V, K]; G fp32 [B, V] (ldg);
+ * lp (optional) [B] the forward logprob of the same pass. */
+void orc_lmhead_logit_grad(const float* Hs, int64_t B, int64_t K, int64_t ldh, const uint16_t* W, int64_t V,
+                           const int32_t* target, const float* coef, float* G, int64_t ldg, float* lp) {
+    for (int64_t b = 0; b < B; ++b) {
+        const float* h = Hs + b * ldh;
+        float* z = G + b * ldg;
+#pragma omp parallel for schedule(static)
+        for (int64_t v = 0; v < V; ++v) z[v] = dot_ks_w16(h, W + v * K, K);
+        float M, S;
+        int64_t b1, b2;
+        lmhead_stats(z, V, &M, &S, &b1, &b2);
+        int32_t t = target[b];
+        if (lp) lp[b] = (t >= 0 && t < V) ? (z[t] - M) - orc_log_f(S) : NAN;
+        for (int64_t v = 0; v < V; ++v) {
+            float p = orc_exp_f(z[v] - M) / S;
+            float q = (v == t ? 1.0f : 0.0f) - p;
+            z[v] = coef[b] * q;
+        }
     }
 }
 

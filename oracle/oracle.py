@@ -55,6 +55,7 @@ def lib():
         L.orc_f16_up.restype = ctypes.c_float
         L.orc_f16_up.argtypes = [ctypes.c_uint16]
         L.orc_round_act_array.argtypes = [f32p, i64, ctypes.c_int, f32p]
+        L.orc_lmhead_logit_grad.argtypes = [f32p, i64, i64, i64, u16p, i64, i32p, f32p, f32p, i64, f32p]
         L.orc_gemm_backward.argtypes = [f32p, i64, i64, i64, f32p, i64, i64, u16p, i64,
                                         f32p, i64, f32p, i64]
         L.orc_gemm_backward_at.argtypes = [ctypes.c_int, f32p, i64, i64, i64, f32p, i64, i64, u16p, i64,
@@ -162,6 +163,23 @@ def gemm(X, W):
     Y = np.empty((M, N), np.float32)
     lib().orc_gemm(_p(X, f32p), M, K, K, _p(W, u16p), N, K, _p(Y, f32p), N)
     return Y
+
+
+def lmhead_logit_grad(Hs, W, target, coef):
+    """Gradient of coef[b] * lp_b with respect to the FP32-pass logits: G [B, V] with
+    G[b, v] = coef[b] * ([v == target_b] - exp_f(z_v - M) / S); also returns lp [B]."""
+    Hs = _c(Hs, np.float32)
+    W = _c(W, np.uint16)
+    target = _c(target, np.int32)
+    coef = _c(coef, np.float32)
+    B, K = Hs.shape
+    V, K2 = W.shape
+    assert K == K2 and target.shape == (B,) and coef.shape == (B,)
+    G = np.empty((B, V), np.float32)
+    lp = np.empty(B, np.float32)
+    lib().orc_lmhead_logit_grad(_p(Hs, f32p), B, K, K, _p(W, u16p), V, _p(target, i32p), _p(coef, f32p),
+                                _p(G, f32p), V, _p(lp, f32p))
+    return G, lp
 
 
 def gemm_backward(dY, X, W, dx=True, dw=True):

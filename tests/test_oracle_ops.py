@@ -190,6 +190,47 @@ def test_gemm_backward_within_bound_and_sampled_outputs(orc):
     assert np.array_equal(bits(orc.gemm_backward_at("dw", dY, X, W, rows, cols)), bits(dW[rows, cols]))
 
 
+# ------------------------------------------------------------ logit gradient --
+
+def test_logit_grad_zero_weights_closed_form(orc):
+    """W = 0: z = 0, M = 0, S = V exactly, p = RN(1/V) for every v, and
+    g_v = RN(coef * RN([v == t] - p))."""
+    V, K = 3000, 64
+    h = synth.normal(401, (3, K))
+    W = np.zeros((V, K), np.uint16)
+    tgt = np.array([0, 2999, 1234], np.int32)
+    coef = np.array([1.0, -0.5, 3.0], np.float32)
+    G, lp = orc.lmhead_logit_grad(h, W, tgt, coef)
+    p = np.float32(1.0) / np.float32(V)
+    for b in range(3):
+        q = np.full(V, -p, np.float32)
+        q[tgt[b]] = np.float32(1.0) - p
+        want = (coef[b] * q).astype(np.float32)
+        assert np.array_equal(bits(G[b]), bits(want))
+    assert np.allclose(lp, -np.log(V), rtol=1e-6)
+
+
+def test_logit_grad_vs_float64_and_forward(orc):
+    """Against the float64 softmax gradient of the float64 logits (within 1e-5 of the largest
+    entry); the rows sum to ~0; lp is the forward's FP32-pass logprob bit for bit."""
+    B, K, V = 4, 256, 2500
+    h = synth.normal(402, (B, K))
+    W = synth.bf16_normal(403, (V, K), 0.1)
+    tgt = synth.uniform_int(404, (B,), V)
+    coef = np.array([1.0, -2.0, 0.25, 1.5], np.float32)
+    G, lp = orc.lmhead_logit_grad(h, W, tgt, coef)
+    z64 = h.astype(np.float64) @ ref64.up(W).T
+    p64 = np.exp(z64 - z64.max(axis=1, keepdims=True))
+    p64 /= p64.sum(axis=1, keepdims=True)
+    onehot = np.zeros_like(p64)
+    onehot[np.arange(B), tgt] = 1.0
+    g64 = coef[:, None].astype(np.float64) * (onehot - p64)
+    assert np.max(np.abs(G - g64)) <= 1e-5 * np.max(np.abs(g64))
+    assert np.all(np.abs(G.astype(np.float64).sum(axis=1)) <= 1e-5 * np.abs(coef))
+    fwd = orc.lmhead(h, W, tgt, mode=2)
+    assert np.array_equal(bits(lp), bits(fwd["logprob"]))
+
+
 # ------------------------------------------------------------------ RMSNorm --
 
 def test_rmsnorm_constant_row_closed_form(orc):
