@@ -187,6 +187,28 @@ int inv_lmhead_logprob_top2(const float* Hs, int64_t B, int64_t K, int64_t ldh,
                             uint8_t* recomputed, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------ *
+ * inv_lmhead_logit_grad -- gradient of coef[b] * lp_b with respect to the logits of the FP32
+ * pass (z_v = dot_KS(h, up(W_v)); the pass every row takes with tau = +inf), lp_b the
+ * log-probability of target[b] -- one token's policy-gradient term:
+ *   p_v = exp_f(z_v - M) / S     (M = z_top1 and S the fixed tree, exactly as the forward)
+ *   G[b, v] = coef[b] * ([v == target[b]] - p_v)
+ * Together with inv_gemm_backward on G (dX: the hidden-state gradient, a sum over the V
+ * logits; dW: the head's weight gradient, a sum over tokens) this is the LM-head backward of
+ * a policy-gradient step, every sum in a fixed order.
+ * Hs: FP32 [B, K] (ldh); W: BF16 [V, K] (row stride K); target: INT32 [B]; coef: FP32 [B]
+ * (device).  G: FP32 [B, V], row stride V (also holds the logits while they are reduced).
+ * logprob: FP32 [B] or NULL.  A target outside [0, V) gives logprob NaN and no +1 term.
+ * Sizes as inv_lmhead_logprob_top2; ws: inv_lmhead_logit_grad_workspace_bytes(B, K, V).
+ * Sources: Meituan page, "principles" (the logprob accumulation is order-sensitive in
+ * training as in inference); "Greedy Decoding Is Not Precision-Invariant", abstract (the
+ * FP32 LM head).
+ * ------------------------------------------------------------------------------------ */
+size_t inv_lmhead_logit_grad_workspace_bytes(int64_t B, int64_t K, int64_t V);
+int inv_lmhead_logit_grad(const float* Hs, int64_t B, int64_t K, int64_t ldh, const uint16_t* W, int64_t V,
+                          const int32_t* target, const float* coef, float* G, float* logprob,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------ *
  * inv_gemm_backward -- fixed-order backward of Y = X up(W)^T (inv_fixed_order_gemm) for an
  * output gradient dY:
  *   dX[m, k] = dot_KS over n of (dY[m, n], up(W[n, k]))   (sum over the N outputs)

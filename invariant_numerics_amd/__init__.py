@@ -11,6 +11,6 @@ from .binding import (  # noqa: F401
     InvError, inv_add, inv_attention_decode, inv_gemm_backward, inv_gemm_backward_workspace_bytes, inv_attention_decode_workspace_bytes,
     inv_attention_prefill, inv_embed, inv_eval_numerics, inv_fixed_order_gemm, inv_gated_gemm,
     inv_get_constants,
-    inv_lmhead_logprob_top2, inv_lmhead_workspace_bytes, inv_mfma_f32_check, inv_mfma32_f32_check, inv_rmsnorm, inv_rope_kv_append,
+    inv_lmhead_logit_grad, inv_lmhead_logit_grad_workspace_bytes, inv_lmhead_logprob_top2, inv_lmhead_workspace_bytes, inv_mfma_f32_check, inv_mfma32_f32_check, inv_rmsnorm, inv_rope_kv_append,
     inv_round_activations, inv_status_string, inv_swiglu,
 )

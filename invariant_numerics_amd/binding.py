@@ -56,6 +56,9 @@ def _load():
         "inv_swiglu": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
         "inv_add": (ctypes.c_int, [vp, vp, i64, i64, i64, i64, vp, i64, vp]),
         "inv_round_activations": (ctypes.c_int, [vp, i64, i64, i64, ctypes.c_int, vp, i64, vp]),
+        "inv_lmhead_logit_grad_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64]),
+        "inv_lmhead_logit_grad": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                                 vp]),
         "inv_gemm_backward_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64]),
         "inv_gemm_backward": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, i64, vp, i64, vp, i64, vp, i64,
                                              vp, ctypes.c_size_t, vp]),
@@ -74,7 +77,8 @@ LIB = _load()
 EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "inv_gated_gemm", "inv_rmsnorm",
            "inv_attention_prefill", "inv_attention_decode_workspace_bytes", "inv_attention_decode",
            "inv_lmhead_workspace_bytes", "inv_lmhead_logprob_top2", "inv_embed", "inv_rope_kv_append",
-           "inv_swiglu", "inv_add", "inv_round_activations", "inv_gemm_backward_workspace_bytes",
+           "inv_swiglu", "inv_add", "inv_round_activations", "inv_lmhead_logit_grad_workspace_bytes",
+           "inv_lmhead_logit_grad", "inv_gemm_backward_workspace_bytes",
            "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check")
 
 
@@ -292,6 +296,28 @@ def inv_add(A, Bm, out=None):
     _check(LIB.inv_add(_p(A), _p(Bm), M, N, _row_ld(A), _row_ld(Bm), _p(out), _row_ld(out), _stream(A)),
            "inv_add")
     return out
+
+
+def inv_lmhead_logit_grad_workspace_bytes(B, K, V):
+    return int(LIB.inv_lmhead_logit_grad_workspace_bytes(B, K, V))
+
+
+def inv_lmhead_logit_grad(Hs, W, target, coef, out=None, logprob=False, ws=None):
+    """Gradient of coef[b] * logprob_b (FP32 head) with respect to the logits: FP32 [B, V].
+    With logprob=True also returns the FP32-pass logprobs [B]."""
+    _dev(Hs, W, target, coef, out, ws)
+    B, K = Hs.shape
+    V = W.shape[0]
+    if out is None:
+        out = torch.empty((B, V), dtype=torch.float32, device=Hs.device)
+    if out.shape != (B, V) or not out.is_contiguous():
+        raise InvError("gradient output must be a contiguous [B, V] FP32 tensor")
+    lp = torch.empty(B, dtype=torch.float32, device=Hs.device) if logprob else None
+    if ws is None:
+        ws = torch.empty(max(1, inv_lmhead_logit_grad_workspace_bytes(B, K, V)), dtype=torch.uint8, device=Hs.device)
+    _check(LIB.inv_lmhead_logit_grad(_p(Hs), B, K, _row_ld(Hs), _p(W), V, _p(target), _p(coef), _p(out), _p(lp),
+                                     _p(ws), ws.numel(), _stream(Hs)), "inv_lmhead_logit_grad")
+    return (out, lp) if logprob else out
 
 
 def inv_gemm_backward_workspace_bytes(M, N, K):

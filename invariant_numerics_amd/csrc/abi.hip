@@ -145,6 +145,26 @@ int inv_lmhead_logprob_top2(const float* Hs, int64_t B, int64_t K, int64_t ldh, 
     return fin(launch_lmhead(a, S(stream)));
 }
 
+size_t inv_lmhead_logit_grad_workspace_bytes(int64_t B, int64_t K, int64_t V) {
+    (void)K;
+    if (B < 1 || V < 2) return 0;
+    return logit_grad_ws_bytes(B, V);
+}
+
+int inv_lmhead_logit_grad(const float* Hs, int64_t B, int64_t K, int64_t ldh, const uint16_t* W, int64_t V,
+                          const int32_t* target, const float* coef, float* G, float* logprob, void* ws,
+                          size_t ws_bytes, void* stream) {
+    if (!Hs || !W || !target || !coef || !G) return INV_ERR_NULL;
+    if (B < 1 || K < 8 || K % 8 != 0 || V < 2 || ldh < K || B > 65535 || K > I32MAX || V > (int64_t)1024 * TV ||
+        B * V > ((int64_t)1 << 40))
+        return INV_ERR_SHAPE;
+    if (!ws || ws_bytes < inv_lmhead_logit_grad_workspace_bytes(B, K, V)) return INV_ERR_WORKSPACE;
+    if (!al16(Hs) || !al16(W) || !al16(ws) || ldh % 4 || (reinterpret_cast<uintptr_t>(G) & 3u))
+        return INV_ERR_ALIGN;
+    LogitGradArgs a{Hs, (int)B, (int)K, ldh, W, (int)V, target, coef, G, logprob, ws};
+    return fin(launch_logit_grad(a, S(stream)));
+}
+
 size_t inv_gemm_backward_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || N < 1 || K < 1) return 0;
     return gemm_backward_ws_bytes(M, N, K);

@@ -41,6 +41,15 @@ struct LmheadArgs {
     void* ws;
 };
 size_t lmhead_ws_bytes(int64_t B, int64_t K, int64_t V);
+struct LogitGradArgs {
+    const float* Hs; int B; int K; int64_t ldh;
+    const uint16_t* W; int V;
+    const int32_t* target; const float* coef;
+    float* G; float* logprob;
+    void* ws;
+};
+size_t logit_grad_ws_bytes(int64_t B, int64_t V);
+hipError_t launch_logit_grad(const LogitGradArgs& a, hipStream_t st);
 size_t gemm_backward_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_backward(const float* dY, int M, int N, int64_t lddy, const float* X, int K, int64_t ldx,
                                 const uint16_t* W, int64_t ldw, float* dX, int64_t lddx, float* dW,

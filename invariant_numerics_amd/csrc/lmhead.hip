@@ -144,6 +144,22 @@ __global__ __launch_bounds__(RED_THREADS) void lmhead_tiles_kernel(
     if (lane == 0) tileS[(int64_t)row * ntiles + u] = acc;
 }
 
+// S = S_0, S = S + S_u for the tiles in ascending order; the tile sums are loaded 16 at a
+// time ahead of the adds
+__device__ __forceinline__ float fold_tiles(const float* __restrict__ ts, int ntiles) {
+    float S = ts[0];
+    int u = 1;
+    for (; u + 16 <= ntiles; u += 16) {
+        float q[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) q[e] = ts[u + e];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) S = S + q[e];
+    }
+    for (; u < ntiles; ++u) S = S + ts[u];
+    return S;
+}
+
 __global__ void lmhead_final_kernel(
     const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau, int mode,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int zoff,
@@ -158,18 +174,7 @@ __global__ void lmhead_final_kernel(
     const Top2 t = merged_top2(part, row, ngrp, V);
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
-    const float* ts = tileS + (int64_t)row * ntiles;
-    // tiles folded in ascending order; their sums are loaded 16 at a time ahead of the adds
-    float S = ts[0];
-    int u = 1;
-    for (; u + 16 <= ntiles; u += 16) {
-        float q[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) q[e] = ts[u + e];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) S = S + q[e];
-    }
-    for (; u < ntiles; ++u) S = S + ts[u];
+    const float S = fold_tiles(tileS + (int64_t)row * ntiles, ntiles);
     const int tg = target[orow];
     const float lp = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
     const float mg = M - zr[t.i2];
@@ -178,6 +183,40 @@ __global__ void lmhead_final_kernel(
     top1[orow] = t.i1;
     top2[orow] = t.i2;
     recomputed[orow] = (uint8_t)(mode != 0 ? 1 : (mg < tau ? 1 : 0));
+}
+
+// Logit gradient, step 1: per row M = z_top1 and S (the forward's fold), and the logprob.
+__global__ void lmhead_rowstats_kernel(const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target,
+                                       const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
+                                       float* __restrict__ stats, float* __restrict__ logprob) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= B) return;
+    const float* zr = z + (int64_t)row * V;
+    const Top2 t = merged_top2(part, row, ngrp, V);
+    const float M = zr[t.i1];
+    const int ntiles = (V + TV - 1) / TV;
+    const float S = fold_tiles(tileS + (int64_t)row * ntiles, ntiles);
+    stats[2 * row] = M;
+    stats[2 * row + 1] = S;
+    if (logprob) {
+        const int tg = target[row];
+        logprob[row] = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
+    }
+}
+
+// Logit gradient, step 2, in place over the logits: p = exp_f(z - M) / S (one rounded
+// division), g = coef * ([v == target] - p).
+__global__ void logit_grad_kernel(float* __restrict__ G, int V, const int32_t* __restrict__ target,
+                                  const float* __restrict__ coef, const float* __restrict__ stats) {
+    const int row = blockIdx.y;
+    const float M = stats[2 * row], S = stats[2 * row + 1], c = coef[row];
+    const int tg = target[row];
+    float* gr = G + (int64_t)row * V;
+    for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < V; v += gridDim.x * blockDim.x) {
+        const float p = exp_f(gr[v] - M) / S;
+        const float q = (v == tg ? 1.0f : 0.0f) - p;
+        gr[v] = c * q;
+    }
 }
 
 // a_P[b, k] = up(bf(h[b, k])); with `both`, also A[B + b, k] = h[b, k] (the FP32 operands)
@@ -274,9 +313,53 @@ hipError_t launch_reduce(const LmheadArgs& a, int mode, const float* Z, const in
     return hipGetLastError();
 }
 
+struct GradWs {
+    size_t part, tiles, stats, total;
+};
+GradWs grad_ws_layout(int64_t B, int64_t V) {
+    GradWs L;
+    const int64_t ngrp = (V + GV - 1) / GV, ntiles = (V + TV - 1) / TV;
+    size_t off = 0;
+    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)B * ngrp);
+    L.tiles = off; off = align_up(off + sizeof(float) * (size_t)B * ntiles);
+    L.stats = off; off = align_up(off + sizeof(float) * 2 * (size_t)B);
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 size_t lmhead_ws_bytes(int64_t B, int64_t K, int64_t V) { return ws_layout(B, K, V).total; }
+
+size_t logit_grad_ws_bytes(int64_t B, int64_t V) { return grad_ws_layout(B, V).total; }
+
+// Logit gradient of coef * lp on the FP32 pass: logits into G (the vocabulary GEMM on h
+// itself), the forward's row reductions (mode 0 of the top-2 and tile kernels), row
+// statistics, then the gradient in place.
+hipError_t launch_logit_grad(const LogitGradArgs& a, hipStream_t st) {
+    const GradWs L = grad_ws_layout(a.B, a.V);
+    char* ws = reinterpret_cast<char*>(a.ws);
+    Top2* part = reinterpret_cast<Top2*>(ws + L.part);
+    float* tiles = reinterpret_cast<float*>(ws + L.tiles);
+    float* stats = reinterpret_cast<float*>(ws + L.stats);
+    hipError_t e;
+    GemmArgs ga{a.Hs, a.B, a.K, a.ldh, a.W, a.V, (int64_t)a.K, nullptr, 0, a.G, (int64_t)a.V, nullptr};
+    if ((e = launch_gemm(ga, st, 1)) != hipSuccess) return e;
+    const int ngrp = (a.V + GV - 1) / GV;
+    dim3 grid(ngrp, a.B);
+    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, a.G, a.V, 0, nullptr, nullptr, 0, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, a.G, a.V, 0, nullptr, nullptr, 0, part,
+                       tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(lmhead_rowstats_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, a.G, a.V, a.B, a.target,
+                       part, ngrp, tiles, stats, a.logprob);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int gx = (a.V + 1023) / 1024;
+    hipLaunchKernelGGL(logit_grad_kernel, dim3(gx < 64 ? gx : 64, a.B), dim3(256), 0, st, a.G, a.V, a.target, a.coef,
+                       stats);
+    return hipGetLastError();
+}
 
 hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     const WsLayout L = ws_layout(a.B, a.K, a.V);

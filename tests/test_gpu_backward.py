@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import assert_bitwise, bf16, f32, host, requires_gpu, say
+from gpu_util import assert_bitwise, bf16, f32, host, i32, requires_gpu, say
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -86,3 +86,46 @@ def test_backward_full_size_sampled(orc, M, N, K):
         assert_bitwise(host(part), dXh[:rows], "dX batch %d" % rows)
     del dX, dW
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,K,V", [(1, 8, 2), (3, 264, 1025), (5, 256, 4096)])
+def test_logit_grad_matches_oracle(orc, B, K, V):
+    say("logit grad", B, K, V)
+    h = synth.normal(8700 + V, (B, K))
+    W = synth.bf16_normal(8701 + V, (V, K), 0.1)
+    tgt = synth.uniform_int(8702 + V, (B,), V)
+    if B > 1:
+        tgt[1] = V + 3                     # outside the vocabulary: no +1 term, logprob NaN
+    coef = synth.normal(8703 + V, (B,))
+    G, lp = inv().inv_lmhead_logit_grad(f32(h), bf16(W), i32(tgt), f32(coef),
+                                        logprob=True)
+    want_g, want_lp = orc.lmhead_logit_grad(h, W, tgt, coef)
+    assert_bitwise(host(G), want_g, "G")
+    got_lp = host(lp)
+    assert np.array_equal(np.isnan(got_lp), np.isnan(want_lp))
+    fin = ~np.isnan(want_lp)
+    assert_bitwise(got_lp[fin], want_lp[fin], "logprob")
+
+
+def test_logit_grad_full_vocab_and_head_backward(orc):
+    """Vocabulary 128256, hidden 4096: four rows of G bitwise equal to the oracle and equal
+    between batch 4 and batch 1; the head backward on G (hidden-state gradient summed over the
+    128256 logits, weight gradient over the 4 tokens) equals the oracle on sampled outputs."""
+    d = synth.c4_inputs(rows=4)
+    h, W, tgt = d["h"], d["w"], d["target"]
+    coef = np.array([1.0, -0.75, 0.5, 2.0], np.float32)
+    say("logit grad full vocab")
+    Wd = bf16(W)
+    G = inv().inv_lmhead_logit_grad(f32(h), Wd, i32(tgt), f32(coef))
+    want_g, _ = orc.lmhead_logit_grad(h, W, tgt, coef)
+    Gh = host(G)
+    assert_bitwise(Gh, want_g, "G full vocab")
+    one = inv().inv_lmhead_logit_grad(f32(h[2:3]), Wd, i32(tgt[2:3]), f32(coef[2:3]))
+    assert_bitwise(host(one)[0], Gh[2], "G batch 1 vs 4")
+    say("head backward on G")
+    dH, dW = inv().inv_gemm_backward(G, f32(h), Wd)
+    rng = np.random.default_rng(9)
+    rx = rng.integers(0, 4, 32); cx = rng.integers(0, 4096, 32)
+    rw = rng.integers(0, 128256, 32); cw = rng.integers(0, 4096, 32)
+    assert_bitwise(host(dH)[rx, cx], orc.gemm_backward_at("dx", want_g, h, W, rx, cx), "dH samples")
+    assert_bitwise(host(dW)[rw, cw], orc.gemm_backward_at("dw", want_g, h, W, rw, cw), "dW samples")
