@@ -469,15 +469,13 @@ hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
 // Workgroup: 4 wavefronts = WN along the weight rows x WK = 4 / WN along K: with WK > 1 the
 // wavefronts of a round take consecutive slices (round r, wavefront wk: slice r * WK + wk)
 // and their slice partials meet in LDS, where one wavefront folds them in ascending slice
-// order into the running total -- the same fold as everywhere else.  Each slice walks four
-// 64-wide chunks staged through LDS (double buffered): the weight tile as BF16 in the order
-// lane group g reads it (k = 4 s + g for s = 0..15: 32 contiguous bytes), the activation
-// tile as FP32 in the same order (64 contiguous bytes).
-constexpr int GV_CH = 64;                 // k per chunk (a quarter slice)
-constexpr int GV_WSEG = 144;              // bytes per (weight row, slice) chunk segment (128 + pad)
-constexpr int GV_XSEG = 68;               // floats per (activation row, slice) chunk segment (64 + pad)
-
-template <int WN, int PD, int ROLE>
+// order into the running total -- the same fold as everywhere else.  Each slice walks
+// CH-wide chunks staged through LDS (double buffered): the weight tile as BF16 in the order
+// lane group g reads it (k = 4 s + g for s = 0..CH/4-1: CH/2 contiguous bytes), the
+// activation tile as FP32 in the same order.  Measured: CH = 64 is best at N >= 12288
+// (128-wide chunks halve the workgroups a CU holds); CH = 128 gains 7% on N = 4096,
+// K = 14336.
+template <int WN, int PD, int CH, int ROLE>
 __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
@@ -486,34 +484,38 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     typedef float f32x4 __attribute__((ext_vector_type(4)));
     constexpr int WK = 4 / WN;
     constexpr int BN = 16 * WN;
-    constexpr int XU = WK;                 // activation float4 per thread and chunk
-    __shared__ __attribute__((aligned(16))) unsigned char Wl[2][BN * WK * GV_WSEG];
-    __shared__ __attribute__((aligned(16))) float Xl[2][16 * WK * GV_XSEG];
+    constexpr int NSTEP = CH / 4;                // matrix steps per chunk
+    constexpr int WSEG = CH * 2 + 16;            // bytes per (weight row, slice) segment (+ pad)
+    constexpr int XSEG = CH + 4;                 // floats per (activation row, slice) segment (+ pad)
+    constexpr int WUN = BN * WK * CH / 8 / 256;  // 16-byte weight loads per thread and chunk
+    constexpr int XU = 16 * WK * CH / 4 / 256;   // activation float4 per thread and chunk
+    __shared__ __attribute__((aligned(16))) unsigned char Wl[2][BN * WK * WSEG];
+    __shared__ __attribute__((aligned(16))) float Xl[2][16 * WK * XSEG];
     __shared__ __attribute__((aligned(16))) float part[WK > 1 ? WK * WN * 64 * 4 : 4];
     if (Mdev) M = min(M, *Mdev);
     if (M <= 0) return;
     const int n0 = blockIdx.x * BN;
     const int S = (K + KS - 1) / KS;
     const int nrounds = (S + WK - 1) / WK;
-    const int nit = nrounds * (KS / GV_CH);
+    const int nit = nrounds * (KS / CH);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 4, r = lane & 15;
     const int wn = wv % WN, wk = wv / WN;
 
     // PD chunks in flight in registers
-    uint4 wr[PD][2];
+    uint4 wr[PD][WUN];
     float4 xr[PD][XU];
-    // global -> registers for chunk `it` (round it / 4, chunk it % 4 of each of its slices);
-    // units past N, K or M are zeros and are not read
-    auto load = [&](int it, uint4 (&wq)[2], float4 (&xq)[XU]) {
-        const int rd = it / (KS / GV_CH), c = it % (KS / GV_CH);
+    // global -> registers for chunk `it` (round it / (KS / CH), chunk it % (KS / CH) of each
+    // of its slices); units past N, K or M are zeros and are not read
+    auto load = [&](int it, uint4 (&wq)[WUN], float4 (&xq)[XU]) {
+        const int rd = it / (KS / CH), c = it % (KS / CH);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < WUN; ++i) {
             const int q = tid + 256 * i;
-            const int c8 = q & 7, rest = q >> 3;
+            const int c8 = q % (CH / 8), rest = q / (CH / 8);
             const int sk = rest % WK, rr = rest / WK;
             const int sl = rd * WK + sk;
-            const int k = sl * KS + c * GV_CH + 8 * c8;
+            const int k = sl * KS + c * CH + 8 * c8;
             wq[i] = make_uint4(0u, 0u, 0u, 0u);
             if ((sl < S) && (k < K) && (n0 + rr < N))
                 wq[i] = *reinterpret_cast<const uint4*>(W + (int64_t)(n0 + rr) * ldw + k);
@@ -521,10 +523,10 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
 #pragma unroll
         for (int j = 0; j < XU; ++j) {
             const int u = tid + 256 * j;
-            const int q4 = u & 15, rest = u >> 4;
+            const int q4 = u % (CH / 4), rest = u / (CH / 4);
             const int sk = rest % WK, m = rest / WK;
             const int sl = rd * WK + sk;
-            const int k = sl * KS + c * GV_CH + 4 * q4;
+            const int k = sl * KS + c * CH + 4 * q4;
             xq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             if ((sl < S) && (k < K) && (m < M))
                 xq[j] = *reinterpret_cast<const float4*>(X + (int64_t)m * ldx + k);
@@ -533,59 +535,66 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     // registers -> LDS in the read order: element k = 8 c8 + e of a weight chunk goes to
     // lane group g = e % 4, step s = 2 c8 + e / 4; element k = 4 q4 + e of an activation chunk
     // to g = e, s = q4
-    auto store = [&](int buf, const uint4 (&wq)[2], const float4 (&xq)[XU]) {
+    auto store = [&](int buf, const uint4 (&wq)[WUN], const float4 (&xq)[XU]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < WUN; ++i) {
             const int q = tid + 256 * i;
-            const int c8 = q & 7, rest = q >> 3;
-            unsigned char* seg = &Wl[buf][rest * GV_WSEG + c8 * 4];
+            const int c8 = q % (CH / 8), rest = q / (CH / 8);
+            unsigned char* seg = &Wl[buf][rest * WSEG + c8 * 4];
             const uint4 v = wq[i];
-            *reinterpret_cast<uint32_t*>(seg + 0 * 32) = (v.x & 0xffffu) | (v.z << 16);
-            *reinterpret_cast<uint32_t*>(seg + 1 * 32) = (v.x >> 16) | (v.z & 0xffff0000u);
-            *reinterpret_cast<uint32_t*>(seg + 2 * 32) = (v.y & 0xffffu) | (v.w << 16);
-            *reinterpret_cast<uint32_t*>(seg + 3 * 32) = (v.y >> 16) | (v.w & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(seg + 0 * (CH / 2)) = (v.x & 0xffffu) | (v.z << 16);
+            *reinterpret_cast<uint32_t*>(seg + 1 * (CH / 2)) = (v.x >> 16) | (v.z & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(seg + 2 * (CH / 2)) = (v.y & 0xffffu) | (v.w << 16);
+            *reinterpret_cast<uint32_t*>(seg + 3 * (CH / 2)) = (v.y >> 16) | (v.w & 0xffff0000u);
         }
 #pragma unroll
         for (int j = 0; j < XU; ++j) {
             const int u = tid + 256 * j;
-            const int q4 = u & 15, rest = u >> 4;
-            float* seg = &Xl[buf][rest * GV_XSEG + q4];
-            seg[0] = xq[j].x;
-            seg[16] = xq[j].y;
-            seg[32] = xq[j].z;
-            seg[48] = xq[j].w;
+            const int q4 = u % (CH / 4), rest = u / (CH / 4);
+            float* seg = &Xl[buf][rest * XSEG + q4];
+            seg[0 * NSTEP] = xq[j].x;
+            seg[1 * NSTEP] = xq[j].y;
+            seg[2 * NSTEP] = xq[j].z;
+            seg[3 * NSTEP] = xq[j].w;
         }
     };
 
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, T = f32x4{0.f, 0.f, 0.f, 0.f};
-    const unsigned char* wseg0 = &Wl[0][((wn * 16 + r) * WK + wk) * GV_WSEG + g * 32];
-    const float* xseg0 = &Xl[0][(r * WK + wk) * GV_XSEG + g * 16];
+    const unsigned char* wseg0 = &Wl[0][((wn * 16 + r) * WK + wk) * WSEG + g * (CH / 2)];
+    const float* xseg0 = &Xl[0][(r * WK + wk) * XSEG + g * NSTEP];
     auto compute = [&](int it) {
         const int buf = it & 1;
-        const int rd = it / (KS / GV_CH), c = it % (KS / GV_CH);
+        const int rd = it / (KS / CH), c = it % (KS / CH);
         const int sl = rd * WK + wk;
-        const int kvalid = sl < S ? min(GV_CH, K - (sl * KS + c * GV_CH)) : 0;
-        const uint4* wp = reinterpret_cast<const uint4*>(wseg0 + buf * (BN * WK * GV_WSEG));
-        const float4* xp = reinterpret_cast<const float4*>(xseg0 + buf * (16 * WK * GV_XSEG));
-        const uint4 w0 = wp[0], w1 = wp[1];
-        const float4 x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
-        const uint32_t wv8[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        const float a[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                             x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-        if (kvalid == GV_CH) {
+        const int kvalid = sl < S ? min(CH, K - (sl * KS + c * CH)) : 0;
+        const uint4* wp = reinterpret_cast<const uint4*>(wseg0 + buf * (BN * WK * WSEG));
+        const float4* xp = reinterpret_cast<const float4*>(xseg0 + buf * (16 * WK * XSEG));
+        uint32_t wv8[NSTEP / 2];
+        float a[NSTEP];
 #pragma unroll
-            for (int st = 0; st < 16; ++st) {
+        for (int q = 0; q < NSTEP / 8; ++q) {
+            const uint4 w = wp[q];
+            wv8[4 * q] = w.x; wv8[4 * q + 1] = w.y; wv8[4 * q + 2] = w.z; wv8[4 * q + 3] = w.w;
+        }
+#pragma unroll
+        for (int q = 0; q < NSTEP / 4; ++q) {
+            const float4 x = xp[q];
+            a[4 * q] = x.x; a[4 * q + 1] = x.y; a[4 * q + 2] = x.z; a[4 * q + 3] = x.w;
+        }
+        if (kvalid == CH) {
+#pragma unroll
+            for (int st = 0; st < NSTEP; ++st) {
                 const float b = (st & 1) ? bf16_hi(wv8[st >> 1]) : bf16_lo(wv8[st >> 1]);
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b, acc, 0, 0, 0);
             }
         } else {
 #pragma unroll
-            for (int st = 0; st < 16; ++st) {
+            for (int st = 0; st < NSTEP; ++st) {
                 const float b = (st & 1) ? bf16_hi(wv8[st >> 1]) : bf16_lo(wv8[st >> 1]);
                 if (4 * st < kvalid) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b, acc, 0, 0, 0);
             }
         }
-        if (c == KS / GV_CH - 1) {
+        if (c == KS / CH - 1) {
             // end of a round: every wavefront holds the slice sum of slice rd * WK + wk
             if constexpr (WK == 1) {
                 if (sl < S) {
@@ -664,10 +673,10 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     }
 }
 
-template <int WN, int PD, int ROLE>
+template <int WN, int PD, int CH, int ROLE>
 hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st) {
     dim3 grid((a.N + 16 * WN - 1) / (16 * WN));
-    hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, ROLE>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, CH, ROLE>), grid, dim3(256), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
 }
@@ -899,8 +908,9 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
     // wavefronts along the rows, two along K); fewer: 16 per workgroup with the slices split
     // over four wavefronts, so the grid still covers the chip.
     if (a.M >= 5 && a.M <= 16) {
-        if (a.N >= 12288) return launch_gemv16<2, 2, ROLE>(a, st);
-        return launch_gemv16<1, 2, ROLE>(a, st);
+        if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE>(a, st);
+        if (a.K >= 8192) return launch_gemv16<1, 2, 128, ROLE>(a, st);   // long K: half slices
+        return launch_gemv16<1, 2, 64, ROLE>(a, st);
     }
     if (a.M <= 4 && a.K <= gemm_skinny_max_k()) {
         if (a.M <= 1) return launch_skinny<1, ROLE>(a, st);
