@@ -472,9 +472,8 @@ hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
 // order into the running total -- the same fold as everywhere else.  Each slice walks
 // CH-wide chunks staged through LDS (double buffered): the weight tile as BF16 in the order
 // lane group g reads it (k = 4 s + g for s = 0..CH/4-1: CH/2 contiguous bytes), the
-// activation tile as FP32 in the same order.  Measured: CH = 64 is best at N >= 12288
-// (128-wide chunks halve the workgroups a CU holds); CH = 128 gains 7% on N = 4096,
-// K = 14336.
+// activation tile as FP32 in the same order.  Measured: 64-wide chunks are best or equal on
+// every decoder shape (128-wide ones halve the workgroups a CU holds at N >= 12288).
 template <int WN, int PD, int CH, int ROLE>
 __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
@@ -506,7 +505,12 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     uint4 wr[PD][WUN];
     float4 xr[PD][XU];
     // global -> registers for chunk `it` (round it / (KS / CH), chunk it % (KS / CH) of each
-    // of its slices); units past N, K or M are zeros and are not read
+    // of its slices).  Every load is issued, unconditionally, from an address clamped into the
+    // operand, so the compiler waits for the oldest chunk only (a load under a branch makes it
+    // wait for every load in flight).  Units past N, K or M then hold other elements of the
+    // operand; none of them reaches a stored output: a weight row past N feeds only its own
+    // (unstored) column, an activation row past M only its own (unstored) row, and k past K
+    // only matrix steps that are never issued.
     auto load = [&](int it, uint4 (&wq)[WUN], float4 (&xq)[XU]) {
         const int rd = it / (KS / CH), c = it % (KS / CH);
 #pragma unroll
@@ -514,22 +518,16 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
             const int q = tid + 256 * i;
             const int c8 = q % (CH / 8), rest = q / (CH / 8);
             const int sk = rest % WK, rr = rest / WK;
-            const int sl = rd * WK + sk;
-            const int k = sl * KS + c * CH + 8 * c8;
-            wq[i] = make_uint4(0u, 0u, 0u, 0u);
-            if ((sl < S) && (k < K) && (n0 + rr < N))
-                wq[i] = *reinterpret_cast<const uint4*>(W + (int64_t)(n0 + rr) * ldw + k);
+            const int k = (rd * WK + sk) * KS + c * CH + 8 * c8;
+            wq[i] = *reinterpret_cast<const uint4*>(W + (int64_t)min(n0 + rr, N - 1) * ldw + min(k, K - 8));
         }
 #pragma unroll
         for (int j = 0; j < XU; ++j) {
             const int u = tid + 256 * j;
             const int q4 = u % (CH / 4), rest = u / (CH / 4);
             const int sk = rest % WK, m = rest / WK;
-            const int sl = rd * WK + sk;
-            const int k = sl * KS + c * CH + 4 * q4;
-            xq[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if ((sl < S) && (k < K) && (m < M))
-                xq[j] = *reinterpret_cast<const float4*>(X + (int64_t)m * ldx + k);
+            const int k = (rd * WK + sk) * KS + c * CH + 4 * q4;
+            xq[j] = *reinterpret_cast<const float4*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
         }
     };
     // registers -> LDS in the read order: element k = 8 c8 + e of a weight chunk goes to
@@ -540,7 +538,9 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         for (int i = 0; i < WUN; ++i) {
             const int q = tid + 256 * i;
             const int c8 = q % (CH / 8), rest = q / (CH / 8);
-            unsigned char* seg = &Wl[buf][rest * WSEG + c8 * 4];
+            // segments slice-major (sk, row): the 16 rows a lane group reads are WSEG apart,
+            // which spreads a 16-lane quarter's 16-byte reads over all 64 banks
+            unsigned char* seg = &Wl[buf][((rest % WK) * BN + rest / WK) * WSEG + c8 * 4];
             const uint4 v = wq[i];
             *reinterpret_cast<uint32_t*>(seg + 0 * (CH / 2)) = (v.x & 0xffffu) | (v.z << 16);
             *reinterpret_cast<uint32_t*>(seg + 1 * (CH / 2)) = (v.x >> 16) | (v.z & 0xffff0000u);
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         for (int j = 0; j < XU; ++j) {
             const int u = tid + 256 * j;
             const int q4 = u % (CH / 4), rest = u / (CH / 4);
-            float* seg = &Xl[buf][rest * XSEG + q4];
+            float* seg = &Xl[buf][((rest % WK) * 16 + rest / WK) * XSEG + q4];
             seg[0 * NSTEP] = xq[j].x;
             seg[1 * NSTEP] = xq[j].y;
             seg[2 * NSTEP] = xq[j].z;
@@ -560,8 +560,8 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     };
 
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, T = f32x4{0.f, 0.f, 0.f, 0.f};
-    const unsigned char* wseg0 = &Wl[0][((wn * 16 + r) * WK + wk) * WSEG + g * (CH / 2)];
-    const float* xseg0 = &Xl[0][(r * WK + wk) * XSEG + g * NSTEP];
+    const unsigned char* wseg0 = &Wl[0][(wk * BN + wn * 16 + r) * WSEG + g * (CH / 2)];
+    const float* xseg0 = &Xl[0][(wk * 16 + r) * XSEG + g * NSTEP];
     auto compute = [&](int it) {
         const int buf = it & 1;
         const int rd = it / (KS / CH), c = it % (KS / CH);
@@ -904,12 +904,12 @@ template <int ROLE>
 hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
     // M is an upper bound when Mdev is set (rows beyond *Mdev are skipped on the device).
     // 5 <= M <= 16: the matrix-core GEMV (the VALU GEMV's per-row accumulators and LDS reads
-    // make it slower from 5 rows on).  At least 12288 weight rows: 32 per workgroup (two
-    // wavefronts along the rows, two along K); fewer: 16 per workgroup with the slices split
-    // over four wavefronts, so the grid still covers the chip.
+    // make it slower from 5 rows on).  Weight rows per workgroup: 64 from 65536 rows (four
+    // wavefronts along the rows), 32 from 12288 (two along the rows, two along K), else 16
+    // with the slices split over four wavefronts, so the grid still covers the chip.
     if (a.M >= 5 && a.M <= 16) {
+        if (a.N >= 65536) return launch_gemv16<4, 2, 64, ROLE>(a, st);
         if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE>(a, st);
-        if (a.K >= 8192) return launch_gemv16<1, 2, 128, ROLE>(a, st);   // long K: half slices
         return launch_gemv16<1, 2, 64, ROLE>(a, st);
     }
     if (a.M <= 4 && a.K <= gemm_skinny_max_k()) {
