@@ -111,3 +111,38 @@ def test_c5_32k_prefill_equals_decode_tail(c5, dec):
         r = dec.decode_step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
         for k in KEYS:
             assert_bitwise(host(r[k]), full[k][t:t + 1], "position %d %s" % (t, k))
+
+
+def test_c5_decode_batch_sizes_to_64(c5):
+    """Decode at a 32k context for batch 64 (rows at different positions, synthetic seeded
+    KV caches) against batch 1, 2, 4, 8, 16 and 32 on the leading rows, and row 63 moved to
+    the front of a batch of one: every output bitwise equal."""
+    import torch
+    from invariant_numerics_amd.decoder import Decoder
+    model, toks = c5
+    say("c5 decode batch 64: caches")
+    B = 64
+    d = Decoder(model, batch=B, tmax=TMAX)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    for k in d.kc + d.vc:
+        k.normal_(generator=g)
+    tok = i32((toks[:, TMAX - 1][np.arange(B) % 3] + np.arange(B, dtype=np.int32)) % synth.C5["vocab"])
+    tgt = i32(toks[:, TMAX - 2][np.arange(B) % 3])
+    pos = torch.tensor([TMAX - 1 - 37 * b for b in range(B)], dtype=torch.int32, device="cuda")
+    say("c5 decode batch 64: step")
+    full = {k: host(v) for k, v in d.decode_step(tok, pos, tgt).items()}
+    for b in (1, 2, 4, 8, 16, 32):
+        say("c5 decode batch", b)
+        r = d.decode_step(tok[:b].contiguous(), pos[:b].contiguous(), tgt[:b].contiguous())
+        for k in KEYS:
+            assert_bitwise(host(r[k]), full[k][:b], "batch %d %s" % (b, k))
+    say("c5 decode row 63 at the front")
+    for kc, vc in zip(d.kc, d.vc):
+        kc[0].copy_(kc[63])
+        vc[0].copy_(vc[63])
+    r = d.decode_step(tok[63:64].contiguous(), pos[63:64].contiguous(), tgt[63:64].contiguous())
+    for k in KEYS:
+        assert_bitwise(host(r[k]), full[k][63:64], "row 63 alone %s" % k)
+    del d
+    torch.cuda.empty_cache()
