@@ -1,4 +1,5 @@
-"""Throughput of the four smaller configurations on one GPU (the C5 decoder is bench.py).
+"""Throughput of the four smaller configurations on one GPU, and decode of the C5 decoder at
+batch 1 to 64 (its prefill scoring is bench.py).
 
 Seeded synthetic inputs from ``synth`` (the same arrays the parity tests use); every timing
 is the median of HIP-event-bracketed repetitions on the current stream, inputs resident in
@@ -10,7 +11,9 @@ HBM.  Prints one JSON object per measurement:
     and 4096 x 14336 weights, rotating over weight copies larger than the 256 MB last-level
     cache so every call reads its weights from HBM;
   * C4: LM head, hidden 4096, vocab 128256, B = 1 .. 256 (bytes count a second weight read
-    when any row is recomputed and B > 16; up to 16 rows the FP32 logits share the sweep).
+    when any row is recomputed and B > 16; up to 16 rows the FP32 logits share the sweep);
+  * C5 decode: graph-replayed decode steps of the 4-layer decoder at a 32k context for
+    B = 1, 4, 16, 64 (seeded random KV caches; bytes = weights + the KV read once).
 Usage: python bench_configs.py
 """
 import json, os, sys
@@ -83,4 +86,30 @@ for B in (1, 2, 4, 8, 16, 32, 64, 128, 256):
     out(config="C4", batch=B, recomputed=nrec, us=round(t * 1e6, 1), tokens_per_s=round(B / t, 1),
         hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3),
         tflops=round(2 * 128256 * 4096 * (B + nrec) / t / 1e12, 2))
+# ---- C5: decode steps of the 4-layer decoder at a 32k context, batch 1 .. 64 (graph replay;
+# KV caches filled with seeded random values, every row at its own position near 32k)
+from invariant_numerics_amd.decoder import Decoder
+cfg = dict(synth.C5)
+T5 = 32768
+model = synth.decoder_model(cfg, T5)
+dec5 = Decoder(model, device=dev, batch=64, tmax=T5)
+g5 = torch.Generator(device=dev); g5.manual_seed(5005)
+for k in dec5.kc + dec5.vc:
+    k.normal_(generator=g5)
+H5, F5, V5, L5 = cfg["hidden"], cfg["ffn"], cfg["vocab"], cfg["layers"]
+QKV5 = (cfg["hq"] + 2 * cfg["hkv"]) * cfg["d"]
+body_w = L5 * 2 * (QKV5 * H5 + H5 * cfg["hq"] * cfg["d"] + 2 * F5 * H5 + H5 * F5)
+head_w = 2 * V5 * H5
+for B in (1, 4, 16, 64):
+    step = dec5.decode_graph(B)
+    tok = torch.randint(0, V5, (B,), dtype=torch.int32, device=dev, generator=g5)
+    tgt = torch.randint(0, V5, (B,), dtype=torch.int32, device=dev, generator=g5)
+    pos = torch.tensor([T5 - 17 - 5 * b for b in range(B)], dtype=torch.int32, device=dev)
+    r = step(tok, pos, tgt)
+    nrec = int(r["recomputed"].sum().item())
+    t = timeit(lambda: step(tok, pos, tgt), reps=10)
+    kv = L5 * 2 * cfg["hkv"] * cfg["d"] * 4 * int((pos + 1).sum().item())
+    by = body_w + head_w * (2 if (nrec and B > 16) else 1) + kv
+    out(config="C5", op="decode", context=T5, batch=B, recomputed=nrec, ms_per_step=round(t * 1e3, 3),
+        tokens_per_s=round(B / t, 1), hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3))
 print("done", flush=True)
