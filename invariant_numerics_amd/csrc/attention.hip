@@ -211,6 +211,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
             if (FAST || sb < nsb) {
                 if (sb + 1 < nsb) st.load(Kc, kvbase, kbase + (sb + 1) * SB, kend, tid);
                 else st.load(Vc, kvbase, kbase, kend, tid);
+                // keep the loads here, ahead of this sub-block's matrix-core work: left to itself
+                // the scheduler sinks them next to their LDS stores, where their whole latency
+                // is waited out
+                __builtin_amdgcn_sched_barrier(0);
                 const float* kvb = KV[buf];
                 if (FAST || kbase + sb * SB <= i0 + 15) {
 #pragma unroll
@@ -291,6 +295,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
                 // last chunk every row is out of range: the stage clamps and stores zeros)
                 if (more) st.load(Vc, kvbase, kb + SB, kend, tid);
                 else st.load(Kc, kvbase, kbase + CHUNK, nkend, tid);
+                __builtin_amdgcn_sched_barrier(0);     // as in the scores
                 const float* kvb = KV[buf];
                 const float* vop = kvb + g * KLD + 8 * r;       // + 4 s KLD at step s
                 const int nmk = min(SB, jv - kb);               // keys of this sub-block on MFMA
