@@ -701,6 +701,9 @@ constexpr int PH = 64;        // elements per slice per phase
 constexpr int WSEG = PH * 2 + 16;   // padded bytes per (row, slice) segment in LDS
 constexpr int XLD = PH + 4;         // padded floats per (m, slice) activation segment
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 template <int MB, int ROLE, int ROWS>
 __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
@@ -721,11 +724,16 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const int n0 = blockIdx.x * ROWS;
 
     // load duty: 8 x 16 bytes of weights and MB * XU x 16 bytes of activations per thread and
-    // phase; DEPTH phases are in flight in registers (two when the activation tile is small)
+    // phase; DEPTH phases are in flight in registers (two when the activation tile is small).
+    // The loads read clamped, in-range addresses with no zero fill: what lands past N, M or K
+    // reaches no stored output (the chains stop at K, rows past N or M are not written), and
+    // with no load under a branch each LDS store waits only as long as it must.  The buffers
+    // are native vectors (copies of the struct types were kept in scratch memory), and a
+    // scheduling barrier keeps the loads ahead of the phase's compute.
     constexpr int DEPTH = MB * XU <= 4 ? 2 : 1;
-    uint4 wpre[DEPTH][8];
-    float4 xpre[DEPTH][MB * XU];
-    auto load = [&](int stg, uint4 (&wp)[8], float4 (&xp)[MB * XU]) {
+    u32x4v wpre[DEPTH][8];
+    f32x4v xpre[DEPTH][MB * XU];
+    auto load = [&](int stg, u32x4v (&wp)[8], f32x4v (&xp)[MB * XU]) {
         const int sg = (stg / (KS / PH)) * SK_LANES;
         const int p = stg % (KS / PH);
 #pragma unroll
@@ -734,9 +742,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
             const int seg = q >> 3, c8 = q & 7;   // segment (row, slice) and chunk in it
             const int rn = seg >> 4, ss = seg & 15;
             const int k = (sg + ss) * KS + p * PH + 8 * c8;
-            const bool in = (n0 + rn < N) && (k < K);
-            const uint4 t = *reinterpret_cast<const uint4*>(W + (int64_t)min(n0 + rn, N - 1) * ldw + min(k, K - 8));
-            wp[i] = in ? t : make_uint4(0u, 0u, 0u, 0u);
+            wp[i] = *reinterpret_cast<const u32x4v*>(W + (int64_t)min(n0 + rn, N - 1) * ldw + min(k, K - 8));
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
@@ -745,25 +751,23 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
                 const int u = tid + NT * j;
                 const int ss = u >> 4, c4 = u & 15;          // 16 slices x 16 float4
                 const int k = (sg + ss) * KS + p * PH + 4 * c4;
-                const bool in = (m < M) && (k < K);
-                const float4 t = *reinterpret_cast<const float4*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
-                xp[m * XU + j] = in ? t : make_float4(0.f, 0.f, 0.f, 0.f);
+                xp[m * XU + j] = *reinterpret_cast<const f32x4v*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
             }
         }
     };
-    auto store = [&](const uint4 (&wp)[8], const float4 (&xp)[MB * XU]) {
+    auto store = [&](const u32x4v (&wp)[8], const f32x4v (&xp)[MB * XU]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int q = tid + NT * i;
             const int seg = q >> 3, c8 = q & 7;
-            *reinterpret_cast<uint4*>(&Wl[seg * WSEG + c8 * 16]) = wp[i];
+            *reinterpret_cast<u32x4v*>(&Wl[seg * WSEG + c8 * 16]) = wp[i];
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
 #pragma unroll
             for (int j = 0; j < XU; ++j) {
                 const int u = tid + NT * j;
-                *reinterpret_cast<float4*>(&Xl[m][u >> 4][(u & 15) * 4]) = xp[m * XU + j];
+                *reinterpret_cast<f32x4v*>(&Xl[m][u >> 4][(u & 15) * 4]) = xp[m * XU + j];
             }
         }
     };
@@ -842,6 +846,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
                 store(wpre[d], xpre[d]);
                 __syncthreads();
                 if (st + d + DEPTH < nstages) load(st + d + DEPTH, wpre[d], xpre[d]);
+                __builtin_amdgcn_sched_barrier(0);
                 compute(st + d);
             }
         }
