@@ -16,7 +16,8 @@ def inv():
 
 
 @pytest.mark.parametrize("M,K,N", [
-    (1, 8, 5), (1, 264, 70), (2, 4096, 130), (3, 520, 257), (5, 1000, 64), (16, 4096, 33),
+    (1, 8, 5), (1, 264, 70), (2, 4096, 130), (3, 520, 257), (4, 8200, 33), (4, 72, 17), (2, 16, 1),
+    (5, 1000, 64), (16, 4096, 33),
     (8, 8, 5), (8, 1000, 12300), (11, 520, 257), (16, 264, 12289), (13, 4104, 70), (9, 8200, 70),
     (17, 264, 129), (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
 ])
