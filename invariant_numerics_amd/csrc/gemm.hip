@@ -22,6 +22,8 @@ namespace {
 constexpr int BK = 32;  // K tile; divides KS, so slice ends fall on tile ends
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // Position of k (0..31) inside a tile row of LDS: the lane half h of an MFMA reads
 // k = h, h+2, ..., h+30 (one per 2-wide MFMA step) as 16 contiguous floats.
@@ -102,50 +104,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
 
     // Per-thread source rows (clamped into range, with validity flags) computed once; each
     // tile advances the pointers by BK.  Elements outside M x K or N x K load as zeros.
-    float4 xr[XV];
-    uint4 wr[WV];
+    // Loads read clamped, in-range addresses with no zero fill: rows past M or N reach only
+    // outputs that are never stored, and columns past K only the k-steps a partial last tile
+    // skips.  One branch-free path, into native vector registers, so nothing waits on a
+    // load before the LDS store that needs it.
+    f32x4v xr[XV];
+    u32x4v wr[WV];
     const float* xp[XV];
     const uint16_t* wp[WV];
-    bool xin[XV], win[WV];
+    int xlim[XV], wlim[WV];
 #pragma unroll
     for (int i = 0; i < XV; ++i) {
         const int idx = tid + i * NT;
         const int row = idx / (BK / 4), q = idx % (BK / 4);
-        xin[i] = m0 + row < M;
         xp[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + 4 * q;
+        xlim[i] = K - 4 - 4 * q;
     }
 #pragma unroll
     for (int i = 0; i < WV; ++i) {
         const int idx = tid + i * NT;
         const int row = idx / (BK / 8), o = idx % (BK / 8);
-        win[i] = n0 + row < N;
         wp[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + 8 * o;
+        wlim[i] = K - 8 - 8 * o;
     }
     const bool interior = (m0 + BM <= M) && (n0 + BN <= N);
     auto load_tile = [&](int k0) {
-        if (interior && k0 + BK <= K) {
 #pragma unroll
-            for (int i = 0; i < XV; ++i) xr[i] = *reinterpret_cast<const float4*>(xp[i] + k0);
+        for (int i = 0; i < XV; ++i) xr[i] = *reinterpret_cast<const f32x4v*>(xp[i] + min(k0, xlim[i]));
 #pragma unroll
-            for (int i = 0; i < WV; ++i) wr[i] = *reinterpret_cast<const uint4*>(wp[i] + k0);
-            return;
-        }
-#pragma unroll
-        for (int i = 0; i < XV; ++i) {
-            const int q = (tid + i * NT) % (BK / 4);
-            const int gk = k0 + 4 * q;
-            const bool in = xin[i] && gk < K;
-            const float4 t = *reinterpret_cast<const float4*>(xp[i] + min(k0, K - 4 - 4 * q));
-            xr[i] = in ? t : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int i = 0; i < WV; ++i) {
-            const int o = (tid + i * NT) % (BK / 8);
-            const int gk = k0 + 8 * o;
-            const bool in = win[i] && gk < K;
-            const uint4 t = *reinterpret_cast<const uint4*>(wp[i] + min(k0, K - 8 - 8 * o));
-            wr[i] = in ? t : make_uint4(0u, 0u, 0u, 0u);
-        }
+        for (int i = 0; i < WV; ++i) wr[i] = *reinterpret_cast<const u32x4v*>(wp[i] + min(k0, wlim[i]));
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -215,6 +202,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
     };
     load_tile(0);
     store_tile(0);
+    load_tile(BK);
     __syncthreads();
     // slice by slice (KS / BK tiles each), so the fold T = T + acc runs once per slice; the
     // loop body sees full tiles only (a partial tile can only be the very last one)
@@ -223,13 +211,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
         const int tend = min(ntf, t + KS / BK);
         for (; t < tend; ++t) {
             const int buf = t & 1;
-            if (t + 1 < nt) load_tile((t + 1) * BK);
             read_frags(buf);
-            // the next tile goes to the other LDS buffer halfway through the k-steps: its loads
-            // have had half the tile's matrix work to arrive, and its stores overlap the rest
-            // instead of waiting at the barrier
+            // halfway through the k-steps the next tile (in registers since the middle of the
+            // previous tile) goes to the other LDS buffer, and the loads of the tile after it
+            // are issued at once into the freed registers: each tile's loads have a whole
+            // tile of matrix work to arrive, and the stores overlap the second half
             steps(0, NS / 2);
             if (t + 1 < nt) store_tile(buf ^ 1);
+            load_tile((t + 2) * BK);
             steps(NS / 2, NS);
             __syncthreads();
         }
@@ -700,9 +689,6 @@ constexpr int SK_LANES = 16;  // slices per group
 constexpr int PH = 64;        // elements per slice per phase
 constexpr int WSEG = PH * 2 + 16;   // padded bytes per (row, slice) segment in LDS
 constexpr int XLD = PH + 4;         // padded floats per (m, slice) activation segment
-
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 template <int MB, int ROLE, int ROWS>
 __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
