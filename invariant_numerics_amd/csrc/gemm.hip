@@ -451,10 +451,11 @@ hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ gemv16 --
-// 5 <= M <= 16 (one 16-row MFMA tile; rows past M are zero operands, never stored).  Matrix
+// 5 <= M <= 16 MT: MT tiles of 16 activation rows (rows past M are never stored).  Matrix
 // cores (v_mfma_f32_16x16x4_f32, four in-order fused multiply-adds per step) with the
 // activation rows as the A operand and 16 weight rows per wavefront as B, so every weight
-// element is read from LDS once per use and the activation chunk once per wavefront.
+// element is read from LDS once per use (and serves all MT row tiles) and the activation
+// chunk once per wavefront.
 // Workgroup: 4 wavefronts = WN along the weight rows x WK = 4 / WN along K: with WK > 1 the
 // wavefronts of a round take consecutive slices (round r, wavefront wk: slice r * WK + wk)
 // and their slice partials meet in LDS, where one wavefront folds them in ascending slice
@@ -463,7 +464,7 @@ hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
 // lane group g reads it (k = 4 s + g for s = 0..CH/4-1: CH/2 contiguous bytes), the
 // activation tile as FP32 in the same order.  Measured: 64-wide chunks are best or equal on
 // every decoder shape (128-wide ones halve the workgroups a CU holds at N >= 12288).
-template <int WN, int PD, int CH, int ROLE>
+template <int WN, int PD, int CH, int ROLE, int MT>
 __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
@@ -476,10 +477,11 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     constexpr int WSEG = CH * 2 + 16;            // bytes per (weight row, slice) segment (+ pad)
     constexpr int XSEG = CH + 4;                 // floats per (activation row, slice) segment (+ pad)
     constexpr int WUN = BN * WK * CH / 8 / 256;  // 16-byte weight loads per thread and chunk
-    constexpr int XU = 16 * WK * CH / 4 / 256;   // activation float4 per thread and chunk
+    constexpr int MR = 16 * MT;                  // activation rows (MT row tiles of 16)
+    constexpr int XU = MR * WK * CH / 4 / 256;   // activation float4 per thread and chunk
     __shared__ __attribute__((aligned(16))) unsigned char Wl[2][BN * WK * WSEG];
-    __shared__ __attribute__((aligned(16))) float Xl[2][16 * WK * XSEG];
-    __shared__ __attribute__((aligned(16))) float part[WK > 1 ? WK * WN * 64 * 4 : 4];
+    __shared__ __attribute__((aligned(16))) float Xl[2][MR * WK * XSEG];
+    __shared__ __attribute__((aligned(16))) float part[WK > 1 ? WK * WN * MT * 64 * 4 : 4];
     if (Mdev) M = min(M, *Mdev);
     if (M <= 0) return;
     const int n0 = blockIdx.x * BN;
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         for (int j = 0; j < XU; ++j) {
             const int u = tid + 256 * j;
             const int q4 = u % (CH / 4), rest = u / (CH / 4);
-            float* seg = &Xl[buf][((rest % WK) * 16 + rest / WK) * XSEG + q4];
+            float* seg = &Xl[buf][((rest % WK) * MR + rest / WK) * XSEG + q4];
             seg[0 * NSTEP] = xq[j].x;
             seg[1 * NSTEP] = xq[j].y;
             seg[2 * NSTEP] = xq[j].z;
@@ -548,70 +550,91 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         }
     };
 
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, T = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[MT], T[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) { acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f}; T[mt] = acc[mt]; }
     const unsigned char* wseg0 = &Wl[0][(wk * BN + wn * 16 + r) * WSEG + g * (CH / 2)];
-    const float* xseg0 = &Xl[0][(wk * 16 + r) * XSEG + g * NSTEP];
+    const float* xseg0 = &Xl[0][(wk * MR + r) * XSEG + g * NSTEP];
     auto compute = [&](int it) {
         const int buf = it & 1;
         const int rd = it / (KS / CH), c = it % (KS / CH);
         const int sl = rd * WK + wk;
         const int kvalid = sl < S ? min(CH, K - (sl * KS + c * CH)) : 0;
         const uint4* wp = reinterpret_cast<const uint4*>(wseg0 + buf * (BN * WK * WSEG));
-        const float4* xp = reinterpret_cast<const float4*>(xseg0 + buf * (16 * WK * XSEG));
+        const float* xb = xseg0 + buf * (MR * WK * XSEG);
         uint32_t wv8[NSTEP / 2];
-        float a[NSTEP];
+        float a[MT][NSTEP];
 #pragma unroll
         for (int q = 0; q < NSTEP / 8; ++q) {
             const uint4 w = wp[q];
             wv8[4 * q] = w.x; wv8[4 * q + 1] = w.y; wv8[4 * q + 2] = w.z; wv8[4 * q + 3] = w.w;
         }
 #pragma unroll
-        for (int q = 0; q < NSTEP / 4; ++q) {
-            const float4 x = xp[q];
-            a[4 * q] = x.x; a[4 * q + 1] = x.y; a[4 * q + 2] = x.z; a[4 * q + 3] = x.w;
+        for (int mt = 0; mt < MT; ++mt) {
+            const float4* xp = reinterpret_cast<const float4*>(xb + mt * 16 * XSEG);
+#pragma unroll
+            for (int q = 0; q < NSTEP / 4; ++q) {
+                const float4 x = xp[q];
+                a[mt][4 * q] = x.x; a[mt][4 * q + 1] = x.y; a[mt][4 * q + 2] = x.z; a[mt][4 * q + 3] = x.w;
+            }
         }
         if (kvalid == CH) {
 #pragma unroll
             for (int st = 0; st < NSTEP; ++st) {
                 const float b = (st & 1) ? bf16_hi(wv8[st >> 1]) : bf16_lo(wv8[st >> 1]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b, acc, 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt][st], b, acc[mt], 0, 0, 0);
             }
         } else {
 #pragma unroll
             for (int st = 0; st < NSTEP; ++st) {
                 const float b = (st & 1) ? bf16_hi(wv8[st >> 1]) : bf16_lo(wv8[st >> 1]);
-                if (4 * st < kvalid) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st], b, acc, 0, 0, 0);
+                if (4 * st < kvalid) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[mt][st], b, acc[mt], 0, 0, 0);
+                }
             }
         }
         if (c == KS / CH - 1) {
             // end of a round: every wavefront holds the slice sum of slice rd * WK + wk
             if constexpr (WK == 1) {
                 if (sl < S) {
-                    if (sl == 0) {
-                        T = acc;
-                    } else {
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) T[v] = T[v] + acc[v];
+                    for (int mt = 0; mt < MT; ++mt) {
+                        if (sl == 0) {
+                            T[mt] = acc[mt];
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) T[mt][v] = T[mt][v] + acc[mt][v];
+                        }
                     }
                 }
             } else {
-                *reinterpret_cast<f32x4*>(&part[((wk * WN + wn) * 64 + lane) * 4]) = acc;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    *reinterpret_cast<f32x4*>(&part[(((wk * WN + wn) * MT + mt) * 64 + lane) * 4]) = acc[mt];
                 __syncthreads();
                 if (wk == 0) {
                     for (int j = 0; j < WK; ++j) {
                         const int sj = rd * WK + j;
                         if (sj >= S) break;
-                        const f32x4 pj = *reinterpret_cast<const f32x4*>(&part[((j * WN + wn) * 64 + lane) * 4]);
-                        if (sj == 0) {
-                            T = pj;
-                        } else {
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) T[v] = T[v] + pj[v];
+                        for (int mt = 0; mt < MT; ++mt) {
+                            const f32x4 pj = *reinterpret_cast<const f32x4*>(&part[(((j * WN + wn) * MT + mt) * 64 + lane) * 4]);
+                            if (sj == 0) {
+                                T[mt] = pj;
+                            } else {
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) T[mt][v] = T[mt][v] + pj[v];
+                            }
                         }
                     }
                 }
             }
-            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
 
@@ -640,32 +663,36 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         const int odd = r & 1;
         const int gc = (n0 + wn * 16 + (r & ~1)) >> 1;
 #pragma unroll
-        for (int vp = 0; vp < 4; vp += 2) {
-            const float a0 = T[vp], a1 = T[vp + 1];
-            const float x0 = __shfl_xor(a0, 1), x1 = __shfl_xor(a1, 1);
-            const float gate = odd ? x1 : a0;
-            const float up = odd ? a1 : x0;
-            const int gm = 4 * g + vp + odd;
-            if (gm < M && n0 + wn * 16 + (r & ~1) < N) Y[(int64_t)gm * ldy + gc] = (gate / (1.0f + exp_f(-gate))) * up;
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int vp = 0; vp < 4; vp += 2) {
+                const float a0 = T[mt][vp], a1 = T[mt][vp + 1];
+                const float x0 = __shfl_xor(a0, 1), x1 = __shfl_xor(a1, 1);
+                const float gate = odd ? x1 : a0;
+                const float up = odd ? a1 : x0;
+                const int gm = 16 * mt + 4 * g + vp + odd;
+                if (gm < M && n0 + wn * 16 + (r & ~1) < N) Y[(int64_t)gm * ldy + gc] = (gate / (1.0f + exp_f(-gate))) * up;
+            }
         return;
     }
     const int gn = n0 + wn * 16 + r;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int gm = 4 * g + v;
-        if (gm < M && gn < N) {
-            float y = T[v];
-            if (R) y = R[(int64_t)gm * ldr + gn] + y;
-            Y[(int64_t)gm * ldy + gn] = y;
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int gm = 16 * mt + 4 * g + v;
+            if (gm < M && gn < N) {
+                float y = T[mt][v];
+                if (R) y = R[(int64_t)gm * ldr + gn] + y;
+                Y[(int64_t)gm * ldy + gn] = y;
+            }
         }
-    }
 }
 
-template <int WN, int PD, int CH, int ROLE>
+template <int WN, int PD, int CH, int ROLE, int MT = 1>
 hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st) {
     dim3 grid((a.N + 16 * WN - 1) / (16 * WN));
-    hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, CH, ROLE>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, CH, ROLE, MT>), grid, dim3(256), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
 }
@@ -903,6 +930,15 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE>(a, st);
         return launch_gemv16<1, 2, 64, ROLE>(a, st);
     }
+    // two 16-row tiles up to M = 32 (measured faster than the 32 x 32 tiles at every decoder
+    // shape); four up to M = 64 only where the tiled kernels have too few tiles (N of 1024 to
+    // 4096: 2-3x faster there, slower at larger N)
+    if (a.M > 16 && a.M <= 32) {
+        if (a.N >= 65536) return launch_gemv16<4, 2, 64, ROLE, 2>(a, st);
+        if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE, 2>(a, st);
+        return launch_gemv16<1, 2, 64, ROLE, 2>(a, st);
+    }
+    if (a.M > 32 && a.M <= 64 && a.N >= 1024 && a.N <= 4096) return launch_gemv16<1, 2, 32, ROLE, 4>(a, st);
     if (a.M <= 4 && a.K <= gemm_skinny_max_k()) {
         if (a.M <= 1) return launch_skinny<1, ROLE>(a, st);
         if (a.M <= 2) return launch_skinny<2, ROLE>(a, st);

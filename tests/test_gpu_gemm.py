@@ -19,7 +19,8 @@ def inv():
     (1, 8, 5), (1, 264, 70), (2, 4096, 130), (3, 520, 257), (4, 8200, 33), (4, 72, 17), (2, 16, 1),
     (5, 1000, 64), (16, 4096, 33),
     (8, 8, 5), (8, 1000, 12300), (11, 520, 257), (16, 264, 12289), (13, 4104, 70), (9, 8200, 70),
-    (17, 264, 129), (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
+    (17, 264, 129), (20, 8200, 2049), (32, 520, 12300), (33, 520, 2050), (64, 1032, 4096),
+    (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
 ])
 def test_gemm_matches_oracle_small(orc, M, K, N):
     say("gemm", M, K, N)
@@ -100,7 +101,8 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
 
 
 @pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (5, 1000, 64), (16, 4096, 130),
-                                   (12, 520, 4200), (9, 264, 6500), (8, 4096, 14336), (6, 8456, 50), (17, 264, 129), (64, 768, 64), (65, 4096, 300),
+                                   (12, 520, 4200), (9, 264, 6500), (8, 4096, 14336), (6, 8456, 50), (17, 264, 129), (24, 520, 1030),
+                                   (48, 264, 1100), (64, 768, 64), (65, 4096, 300),
                                    (300, 1032, 257)])
 def test_gated_gemm_equals_gemm_then_swiglu(orc, M, K, F):
     """inv_gated_gemm on gate/up rows interleaved equals inv_fixed_order_gemm followed by
