@@ -740,7 +740,8 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     // phase; DEPTH phases are in flight in registers (two when the activation tile is small).
     // The loads read clamped, in-range addresses with no zero fill: what lands past N, M or K
     // reaches no stored output (the chains stop at K, rows past N or M are not written), and
-    // with no load under a branch each LDS store waits only as long as it must.  The buffers
+    // with no per-element condition around a load the compiler no longer turns the zero fill
+    // into a branch that makes each LDS store wait for every load in flight.  The buffers
     // are native vectors (copies of the struct types were kept in scratch memory), and a
     // scheduling barrier keeps the loads ahead of the phase's compute.
     constexpr int DEPTH = MB * XU <= 4 ? 2 : 1;
@@ -930,9 +931,9 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE>(a, st);
         return launch_gemv16<1, 2, 64, ROLE>(a, st);
     }
-    // two 16-row tiles up to M = 32 (measured faster than the 32 x 32 tiles at every decoder
-    // shape); four up to M = 64 only where the tiled kernels have too few tiles (N of 1024 to
-    // 4096: 2-3x faster there, slower at larger N)
+    // two 16-row tiles up to M = 32 (measured faster than the 32 x 32 tiles, or equal, at
+    // every decoder shape); four up to M = 64 only where the tiled kernels have too few tiles
+    // (N of 1024 to 4096: 1.4-1.6x faster there, slower at larger N)
     if (a.M > 16 && a.M <= 32) {
         if (a.N >= 65536) return launch_gemv16<4, 2, 64, ROLE, 2>(a, st);
         if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE, 2>(a, st);
