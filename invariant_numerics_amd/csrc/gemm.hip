@@ -102,8 +102,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
     const int h = lane >> 5, c = lane & 31;
     const int wm0 = (wv / WGN) * WM, wn0 = (wv % WGN) * WN;
 
-    // Per-thread source rows (clamped into range, with validity flags) computed once; each
-    // tile advances the pointers by BK.  Elements outside M x K or N x K load as zeros.
+    // Per-thread source rows (clamped into range) and their last in-range k offsets are
+    // computed once; a tile's loads add its k0, clamped to those offsets.
     // Loads read clamped, in-range addresses with no zero fill: rows past M or N reach only
     // outputs that are never stored, and columns past K only the k-steps a partial last tile
     // skips.  One branch-free path, into native vector registers, so nothing waits on a
