@@ -396,6 +396,15 @@ void orc_rope(const float* X, int64_t M, int64_t nh, int64_t D, int64_t ldx,
                      sin_t + (int64_t)pos[m] * (D / 2), D, Y + m * ldy + h * D);
 }
 
+/* Threads the oracle's parallel loops may use (they split independent outputs only, so the
+ * bits do not depend on it); n < 1 restores the OpenMP default.  Returns the new maximum. */
+int orc_set_threads(int n) {
+    static int deflt = 0;
+    if (deflt == 0) deflt = omp_get_max_threads();
+    omp_set_num_threads(n >= 1 ? n : deflt);
+    return omp_get_max_threads();
+}
+
 /* ------------------------------------------------------------ attention -- */
 static inline float ld_elem(const void* p, int dt, int64_t i) {
     return dt ? ((const float*)p)[i] : orc_bf16_up(((const uint16_t*)p)[i]);
@@ -504,12 +513,21 @@ void orc_swiglu(const float* G, const float* U, int64_t M, int64_t F, int64_t ld
  *   lp = (z_target - M) - log_f(S)                                                    */
 /* Row statistics of logits z[0..V): top-2 (lowest index first on ties), M = z_top1 and S, the
  * fixed tree of exp_f(z_v - M) (tiles of 1024, 64 lanes, pairwise lane tree, tiles folded in
- * ascending order). */
+ * ascending order).
+ * NaN logits are unordered, so they never take part in the top-2: top1 is the lowest index
+ * of the largest non-NaN logit and top2 the lowest index != top1 of the largest non-NaN
+ * logit of the rest.  Where no such index exists the choice falls back to index 0 for top1
+ * and to the lowest index != top1 for top2 (a row of NaN logits gives (0, 1)).  Any NaN in
+ * the row still reaches S, and through it the logprob. */
 static void lmhead_stats(const float* z, int64_t V, float* Mout, float* Sout, int64_t* t1, int64_t* t2) {
-    int64_t b1 = 0;
-    for (int64_t v = 1; v < V; ++v) if (z[v] > z[b1]) b1 = v;
-    int64_t b2 = (b1 == 0) ? 1 : 0;
-    for (int64_t v = 0; v < V; ++v) if (v != b1 && z[v] > z[b2]) b2 = v;
+    int64_t b1 = -1;
+    for (int64_t v = 0; v < V; ++v)
+        if (z[v] == z[v] && (b1 < 0 || z[v] > z[b1])) b1 = v;
+    if (b1 < 0) b1 = 0;
+    int64_t b2 = -1;
+    for (int64_t v = 0; v < V; ++v)
+        if (v != b1 && z[v] == z[v] && (b2 < 0 || z[v] > z[b2])) b2 = v;
+    if (b2 < 0) b2 = (b1 == 0) ? 1 : 0;
     float M = z[b1];
     float S = 0.0f;
     int64_t ntiles = (V + ORC_TV - 1) / ORC_TV;
@@ -531,6 +549,15 @@ static void lmhead_stats(const float* z, int64_t V, float* Mout, float* Sout, in
     *Sout = S;
     *t1 = b1;
     *t2 = b2;
+}
+
+/* The same row statistics for a caller-supplied logit row (the test suite pins the tile/lane
+ * tree of S with it). */
+void orc_lmhead_stats(const float* z, int64_t V, float* M, float* S, int32_t* top1, int32_t* top2) {
+    int64_t b1, b2;
+    lmhead_stats(z, V, M, S, &b1, &b2);
+    *top1 = (int32_t)b1;
+    *top2 = (int32_t)b2;
 }
 
 static void lmhead_pass(const float* a, int64_t K, const uint16_t* W, int64_t ldw, int64_t V,

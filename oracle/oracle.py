@@ -67,6 +67,9 @@ def lib():
         L.orc_attention.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                     i64, i64, i64, i64, i64, i64, i64, ctypes.c_float, f32p]
         L.orc_swiglu.argtypes = [f32p, f32p, i64, i64, i64, i64, f32p, i64]
+        L.orc_set_threads.restype = ctypes.c_int
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_lmhead_stats.argtypes = [f32p, i64, f32p, f32p, i32p, i32p]
         L.orc_lmhead.argtypes = [f32p, i64, i64, i64, u16p, i64, i32p, ctypes.c_float, ctypes.c_int,
                                  f32p, f32p, i32p, i32p, u8p]
         L.orc_decoder.argtypes = [i32p, i64, i64, i64, i64, i64, i64, i64, i64,
@@ -140,6 +143,12 @@ def dot_ks(x, w):
     w = _c(w, np.float32)
     assert x.shape == w.shape and x.ndim == 1
     return np.float32(lib().orc_dot_ks(_p(x, f32p), _p(w, f32p), x.size))
+
+
+def set_threads(n):
+    """Threads of the oracle's parallel loops (independent outputs only); 0 = default.
+    Returns the count now in effect."""
+    return int(lib().orc_set_threads(int(n)))
 
 
 def constants():
@@ -265,6 +274,19 @@ def swiglu(G, U):
     Hh = np.empty_like(G)
     lib().orc_swiglu(_p(G, f32p), _p(U, f32p), M, F, F, F, _p(Hh, f32p), F)
     return Hh
+
+
+def lmhead_stats(z):
+    """Row statistics of one FP32 logit row: (M, S, top1, top2) with S the fixed tile/lane
+    tree of exp_f(z_v - M)."""
+    z = _c(z, np.float32)
+    assert z.ndim == 1 and z.size >= 2
+    M = np.zeros(1, np.float32)
+    S = np.zeros(1, np.float32)
+    t1 = np.zeros(1, np.int32)
+    t2 = np.zeros(1, np.int32)
+    lib().orc_lmhead_stats(_p(z, f32p), z.size, _p(M, f32p), _p(S, f32p), _p(t1, i32p), _p(t2, i32p))
+    return M[0], S[0], int(t1[0]), int(t2[0])
 
 
 def lmhead(Hs, W, target, tau=np.float32(0.1), mode=0):

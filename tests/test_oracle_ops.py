@@ -532,3 +532,25 @@ def test_oracle_greedy_consistent_with_scoring(orc, tiny_model):
     assert np.array_equal(r["top1"][len(prompt) - 1:-1], g["tokens"])
     assert np.array_equal(bits(r["margin"][len(prompt) - 1:-1]), bits(g["margin"]))
     assert np.array_equal(g["top1"], g["tokens"])
+
+
+def test_lmhead_nan_logits_never_win(orc):
+    """NaN logits are unordered, so they take no part in the top-2: NaN at index 0 or 1 or in
+    the middle leaves the finite logits' lowest-index maximum pair; a row with one finite
+    logit pairs it with the lowest other index; an all-NaN row gives (0, 1)."""
+    z = synth.normal(231, (3000,), 1.0)
+    order = np.lexsort((np.arange(3000), -z))
+    for nan_at in ([0], [1], [0, 1], [int(order[0])], [int(order[1]), 5]):
+        y = z.copy()
+        y[nan_at] = np.nan
+        fin = [v for v in order if v not in nan_at]
+        M, S, t1, t2 = orc.lmhead_stats(y)
+        assert (t1, t2) == (fin[0], fin[1]), nan_at
+        assert M == z[fin[0]] and np.isnan(S)
+    y = np.full(16, np.nan, np.float32)
+    assert orc.lmhead_stats(y)[2:] == (0, 1)
+    y[9] = 2.0
+    assert orc.lmhead_stats(y)[2:] == (9, 0)
+    y[:] = np.nan
+    y[0] = -1.0
+    assert orc.lmhead_stats(y)[2:] == (0, 1)
