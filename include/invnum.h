@@ -308,6 +308,29 @@ int inv_mfma_f32_check(const float* A, const float* B, const float* C, float* D,
 int inv_mfma32_f32_check(const float* A, const float* B, const float* C, float* D, int64_t ntests,
                          void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * inv_kernel_route -- host-only query (enqueues nothing, touches no device): the name of
+ * the kernel instantiation that a call with these sizes launches, written as a
+ * NUL-terminated string into name[0 .. cap-1] (truncated to fit).  The choice is launch
+ * geometry only: every route computes the same bits, which the test suite checks across
+ * sizes and against the CPU check.  Used by the tests and the benchmark to state which
+ * kernels a check covers.
+ *   op INV_ROUTE_GEMM:         inv_fixed_order_gemm with M = a activation rows, N = b
+ *                              weight rows (K does not change the route);
+ *   op INV_ROUTE_GATED_GEMM:   inv_gated_gemm with M = a, N2 = b;
+ *   op INV_ROUTE_LMHEAD_GEMM:  the vocabulary projection inside inv_lmhead_logprob_top2
+ *                              for B = a rows, V = b entries and tau > 0 (up to 16 rows
+ *                              the primary and FP32 operand rows share one projection of
+ *                              2B rows; with tau <= 0 it is the route of a rows);
+ *   op INV_ROUTE_ATTN_PREFILL: inv_attention_prefill with B * Hq = a and Tq = b.
+ * Returns INV_OK, INV_ERR_NULL (name NULL or cap 0), INV_ERR_DTYPE (unknown op) or
+ * INV_ERR_SHAPE (a or b < 1).
+ * ------------------------------------------------------------------------------------ */
+enum inv_route_op {
+    INV_ROUTE_GEMM = 0, INV_ROUTE_GATED_GEMM = 1, INV_ROUTE_LMHEAD_GEMM = 2, INV_ROUTE_ATTN_PREFILL = 3
+};
+int inv_kernel_route(int op, int64_t a, int64_t b, char* name, size_t cap);
+
 #ifdef __cplusplus
 }
 #endif

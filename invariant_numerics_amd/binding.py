@@ -65,6 +65,7 @@ def _load():
         "inv_eval_numerics": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, vp]),
         "inv_mfma_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
         "inv_mfma32_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
+        "inv_kernel_route": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_char_p, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -79,7 +80,8 @@ EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "in
            "inv_lmhead_workspace_bytes", "inv_lmhead_logprob_top2", "inv_embed", "inv_rope_kv_append",
            "inv_swiglu", "inv_add", "inv_round_activations", "inv_lmhead_logit_grad_workspace_bytes",
            "inv_lmhead_logit_grad", "inv_gemm_backward_workspace_bytes",
-           "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check")
+           "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check",
+           "inv_kernel_route")
 
 
 def _check(status, what):
@@ -130,6 +132,20 @@ def inv_get_constants():
     _check(LIB.inv_get_constants(ctypes.byref(c)), "inv_get_constants")
     return dict(ks=c.ks, chunk=c.chunk, vocab_tile=c.vocab_tile, lanes=c.lanes,
                 float_consts=[c.float_consts[i] for i in range(c.n_float)])
+
+
+ROUTE_OPS = {"gemm": 0, "gated_gemm": 1, "lmhead_gemm": 2, "attention_prefill": 3}
+
+
+def inv_kernel_route(op, a, b):
+    """Name of the kernel instantiation a call launches (host-only query): op "gemm" (a = M,
+    b = N), "gated_gemm" (a = M, b = N2), "lmhead_gemm" (a = B, b = V, tau > 0) or
+    "attention_prefill" (a = B * Hq, b = Tq)."""
+    if op not in ROUTE_OPS:
+        raise InvError("unknown route op %r" % (op,))
+    buf = ctypes.create_string_buffer(128)
+    _check(LIB.inv_kernel_route(ROUTE_OPS[op], int(a), int(b), buf, len(buf)), "inv_kernel_route")
+    return buf.value.decode()
 
 
 def inv_attention_decode_workspace_bytes(B, Tmax, Hq, D):

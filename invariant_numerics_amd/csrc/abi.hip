@@ -5,6 +5,7 @@
 #include "kernels.h"
 #include "numerics.h"
 
+#include <stdio.h>
 #include <string.h>
 
 using namespace invnum;
@@ -258,6 +259,33 @@ int inv_mfma32_f32_check(const float* A, const float* B, const float* C, float* 
     if (!A || !B || !C || !D) return INV_ERR_NULL;
     if (ntests < 1) return INV_ERR_SHAPE;
     return fin(launch_mfma32_check(A, B, C, D, ntests, S(stream)));
+}
+
+int inv_kernel_route(int op, int64_t a, int64_t b, char* name, size_t cap) {
+    if (!name || cap == 0) return INV_ERR_NULL;
+    if (a < 1 || b < 1) return INV_ERR_SHAPE;
+    char buf[96];
+    const char* role = "0";
+    int64_t M = a, N = b;
+    switch (op) {
+        case INV_ROUTE_GEMM: break;
+        case INV_ROUTE_GATED_GEMM: role = "2"; break;
+        case INV_ROUTE_LMHEAD_GEMM: role = "1"; M = lmhead_projection_rows(a, 1.0f); break;
+        case INV_ROUTE_ATTN_PREFILL: {
+            const int nw = attention_prefill_waves(1, b, a);
+            snprintf(buf, sizeof(buf), "attn_prefill_kernel<DT,%d,%d>", nw, nw == 8 ? 64 : 32);
+            snprintf(name, cap, "%s", buf);
+            return INV_OK;
+        }
+        default: return INV_ERR_DTYPE;
+    }
+    // the template name with its ROLE argument filled in
+    const char* t = gemm_route_name(gemm_route(M, N));
+    const char* r = strstr(t, "ROLE");
+    if (r) snprintf(buf, sizeof(buf), "%.*s%s%s", (int)(r - t), t, role, r + 4);
+    else snprintf(buf, sizeof(buf), "%s", t);
+    snprintf(name, cap, "%s", buf);
+    return INV_OK;
 }
 
 }  // extern "C"

@@ -676,12 +676,16 @@ hipError_t launch_prefill_nw(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// 128-row workgroups (8 wavefronts, 64-key sub-blocks) when they give at least two per CU;
+// else 64-row ones (4 wavefronts, 32-key sub-blocks) for twice the grid.  The rows' bits do
+// not depend on the choice.
+int attention_prefill_waves(int64_t B, int64_t Tq, int64_t Hq) {
+    const int64_t wg128 = ((Tq + 127) / 128) * Hq * B;
+    return wg128 >= 512 ? 8 : 4;
+}
+
 hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
-    // 128-row workgroups (8 wavefronts, 64-key sub-blocks) when they give at least two per
-    // CU; else 64-row ones (4 wavefronts, 32-key sub-blocks) for twice the grid.  The rows'
-    // bits do not depend on the choice.
-    const int64_t wg128 = (int64_t)((a.Tq + 127) / 128) * a.Hq * a.B;
-    if (wg128 >= 512) return launch_prefill_nw<8, 64>(a, st);
+    if (attention_prefill_waves(a.B, a.Tq, a.Hq) == 8) return launch_prefill_nw<8, 64>(a, st);
     return launch_prefill_nw<4, 32>(a, st);
 }
 

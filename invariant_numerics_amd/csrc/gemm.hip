@@ -893,65 +893,87 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int MB, int ROLE>
+template <int MB, int ROLE, int ROWS>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
-    // 16-row workgroups once they give >= 4 per CU; else 4-row (one wavefront) workgroups so
-    // the small projections still spread evenly over the CUs
-    if constexpr (MB <= 2) {
-        if (a.N < 16 * 1024) {
-            dim3 grid((a.N + 3) / 4);
-            hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, 4>), grid, dim3(4 * SK_LANES), 0, st,
-                               a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
-            return hipGetLastError();
-        }
-    }
-    {
-        dim3 grid((a.N + 15) / 16);
-        hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, 16>), grid, dim3(16 * SK_LANES), 0, st,
-                           a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
-    }
+    dim3 grid((a.N + ROWS - 1) / ROWS);
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, ROWS>), grid, dim3(ROWS * SK_LANES), 0, st,
+                       a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t gemm_skinny_max_k() {
-    return (int64_t)1 << 30;   // slices are folded group by group: no K limit
+// Kernel choice for M rows and N weight rows (launch geometry only: the order of every
+// output's sum is the same on every route, which the tests check across M).
+//   M <= 4: the VALU GEMV (16-row workgroups, or 4-row ones for N < 16384 and M <= 2 so the
+//     small projections still spread evenly over the CUs);
+//   5 <= M <= 16: the matrix-core GEMV with one 16-row tile (the VALU GEMV's per-row
+//     accumulators and LDS reads make it slower from 5 rows on); weight rows per workgroup:
+//     64 from N = 65536 (four wavefronts along the rows), 32 from 12288 (two along the rows,
+//     two along K), else 16 with the slices split over four wavefronts;
+//   17 <= M <= 32: the same with two row tiles (measured faster than the 32 x 32 tiles, or
+//     equal, at every decoder shape); 33 <= M <= 64 with N of 1024 to 4096: four row tiles
+//     (1.4-1.6x faster there than the tiled kernels, slower at larger N);
+//   other M <= 64: 32 x 32 tiles when the 64 x 64 grid would have fewer than SMALL_BELOW
+//     tiles, else 64 x 64;
+//   M > 64: 128 x 256 when that gives at least one workgroup per CU, else 64 x 64 (e.g.
+//     M = 512, N = 4096: 64 large tiles, 512 small ones, 3x faster).
+GemmRoute gemm_route(int64_t M, int64_t N) {
+    if (M <= 1) return N < 16 * 1024 ? GR_SKINNY_M1_R4 : GR_SKINNY_M1_R16;
+    if (M <= 2) return N < 16 * 1024 ? GR_SKINNY_M2_R4 : GR_SKINNY_M2_R16;
+    if (M <= 4) return GR_SKINNY_M4_R16;
+    if (M <= 16) return N >= 65536 ? GR_GEMV16_WN4 : (N >= 12288 ? GR_GEMV16_WN2 : GR_GEMV16_WN1);
+    if (M <= 32) return N >= 65536 ? GR_GEMV32_WN4 : (N >= 12288 ? GR_GEMV32_WN2 : GR_GEMV32_WN1);
+    if (M <= 64 && N >= 1024 && N <= 4096) return GR_GEMV64;
+    const int64_t big = ((M + 127) / 128) * ((N + 255) / 256);
+    const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
+    if (M <= 64 && mid < SMALL_BELOW) return GR_SMALL32;
+    if (M <= 64 || big < 256) return GR_TILE64;
+    return GR_TILE128x256;
+}
+
+const char* gemm_route_name(GemmRoute r) {
+    switch (r) {
+        case GR_SKINNY_M1_R4: return "gemm_skinny_kernel<1,ROLE,4>";
+        case GR_SKINNY_M1_R16: return "gemm_skinny_kernel<1,ROLE,16>";
+        case GR_SKINNY_M2_R4: return "gemm_skinny_kernel<2,ROLE,4>";
+        case GR_SKINNY_M2_R16: return "gemm_skinny_kernel<2,ROLE,16>";
+        case GR_SKINNY_M4_R16: return "gemm_skinny_kernel<4,ROLE,16>";
+        case GR_GEMV16_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,1>";
+        case GR_GEMV16_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,1>";
+        case GR_GEMV16_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,1>";
+        case GR_GEMV32_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,2>";
+        case GR_GEMV32_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,2>";
+        case GR_GEMV32_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,2>";
+        case GR_GEMV64: return "gemm_gemv16_kernel<1,2,32,ROLE,4>";
+        case GR_SMALL32: return "gemm_small_kernel<ROLE>";
+        case GR_TILE64: return "gemm_mfma_kernel<64,64,2,2,ROLE>";
+        case GR_TILE128x256: return "gemm_mfma_kernel<128,256,2,4,ROLE>";
+        default: return "unknown";
+    }
 }
 
 template <int ROLE>
 hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
-    // M is an upper bound when Mdev is set (rows beyond *Mdev are skipped on the device).
-    // 5 <= M <= 16: the matrix-core GEMV (the VALU GEMV's per-row accumulators and LDS reads
-    // make it slower from 5 rows on).  Weight rows per workgroup: 64 from 65536 rows (four
-    // wavefronts along the rows), 32 from 12288 (two along the rows, two along K), else 16
-    // with the slices split over four wavefronts, so the grid still covers the chip.
-    if (a.M >= 5 && a.M <= 16) {
-        if (a.N >= 65536) return launch_gemv16<4, 2, 64, ROLE>(a, st);
-        if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE>(a, st);
-        return launch_gemv16<1, 2, 64, ROLE>(a, st);
+    // M is an upper bound when Mdev is set (rows beyond *Mdev are skipped on the device)
+    switch (gemm_route(a.M, a.N)) {
+        case GR_SKINNY_M1_R4: return launch_skinny<1, ROLE, 4>(a, st);
+        case GR_SKINNY_M1_R16: return launch_skinny<1, ROLE, 16>(a, st);
+        case GR_SKINNY_M2_R4: return launch_skinny<2, ROLE, 4>(a, st);
+        case GR_SKINNY_M2_R16: return launch_skinny<2, ROLE, 16>(a, st);
+        case GR_SKINNY_M4_R16: return launch_skinny<4, ROLE, 16>(a, st);
+        case GR_GEMV16_WN1: return launch_gemv16<1, 2, 64, ROLE>(a, st);
+        case GR_GEMV16_WN2: return launch_gemv16<2, 2, 64, ROLE>(a, st);
+        case GR_GEMV16_WN4: return launch_gemv16<4, 2, 64, ROLE>(a, st);
+        case GR_GEMV32_WN1: return launch_gemv16<1, 2, 64, ROLE, 2>(a, st);
+        case GR_GEMV32_WN2: return launch_gemv16<2, 2, 64, ROLE, 2>(a, st);
+        case GR_GEMV32_WN4: return launch_gemv16<4, 2, 64, ROLE, 2>(a, st);
+        case GR_GEMV64: return launch_gemv16<1, 2, 32, ROLE, 4>(a, st);
+        case GR_SMALL32: return launch_small<ROLE>(a, st);
+        case GR_TILE64: return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
+        case GR_TILE128x256: return launch_tiled<128, 256, 2, 4, ROLE>(a, st);
+        default: return hipErrorInvalidValue;
     }
-    // two 16-row tiles up to M = 32 (measured faster than the 32 x 32 tiles, or equal, at
-    // every decoder shape); four up to M = 64 only where the tiled kernels have too few tiles
-    // (N of 1024 to 4096: 1.4-1.6x faster there, slower at larger N)
-    if (a.M > 16 && a.M <= 32) {
-        if (a.N >= 65536) return launch_gemv16<4, 2, 64, ROLE, 2>(a, st);
-        if (a.N >= 12288) return launch_gemv16<2, 2, 64, ROLE, 2>(a, st);
-        return launch_gemv16<1, 2, 64, ROLE, 2>(a, st);
-    }
-    if (a.M > 32 && a.M <= 64 && a.N >= 1024 && a.N <= 4096) return launch_gemv16<1, 2, 32, ROLE, 4>(a, st);
-    if (a.M <= 4 && a.K <= gemm_skinny_max_k()) {
-        if (a.M <= 1) return launch_skinny<1, ROLE>(a, st);
-        if (a.M <= 2) return launch_skinny<2, ROLE>(a, st);
-        return launch_skinny<4, ROLE>(a, st);
-    }
-    // the large tile only when it gives at least one workgroup per CU; below that the 64 x 64
-    // tile's 8x larger grid wins (e.g. M = 512, N = 4096: 64 large tiles, 512 small ones)
-    const int64_t big = ((a.M + 127) / 128) * (int64_t)((a.N + 255) / 256);
-    const int64_t mid = ((a.M + 63) / 64) * (int64_t)((a.N + 63) / 64);
-    if (a.M <= 64 && (a.M <= 32 || mid < SMALL_BELOW)) return launch_small<ROLE>(a, st);
-    if (a.M <= 64 || big < 256) return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
-    return launch_tiled<128, 256, 2, 4, ROLE>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role) {

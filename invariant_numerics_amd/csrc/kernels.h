@@ -17,7 +17,14 @@ struct GemmArgs {
 // role 0: activation projections; role 1: the LM head's vocabulary projection; role 2: gated
 // projection (W rows interleaved gate/up, Y[m][i] = silu(gate) * up, N even, R unused)
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role = 0);
-int64_t gemm_skinny_max_k();
+// the kernel a GEMM of M activation rows and N weight rows runs on (every role routes alike)
+enum GemmRoute : int {
+    GR_SKINNY_M1_R4, GR_SKINNY_M1_R16, GR_SKINNY_M2_R4, GR_SKINNY_M2_R16, GR_SKINNY_M4_R16,
+    GR_GEMV16_WN1, GR_GEMV16_WN2, GR_GEMV16_WN4, GR_GEMV32_WN1, GR_GEMV32_WN2, GR_GEMV32_WN4,
+    GR_GEMV64, GR_SMALL32, GR_TILE64, GR_TILE128x256
+};
+GemmRoute gemm_route(int64_t M, int64_t N);
+const char* gemm_route_name(GemmRoute r);   // kernel template with ROLE left symbolic
 
 hipError_t launch_rmsnorm(const float* X, int M, int H, int64_t ldx, const uint16_t* g, float eps,
                           float* Y, int64_t ldy, hipStream_t st);
@@ -30,6 +37,8 @@ struct AttnArgs {
     float* O;
 };
 hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st);
+// 8 (128-row workgroups) or 4 (64-row workgroups): wavefronts per prefill workgroup
+int attention_prefill_waves(int64_t B, int64_t Tq, int64_t Hq);
 hipError_t launch_attention_decode(const AttnArgs& a, const int32_t* pos, float* ws,
                                    hipStream_t st);
 
@@ -41,6 +50,8 @@ struct LmheadArgs {
     void* ws;
 };
 size_t lmhead_ws_bytes(int64_t B, int64_t K, int64_t V);
+// activation rows of the vocabulary projection for B rows at threshold tau
+int64_t lmhead_projection_rows(int64_t B, float tau);
 struct LogitGradArgs {
     const float* Hs; int B; int K; int64_t ldh;
     const uint16_t* W; int V;

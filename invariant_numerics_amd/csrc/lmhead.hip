@@ -331,6 +331,10 @@ GradWs grad_ws_layout(int64_t B, int64_t V) {
 
 size_t lmhead_ws_bytes(int64_t B, int64_t K, int64_t V) { return ws_layout(B, K, V).total; }
 
+int64_t lmhead_projection_rows(int64_t B, float tau) {
+    return (tau > 0.0f && B <= LM_FUSED_MAX_B) ? 2 * B : B;
+}
+
 size_t logit_grad_ws_bytes(int64_t B, int64_t V) { return grad_ws_layout(B, V).total; }
 
 // Logit gradient of coef * lp on the FP32 pass: logits into G (the vocabulary GEMM on h

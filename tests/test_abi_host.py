@@ -105,3 +105,30 @@ def test_elementwise_argument_validation(inv):
     assert L.inv_rmsnorm(FAKE, 4, 32768, 32768, FAKE, 1e-5, FAKE, 32768, None) == -6
     assert L.inv_eval_numerics(3, FAKE, FAKE, 4, None) == -4
     assert L.inv_swiglu(FAKE, FAKE, 2, 8, 4, 8, FAKE, 8, None) == -2
+
+
+def test_kernel_route_names(inv):
+    """The route query names the instantiation each shape class reaches (the tests that
+    compare the benchmarked kernels with the oracle assert their shapes with it)."""
+    r = inv.inv_kernel_route
+    assert r("gemm", 1, 4096) == "gemm_skinny_kernel<1,0,4>"
+    assert r("gemm", 1, 28672) == "gemm_skinny_kernel<1,0,16>"
+    assert r("gemm", 3, 4096) == "gemm_skinny_kernel<4,0,16>"
+    assert r("gemm", 16, 4096) == "gemm_gemv16_kernel<1,2,64,0,1>"
+    assert r("gemm", 32, 14336) == "gemm_gemv16_kernel<2,2,64,0,2>"
+    assert r("gemm", 64, 4096) == "gemm_gemv16_kernel<1,2,32,0,4>"
+    assert r("gemm", 64, 8192) == "gemm_small_kernel<0>"
+    assert r("gemm", 64, 16384) == "gemm_mfma_kernel<64,64,2,2,0>"
+    assert r("gemm", 512, 4096) == "gemm_mfma_kernel<64,64,2,2,0>"
+    assert r("gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,0>"
+    assert r("gemm", 16384, 6144) == "gemm_mfma_kernel<128,256,2,4,0>"
+    assert r("gated_gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,2>"
+    assert r("gated_gemm", 1, 28672) == "gemm_skinny_kernel<1,2,16>"
+    assert r("lmhead_gemm", 1, 128256) == "gemm_skinny_kernel<2,1,16>"
+    assert r("lmhead_gemm", 8, 128256) == "gemm_gemv16_kernel<4,2,64,1,1>"
+    assert r("lmhead_gemm", 32767, 128256) == "gemm_mfma_kernel<128,256,2,4,1>"
+    assert r("attention_prefill", 4 * 32, 512) == "attn_prefill_kernel<DT,8,64>"
+    assert r("attention_prefill", 8, 2048) == "attn_prefill_kernel<DT,4,32>"
+    assert inv.LIB.inv_kernel_route(9, 1, 1, ctypes.create_string_buffer(8), 8) == -4
+    assert inv.LIB.inv_kernel_route(0, 0, 1, ctypes.create_string_buffer(8), 8) == -2
+    assert inv.LIB.inv_kernel_route(0, 1, 1, None, 8) == -1

@@ -129,3 +129,31 @@ def test_nan_rows_stay_in_bounds(orc):
     rows = [0, 2, 3]
     want = orc.lmhead(d["h"][rows], d["w"], d["target"][rows])
     check({k: v[rows] for k, v in got.items()}, want, "finite rows")
+
+
+def test_partly_nan_rows_match_oracle(orc):
+    """Rows with NaN logits among finite ones (an infinite product sum meeting its negative in
+    the slice fold): NaN never takes part in the top-2, so top-1, top-2, margin and the
+    recompute flag come from the finite logits, and the logprob is NaN (the NaN terms reach
+    the denominator).  NaN at vocabulary index 0, at index 1, at both, and in the middle."""
+    say("lmhead partly-NaN rows")
+    K, V = 512, 3000
+    W = synth.bf16_normal(9300, (V, K), 0.1)
+    W[:, [0, 1, 2, 256, 257, 258]] = 0
+    for v, c in ((0, 0), (1, 1), (2000, 2)):          # vocabulary row v: +2 at column c, -2 at c + 256
+        W[v, c], W[v, c + 256] = 0x4000, 0xC000
+    h = synth.normal(9301, (5, K))
+    big = np.float32(3e38)
+    for r, cols in ((0, [0]), (1, [1]), (2, [0, 1]), (3, [2])):
+        for c in cols:
+            h[r, c] = h[r, c + 256] = big                 # row 4 stays finite
+    tgt = np.array([0, 5, 1, 2000, 7], np.int32)
+    for tau in (0.1, np.inf):
+        got = run(h, W, tgt, tau=tau)
+        want = orc.lmhead(h, W, tgt, tau=np.float32(tau))
+        for k in ("margin", "top1", "top2", "recomputed"):
+            assert_bitwise(got[k], want[k], "tau=%s %s" % (tau, k))
+        assert np.array_equal(np.isnan(got["logprob"]), np.isnan(want["logprob"]))
+        assert np.isnan(want["logprob"][:4]).all() and np.isfinite(want["margin"]).all()
+        assert_bitwise(got["logprob"][4:], want["logprob"][4:], "finite row")
+        assert want["top1"][0] != 0 and want["top1"][1] != 1 and 0 not in want["top1"][2:3]
