@@ -308,6 +308,19 @@ int inv_mfma_f32_check(const float* A, const float* B, const float* C, float* D,
 int inv_mfma32_f32_check(const float* A, const float* B, const float* C, float* D, int64_t ntests,
                          void* stream);
 
+/* Diagnostic: runs one v_mfma_f32_16x16x32_bf16 per test, in lane form.  Test t supplies,
+ * for each lane l = 0..63 of one wavefront, the lane's 8 A operands and 8 B operands (BF16
+ * bit patterns at A + 8 (64 t + l) and B + 8 (64 t + l)) and its 4 FP32 accumulator values
+ * (C + 4 (64 t + l)); the lane's 4 results are written to D + 4 (64 t + l).  Which matrix
+ * element each lane register holds is left to the caller (the test suite pins it with
+ * small-integer operands, where every summation order gives the exact result).  Used to
+ * test candidate models of the instruction's accumulation ("Greedy Decoding Is Not
+ * Precision-Invariant", abstract: a BF16 LM head) against the CPU before any use; the
+ * library's BF16 pass does not use this instruction.  Status: INV_ERR_NULL for a null
+ * pointer, INV_ERR_SHAPE for ntests < 1. */
+int inv_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t ntests,
+                        void* stream);
+
 /* ------------------------------------------------------------------------------------
  * inv_kernel_route -- host-only query (enqueues nothing, touches no device): the name of
  * the kernel instantiation that a call with these sizes launches, written as a

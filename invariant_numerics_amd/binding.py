@@ -65,6 +65,7 @@ def _load():
         "inv_eval_numerics": (ctypes.c_int, [ctypes.c_int, vp, vp, i64, vp]),
         "inv_mfma_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
         "inv_mfma32_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
+        "inv_mfma_bf16_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
         "inv_kernel_route": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_char_p, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
@@ -81,7 +82,7 @@ EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "in
            "inv_swiglu", "inv_add", "inv_round_activations", "inv_lmhead_logit_grad_workspace_bytes",
            "inv_lmhead_logit_grad", "inv_gemm_backward_workspace_bytes",
            "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check",
-           "inv_kernel_route")
+           "inv_mfma_bf16_check", "inv_kernel_route")
 
 
 def _check(status, what):
@@ -412,4 +413,20 @@ def inv_mfma32_f32_check(A, B, C, out=None):
     if out is None:
         out = torch.empty_like(C)
     _check(LIB.inv_mfma32_f32_check(_p(A), _p(B), _p(C), _p(out), n, _stream(A)), "inv_mfma32_f32_check")
+    return out
+
+
+def inv_mfma_bf16_check(A, B, C, out=None):
+    """Lane form of one v_mfma_f32_16x16x32_bf16 per test: A, B [n, 64, 8] BF16 (bits), C
+    [n, 64, 4] FP32 -> D [n, 64, 4], each lane's registers as the instruction leaves them."""
+    _dev(A, B, C, out)
+    n = A.shape[0]
+    if tuple(A.shape) != (n, 64, 8) or tuple(B.shape) != (n, 64, 8) or tuple(C.shape) != (n, 64, 4):
+        raise InvError("shapes: A, B [n, 64, 8] (BF16), C [n, 64, 4] (FP32)")
+    _bf16(A)
+    _bf16(B)
+    _f32(C)
+    if out is None:
+        out = torch.empty_like(C)
+    _check(LIB.inv_mfma_bf16_check(_p(A), _p(B), _p(C), _p(out), n, _stream(A)), "inv_mfma_bf16_check")
     return out

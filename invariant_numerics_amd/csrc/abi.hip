@@ -261,6 +261,13 @@ int inv_mfma32_f32_check(const float* A, const float* B, const float* C, float* 
     return fin(launch_mfma32_check(A, B, C, D, ntests, S(stream)));
 }
 
+int inv_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t ntests,
+                        void* stream) {
+    if (!A || !B || !C || !D) return INV_ERR_NULL;
+    if (ntests < 1) return INV_ERR_SHAPE;
+    return fin(launch_mfma_bf16_check(A, B, C, D, ntests, S(stream)));
+}
+
 int inv_kernel_route(int op, int64_t a, int64_t b, char* name, size_t cap) {
     if (!name || cap == 0) return INV_ERR_NULL;
     if (a < 1 || b < 1) return INV_ERR_SHAPE;

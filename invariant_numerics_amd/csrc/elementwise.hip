@@ -261,6 +261,34 @@ __global__ __launch_bounds__(64) void mfma32_check_kernel(const float* __restric
     }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// One v_mfma_f32_16x16x32_bf16 per test, in lane form: test t supplies for each lane l of the
+// wavefront its 8 A operands (BF16 bits, A + (64 t + l) * 8), its 8 B operands (same layout in
+// B) and its 4 accumulator values (C + (64 t + l) * 4), and receives the lane's 4 results at
+// D + (64 t + l) * 4.  The mapping of matrix elements to lanes is left to the caller.
+__global__ __launch_bounds__(64) void mfma_bf16_check_kernel(const uint16_t* __restrict__ A,
+                                                             const uint16_t* __restrict__ B,
+                                                             const float* __restrict__ C,
+                                                             float* __restrict__ D, int64_t ntest) {
+    const int l = threadIdx.x;
+    for (int64_t t = blockIdx.x; t < ntest; t += gridDim.x) {
+        const int64_t o = t * 64 + l;
+        bf16x8_t a, b;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[i] = __builtin_bit_cast(__bf16, A[o * 8 + i]);
+            b[i] = __builtin_bit_cast(__bf16, B[o * 8 + i]);
+        }
+        f32x4_t c;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) c[v] = C[o * 4 + v];
+        const f32x4_t d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) D[o * 4 + v] = d[v];
+    }
+}
+
 inline int grid_for(int64_t work, int block) {
     int64_t g = (work + block - 1) / block;
     if (g > 65536) g = 65536;
@@ -354,6 +382,13 @@ hipError_t launch_mfma32_check(const float* A, const float* B, const float* C, f
                                hipStream_t st) {
     const int grid = (int)(ntest < 4096 ? ntest : 4096);
     hipLaunchKernelGGL(mfma32_check_kernel, dim3(grid), dim3(64), 0, st, A, B, C, D, ntest);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t ntest,
+                                  hipStream_t st) {
+    const int grid = (int)(ntest < 4096 ? ntest : 4096);
+    hipLaunchKernelGGL(mfma_bf16_check_kernel, dim3(grid), dim3(64), 0, st, A, B, C, D, ntest);
     return hipGetLastError();
 }
 

@@ -84,5 +84,7 @@ hipError_t launch_mfma_check(const float* A, const float* B, const float* C, flo
                              hipStream_t st);
 hipError_t launch_mfma32_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
                                hipStream_t st);
+hipError_t launch_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t ntest,
+                                  hipStream_t st);
 
 }  // namespace invnum

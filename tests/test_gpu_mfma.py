@@ -62,3 +62,4 @@ def test_mfma32_f32_is_sequential_fma(orc, kind):
     A, B, C = operands(kind, 32, 2, 12)
     D = host(inv.inv_mfma32_f32_check(f32(A), f32(B), f32(C)))
     assert_bitwise(D, oracle_chain(orc, A, B, C), kind)
+
