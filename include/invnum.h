@@ -158,6 +158,27 @@ int inv_attention_decode(int dtype, const void* Q, const void* Kc, const void* V
                          int64_t Hq, int64_t Hkv, int64_t D, float scale,
                          float* O, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * inv_attention_decode_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation, arguments and bits as inv_attention_decode, without the workspace
+ * arguments.  The chunk partials go to a device array the library owns, of
+ * inv_attention_decode_noalloc_max_bytes() bytes (32 MiB) on each GPU, held until the
+ * process ends; nothing is allocated, here or by any routine it calls.
+ *   Limit: inv_attention_decode_workspace_bytes(B, Tmax, Hq, D) must not exceed that size
+ *   (e.g. B <= 15 rows of 32 query heads at Tmax = 32768), else INV_ERR_WORKSPACE and
+ *   nothing is enqueued.
+ *   Every call on one GPU shares the array: calls that overlap on the same GPU (other
+ *   streams, other host threads) race and must be ordered by the caller.  Nothing needs
+ *   clearing between calls: every partial the call reads it has written itself.
+ * Other status codes as inv_attention_decode; INV_ERR_LAUNCH also when the array's device
+ * address cannot be obtained.
+ * ------------------------------------------------------------------------------------ */
+size_t inv_attention_decode_noalloc_max_bytes(void);
+int inv_attention_decode_noalloc(int dtype, const void* Q, const void* Kc, const void* Vc, const int32_t* pos,
+                                 int64_t B, int64_t Tmax, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                                 float* O, void* stream);
+
 /* Workspace for inv_lmhead_logprob_top2. */
 size_t inv_lmhead_workspace_bytes(int64_t B, int64_t K, int64_t V);
 

@@ -47,6 +47,9 @@ def _load():
         "inv_attention_decode_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64, i64]),
         "inv_attention_decode": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                                 ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
+        "inv_attention_decode_noalloc_max_bytes": (ctypes.c_size_t, []),
+        "inv_attention_decode_noalloc": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                        ctypes.c_float, vp, vp]),
         "inv_lmhead_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64]),
         "inv_lmhead_logprob_top2": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, vp, ctypes.c_float, vp, vp,
                                                    vp, vp, vp, vp, ctypes.c_size_t, vp]),
@@ -82,7 +85,8 @@ EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "in
            "inv_swiglu", "inv_add", "inv_round_activations", "inv_lmhead_logit_grad_workspace_bytes",
            "inv_lmhead_logit_grad", "inv_gemm_backward_workspace_bytes",
            "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check",
-           "inv_mfma_bf16_check", "inv_kernel_route")
+           "inv_mfma_bf16_check", "inv_kernel_route", "inv_attention_decode_noalloc",
+           "inv_attention_decode_noalloc_max_bytes")
 
 
 def _check(status, what):
@@ -243,6 +247,22 @@ def inv_attention_decode(Q, Kc, Vc, pos, scale=None, out=None, ws=None):
     _check(LIB.inv_attention_decode(_dtype_code(Q), _p(Q), _p(Kc), _p(Vc), _p(pos), B, Tmax, Hq, Hkv, D,
                                     _scale(D, scale), _p(out), _p(ws), ws.numel() * ws.element_size(),
                                     _stream(Q)), "inv_attention_decode")
+    return out
+
+
+def inv_attention_decode_noalloc_max_bytes():
+    return int(LIB.inv_attention_decode_noalloc_max_bytes())
+
+
+def inv_attention_decode_noalloc(Q, Kc, Vc, pos, out, scale=None):
+    """inv_attention_decode without a workspace (the library's own per-GPU array holds the
+    chunk partials, up to inv_attention_decode_noalloc_max_bytes()); ``out`` [B, Hq, D] FP32 is
+    required, so nothing is allocated here either.  Calls that overlap on one GPU race."""
+    _dev(Q, Kc, Vc, pos, out)
+    B, Hq, D = Q.shape
+    _, Hkv, Tmax, _ = Kc.shape
+    _check(LIB.inv_attention_decode_noalloc(_dtype_code(Q), _p(Q), _p(Kc), _p(Vc), _p(pos), B, Tmax, Hq, Hkv, D,
+                                            _scale(D, scale), _p(out), _stream(Q)), "inv_attention_decode_noalloc")
     return out
 
 

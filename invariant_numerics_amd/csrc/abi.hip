@@ -125,6 +125,22 @@ int inv_attention_decode(int dtype, const void* Q, const void* Kc, const void* V
     return fin(launch_attention_decode(a, pos, reinterpret_cast<float*>(ws), S(stream)));
 }
 
+size_t inv_attention_decode_noalloc_max_bytes(void) { return DECODE_SCRATCH_BYTES; }
+
+int inv_attention_decode_noalloc(int dtype, const void* Q, const void* Kc, const void* Vc, const int32_t* pos,
+                                 int64_t B, int64_t Tmax, int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                                 float* O, void* stream) {
+    if (!pos) return INV_ERR_NULL;
+    int st = check_attn(dtype, Q, Kc, Vc, O, B, 1, 0, Tmax, Hq, Hkv, D);
+    if (st != INV_OK) return st;
+    if (Tmax > (int64_t)4096 * CHUNK) return INV_ERR_UNSUPPORTED;
+    if (inv_attention_decode_workspace_bytes(B, Tmax, Hq, D) > DECODE_SCRATCH_BYTES) return INV_ERR_WORKSPACE;
+    float* ws = nullptr;
+    if (decode_scratch(&ws) != hipSuccess) return INV_ERR_LAUNCH;
+    AttnArgs a{dtype, Q, Kc, Vc, (int)B, 1, 0, (int)Tmax, (int)Hq, (int)Hkv, (int)D, scale, O};
+    return fin(launch_attention_decode(a, pos, ws, S(stream)));
+}
+
 size_t inv_lmhead_workspace_bytes(int64_t B, int64_t K, int64_t V) {
     if (B < 1 || K < 1 || V < 1) return 0;
     return lmhead_ws_bytes(B, K, V);

@@ -15,6 +15,7 @@
 #include "numerics.h"
 #include "kernels.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace invnum {
@@ -710,6 +711,37 @@ hipError_t launch_partial_dt(const AttnArgs& a, const int32_t* pos, float* ws, i
 }
 
 }  // namespace
+
+// Scratch memory of the allocation-free decode entry point: the chunk partials of one call
+// (B * Hq * ceil(Tmax / 256) * (D + 2) floats) for callers that cannot allocate.  Each GPU the
+// library runs on holds its own copy until the process ends; every call on that GPU shares it,
+// so calls that overlap on one GPU race.  Nothing needs clearing: the partial kernel writes
+// every (row, head, chunk) entry the merge reads, in the same call.
+static __device__ __align__(256) unsigned char scratch[DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[MAX_DEVICES];   // device address of `scratch` on each GPU, looked up once
+}  // namespace
+
+// The device address of the current GPU's copy of `scratch`, looked up with that GPU current the
+// first time it is needed (the array's name on the host is only a stand-in for the symbol).
+hipError_t decode_scratch(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *out = reinterpret_cast<float*>(scratch_ptr[dev]);
+    return hipSuccess;
+}
 
 hipError_t launch_attention_decode(const AttnArgs& a, const int32_t* pos, float* ws, hipStream_t st) {
     const int nchunks = (a.Tmax + CHUNK - 1) / CHUNK;

@@ -41,6 +41,10 @@ hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st);
 int attention_prefill_waves(int64_t B, int64_t Tq, int64_t Hq);
 hipError_t launch_attention_decode(const AttnArgs& a, const int32_t* pos, float* ws,
                                    hipStream_t st);
+// size of the library-owned partials array of the allocation-free decode entry point, and its
+// device address on the current GPU
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)32 << 20;
+hipError_t decode_scratch(float** out);
 
 struct LmheadArgs {
     const float* Hs; int B; int K; int64_t ldh;

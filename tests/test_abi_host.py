@@ -132,3 +132,17 @@ def test_kernel_route_names(inv):
     assert inv.LIB.inv_kernel_route(9, 1, 1, ctypes.create_string_buffer(8), 8) == -4
     assert inv.LIB.inv_kernel_route(0, 0, 1, ctypes.create_string_buffer(8), 8) == -2
     assert inv.LIB.inv_kernel_route(0, 1, 1, None, 8) == -1
+
+
+def test_decode_noalloc_rejects_oversized_calls(inv):
+    """The allocation-free decode checks its size against the library's fixed array before
+    anything else: too many rows for the array is INV_ERR_WORKSPACE, nothing launched."""
+    L = inv.LIB
+    cap = inv.inv_attention_decode_noalloc_max_bytes()
+    assert cap == 32 << 20
+    per_row = inv.inv_attention_decode_workspace_bytes(1, 32768, 32, 128)
+    assert per_row * 15 <= cap < per_row * 16
+    f = L.inv_attention_decode_noalloc
+    assert f(1, FAKE, FAKE, FAKE, FAKE, 16, 32768, 32, 8, 128, 1.0, FAKE, None) == -5
+    assert f(1, FAKE, FAKE, FAKE, None, 1, 32768, 32, 8, 128, 1.0, FAKE, None) == -1
+    assert f(1, FAKE, FAKE, FAKE, FAKE, 1, 32768, 32, 8, 64, 1.0, FAKE, None) == -6
