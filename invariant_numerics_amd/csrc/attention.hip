@@ -580,14 +580,24 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
     }
 }
 
-constexpr int MAXCH = 4096;   // chunks per merge workgroup held in LDS (Tmax <= 1M)
+constexpr int MBAT = 32;      // chunk partials requested per register batch of the merge
 
-__global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* __restrict__ pos,
-                                                                int Hq, int Tmax, int nchunks,
-                                                                const float* __restrict__ ws,
-                                                                float* __restrict__ O) {
-    __shared__ __attribute__((aligned(16))) float Mc[MAXCH];
-    __shared__ float Lc[MAXCH], Al[MAXCH], Be[MAXCH], Mr[MAXCH];
+// One workgroup of D threads per (row b, query head h); thread d folds o[d].  The chunk maxima
+// and sums of the row go to LDS sized for the call's chunk count (5 floats per chunk), the
+// running maximum is scanned by one thread exactly as the fold takes it, every chunk's
+// (alpha, beta) pair is evaluated in parallel, and each thread's o_c[d] values are requested
+// MBAT at a time, the next batch while the current one is folded.
+__global__ __launch_bounds__(D) void attn_decode_merge_kernel(const int32_t* __restrict__ pos,
+                                                              int Hq, int Tmax, int nchunks,
+                                                              const float* __restrict__ ws,
+                                                              float* __restrict__ O) {
+    extern __shared__ __attribute__((aligned(16))) float mlds[];
+    const int n4 = (nchunks + 3) & ~3;  // per-array stride, whole float4s
+    float* Mc = mlds;                   // chunk maxima
+    float* Mr = Mc + n4;                // running maximum after chunk c
+    float* Lc = Mr + n4;
+    float* Al = Lc + n4;
+    float* Be = Al + n4;
     const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
     const int p = pos[b];
     if (p < 0 || p >= Tmax) {
@@ -597,17 +607,13 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const int32_t* _
     const int nc = p / CHUNK + 1;
     const int D2 = D + 2;
     const float* src = ws + ((int64_t)b * Hq + h) * nchunks * D2;
-    // chunk partials o_c[d] for c = 1.. stream through two register batches; the first batch
-    // is requested before the maxima are scanned (indices past nc - 1 repeat nc - 1: valid
-    // addresses whose values are never folded)
-    constexpr int MBAT = 32;
+    // the first batch of partials o_c[d], c = 1.., is requested before the maxima are scanned
+    // (indices past nc - 1 repeat nc - 1: valid addresses whose values are never folded)
     float cur[MBAT], nxt[MBAT];
 #pragma unroll
-    for (int u = 0; u < MBAT; ++u) {
-        cur[u] = src[(int64_t)min(1 + u, nc - 1) * D2 + 2 + d];
-        nxt[u] = 0.0f;
-    }
+    for (int u = 0; u < MBAT; ++u) cur[u] = src[(int64_t)min(1 + u, nc - 1) * D2 + 2 + d];
     for (int c = d; c < nc; c += D) { Mc[c] = src[(int64_t)c * D2]; Lc[c] = src[(int64_t)c * D2 + 1]; }
+    for (int c = nc + d; c < ((nc + 3) & ~3); c += D) Mc[c] = 0.0f;   // padding of the last float4
     __syncthreads();
     if (d == 0) {                                 // running maximum, exactly as the fold takes it
         float m = Mc[0];
@@ -748,8 +754,11 @@ hipError_t launch_attention_decode(const AttnArgs& a, const int32_t* pos, float*
     hipError_t e = a.dtype == 1 ? launch_partial_dt<1>(a, pos, ws, nchunks, st)
                                 : launch_partial_dt<0>(a, pos, ws, nchunks, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(a.Hq, a.B), dim3(D), 0, st, pos, a.Hq, a.Tmax,
-                       nchunks, ws, a.O);
+    // LDS: maxima, running maxima, sums and both factors of every chunk (the chunk count
+    // rounded up to whole float4s for the scan's vector reads)
+    const int nch4 = (nchunks + 3) & ~3;
+    hipLaunchKernelGGL(attn_decode_merge_kernel, dim3(a.Hq, a.B), dim3(D), 5 * nch4 * sizeof(float), st, pos,
+                       a.Hq, a.Tmax, nchunks, ws, a.O);
     return hipGetLastError();
 }
 

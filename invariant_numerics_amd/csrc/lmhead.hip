@@ -11,11 +11,12 @@
 //   5. z = fixed-order GEMM(h_F, W) on the first `count` rows (count read on the device)
 //   6. row reduce of those rows; results overwrite the flagged rows' outputs.
 // Up to LM_FUSED_MAX_B rows, the FP32 logits of every row are computed by the same GEMM as
-// the primary ones (operand rows a_P | h, so the weights stream from memory once); step 5
-// disappears and step 6 reads the flagged rows' FP32 logits from the second half of z.  A
-// GEMM row depends on nothing but its own operand row, so these are the same bits as the
-// separate pass.  With tau <= 0 no row can be flagged (margins are >= 0 or NaN), and steps
-// 4-6 are skipped.
+// the primary ones (operand rows a_P | h, so the weights stream from memory once), and one
+// row reduce runs over all 2B logit rows; its last kernel writes, per row, the primary
+// result or, when the primary margin is below tau, the FP32 one.  A GEMM row and a reduced
+// row depend on nothing but their own operand row, so these are the same bits as the
+// separate pass (steps 4-6 disappear).  With tau <= 0 no row can be flagged (margins are
+// >= 0 or NaN), and steps 4-6 are skipped.
 //
 // Row reduce order (identical for both passes):
 //   top1 = lowest index of the maximum; top2 = lowest index != top1 of the maximum of the
@@ -59,28 +60,23 @@ __device__ __forceinline__ void top2_merge(Top2& t, const Top2& o) {
 //                 M = z_top1, then one wavefront per tile of its group sums exp_f(z - M) in the
 //                 pinned lane order and combines the 64 lanes pairwise -> S_u;
 //   final_kernel  one thread per row: S = S_0, S = S + S_u ascending; lp; margin; flags.
-// mode 0: P pass over rows 0..B-1 (output row = row); mode 1: F pass over the first *count
-// rows of the compacted list (output row = idx[row]); mode 2: the same rows, whose FP32
-// logits sit at z row B + idx[row] (computed beside the P ones).
+// mode 0: rows 0..gridDim.y-1 as they are (output row = row); mode 1: F pass over the first
+// *count rows of the compacted list (output row = idx[row]).
 constexpr int GROUP = 4;                 // tiles per workgroup
 constexpr int LM_FUSED_MAX_B = 16;       // batch sizes whose FP32 logits share the primary GEMM
 
-// z row read by reduce row `row`: mode 0 (P pass) the row itself; mode 1 (separate F pass)
-// the compacted row; mode 2 (F logits computed beside the P ones) row zoff + idx[row].
-__device__ __forceinline__ const float* zrow(const float* z, int V, int mode, int row, int zoff,
-                                             const int32_t* idx) {
-    const int r = mode == 2 ? zoff + idx[row] : row;
-    return z + (int64_t)r * V;
+__device__ __forceinline__ const float* zrow(const float* z, int V, int row) {
+    return z + (int64_t)row * V;
 }
 constexpr int GV = GROUP * TV;           // vocabulary entries per workgroup
 
 __global__ __launch_bounds__(RED_THREADS) void lmhead_top2_kernel(
     const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ idx, int zoff, Top2* __restrict__ part) {
+    Top2* __restrict__ part) {
     __shared__ Top2 wtop[RED_THREADS / 64];
     const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
     if (mode != 0 && row >= *count) return;
-    const float* zr = zrow(z, V, mode, row, zoff, idx);
+    const float* zr = zrow(z, V, row);
     const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
     Top2 t = {-__builtin_inff(), 0x7fffffff, -__builtin_inff(), 0x7fffffff};
     const int v0 = grp * GV, v1 = min(V, v0 + GV);
@@ -122,10 +118,10 @@ __device__ __forceinline__ Top2 merged_top2(const Top2* __restrict__ part, int r
 
 __global__ __launch_bounds__(RED_THREADS) void lmhead_tiles_kernel(
     const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
-    const int32_t* __restrict__ idx, int zoff, const Top2* __restrict__ part, float* __restrict__ tileS) {
+    const Top2* __restrict__ part, float* __restrict__ tileS) {
     const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
     if (mode != 0 && row >= *count) return;
-    const float* zr = zrow(z, V, mode, row, zoff, idx);
+    const float* zr = zrow(z, V, row);
     const Top2 t = merged_top2(part, row, ngrp, V);
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
@@ -160,9 +156,32 @@ __device__ __forceinline__ float fold_tiles(const float* __restrict__ ts, int nt
     return S;
 }
 
+struct RowOut {
+    float lp, mg; int t1, t2;
+};
+
+// lp, margin and the top-2 of reduced row `row` (its logits, partial top-2 pairs and tile sums)
+__device__ __forceinline__ RowOut row_result(const float* __restrict__ z, int V, int row, int tg,
+                                             const Top2* __restrict__ part, int ngrp,
+                                             const float* __restrict__ tileS) {
+    const float* zr = zrow(z, V, row);
+    const Top2 t = merged_top2(part, row, ngrp, V);
+    const float M = zr[t.i1];
+    const int ntiles = (V + TV - 1) / TV;
+    const float S = fold_tiles(tileS + (int64_t)row * ntiles, ntiles);
+    RowOut r;
+    r.lp = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
+    r.mg = M - zr[t.i2];
+    r.t1 = t.i1;
+    r.t2 = t.i2;
+    return r;
+}
+
+// mode 0: output row = reduced row, flag = (margin < tau); mode 1: reduced row `row` is the F
+// pass of compacted row idx[row] (flag 1)
 __global__ void lmhead_final_kernel(
     const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau, int mode,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int zoff,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
     const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
     float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
     int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
@@ -170,19 +189,32 @@ __global__ void lmhead_final_kernel(
     if (row >= B) return;
     if (mode != 0 && row >= *count) return;
     const int orow = mode != 0 ? idx[row] : row;
-    const float* zr = zrow(z, V, mode, row, zoff, idx);
-    const Top2 t = merged_top2(part, row, ngrp, V);
-    const float M = zr[t.i1];
-    const int ntiles = (V + TV - 1) / TV;
-    const float S = fold_tiles(tileS + (int64_t)row * ntiles, ntiles);
-    const int tg = target[orow];
-    const float lp = (tg >= 0 && tg < V) ? (zr[tg] - M) - log_f(S) : __builtin_nanf("");
-    const float mg = M - zr[t.i2];
-    logprob[orow] = lp;
-    margin[orow] = mg;
-    top1[orow] = t.i1;
-    top2[orow] = t.i2;
-    recomputed[orow] = (uint8_t)(mode != 0 ? 1 : (mg < tau ? 1 : 0));
+    const RowOut r = row_result(z, V, row, target[orow], part, ngrp, tileS);
+    logprob[orow] = r.lp;
+    margin[orow] = r.mg;
+    top1[orow] = r.t1;
+    top2[orow] = r.t2;
+    recomputed[orow] = (uint8_t)(mode != 0 ? 1 : (r.mg < tau ? 1 : 0));
+}
+
+// Rows 0..B-1 are the primary pass and rows B..2B-1 the FP32 pass of the same hidden states:
+// output row b takes the FP32 result when the primary margin is below tau (strict; NaN never).
+__global__ void lmhead_final_select_kernel(
+    const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau,
+    const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
+    float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
+    int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= B) return;
+    const int tg = target[row];
+    RowOut r = row_result(z, V, row, tg, part, ngrp, tileS);
+    const bool flag = r.mg < tau;
+    if (flag) r = row_result(z, V, B + row, tg, part, ngrp, tileS);
+    logprob[row] = r.lp;
+    margin[row] = r.mg;
+    top1[row] = r.t1;
+    top2[row] = r.t2;
+    recomputed[row] = (uint8_t)(flag ? 1 : 0);
 }
 
 // Logit gradient, step 1: per row M = z_top1 and S (the forward's fold), and the logprob.
@@ -289,26 +321,32 @@ WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
     L.z = off; off = align_up(off + sizeof(float) * (size_t)zrows * V);
     L.idx = off; off = align_up(off + sizeof(int32_t) * (size_t)B);
     L.count = off; off = align_up(off + sizeof(int32_t));
-    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)B * ngrp);
-    L.tiles = off; off = align_up(off + sizeof(float) * (size_t)B * ntiles);
+    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)zrows * ngrp);
+    L.tiles = off; off = align_up(off + sizeof(float) * (size_t)zrows * ntiles);
     L.total = off;
     return L;
+}
+
+// top-2 partials and tile sums of `rows` logit rows (mode 0: all of them; mode 1: the first
+// *count, the compacted F rows)
+hipError_t launch_row_stats(const float* Z, int V, int rows, int mode, const int32_t* count, Top2* part,
+                            float* tiles, hipStream_t st) {
+    const int ngrp = (V + GV - 1) / GV;
+    dim3 grid(ngrp, rows);
+    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, Z, V, mode, count, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, Z, V, mode, count, part, tiles);
+    return hipGetLastError();
 }
 
 hipError_t launch_reduce(const LmheadArgs& a, int mode, const float* Z, const int32_t* idx,
                          const int32_t* count, Top2* part, float* tiles, hipStream_t st) {
     const int ngrp = (a.V + GV - 1) / GV;
-    const int zoff = a.B;                       // mode 2: the F rows follow the B primary rows
-    dim3 grid(ngrp, a.B);
-    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, idx, zoff,
-                       part);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_row_stats(Z, a.V, a.B, mode, count, part, tiles, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, Z, a.V, mode, count, idx, zoff,
-                       part, tiles);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_final_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, Z, a.V, a.B, a.target,
-                       a.tau, mode, idx, count, zoff, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
+                       a.tau, mode, idx, count, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
                        a.recomputed);
     return hipGetLastError();
 }
@@ -350,12 +388,7 @@ hipError_t launch_logit_grad(const LogitGradArgs& a, hipStream_t st) {
     GemmArgs ga{a.Hs, a.B, a.K, a.ldh, a.W, a.V, (int64_t)a.K, nullptr, 0, a.G, (int64_t)a.V, nullptr};
     if ((e = launch_gemm(ga, st, 1)) != hipSuccess) return e;
     const int ngrp = (a.V + GV - 1) / GV;
-    dim3 grid(ngrp, a.B);
-    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, a.G, a.V, 0, nullptr, nullptr, 0, part);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, a.G, a.V, 0, nullptr, nullptr, 0, part,
-                       tiles);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_row_stats(a.G, a.V, a.B, 0, nullptr, part, tiles, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_rowstats_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, a.G, a.V, a.B, a.target,
                        part, ngrp, tiles, stats, a.logprob);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -389,12 +422,20 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     GemmArgs ga{A, rows, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, nullptr};
     if ((e = launch_gemm(ga, st, 1)) != hipSuccess) return e;
 
+    if (fused) {
+        // both passes' rows in one reduce; the last kernel picks each row's pass
+        if ((e = launch_row_stats(Z, a.V, 2 * a.B, 0, nullptr, part, tiles, st)) != hipSuccess) return e;
+        const int ngrp = (a.V + GV - 1) / GV;
+        hipLaunchKernelGGL(lmhead_final_select_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, Z, a.V, a.B,
+                           a.target, a.tau, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
+                           a.recomputed);
+        return hipGetLastError();
+    }
     if ((e = launch_reduce(a, 0, Z, nullptr, nullptr, part, tiles, st)) != hipSuccess) return e;
     if (!recompute) return hipSuccess;
 
     hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, a.recomputed, a.B, idx, count);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (fused) return launch_reduce(a, 2, Z, idx, count, part, tiles, st);
     hipLaunchKernelGGL(gather_rows_kernel, dim3(a.B), dim3(256), 0, st, a.Hs, a.K, a.ldh, idx, count, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
