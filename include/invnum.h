@@ -343,6 +343,26 @@ int inv_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, fl
                         void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * inv_qkv_rope_kv_append -- the QKV projection of a decoder layer followed by the RoPE
+ * rotation and the KV-cache append: bit for bit inv_fixed_order_gemm(X, Wqkv) and then
+ * inv_rope_kv_append (FP32 output format) on its output.  Wqkv is [(Hq + 2 Hkv) D, K] BF16,
+ * q rows | k rows | v rows, as for those calls.  For one to four rows with D = 128 both run
+ * as one GEMV launch: the weight rows of each rotated head are visited in rotate-half pairs
+ * (d, d + 64), whose two outputs are folded by neighbouring threads that rotate and store
+ * them (no change to any sum: the rows are only read in another order); otherwise the
+ * projection goes to the workspace (inv_qkv_rope_kv_append_workspace_bytes, 0 when fused)
+ * and the rotation kernel follows.  Arguments and layouts as for inv_fixed_order_gemm and
+ * inv_rope_kv_append: X [M, K] FP32 (ldx), seq/pos [M] int32 (rows outside the cache are
+ * skipped), tables [Tmax, D/2] FP32, Qout [M, Hq, D], caches [Bcache, Hkv, Tmax, D] FP32.
+ * Errors: INV_ERR_NULL, INV_ERR_SHAPE, INV_ERR_ALIGN, INV_ERR_WORKSPACE, INV_ERR_LAUNCH.
+ * ------------------------------------------------------------------------------------ */
+size_t inv_qkv_rope_kv_append_workspace_bytes(int64_t M, int64_t Hq, int64_t Hkv, int64_t D);
+int inv_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* Wqkv, int64_t ldw,
+                           int64_t Hq, int64_t Hkv, int64_t D, const int32_t* seq, const int32_t* pos,
+                           const float* cos_t, const float* sin_t, int64_t Tmax, int64_t Bcache, float* Qout,
+                           float* Kc, float* Vc, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * inv_kernel_route -- host-only query (enqueues nothing, touches no device): the name of
  * the kernel instantiation that a call with these sizes launches, written as a
  * NUL-terminated string into name[0 .. cap-1] (truncated to fit).  The choice is launch

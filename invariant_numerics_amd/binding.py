@@ -8,6 +8,7 @@ fails, and a non-zero status raises ``InvError``.
 """
 import ctypes
 import os
+import struct
 
 import torch
 
@@ -69,6 +70,9 @@ def _load():
         "inv_mfma_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
         "inv_mfma32_f32_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
         "inv_mfma_bf16_check": (ctypes.c_int, [vp, vp, vp, vp, i64, vp]),
+        "inv_qkv_rope_kv_append_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64, i64]),
+        "inv_qkv_rope_kv_append": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, i64, i64, i64, vp, vp, vp, vp, i64,
+                                                  i64, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "inv_kernel_route": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_char_p, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
@@ -86,7 +90,8 @@ EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "in
            "inv_lmhead_logit_grad", "inv_gemm_backward_workspace_bytes",
            "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check",
            "inv_mfma_bf16_check", "inv_kernel_route", "inv_attention_decode_noalloc",
-           "inv_attention_decode_noalloc_max_bytes")
+           "inv_attention_decode_noalloc_max_bytes", "inv_qkv_rope_kv_append_workspace_bytes",
+           "inv_qkv_rope_kv_append")
 
 
 def _check(status, what):
@@ -205,6 +210,31 @@ def inv_rmsnorm(X, gamma, eps=1e-5, out=None):
     return out
 
 
+def _ws(need, ws, dev):
+    if need == 0:
+        return None
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    return ws
+
+
+def inv_qkv_rope_kv_append(X, Wqkv, Hq, Hkv, D, seq, pos, cos_t, sin_t, Qout, Kc, Vc, ws=None):
+    """QKV projection of X (fp32 [M, K]) with RoPE and the KV append (FP32): Qout [M, Hq, D]
+    and the caches [Bcache, Hkv, Tmax, D] are written; one launch for up to four rows."""
+    _dev(X, Wqkv, seq, pos, cos_t, sin_t, Qout, Kc, Vc, ws)
+    _f32(X)
+    _bf16(Wqkv)
+    M, K = X.shape
+    Bc, _, Tmax, _ = Kc.shape
+    need = int(LIB.inv_qkv_rope_kv_append_workspace_bytes(M, Hq, Hkv, D))
+    ws = _ws(need, ws, X.device)
+    _check(LIB.inv_qkv_rope_kv_append(_p(X), M, K, _row_ld(X), _p(Wqkv), _row_ld(Wqkv), Hq, Hkv, D, _p(seq), _p(pos),
+                                      _p(cos_t), _p(sin_t), Tmax, Bc, _p(Qout), _p(Kc), _p(Vc), _p(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(X)),
+           "inv_qkv_rope_kv_append")
+    return Qout
+
+
 def _dtype_code(t):
     if t.dtype == torch.float32:
         return INV_F32
@@ -212,10 +242,15 @@ def _dtype_code(t):
     return INV_BF16
 
 
+# the pinned attention scale RN(1 / sqrt(128)) (head dim 128, the only one the library runs)
+SCALE_D128 = struct.unpack("<f", struct.pack("<I", 0x3DB504F3))[0]
+
+
 def _scale(D, scale):
     if scale is None:
-        scale = float(torch.tensor(1.0, dtype=torch.float32) / torch.sqrt(torch.tensor(float(D),
-                                                                                    dtype=torch.float32)))
+        if D != 128:
+            raise InvError("head dim 128 expected (pass scale explicitly otherwise)")
+        scale = SCALE_D128
     return float(scale)
 
 

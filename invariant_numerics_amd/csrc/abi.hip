@@ -83,6 +83,38 @@ int inv_rmsnorm(const float* X, int64_t M, int64_t H, int64_t ldx, const uint16_
     return fin(launch_rmsnorm(X, (int)M, (int)H, ldx, gamma, eps, Y, ldy, S(stream)));
 }
 
+size_t inv_qkv_rope_kv_append_workspace_bytes(int64_t M, int64_t Hq, int64_t Hkv, int64_t D) {
+    if (M < 1 || Hq < 1 || Hkv < 0 || D < 1) return 0;
+    if (qkv_rope_fusable(M, D)) return 0;
+    return sizeof(float) * (size_t)(M * (Hq + 2 * Hkv) * D);
+}
+
+int inv_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* Wqkv, int64_t ldw,
+                           int64_t Hq, int64_t Hkv, int64_t D, const int32_t* seq, const int32_t* pos,
+                           const float* cos_t, const float* sin_t, int64_t Tmax, int64_t Bcache, float* Qout,
+                           float* Kc, float* Vc, void* ws, size_t ws_bytes, void* stream) {
+    if (!X || !Wqkv || !seq || !pos || !cos_t || !sin_t || !Qout || !Kc || !Vc) return INV_ERR_NULL;
+    if (M < 1 || K < 8 || K % 8 != 0 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 != 0 || Tmax < 1 || Bcache < 1 ||
+        ldx < K || ldw < K || M > I32MAX || K > I32MAX || Tmax > I32MAX || Bcache > I32MAX ||
+        (Hq + 2 * Hkv) * D > I32MAX)
+        return INV_ERR_SHAPE;
+    if (!al16(X) || !al16(Wqkv) || ldx % 4 || ldw % 8) return INV_ERR_ALIGN;
+    const int64_t N = (Hq + 2 * Hkv) * D;
+    const size_t need = inv_qkv_rope_kv_append_workspace_bytes(M, Hq, Hkv, D);
+    if (need && (!ws || ws_bytes < need)) return INV_ERR_WORKSPACE;
+    if (need && !al16(ws)) return INV_ERR_ALIGN;
+    if (!need) {
+        GemmArgs a{X, (int)M, (int)K, ldx, Wqkv, (int)N, ldw, nullptr, 0, nullptr, 0, nullptr};
+        RopeArgs ra{(int)Hq, (int)Hkv, seq, pos, cos_t, sin_t, (int)Tmax, (int)Bcache, Qout, Kc, Vc};
+        return fin(launch_qkv_rope(a, ra, S(stream)));
+    }
+    float* qkv = reinterpret_cast<float*>(ws);
+    GemmArgs a{X, (int)M, (int)K, ldx, Wqkv, (int)N, ldw, nullptr, 0, qkv, N, nullptr};
+    if (launch_gemm(a, S(stream), 0) != hipSuccess) return INV_ERR_LAUNCH;
+    return fin(launch_rope_kv_append(qkv, (int)M, N, (int)Hq, (int)Hkv, (int)D, seq, pos, cos_t, sin_t, (int)Tmax,
+                                     (int)Bcache, Qout, Kc, Vc, INV_F32, S(stream)));
+}
+
 static int check_attn(int dtype, const void* Q, const void* Kc, const void* Vc, const float* O,
                       int64_t B, int64_t Tq, int64_t q_start, int64_t Tmax, int64_t Hq, int64_t Hkv,
                       int64_t D) {

@@ -438,9 +438,9 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
     }
 }
 
-// 32 x 32 tiles for M <= 32 (a 64-row tile would be half padding) and for M <= 64 when the
-// 64 x 64 grid would have fewer than SMALL_BELOW tiles
-constexpr int64_t SMALL_BELOW = 256;
+// 32 x 32 tiles when the 64 x 64 grid would have fewer than SMALL_BELOW tiles (two per CU;
+// one per CU for M <= 64)
+constexpr int64_t SMALL_BELOW = 512;
 
 template <int ROLE>
 hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
@@ -464,21 +464,23 @@ hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
 // lane group g reads it (k = 4 s + g for s = 0..CH/4-1: CH/2 contiguous bytes), the
 // activation tile as FP32 in the same order.  Measured: 64-wide chunks are best or equal on
 // every decoder shape (128-wide ones halve the workgroups a CU holds at N >= 12288).
-template <int WN, int PD, int CH, int ROLE, int MT>
-__global__ __launch_bounds__(256) void gemm_gemv16_kernel(
+template <int WN, int PD, int CH, int ROLE, int MT, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
     float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    constexpr int WK = 4 / WN;
+    constexpr int NT = 64 * NW;                  // threads
+    constexpr int WK = NW / WN;
     constexpr int BN = 16 * WN;
     constexpr int NSTEP = CH / 4;                // matrix steps per chunk
     constexpr int WSEG = CH * 2 + 16;            // bytes per (weight row, slice) segment (+ pad)
     constexpr int XSEG = CH + 4;                 // floats per (activation row, slice) segment (+ pad)
-    constexpr int WUN = BN * WK * CH / 8 / 256;  // 16-byte weight loads per thread and chunk
+    constexpr int WUN = BN * WK * CH / 8 / NT;   // 16-byte weight loads per thread and chunk
     constexpr int MR = 16 * MT;                  // activation rows (MT row tiles of 16)
-    constexpr int XU = MR * WK * CH / 4 / 256;   // activation float4 per thread and chunk
+    constexpr int XU = MR * WK * CH / 4 / NT;    // activation float4 per thread and chunk
+    static_assert(BN * WK * CH % (8 * NT) == 0 && MR * WK * CH % (4 * NT) == 0, "tile / thread split");
     __shared__ __attribute__((aligned(16))) unsigned char Wl[2][BN * WK * WSEG];
     __shared__ __attribute__((aligned(16))) float Xl[2][MR * WK * XSEG];
     __shared__ __attribute__((aligned(16))) float part[WK > 1 ? WK * WN * MT * 64 * 4 : 4];
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         const int rd = it / (KS / CH), c = it % (KS / CH);
 #pragma unroll
         for (int i = 0; i < WUN; ++i) {
-            const int q = tid + 256 * i;
+            const int q = tid + NT * i;
             const int c8 = q % (CH / 8), rest = q / (CH / 8);
             const int sk = rest % WK, rr = rest / WK;
             const int k = (rd * WK + sk) * KS + c * CH + 8 * c8;
@@ -514,7 +516,7 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         }
 #pragma unroll
         for (int j = 0; j < XU; ++j) {
-            const int u = tid + 256 * j;
+            const int u = tid + NT * j;
             const int q4 = u % (CH / 4), rest = u / (CH / 4);
             const int sk = rest % WK, m = rest / WK;
             const int k = (rd * WK + sk) * KS + c * CH + 4 * q4;
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
     auto store = [&](int buf, const uint4 (&wq)[WUN], const float4 (&xq)[XU]) {
 #pragma unroll
         for (int i = 0; i < WUN; ++i) {
-            const int q = tid + 256 * i;
+            const int q = tid + NT * i;
             const int c8 = q % (CH / 8), rest = q / (CH / 8);
             // segments slice-major (sk, row): the 16 rows a lane group reads are WSEG apart,
             // which spreads a 16-lane quarter's 16-byte reads over all 64 banks
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         }
 #pragma unroll
         for (int j = 0; j < XU; ++j) {
-            const int u = tid + 256 * j;
+            const int u = tid + NT * j;
             const int q4 = u % (CH / 4), rest = u / (CH / 4);
             float* seg = &Xl[buf][((rest % WK) * MR + rest / WK) * XSEG + q4];
             seg[0 * NSTEP] = xq[j].x;
@@ -689,10 +691,10 @@ __global__ __launch_bounds__(256) void gemm_gemv16_kernel(
         }
 }
 
-template <int WN, int PD, int CH, int ROLE, int MT = 1>
+template <int WN, int PD, int CH, int ROLE, int MT = 1, int NW = 4>
 hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st) {
     dim3 grid((a.N + 16 * WN - 1) / (16 * WN));
-    hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, CH, ROLE, MT>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, CH, ROLE, MT, NW>), grid, dim3(64 * NW), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
 }
@@ -716,13 +718,24 @@ constexpr int SK_LANES = 16;  // slices per group
 constexpr int PH = 64;        // elements per slice per phase
 constexpr int WSEG = PH * 2 + 16;   // padded bytes per (row, slice) segment in LDS
 constexpr int XLD = PH + 4;         // padded floats per (m, slice) activation segment
+constexpr int RD = 128;             // rotary head dim of the fused QKV projection
+
+// ROLE 3 (QKV projection with RoPE and KV append): weight row of logical output o.  Within
+// each rotated (q or k) head the outputs run over the rotate-half pairs, (d = 0, d = 64),
+// (1, 65), ..., so a pair's two outputs sit on adjacent folding threads; value rows keep
+// their order.
+__device__ __forceinline__ int qkv_row(int o, int rot) {
+    if (o >= rot) return o;
+    const int j = o & (RD - 1), pr = j >> 1;
+    return (o & ~(RD - 1)) + ((j & 1) ? pr + RD / 2 : pr);
+}
 
 template <int MB, int ROLE, int ROWS>
 __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
-    float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev) {
+    float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev, RopeArgs ra) {
     constexpr int NT = ROWS * SK_LANES;          // threads
     constexpr int XU = SK_LANES * (PH / 4) / NT; // activation float4 per thread, row and phase
     __shared__ __attribute__((aligned(16))) unsigned char Wl[ROWS * SK_LANES * WSEG];
@@ -735,6 +748,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const int sl = tid % SK_LANES;
     const int nl = tid / SK_LANES;
     const int n0 = blockIdx.x * ROWS;
+    const int rot = ROLE == 3 ? (ra.Hq + ra.Hkv) * RD : 0;     // rotated outputs (ROLE 3)
 
     // load duty: 8 x 16 bytes of weights and MB * XU x 16 bytes of activations per thread and
     // phase; DEPTH phases are in flight in registers (two when the activation tile is small).
@@ -756,7 +770,9 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
             const int seg = q >> 3, c8 = q & 7;   // segment (row, slice) and chunk in it
             const int rn = seg >> 4, ss = seg & 15;
             const int k = (sg + ss) * KS + p * PH + 8 * c8;
-            wp[i] = *reinterpret_cast<const u32x4v*>(W + (int64_t)min(n0 + rn, N - 1) * ldw + min(k, K - 8));
+            int wrow = min(n0 + rn, N - 1);
+            if constexpr (ROLE == 3) wrow = qkv_row(wrow, rot);
+            wp[i] = *reinterpret_cast<const u32x4v*>(W + (int64_t)wrow * ldw + min(k, K - 8));
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
@@ -875,6 +891,36 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
         }
         return;
     }
+    if constexpr (ROLE == 3) {
+        // RoPE and KV append: a rotate-half pair (x_i, x_{i+64}) sits on threads fr, fr ^ 1;
+        // y_i = x_i c - x_{i+64} s and y_{i+64} = x_i s + x_{i+64} c, each product rounded, as
+        // the standalone RoPE kernel computes them.  q goes to Qout [M, Hq, 128], rotated k and
+        // plain v into the caches at (seq[m], pos[m]); a row outside the cache is skipped.
+        const float other = __shfl_xor(T, 1);
+        const int o = n0 + fr;
+        if (folder && fm < M && o < N) {
+            const int p = ra.pos[fm], sq = ra.seq[fm];
+            if (p >= 0 && p < ra.Tmax && sq >= 0 && sq < ra.Bcache) {
+                const int head = o / RD;
+                if (o < rot) {
+                    const int j = o & (RD - 1), i = j >> 1, hi = j & 1;
+                    const float a = hi ? other : T, b = hi ? T : other;
+                    const float cs = ra.cos_t[(int64_t)p * (RD / 2) + i];
+                    const float sn = ra.sin_t[(int64_t)p * (RD / 2) + i];
+                    const float y = hi ? (a * sn) + (b * cs) : (a * cs) - (b * sn);
+                    const int d = hi ? i + RD / 2 : i;
+                    if (head < ra.Hq)
+                        ra.Qout[((int64_t)fm * ra.Hq + head) * RD + d] = y;
+                    else
+                        ra.Kc[(((int64_t)sq * ra.Hkv + head - ra.Hq) * ra.Tmax + p) * RD + d] = y;
+                } else {
+                    const int gv = head - ra.Hq - ra.Hkv, d = o & (RD - 1);
+                    ra.Vc[(((int64_t)sq * ra.Hkv + gv) * ra.Tmax + p) * RD + d] = T;
+                }
+            }
+        }
+        return;
+    }
     if (folder) {
         const int gn = n0 + fr;
         if (fm < M && gn < N) {
@@ -894,10 +940,10 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
 }
 
 template <int MB, int ROLE, int ROWS>
-hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra = RopeArgs{}) {
     dim3 grid((a.N + ROWS - 1) / ROWS);
     hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, ROWS>), grid, dim3(ROWS * SK_LANES), 0, st,
-                       a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
+                       a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev, ra);
     return hipGetLastError();
 }
 
@@ -914,10 +960,11 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
 //   17 <= M <= 32: the same with two row tiles (measured faster than the 32 x 32 tiles, or
 //     equal, at every decoder shape); 33 <= M <= 64 with N of 1024 to 4096: four row tiles
 //     (1.4-1.6x faster there than the tiled kernels, slower at larger N);
-//   other M <= 64: 32 x 32 tiles when the 64 x 64 grid would have fewer than SMALL_BELOW
-//     tiles, else 64 x 64;
-//   M > 64: 128 x 256 when that gives at least one workgroup per CU, else 64 x 64 (e.g.
-//     M = 512, N = 4096: 64 large tiles, 512 small ones, 3x faster).
+//   other M: 32 x 32 tiles while the 64 x 64 grid would have fewer than SMALL_BELOW (512)
+//     tiles, two per CU (256 for M <= 64) (M = 128 / 257 at N = 4096: 1.36 / 1.29x faster
+//     than 64 x 64, and the same for the down projection; equal or slower from 512 tiles on);
+//   M > 64 otherwise: 128 x 256 when that gives at least one workgroup per CU, else 64 x 64
+//     (e.g. M = 512, N = 4096: 64 large tiles, 512 small ones, 3x faster).
 GemmRoute gemm_route(int64_t M, int64_t N) {
     if (M <= 1) return N < 16 * 1024 ? GR_SKINNY_M1_R4 : GR_SKINNY_M1_R16;
     if (M <= 2) return N < 16 * 1024 ? GR_SKINNY_M2_R4 : GR_SKINNY_M2_R16;
@@ -927,7 +974,7 @@ GemmRoute gemm_route(int64_t M, int64_t N) {
     if (M <= 64 && N >= 1024 && N <= 4096) return GR_GEMV64;
     const int64_t big = ((M + 127) / 128) * ((N + 255) / 256);
     const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
-    if (M <= 64 && mid < SMALL_BELOW) return GR_SMALL32;
+    if (mid < (M <= 64 ? SMALL_BELOW / 2 : SMALL_BELOW)) return GR_SMALL32;
     if (M <= 64 || big < 256) return GR_TILE64;
     return GR_TILE128x256;
 }
@@ -972,6 +1019,22 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         case GR_SMALL32: return launch_small<ROLE>(a, st);
         case GR_TILE64: return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
         case GR_TILE128x256: return launch_tiled<128, 256, 2, 4, ROLE>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool qkv_rope_fusable(int64_t M, int64_t D) { return M >= 1 && M <= 4 && D == RD; }
+
+// the QKV projection of up to four rows with RoPE and the KV append in the VALU GEMV's epilogue
+// (same weight rows per workgroup as the plain projection of these sizes)
+hipError_t launch_qkv_rope(const GemmArgs& a, const RopeArgs& ra, hipStream_t st) {
+    if (!qkv_rope_fusable(a.M, RD)) return hipErrorInvalidValue;
+    switch (gemm_route(a.M, a.N)) {
+        case GR_SKINNY_M1_R4: return launch_skinny<1, 3, 4>(a, st, ra);
+        case GR_SKINNY_M1_R16: return launch_skinny<1, 3, 16>(a, st, ra);
+        case GR_SKINNY_M2_R4: return launch_skinny<2, 3, 4>(a, st, ra);
+        case GR_SKINNY_M2_R16: return launch_skinny<2, 3, 16>(a, st, ra);
+        case GR_SKINNY_M4_R16: return launch_skinny<4, 3, 16>(a, st, ra);
         default: return hipErrorInvalidValue;
     }
 }

@@ -7,6 +7,15 @@
 
 namespace invnum {
 
+// RoPE and KV-append targets of the fused QKV projection (role 3): rotary head dim 128
+struct RopeArgs {
+    int Hq, Hkv;
+    const int32_t* seq; const int32_t* pos;
+    const float* cos_t; const float* sin_t;   // [Tmax, 64]
+    int Tmax, Bcache;
+    float* Qout; float* Kc; float* Vc;
+};
+
 struct GemmArgs {
     const float* X; int M; int K; int64_t ldx;
     const uint16_t* W; int N; int64_t ldw;
@@ -25,6 +34,10 @@ enum GemmRoute : int {
 };
 GemmRoute gemm_route(int64_t M, int64_t N);
 const char* gemm_route_name(GemmRoute r);   // kernel template with ROLE left symbolic
+// QKV projection of up to four rows (head dim 128) with RoPE and the KV append done by the
+// VALU GEMV's epilogue (role 3); the caller runs the projection and rope_kv_append otherwise
+bool qkv_rope_fusable(int64_t M, int64_t D);
+hipError_t launch_qkv_rope(const GemmArgs& a, const RopeArgs& ra, hipStream_t st);
 
 hipError_t launch_rmsnorm(const float* X, int M, int H, int64_t ldx, const uint16_t* g, float eps,
                           float* Y, int64_t ldy, hipStream_t st);

@@ -103,11 +103,18 @@ class Decoder:
         x = inv.inv_embed(ids, self.emb)
         n = torch.empty_like(x)
         q = torch.empty((M, Hq, D), dtype=torch.float32, device=self.dev)
+        # up to four rows (decode): RoPE with the KV append runs in the QKV projection's epilogue
+        # (same bits, one launch fewer per layer)
+        fused = M <= 4 and self.gemm_events is None
         for li, w in enumerate(self.layers):
             inv.inv_rmsnorm(x, w["g1"], self.eps, out=n)
-            qkv = self._gemm(n, w["wqkv"])
-            inv.inv_rope_kv_append(qkv, Hq, Hkv, D, seq, pos, self.cos, self.sin, q, self.kc[li], self.vc[li])
-            del qkv
+            if fused:
+                inv.inv_qkv_rope_kv_append(n, w["wqkv"], Hq, Hkv, D, seq, pos, self.cos, self.sin, q,
+                                           self.kc[li], self.vc[li])
+            else:
+                qkv = self._gemm(n, w["wqkv"])
+                inv.inv_rope_kv_append(qkv, Hq, Hkv, D, seq, pos, self.cos, self.sin, q, self.kc[li], self.vc[li])
+                del qkv
             att = attend(q, li)
             self._gemm(att.view(M, Hq * D), w["wo"], R=x, out=x)
             del att

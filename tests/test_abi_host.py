@@ -120,6 +120,9 @@ def test_kernel_route_names(inv):
     assert r("gemm", 64, 8192) == "gemm_small_kernel<0>"
     assert r("gemm", 64, 16384) == "gemm_mfma_kernel<64,64,2,2,0>"
     assert r("gemm", 512, 4096) == "gemm_mfma_kernel<64,64,2,2,0>"
+    assert r("gemm", 257, 4096) == "gemm_small_kernel<0>"
+    assert r("gemm", 128, 4096) == "gemm_small_kernel<0>"
+    assert r("gemm", 257, 14336) == "gemm_mfma_kernel<64,64,2,2,0>"
     assert r("gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,0>"
     assert r("gemm", 16384, 6144) == "gemm_mfma_kernel<128,256,2,4,0>"
     assert r("gated_gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,2>"

@@ -171,3 +171,17 @@ def test_constants_are_exact_roundings(orc):
            [float(hi16), exact.rn32(ln2 - hi16)] + [exact.rn32(Fraction(2, 2 * k + 1)) for k in range(1, 6)]
     assert [exact.bits32(float(v)) for v in fc] == [exact.bits32(v) for v in want]
     assert list(ic) == [256, 256, 1024, 64]
+
+
+def test_attention_scale_is_exact_rounding():
+    """The attention scale is RN(1/sqrt(128)) = 0x3DB504F3 (exact rational rounding of
+    sqrt(2)/16), the value the binding passes by default and the oracle computes as
+    1/sqrt(128) in binary32."""
+    import decimal
+    from fractions import Fraction
+    decimal.getcontext().prec = 60
+    want = exact.rn32(Fraction(decimal.Decimal(2).sqrt() / 16))
+    assert exact.bits32(want) == 0x3DB504F3
+    assert (np.float32(1.0) / np.sqrt(np.float32(128))).view(np.uint32) == 0x3DB504F3
+    from invariant_numerics_amd import binding
+    assert exact.bits32(binding.SCALE_D128) == 0x3DB504F3
