@@ -580,13 +580,16 @@ __global__ __launch_bounds__(256) void attn_decode_partial_kernel(
     }
 }
 
-constexpr int MBAT = 32;      // chunk partials requested per register batch of the merge
+constexpr int MB1 = 128;      // chunk partials requested at once (a 32k context: 128 chunks)
+constexpr int MBAT = 32;      // further partials per register batch beyond those
+constexpr int MFG = 16;       // merge factors read from LDS per group
 
 // One workgroup of D threads per (row b, query head h); thread d folds o[d].  The chunk maxima
 // and sums of the row go to LDS sized for the call's chunk count (5 floats per chunk), the
-// running maximum is scanned by one thread exactly as the fold takes it, every chunk's
-// (alpha, beta) pair is evaluated in parallel, and each thread's o_c[d] values are requested
-// MBAT at a time, the next batch while the current one is folded.
+// running maximum is scanned by one thread exactly as the fold takes it, and every chunk's
+// (alpha, beta) pair is evaluated in parallel.  Each thread requests its first MB1 partials
+// o_c[d] in one go, before the scan (a 32k context needs no more), and further ones MBAT at a
+// time, the next batch while the current one is folded.
 __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const int32_t* __restrict__ pos,
                                                               int Hq, int Tmax, int nchunks,
                                                               const float* __restrict__ ws,
@@ -607,11 +610,11 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const int32_t* __r
     const int nc = p / CHUNK + 1;
     const int D2 = D + 2;
     const float* src = ws + ((int64_t)b * Hq + h) * nchunks * D2;
-    // the first batch of partials o_c[d], c = 1.., is requested before the maxima are scanned
-    // (indices past nc - 1 repeat nc - 1: valid addresses whose values are never folded)
-    float cur[MBAT], nxt[MBAT];
+    // partials o_c[d] of chunks 1 .. MB1 (indices past nc - 1 repeat nc - 1: valid addresses
+    // whose values are never folded)
+    float ov[MB1];
 #pragma unroll
-    for (int u = 0; u < MBAT; ++u) cur[u] = src[(int64_t)min(1 + u, nc - 1) * D2 + 2 + d];
+    for (int u = 0; u < MB1; ++u) ov[u] = src[(int64_t)min(1 + u, nc - 1) * D2 + 2 + d];
     for (int c = d; c < nc; c += D) { Mc[c] = src[(int64_t)c * D2]; Lc[c] = src[(int64_t)c * D2 + 1]; }
     for (int c = nc + d; c < ((nc + 3) & ~3); c += D) Mc[c] = 0.0f;   // padding of the last float4
     __syncthreads();
@@ -636,35 +639,47 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const int32_t* __r
     }
     __syncthreads();
     float l = Lc[0], o = src[2 + d];
-    for (int c0 = 1; c0 < nc; c0 += MBAT) {
-        if (c0 + MBAT < nc) {
+    // chunks 1 .. MB1 from the registers requested first; the factors of MFG chunks are read
+    // from LDS ahead of their part of the serial fold
 #pragma unroll
-            for (int u = 0; u < MBAT; ++u) nxt[u] = src[(int64_t)min(c0 + MBAT + u, nc - 1) * D2 + 2 + d];
-        }
-        // this batch's factors, read from LDS ahead of the serial fold
-        float fa[MBAT], fb[MBAT], fl[MBAT];
+    for (int g0 = 0; g0 < MB1; g0 += MFG) {
+        if (1 + g0 < nc) {
+            float fa[MFG], fb[MFG], fl[MFG];
 #pragma unroll
-        for (int u = 0; u < MBAT; ++u) {
-            const int cc = min(c0 + u, nc - 1);
-            fa[u] = Al[cc]; fb[u] = Be[cc]; fl[u] = Lc[cc];
-        }
-        if (c0 + MBAT <= nc) {
-#pragma unroll
-            for (int u = 0; u < MBAT; ++u) {
-                l = (l * fa[u]) + (fl[u] * fb[u]);
-                o = (o * fa[u]) + (cur[u] * fb[u]);
+            for (int u = 0; u < MFG; ++u) {
+                const int cc = min(1 + g0 + u, nc - 1);
+                fa[u] = Al[cc]; fb[u] = Be[cc]; fl[u] = Lc[cc];
             }
-        } else {
 #pragma unroll
-            for (int u = 0; u < MBAT; ++u) {
-                if (c0 + u < nc) {
+            for (int u = 0; u < MFG; ++u) {
+                if (1 + g0 + u < nc) {
                     l = (l * fa[u]) + (fl[u] * fb[u]);
-                    o = (o * fa[u]) + (cur[u] * fb[u]);
+                    o = (o * fa[u]) + (ov[g0 + u] * fb[u]);
                 }
             }
         }
+    }
+    // longer contexts: the remaining chunks, MBAT partials at a time
+    if (1 + MB1 < nc) {
+        float cur[MBAT], nxt[MBAT];
 #pragma unroll
-        for (int u = 0; u < MBAT; ++u) cur[u] = nxt[u];
+        for (int u = 0; u < MBAT; ++u) cur[u] = src[(int64_t)min(1 + MB1 + u, nc - 1) * D2 + 2 + d];
+        for (int c0 = 1 + MB1; c0 < nc; c0 += MBAT) {
+            if (c0 + MBAT < nc) {
+#pragma unroll
+                for (int u = 0; u < MBAT; ++u) nxt[u] = src[(int64_t)min(c0 + MBAT + u, nc - 1) * D2 + 2 + d];
+            }
+#pragma unroll
+            for (int u = 0; u < MBAT; ++u) {
+                const int cc = c0 + u;
+                if (cc < nc) {
+                    l = (l * Al[cc]) + (Lc[cc] * Be[cc]);
+                    o = (o * Al[cc]) + (cur[u] * Be[cc]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < MBAT; ++u) cur[u] = nxt[u];
+        }
     }
     O[((int64_t)b * Hq + h) * D + d] = o / l;
 }

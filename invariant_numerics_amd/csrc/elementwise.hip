@@ -13,17 +13,22 @@ namespace {
 // 16-byte loads (up to 4 per thread in flight, together with the gains they will meet);
 // thread s then runs the slice chain ss_s = fma(x_k, x_k, ss_s) over k in slice s
 // (ascending); thread 0 folds the slices in order and evaluates r = 1 / sqrt(ss / H + eps);
-// finally every thread writes y_k = (x_k * r) * up(g_k).
+// finally every thread writes y_k = (x_k * r) * up(g_k).  In LDS each 256-float slice is
+// followed by 4 floats of padding (x_k at k + 4 (k / 256)), so the chain threads' reads fall on
+// different banks, and each chain reads 64 elements ahead of its fused multiply-adds.
 constexpr int RN_T = 256;     // threads per row
 constexpr int RN_U = 4;       // float4 per thread per batch
+constexpr int RN_PAD = 4;     // floats of padding after each slice in LDS
+constexpr int RN_CH = 16;     // float4 read ahead by a chain thread
+__device__ __forceinline__ int rn_at(int k) { return k + RN_PAD * (k / KS); }
 
 __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(const float* __restrict__ X, int H, int64_t ldx,
                                                        const uint16_t* __restrict__ g, float eps,
                                                        float* __restrict__ Y, int64_t ldy) {
-    extern __shared__ float lds[];  // [H] row, then [S] slice partials, then r
+    extern __shared__ float lds[];  // [H + 4 S] padded row, then [S] slice partials, then r
     const int S = (H + KS - 1) / KS;
     float* xs = lds;
-    float* part = lds + H;
+    float* part = lds + H + RN_PAD * S;
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const float* x = X + (int64_t)row * ldx;
@@ -37,7 +42,7 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(const float* __restrict__
 #pragma unroll
         for (int u = 0; u < RN_U; ++u) {
             const int i = i0 + u * RN_T * 4;
-            if (i < H) *reinterpret_cast<float4*>(xs + i) = v[u];
+            if (i < H) *reinterpret_cast<float4*>(xs + rn_at(i)) = v[u];
         }
     }
     // the first batch of gains is requested before the reduction and used after it
@@ -49,14 +54,22 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(const float* __restrict__
     }
     __syncthreads();
     for (int s = tid; s < S; s += RN_T) {
-        const int k0 = s * KS, k1 = min(H, k0 + KS);
+        const int n = min(KS, H - s * KS);       // a multiple of 8
+        const float* sx = xs + s * (KS + RN_PAD);
         float c = 0.0f;
-        for (int k = k0; k < k1; k += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(xs + k);
-            c = __builtin_fmaf(v.x, v.x, c);
-            c = __builtin_fmaf(v.y, v.y, c);
-            c = __builtin_fmaf(v.z, v.z, c);
-            c = __builtin_fmaf(v.w, v.w, c);
+        for (int kb = 0; kb < n; kb += 4 * RN_CH) {
+            float4 v[RN_CH];
+#pragma unroll
+            for (int u = 0; u < RN_CH; ++u) v[u] = *reinterpret_cast<const float4*>(sx + min(kb + 4 * u, n - 4));
+#pragma unroll
+            for (int u = 0; u < RN_CH; ++u) {
+                if (kb + 4 * u < n) {
+                    c = __builtin_fmaf(v[u].x, v[u].x, c);
+                    c = __builtin_fmaf(v[u].y, v[u].y, c);
+                    c = __builtin_fmaf(v[u].z, v[u].z, c);
+                    c = __builtin_fmaf(v[u].w, v[u].w, c);
+                }
+            }
         }
         part[s] = c;
     }
@@ -80,7 +93,7 @@ __global__ __launch_bounds__(RN_T) void rmsnorm_kernel(const float* __restrict__
         for (int u = 0; u < RN_U; ++u) {
             const int i = i0 + u * RN_T * 4;
             if (i < H) {
-                const float4 v = *reinterpret_cast<const float4*>(xs + i);
+                const float4 v = *reinterpret_cast<const float4*>(xs + rn_at(i));
                 float4 o;
                 o.x = (v.x * r) * bf16_lo(gg[u].x);
                 o.y = (v.y * r) * bf16_hi(gg[u].x);
@@ -301,7 +314,7 @@ inline int grid_for(int64_t work, int block) {
 hipError_t launch_rmsnorm(const float* X, int M, int H, int64_t ldx, const uint16_t* g, float eps,
                           float* Y, int64_t ldy, hipStream_t st) {
     const int S = (H + KS - 1) / KS;
-    const size_t lds = sizeof(float) * ((size_t)H + S + 1);
+    const size_t lds = sizeof(float) * ((size_t)H + RN_PAD * S + S + 1);
     hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(RN_T), lds, st, X, H, ldx, g, eps, Y, ldy);
     return hipGetLastError();
 }

@@ -956,7 +956,9 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra =
 //   5 <= M <= 16: the matrix-core GEMV with one 16-row tile (the VALU GEMV's per-row
 //     accumulators and LDS reads make it slower from 5 rows on); weight rows per workgroup:
 //     64 from N = 65536 (four wavefronts along the rows), 32 from 12288 (two along the rows,
-//     two along K), else 16 with the slices split over four wavefronts;
+//     two along K), else 16 with the slices split over four wavefronts, or over eight for
+//     N = 2048..4096, where there are only N / 16 workgroups (12-18% faster at N = 4096 for
+//     K = 4096 and 14336, slower at N = 6144);
 //   17 <= M <= 32: the same with two row tiles (measured faster than the 32 x 32 tiles, or
 //     equal, at every decoder shape); 33 <= M <= 64 with N of 1024 to 4096: four row tiles
 //     (1.4-1.6x faster there than the tiled kernels, slower at larger N);
@@ -969,7 +971,11 @@ GemmRoute gemm_route(int64_t M, int64_t N) {
     if (M <= 1) return N < 16 * 1024 ? GR_SKINNY_M1_R4 : GR_SKINNY_M1_R16;
     if (M <= 2) return N < 16 * 1024 ? GR_SKINNY_M2_R4 : GR_SKINNY_M2_R16;
     if (M <= 4) return GR_SKINNY_M4_R16;
-    if (M <= 16) return N >= 65536 ? GR_GEMV16_WN4 : (N >= 12288 ? GR_GEMV16_WN2 : GR_GEMV16_WN1);
+    if (M <= 16) {
+        if (N >= 65536) return GR_GEMV16_WN4;
+        if (N >= 12288) return GR_GEMV16_WN2;
+        return (N >= 2048 && N <= 4096) ? GR_GEMV16_WN1_W8 : GR_GEMV16_WN1;
+    }
     if (M <= 32) return N >= 65536 ? GR_GEMV32_WN4 : (N >= 12288 ? GR_GEMV32_WN2 : GR_GEMV32_WN1);
     if (M <= 64 && N >= 1024 && N <= 4096) return GR_GEMV64;
     const int64_t big = ((M + 127) / 128) * ((N + 255) / 256);
@@ -986,13 +992,14 @@ const char* gemm_route_name(GemmRoute r) {
         case GR_SKINNY_M2_R4: return "gemm_skinny_kernel<2,ROLE,4>";
         case GR_SKINNY_M2_R16: return "gemm_skinny_kernel<2,ROLE,16>";
         case GR_SKINNY_M4_R16: return "gemm_skinny_kernel<4,ROLE,16>";
-        case GR_GEMV16_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,1>";
-        case GR_GEMV16_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,1>";
-        case GR_GEMV16_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,1>";
-        case GR_GEMV32_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,2>";
-        case GR_GEMV32_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,2>";
-        case GR_GEMV32_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,2>";
-        case GR_GEMV64: return "gemm_gemv16_kernel<1,2,32,ROLE,4>";
+        case GR_GEMV16_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,1,4>";
+        case GR_GEMV16_WN1_W8: return "gemm_gemv16_kernel<1,2,64,ROLE,1,8>";
+        case GR_GEMV16_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,1,4>";
+        case GR_GEMV16_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,1,4>";
+        case GR_GEMV32_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,2,4>";
+        case GR_GEMV32_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,2,4>";
+        case GR_GEMV32_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,2,4>";
+        case GR_GEMV64: return "gemm_gemv16_kernel<1,2,32,ROLE,4,4>";
         case GR_SMALL32: return "gemm_small_kernel<ROLE>";
         case GR_TILE64: return "gemm_mfma_kernel<64,64,2,2,ROLE>";
         case GR_TILE128x256: return "gemm_mfma_kernel<128,256,2,4,ROLE>";
@@ -1010,6 +1017,7 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         case GR_SKINNY_M2_R16: return launch_skinny<2, ROLE, 16>(a, st);
         case GR_SKINNY_M4_R16: return launch_skinny<4, ROLE, 16>(a, st);
         case GR_GEMV16_WN1: return launch_gemv16<1, 2, 64, ROLE>(a, st);
+        case GR_GEMV16_WN1_W8: return launch_gemv16<1, 2, 64, ROLE, 1, 8>(a, st);
         case GR_GEMV16_WN2: return launch_gemv16<2, 2, 64, ROLE>(a, st);
         case GR_GEMV16_WN4: return launch_gemv16<4, 2, 64, ROLE>(a, st);
         case GR_GEMV32_WN1: return launch_gemv16<1, 2, 64, ROLE, 2>(a, st);

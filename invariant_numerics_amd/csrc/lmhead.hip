@@ -116,16 +116,35 @@ __device__ __forceinline__ Top2 merged_top2(const Top2* __restrict__ part, int r
     return t;
 }
 
+// The same top-2 computed by a whole wavefront: lanes read the partial pairs in parallel and
+// merge them in a shuffle tree (the merge is order free, so the result is the serial one's);
+// every lane returns it.
+__device__ __forceinline__ Top2 merged_top2_wave(const Top2* __restrict__ part, int row, int ngrp, int V,
+                                                 int lane) {
+    const Top2* pr = part + (int64_t)row * ngrp;
+    Top2 t = {-__builtin_inff(), 0x7fffffff, -__builtin_inff(), 0x7fffffff};
+    for (int k = lane; k < ngrp; k += 64) top2_merge(t, pr[k]);
+    for (int off = 32; off >= 1; off >>= 1) {
+        Top2 o;
+        o.v1 = __shfl_xor(t.v1, off); o.i1 = __shfl_xor(t.i1, off);
+        o.v2 = __shfl_xor(t.v2, off); o.i2 = __shfl_xor(t.i2, off);
+        top2_merge(t, o);
+    }
+    if (t.i1 < 0 || t.i1 >= V) t.i1 = 0;
+    if (t.i2 < 0 || t.i2 >= V || t.i2 == t.i1) t.i2 = (t.i1 == 0) ? 1 : 0;
+    return t;
+}
+
 __global__ __launch_bounds__(RED_THREADS) void lmhead_tiles_kernel(
     const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
     const Top2* __restrict__ part, float* __restrict__ tileS) {
     const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
     if (mode != 0 && row >= *count) return;
     const float* zr = zrow(z, V, row);
-    const Top2 t = merged_top2(part, row, ngrp, V);
+    const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+    const Top2 t = merged_top2_wave(part, row, ngrp, V, lane);
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
-    const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
     const int u = grp * GROUP + w;                       // this wavefront's tile
     if (u >= ntiles) return;
     float acc = 0.0f;
@@ -199,22 +218,57 @@ __global__ void lmhead_final_kernel(
 
 // Rows 0..B-1 are the primary pass and rows B..2B-1 the FP32 pass of the same hidden states:
 // output row b takes the FP32 result when the primary margin is below tau (strict; NaN never).
-__global__ void lmhead_final_select_kernel(
+// One workgroup of two wavefronts per output row: wavefront 0 finishes row b, wavefront 1 row
+// B + b.  Each merges its row's partial top-2 pairs in parallel, stages the tile sums in LDS
+// (all requested at once) and lets one lane fold them in ascending order.
+constexpr int SEL_MAXT = 1024;           // tiles per row held in LDS (V <= 1024 tiles)
+
+__global__ __launch_bounds__(128) void lmhead_final_select_kernel(
     const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau,
     const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
     float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
     int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
-    const int row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= B) return;
-    const int tg = target[row];
-    RowOut r = row_result(z, V, row, tg, part, ngrp, tileS);
-    const bool flag = r.mg < tau;
-    if (flag) r = row_result(z, V, B + row, tg, part, ngrp, tileS);
-    logprob[row] = r.lp;
-    margin[row] = r.mg;
-    top1[row] = r.t1;
-    top2[row] = r.t2;
-    recomputed[row] = (uint8_t)(flag ? 1 : 0);
+    __shared__ __attribute__((aligned(16))) float ts[2][SEL_MAXT];
+    __shared__ RowOut res[2];
+    const int b = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = w == 0 ? b : B + b;
+    const int tg = target[b];
+    const Top2 t = merged_top2_wave(part, row, ngrp, V, lane);
+    const int ntiles = (V + TV - 1) / TV;
+    const float* tr = tileS + (int64_t)row * ntiles;
+    for (int u = lane; u < ntiles; u += 64) ts[w][u] = tr[u];
+    for (int u = ntiles + lane; u < ((ntiles + 3) & ~3); u += 64) ts[w][u] = 0.0f;   // last float4's padding
+    __syncthreads();
+    if (lane == 0) {
+        const float* zr = zrow(z, V, row);
+        const float M = zr[t.i1];
+        const float z2 = zr[t.i2];
+        const float zt = (tg >= 0 && tg < V) ? zr[tg] : 0.0f;
+        float S = ts[w][0];
+        int u = 1;
+        for (; u < 4 && u < ntiles; ++u) S = S + ts[w][u];
+        for (; u + 4 <= ntiles; u += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(&ts[w][u]);
+            S = S + q.x; S = S + q.y; S = S + q.z; S = S + q.w;
+        }
+        for (; u < ntiles; ++u) S = S + ts[w][u];
+        RowOut r;
+        r.lp = (tg >= 0 && tg < V) ? (zt - M) - log_f(S) : __builtin_nanf("");
+        r.mg = M - z2;
+        r.t1 = t.i1;
+        r.t2 = t.i2;
+        res[w] = r;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const bool flag = res[0].mg < tau;
+        const RowOut r = flag ? res[1] : res[0];
+        logprob[b] = r.lp;
+        margin[b] = r.mg;
+        top1[b] = r.t1;
+        top2[b] = r.t2;
+        recomputed[b] = (uint8_t)(flag ? 1 : 0);
+    }
 }
 
 // Logit gradient, step 1: per row M = z_top1 and S (the forward's fold), and the logprob.
@@ -426,7 +480,7 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
         // both passes' rows in one reduce; the last kernel picks each row's pass
         if ((e = launch_row_stats(Z, a.V, 2 * a.B, 0, nullptr, part, tiles, st)) != hipSuccess) return e;
         const int ngrp = (a.V + GV - 1) / GV;
-        hipLaunchKernelGGL(lmhead_final_select_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, Z, a.V, a.B,
+        hipLaunchKernelGGL(lmhead_final_select_kernel, dim3(a.B), dim3(128), 0, st, Z, a.V, a.B,
                            a.target, a.tau, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
                            a.recomputed);
         return hipGetLastError();

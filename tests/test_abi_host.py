@@ -114,9 +114,10 @@ def test_kernel_route_names(inv):
     assert r("gemm", 1, 4096) == "gemm_skinny_kernel<1,0,4>"
     assert r("gemm", 1, 28672) == "gemm_skinny_kernel<1,0,16>"
     assert r("gemm", 3, 4096) == "gemm_skinny_kernel<4,0,16>"
-    assert r("gemm", 16, 4096) == "gemm_gemv16_kernel<1,2,64,0,1>"
-    assert r("gemm", 32, 14336) == "gemm_gemv16_kernel<2,2,64,0,2>"
-    assert r("gemm", 64, 4096) == "gemm_gemv16_kernel<1,2,32,0,4>"
+    assert r("gemm", 16, 4096) == "gemm_gemv16_kernel<1,2,64,0,1,8>"
+    assert r("gemm", 16, 6144) == "gemm_gemv16_kernel<1,2,64,0,1,4>"
+    assert r("gemm", 32, 14336) == "gemm_gemv16_kernel<2,2,64,0,2,4>"
+    assert r("gemm", 64, 4096) == "gemm_gemv16_kernel<1,2,32,0,4,4>"
     assert r("gemm", 64, 8192) == "gemm_small_kernel<0>"
     assert r("gemm", 64, 16384) == "gemm_mfma_kernel<64,64,2,2,0>"
     assert r("gemm", 512, 4096) == "gemm_mfma_kernel<64,64,2,2,0>"
@@ -128,7 +129,7 @@ def test_kernel_route_names(inv):
     assert r("gated_gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,2>"
     assert r("gated_gemm", 1, 28672) == "gemm_skinny_kernel<1,2,16>"
     assert r("lmhead_gemm", 1, 128256) == "gemm_skinny_kernel<2,1,16>"
-    assert r("lmhead_gemm", 8, 128256) == "gemm_gemv16_kernel<4,2,64,1,1>"
+    assert r("lmhead_gemm", 8, 128256) == "gemm_gemv16_kernel<4,2,64,1,1,4>"
     assert r("lmhead_gemm", 32767, 128256) == "gemm_mfma_kernel<128,256,2,4,1>"
     assert r("attention_prefill", 4 * 32, 512) == "attn_prefill_kernel<DT,8,64>"
     assert r("attention_prefill", 8, 2048) == "attn_prefill_kernel<DT,4,32>"
