@@ -618,19 +618,50 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const int32_t* __r
     for (int c = d; c < nc; c += D) { Mc[c] = src[(int64_t)c * D2]; Lc[c] = src[(int64_t)c * D2 + 1]; }
     for (int c = nc + d; c < ((nc + 3) & ~3); c += D) Mc[c] = 0.0f;   // padding of the last float4
     __syncthreads();
-    if (d == 0) {                                 // running maximum, exactly as the fold takes it
-        float m = Mc[0];
-        Mr[0] = m;
-        int c = 1;
-        for (; c < 4 && c < nc; ++c) { const float mc = Mc[c]; m = (mc > m) ? mc : m; Mr[c] = m; }
-        for (; c + 4 <= nc; c += 4) {
-            const float4 q = *reinterpret_cast<const float4*>(&Mc[c]);
-            m = (q.x > m) ? q.x : m; Mr[c] = m;
-            m = (q.y > m) ? q.y : m; Mr[c + 1] = m;
-            m = (q.z > m) ? q.z : m; Mr[c + 2] = m;
-            m = (q.w > m) ? q.w : m; Mr[c + 3] = m;
+    // Running maximum Mr[c] = max(Mr[c - 1], Mc[c]) in the fold's comparison (the later value
+    // only when strictly greater).  Without NaN among the maxima that comparison is associative
+    // (ties can differ only in the sign of a zero, which no factor sees: exp_f(+-0) = 1), so
+    // each thread scans a contiguous segment from the maximum of the segments before it; any
+    // NaN sends the whole scan to one thread, in order.
+    const int per = (nc + D - 1) / D;
+    const int s0 = min(nc, d * per), s1 = min(nc, s0 + per);
+    float seg = -__builtin_inff();
+    int nan = 0;
+    for (int c = s0; c < s1; ++c) {
+        const float mc = Mc[c];
+        nan |= mc != mc;
+        seg = (mc > seg) ? mc : seg;
+    }
+    if (__syncthreads_or(nan)) {
+        if (d == 0) {
+            float m = Mc[0];
+            Mr[0] = m;
+            for (int c = 1; c < nc; ++c) { const float mc = Mc[c]; m = (mc > m) ? mc : m; Mr[c] = m; }
         }
-        for (; c < nc; ++c) { const float mc = Mc[c]; m = (mc > m) ? mc : m; Mr[c] = m; }
+    } else {
+        // exclusive prefix maximum of the segment maxima over the D threads
+        const int lane = d & 63, wv = d >> 6;
+        float incl = seg;
+        for (int off = 1; off < 64; off <<= 1) {
+            const float t = __shfl_up(incl, off);
+            if (lane >= off) incl = (incl > t) ? incl : t;
+        }
+        float excl = __shfl_up(incl, 1);
+        if (lane == 0) excl = -__builtin_inff();
+        // the first wavefront's total, through an Mr entry rewritten below (after the barrier)
+        if (lane == 63 && wv == 0) Mr[n4 - 1] = incl;
+        __syncthreads();
+        if (wv == 1) {
+            const float w0 = Mr[n4 - 1];
+            excl = (excl > w0) ? excl : w0;
+        }
+        __syncthreads();
+        float m = excl;
+        for (int c = s0; c < s1; ++c) {
+            const float mc = Mc[c];
+            m = (c == 0) ? mc : ((mc > m) ? mc : m);
+            Mr[c] = m;
+        }
     }
     __syncthreads();
     for (int c = 1 + d; c < nc; c += D) {
