@@ -342,6 +342,22 @@ int inv_mfma32_f32_check(const float* A, const float* B, const float* C, float* 
 int inv_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t ntests,
                         void* stream);
 
+/* Diagnostic (measurement, not part of the method): reads `bytes` (a multiple of 16) at src
+ * with 16-byte loads from `grid` workgroups of 256 threads and writes one checksum per
+ * workgroup to sink[grid] (so the loads are kept).  Timed by the benchmarks for the practical
+ * HBM read rate of a plain stream, the ceiling the memory-bound kernels are compared with.
+ * Status: INV_ERR_NULL, INV_ERR_SHAPE (bytes, grid out of range), INV_ERR_ALIGN. */
+int inv_read_stream_probe(const void* src, int64_t bytes, uint32_t* sink, int64_t grid, void* stream);
+
+/* Diagnostic (measurement): every one of 256 x waves_per_cu / 4 workgroups of four wavefronts
+ * issues `iters` rounds of 8 independent FP32 matrix instructions (shape 0:
+ * v_mfma_f32_16x16x4_f32, shape 1: v_mfma_f32_32x32x2_f32) on register operands and writes its
+ * accumulators to out[grid * 256].  Flops per launch = grid * 4 * iters * 8 * 2048 (shape 0)
+ * or * 4096 (shape 1); timed by the benchmarks for the instruction rates at 1-8 wavefronts
+ * per SIMD.  Status: INV_ERR_NULL, INV_ERR_DTYPE (shape), INV_ERR_SHAPE (iters < 1,
+ * waves_per_cu not a multiple of 4 in 4..32). */
+int inv_mfma_rate_probe(int shape, int64_t iters, int64_t waves_per_cu, float* out, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * inv_qkv_rope_kv_append -- the QKV projection of a decoder layer followed by the RoPE
  * rotation and the KV-cache append: bit for bit inv_fixed_order_gemm(X, Wqkv) and then

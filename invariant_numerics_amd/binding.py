@@ -73,6 +73,8 @@ def _load():
         "inv_qkv_rope_kv_append_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64, i64]),
         "inv_qkv_rope_kv_append": (ctypes.c_int, [vp, i64, i64, i64, vp, i64, i64, i64, i64, vp, vp, vp, vp, i64,
                                                   i64, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "inv_read_stream_probe": (ctypes.c_int, [vp, i64, vp, i64, vp]),
+        "inv_mfma_rate_probe": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp]),
         "inv_kernel_route": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_char_p, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
@@ -91,7 +93,7 @@ EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "in
            "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check",
            "inv_mfma_bf16_check", "inv_kernel_route", "inv_attention_decode_noalloc",
            "inv_attention_decode_noalloc_max_bytes", "inv_qkv_rope_kv_append_workspace_bytes",
-           "inv_qkv_rope_kv_append")
+           "inv_qkv_rope_kv_append", "inv_read_stream_probe", "inv_mfma_rate_probe")
 
 
 def _check(status, what):
@@ -484,4 +486,27 @@ def inv_mfma_bf16_check(A, B, C, out=None):
     if out is None:
         out = torch.empty_like(C)
     _check(LIB.inv_mfma_bf16_check(_p(A), _p(B), _p(C), _p(out), n, _stream(A)), "inv_mfma_bf16_check")
+    return out
+
+
+def inv_read_stream_probe(src, grid=4096, sink=None):
+    """Read every byte of the device tensor ``src`` once (diagnostic stream); returns the
+    per-workgroup checksums [grid] (uint32 stored as int32)."""
+    _dev(src, sink)
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(grid, dtype=torch.int32, device=src.device)
+    _check(LIB.inv_read_stream_probe(_p(src), nbytes - nbytes % 16, _p(sink), grid, _stream(src)),
+           "inv_read_stream_probe")
+    return sink
+
+
+def inv_mfma_rate_probe(shape, iters, waves_per_cu, out=None, device="cuda"):
+    """Back-to-back FP32 matrix instructions (shape 0: 16x16x4, 1: 32x32x2) at waves_per_cu
+    wavefronts per CU; returns the output buffer (flops: grid * 4 * iters * 8 * 2048 or 4096)."""
+    grid = 256 * waves_per_cu // 4
+    if out is None:
+        out = torch.empty(grid * 256, dtype=torch.float32, device=device)
+    _check(LIB.inv_mfma_rate_probe(int(shape), int(iters), int(waves_per_cu), _p(out),
+                                   torch.cuda.current_stream(out.device).cuda_stream), "inv_mfma_rate_probe")
     return out

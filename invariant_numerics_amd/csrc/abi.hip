@@ -316,6 +316,20 @@ int inv_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, fl
     return fin(launch_mfma_bf16_check(A, B, C, D, ntests, S(stream)));
 }
 
+int inv_read_stream_probe(const void* src, int64_t bytes, uint32_t* sink, int64_t grid, void* stream) {
+    if (!src || !sink) return INV_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0 || grid < 1 || grid > 65536) return INV_ERR_SHAPE;
+    if (!al16(src)) return INV_ERR_ALIGN;
+    return fin(launch_read_stream(src, bytes, sink, (int)grid, S(stream)));
+}
+
+int inv_mfma_rate_probe(int shape, int64_t iters, int64_t waves_per_cu, float* out, void* stream) {
+    if (!out) return INV_ERR_NULL;
+    if (shape != 0 && shape != 1) return INV_ERR_DTYPE;
+    if (iters < 1 || waves_per_cu < 4 || waves_per_cu > 32 || waves_per_cu % 4 != 0) return INV_ERR_SHAPE;
+    return fin(launch_mfma_rate(shape, iters, (int)waves_per_cu, out, S(stream)));
+}
+
 int inv_kernel_route(int op, int64_t a, int64_t b, char* name, size_t cap) {
     if (!name || cap == 0) return INV_ERR_NULL;
     if (a < 1 || b < 1) return INV_ERR_SHAPE;

@@ -302,6 +302,69 @@ __global__ __launch_bounds__(64) void mfma_bf16_check_kernel(const uint16_t* __r
     }
 }
 
+// Read-stream probe: every thread reads 16-byte units of src (grid-stride over n16 units,
+// four in flight) and adds their bits into a per-workgroup checksum, so the loads cannot be
+// dropped; the practical HBM read rate of a plain streaming kernel.
+__global__ __launch_bounds__(256) void read_stream_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+    __shared__ uint32_t acc[4];
+    uint32_t x = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        x += a.x ^ a.y ^ a.z ^ a.w;
+        x += b.x ^ b.y ^ b.z ^ b.w;
+        x += c.x ^ c.y ^ c.z ^ c.w;
+        x += d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) { const uint4 a = src[i]; x += a.x ^ a.y ^ a.z ^ a.w; }
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if ((threadIdx.x & 63) == 0) acc[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) sink[blockIdx.x] = acc[0] + acc[1] + acc[2] + acc[3];
+}
+
+// Matrix-core rate probe: each wavefront issues `iters` rounds of 8 independent FP32 matrix
+// instructions (shape 0: 16x16x4, shape 1: 32x32x2) on register operands, with no memory
+// traffic, and stores its accumulators once so the work is kept.
+template <int SHAPE>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int64_t iters, float* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const float a = 1.0f + lane * 1e-3f, b = 1.0f - lane * 1e-3f;
+    if constexpr (SHAPE == 0) {
+        f32x4_t acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
+        }
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+        out[blockIdx.x * (int64_t)blockDim.x + threadIdx.x] = t;
+    } else {
+        f32x16_t acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b, a, acc[j], 0, 0, 0);
+        }
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) t += acc[j][v];
+        out[blockIdx.x * (int64_t)blockDim.x + threadIdx.x] = t;
+    }
+}
+
 inline int grid_for(int64_t work, int block) {
     int64_t g = (work + block - 1) / block;
     if (g > 65536) g = 65536;
@@ -402,6 +465,22 @@ hipError_t launch_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const fl
                                   hipStream_t st) {
     const int grid = (int)(ntest < 4096 ? ntest : 4096);
     hipLaunchKernelGGL(mfma_bf16_check_kernel, dim3(grid), dim3(64), 0, st, A, B, C, D, ntest);
+    return hipGetLastError();
+}
+
+hipError_t launch_read_stream(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t st) {
+    hipLaunchKernelGGL(read_stream_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<const uint4*>(src),
+                       bytes / 16, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_rate(int shape, int64_t iters, int waves_per_cu, float* out, hipStream_t st) {
+    // 256 CUs x waves_per_cu wavefronts in workgroups of 4 (one per SIMD)
+    const int grid = 256 * waves_per_cu / 4;
+    if (shape == 0)
+        hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(grid), dim3(256), 0, st, iters, out);
+    else
+        hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(grid), dim3(256), 0, st, iters, out);
     return hipGetLastError();
 }
 

@@ -101,6 +101,8 @@ hipError_t launch_mfma_check(const float* A, const float* B, const float* C, flo
                              hipStream_t st);
 hipError_t launch_mfma32_check(const float* A, const float* B, const float* C, float* D, int64_t ntest,
                                hipStream_t st);
+hipError_t launch_read_stream(const void* src, int64_t bytes, uint32_t* sink, int grid, hipStream_t st);
+hipError_t launch_mfma_rate(int shape, int64_t iters, int waves_per_cu, float* out, hipStream_t st);
 hipError_t launch_mfma_bf16_check(const uint16_t* A, const uint16_t* B, const float* C, float* D, int64_t ntest,
                                   hipStream_t st);
 

@@ -150,3 +150,15 @@ def test_decode_noalloc_rejects_oversized_calls(inv):
     assert f(1, FAKE, FAKE, FAKE, FAKE, 16, 32768, 32, 8, 128, 1.0, FAKE, None) == -5
     assert f(1, FAKE, FAKE, FAKE, None, 1, 32768, 32, 8, 128, 1.0, FAKE, None) == -1
     assert f(1, FAKE, FAKE, FAKE, FAKE, 1, 32768, 32, 8, 64, 1.0, FAKE, None) == -6
+
+
+def test_probe_argument_validation(inv):
+    """The two measurement probes validate their arguments before launching anything."""
+    L = inv.LIB
+    assert L.inv_read_stream_probe(None, 1024, FAKE, 64, None) == -1
+    assert L.inv_read_stream_probe(FAKE, 1000, FAKE, 64, None) == -2      # not a multiple of 16
+    assert L.inv_read_stream_probe(FAKE, 1024, FAKE, 0, None) == -2
+    assert L.inv_mfma_rate_probe(2, 10, 8, FAKE, None) == -4              # no such instruction
+    assert L.inv_mfma_rate_probe(0, 10, 6, FAKE, None) == -2              # not a multiple of 4
+    assert L.inv_mfma_rate_probe(1, 0, 8, FAKE, None) == -2
+    assert L.inv_mfma_rate_probe(1, 10, 8, None, None) == -1
