@@ -170,40 +170,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
     const int nt = (K + BK - 1) / BK;              // plus a partial last tile when K % BK != 0
     const int nslices = (K + KS - 1) / KS;
     constexpr int NS = BK / 2;                     // MFMA k-steps per tile
-    float a[TI][NS], b[TJ][NS];
-    auto read_frags = [&](int buf) {
+    // Full tiles run in four groups of four k-steps.  The operands of a group sit in one of
+    // two register sets; the LDS reads of the next group go out while the current group's
+    // matrix instructions run, and the first group of the next tile is read right after the
+    // barrier, so no group waits for LDS and the barrier sits between queued matrix work.
+    constexpr int GS = 4, NG = NS / GS;            // k-steps per group, groups per tile
+    static_assert(NG == 4, "four groups per tile");
+    float ga[2][TI][GS], gb[2][TJ][GS];
+    auto read_group = [&](int buf, int g, float (&fa)[TI][GS], float (&fb)[TJ][GS]) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-            const float4* src = reinterpret_cast<const float4*>(&As[buf][wm0 + i * 32 + c][h * 16]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = src[q];
-                a[i][4 * q] = v.x; a[i][4 * q + 1] = v.y; a[i][4 * q + 2] = v.z; a[i][4 * q + 3] = v.w;
-            }
+            const float4 v = *reinterpret_cast<const float4*>(&As[buf][wm0 + i * 32 + c][h * 16 + GS * g]);
+            fa[i][0] = v.x; fa[i][1] = v.y; fa[i][2] = v.z; fa[i][3] = v.w;
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-            const float4* src = reinterpret_cast<const float4*>(&Bs[buf][wn0 + j * 32 + c][h * 16]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 v = src[q];
-                b[j][4 * q] = v.x; b[j][4 * q + 1] = v.y; b[j][4 * q + 2] = v.z; b[j][4 * q + 3] = v.w;
-            }
+            const float4 v = *reinterpret_cast<const float4*>(&Bs[buf][wn0 + j * 32 + c][h * 16 + GS * g]);
+            fb[j][0] = v.x; fb[j][1] = v.y; fb[j][2] = v.z; fb[j][3] = v.w;
         }
     };
-    auto steps = [&](const int s0, const int s1) {
+    auto group = [&](const float (&fa)[TI][GS], const float (&fb)[TJ][GS]) {
 #pragma unroll
-        for (int s = s0; s < s1; ++s)
+        for (int s = 0; s < GS; ++s)
 #pragma unroll
             for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int j = 0; j < TJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][s], fb[j][s], acc[i][j], 0, 0, 0);
     };
     load_tile(0);
     store_tile(0);
     load_tile(BK);
     __syncthreads();
+    read_group(0, 0, ga[0], gb[0]);
     // slice by slice (KS / BK tiles each), so the fold T = T + acc runs once per slice; the
     // loop body sees full tiles only (a partial tile can only be the very last one)
     int t = 0;
@@ -211,24 +210,67 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_mfma_kernel(
         const int tend = min(ntf, t + KS / BK);
         for (; t < tend; ++t) {
             const int buf = t & 1;
-            read_frags(buf);
-            // halfway through the k-steps the next tile (in registers since the middle of the
-            // previous tile) goes to the other LDS buffer, and the loads of the tile after it
-            // are issued at once into the freed registers: each tile's loads have a whole
-            // tile of matrix work to arrive, and the stores overlap the second half
-            steps(0, NS / 2);
-            if (t + 1 < nt) store_tile(buf ^ 1);
+            // group 0 (read during the previous tile), reading group 1.  The scheduling
+            // barriers keep each group's LDS reads ahead of the previous group's matrix
+            // instructions (left alone, the compiler sinks them to just before their use).
+            read_group(buf, 1, ga[1], gb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            group(ga[0], gb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            // group 1, reading group 2; the next tile (in registers since the previous
+            // tile) goes to the other LDS buffer, and the loads of the tile after it are
+            // issued into the freed registers: a whole tile of matrix work to arrive
+            // (past the last tile the stored values are never read).  The staging
+            // instructions are spread between the matrix instructions, so they issue while
+            // the matrix pipe works.
+            read_group(buf, 2, ga[0], gb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            store_tile(buf ^ 1);
             load_tile((t + 2) * BK);
-            steps(NS / 2, NS);
+            group(ga[1], gb[1]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+                __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // one LDS store
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // group 2, reading group 3
+            read_group(buf, 3, ga[1], gb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            group(ga[0], gb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            // every wavefront's reads of this tile are issued and the next tile is stored
             __syncthreads();
+            // group 3, reading group 0 of the next tile (past the last tile: unused values
+            // from inside the buffer)
+            read_group(buf ^ 1, 0, ga[0], gb[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            group(ga[1], gb[1]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         if (t == ntf && ntf < nt && sl == nslices - 1) {
             // partial last tile: only the k-steps below K (zero padding is never multiplied in)
             const int kend = K - t * BK;
-            read_frags(t & 1);
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                if (2 * s < kend) steps(s, s + 1);
+            for (int g = 0; g < NG; ++g) {
+                read_group(t & 1, g, ga[1], gb[1]);
+#pragma unroll
+                for (int s = 0; s < GS; ++s)
+                    if (2 * (GS * g + s) < kend)
+#pragma unroll
+                        for (int i = 0; i < TI; ++i)
+#pragma unroll
+                            for (int j = 0; j < TJ; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[1][i][s], gb[1][j][s], acc[i][j],
+                                                                                0, 0, 0);
+            }
             ++t;
         }
         // the slice is complete: fold it into T in slice order, restart the accumulator
