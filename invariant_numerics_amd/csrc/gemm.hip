@@ -536,6 +536,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
     const int g = lane >> 4, r = lane & 15;
     const int wn = wv % WN, wk = wv / WN;
 
+    // Which (slice of the round, row) a staging unit belongs to.  A weight unit is the CH/8
+    // lanes that read one CH-wide row segment (16 bytes each, contiguous in memory), an
+    // activation unit the CH/4 lanes of one row segment.  The units of one 64-lane store
+    // instruction go to rows whose LDS segments start in different banks: rows RSW (weights)
+    // or RSX (activations) apart, so the 4-byte scatter stores below are conflict free
+    // (64-wide chunks: weight rows 2 x 144 bytes and activation rows 4 x 272 bytes apart; 32-wide:
+    // 1 x 80 and 2 x 144).  Any bijection would do: the mapping only decides which thread
+    // moves which element.
+    static_assert(CH == 64 || CH == 32, "chunk width");
+    constexpr int UW = 512 / CH, RSW = 16 / UW;  // weight units per instruction, row step
+    constexpr int UX = 256 / CH, RSX = 16 / UX;  // activation units per instruction, row step
+    auto wunit = [&](int rest, int& sk, int& rr) {
+        sk = rest / BN;
+        rr = RSW * (rest % UW) + (rest / UW) % RSW + 16 * ((rest / 16) % WN);
+    };
+    auto xunit = [&](int rest, int& sk, int& m) {
+        sk = rest / MR;
+        m = RSX * (rest % UX) + (rest / UX) % RSX + 16 * ((rest / 16) % MT);
+    };
     // PD chunks in flight in registers
     uint4 wr[PD][WUN];
     float4 xr[PD][XU];
@@ -551,16 +570,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
 #pragma unroll
         for (int i = 0; i < WUN; ++i) {
             const int q = tid + NT * i;
-            const int c8 = q % (CH / 8), rest = q / (CH / 8);
-            const int sk = rest % WK, rr = rest / WK;
+            const int c8 = q % (CH / 8);
+            int sk, rr;
+            wunit(q / (CH / 8), sk, rr);
             const int k = (rd * WK + sk) * KS + c * CH + 8 * c8;
             wq[i] = *reinterpret_cast<const uint4*>(W + (int64_t)min(n0 + rr, N - 1) * ldw + min(k, K - 8));
         }
 #pragma unroll
         for (int j = 0; j < XU; ++j) {
             const int u = tid + NT * j;
-            const int q4 = u % (CH / 4), rest = u / (CH / 4);
-            const int sk = rest % WK, m = rest / WK;
+            const int q4 = u % (CH / 4);
+            int sk, m;
+            xunit(u / (CH / 4), sk, m);
             const int k = (rd * WK + sk) * KS + c * CH + 4 * q4;
             xq[j] = *reinterpret_cast<const float4*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
         }
@@ -572,10 +593,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
 #pragma unroll
         for (int i = 0; i < WUN; ++i) {
             const int q = tid + NT * i;
-            const int c8 = q % (CH / 8), rest = q / (CH / 8);
+            const int c8 = q % (CH / 8);
+            int sk, rr;
+            wunit(q / (CH / 8), sk, rr);
             // segments slice-major (sk, row): the 16 rows a lane group reads are WSEG apart,
             // which spreads a 16-lane quarter's 16-byte reads over all 64 banks
-            unsigned char* seg = &Wl[buf][((rest % WK) * BN + rest / WK) * WSEG + c8 * 4];
+            unsigned char* seg = &Wl[buf][(sk * BN + rr) * WSEG + c8 * 4];
             const uint4 v = wq[i];
             *reinterpret_cast<uint32_t*>(seg + 0 * (CH / 2)) = (v.x & 0xffffu) | (v.z << 16);
             *reinterpret_cast<uint32_t*>(seg + 1 * (CH / 2)) = (v.x >> 16) | (v.z & 0xffff0000u);
@@ -585,8 +608,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
 #pragma unroll
         for (int j = 0; j < XU; ++j) {
             const int u = tid + NT * j;
-            const int q4 = u % (CH / 4), rest = u / (CH / 4);
-            float* seg = &Xl[buf][((rest % WK) * MR + rest / WK) * XSEG + q4];
+            const int q4 = u % (CH / 4);
+            int sk, m;
+            xunit(u / (CH / 4), sk, m);
+            float* seg = &Xl[buf][(sk * MR + m) * XSEG + q4];
             seg[0 * NSTEP] = xq[j].x;
             seg[1 * NSTEP] = xq[j].y;
             seg[2 * NSTEP] = xq[j].z;
