@@ -141,6 +141,23 @@ int inv_attention_prefill(int dtype, const void* Q, const void* Kc, const void* 
                           int64_t Hq, int64_t Hkv, int64_t D, float scale,
                           float* O, void* stream);
 
+/* inv_attention_prefill_ws -- the same results as inv_attention_prefill, bit for bit, with a
+ * caller-supplied workspace that lets small grids (64-row blocks giving fewer than two
+ * workgroups per compute unit, e.g. 8 heads x 2048 rows) spread the long rows' chunks over more
+ * workgroups: each chunk's (m_c, l_c, o_c) is stored and then folded in ascending chunk order
+ * with the decode merge's arithmetic -- the order the single-task loop folds them in.
+ * inv_attention_prefill_workspace_bytes returns the bytes needed (0: this shape runs as one
+ * task per block and ws may be null).  ws: device memory, 16-byte aligned, owned by the caller,
+ * contents on entry ignored.  Status as inv_attention_prefill, plus INV_ERR_WORKSPACE when a
+ * nonzero size is needed and ws is null or ws_bytes is smaller, INV_ERR_ALIGN.
+ * Sources: Meituan page, "key practices" (the decode accumulation path; fixed KV chunks). */
+size_t inv_attention_prefill_workspace_bytes(int64_t B, int64_t Tq, int64_t q_start, int64_t Hq,
+                                             int64_t D);
+int inv_attention_prefill_ws(int dtype, const void* Q, const void* Kc, const void* Vc,
+                             int64_t B, int64_t Tq, int64_t q_start, int64_t Tmax,
+                             int64_t Hq, int64_t Hkv, int64_t D, float scale,
+                             float* O, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace for inv_attention_decode: B * Hq * ceil(Tmax/256) * (D + 2) floats. */
 size_t inv_attention_decode_workspace_bytes(int64_t B, int64_t Tmax, int64_t Hq, int64_t D);
 

@@ -75,6 +75,9 @@ def _load():
                                                   i64, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "inv_read_stream_probe": (ctypes.c_int, [vp, i64, vp, i64, vp]),
         "inv_mfma_rate_probe": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp]),
+        "inv_attention_prefill_workspace_bytes": (ctypes.c_size_t, [i64, i64, i64, i64, i64]),
+        "inv_attention_prefill_ws": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                                    ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
         "inv_kernel_route": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_char_p, ctypes.c_size_t]),
     }
     for name, (res, args) in sig.items():
@@ -93,7 +96,8 @@ EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "in
            "inv_gemm_backward", "inv_eval_numerics", "inv_mfma_f32_check", "inv_mfma32_f32_check",
            "inv_mfma_bf16_check", "inv_kernel_route", "inv_attention_decode_noalloc",
            "inv_attention_decode_noalloc_max_bytes", "inv_qkv_rope_kv_append_workspace_bytes",
-           "inv_qkv_rope_kv_append", "inv_read_stream_probe", "inv_mfma_rate_probe")
+           "inv_qkv_rope_kv_append", "inv_read_stream_probe", "inv_mfma_rate_probe",
+           "inv_attention_prefill_workspace_bytes", "inv_attention_prefill_ws")
 
 
 def _check(status, what):
@@ -256,9 +260,14 @@ def _scale(D, scale):
     return float(scale)
 
 
-def inv_attention_prefill(Q, Kc, Vc, q_start=0, scale=None, out=None):
-    """Q [B, Tq, Hq, D]; Kc, Vc [B, Hkv, Tmax, D]; returns fp32 [B, Tq, Hq, D]."""
-    _dev(Q, Kc, Vc, out)
+def inv_attention_prefill_workspace_bytes(B, Tq, q_start, Hq, D):
+    return int(LIB.inv_attention_prefill_workspace_bytes(B, Tq, q_start, Hq, D))
+
+
+def inv_attention_prefill(Q, Kc, Vc, q_start=0, scale=None, out=None, split=True, ws=None):
+    """Q [B, Tq, Hq, D]; Kc, Vc [B, Hkv, Tmax, D]; returns fp32 [B, Tq, Hq, D].  split: use the
+    workspace form (inv_attention_prefill_ws) when the shape has a split path; the same bits."""
+    _dev(Q, Kc, Vc, out, ws)
     B, Tq, Hq, D = Q.shape
     _, Hkv, Tmax, _ = Kc.shape
     for t in (Q, Kc, Vc):
@@ -266,6 +275,13 @@ def inv_attention_prefill(Q, Kc, Vc, q_start=0, scale=None, out=None):
             raise InvError("contiguous tensors expected")
     if out is None:
         out = torch.empty((B, Tq, Hq, D), dtype=torch.float32, device=Q.device)
+    need = inv_attention_prefill_workspace_bytes(B, Tq, q_start, Hq, D) if split else 0
+    if need:
+        ws = _ws(need, ws, Q.device)
+        _check(LIB.inv_attention_prefill_ws(_dtype_code(Q), _p(Q), _p(Kc), _p(Vc), B, Tq, q_start, Tmax, Hq, Hkv,
+                                            D, _scale(D, scale), _p(out), _p(ws), ws.numel() * ws.element_size(),
+                                            _stream(Q)), "inv_attention_prefill_ws")
+        return out
     _check(LIB.inv_attention_prefill(_dtype_code(Q), _p(Q), _p(Kc), _p(Vc), B, Tq, q_start, Tmax, Hq, Hkv,
                                      D, _scale(D, scale), _p(out), _stream(Q)), "inv_attention_prefill")
     return out

@@ -135,7 +135,25 @@ int inv_attention_prefill(int dtype, const void* Q, const void* Kc, const void* 
     if (st != INV_OK) return st;
     AttnArgs a{dtype, Q, Kc, Vc, (int)B, (int)Tq, (int)q_start, (int)Tmax, (int)Hq, (int)Hkv, (int)D,
                scale, O};
-    return fin(launch_attention_prefill(a, S(stream)));
+    return fin(launch_attention_prefill(a, nullptr, 0, S(stream)));
+}
+
+size_t inv_attention_prefill_workspace_bytes(int64_t B, int64_t Tq, int64_t q_start, int64_t Hq, int64_t D) {
+    if (B < 1 || Tq < 1 || q_start < 0 || Hq < 1 || D != 128) return 0;
+    return prefill_split_ws_bytes(B, Tq, q_start, Hq);
+}
+
+int inv_attention_prefill_ws(int dtype, const void* Q, const void* Kc, const void* Vc, int64_t B,
+                             int64_t Tq, int64_t q_start, int64_t Tmax, int64_t Hq, int64_t Hkv,
+                             int64_t D, float scale, float* O, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_attn(dtype, Q, Kc, Vc, O, B, Tq, q_start, Tmax, Hq, Hkv, D);
+    if (st != INV_OK) return st;
+    const size_t need = inv_attention_prefill_workspace_bytes(B, Tq, q_start, Hq, D);
+    if (need && (!ws || ws_bytes < need)) return INV_ERR_WORKSPACE;
+    if (need && !al16(ws)) return INV_ERR_ALIGN;
+    AttnArgs a{dtype, Q, Kc, Vc, (int)B, (int)Tq, (int)q_start, (int)Tmax, (int)Hq, (int)Hkv, (int)D,
+               scale, O};
+    return fin(launch_attention_prefill(a, need ? reinterpret_cast<float*>(ws) : nullptr, ws_bytes, S(stream)));
 }
 
 size_t inv_attention_decode_workspace_bytes(int64_t B, int64_t Tmax, int64_t Hq, int64_t D) {

@@ -15,6 +15,7 @@
 #include "numerics.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -83,22 +84,34 @@ __device__ __forceinline__ void load4(const void* base, int64_t off, float* v) {
 }
 
 // Global -> register -> LDS staging of one SBK-key sub-block of K or V (fp32 in LDS) by NT
-// threads.  Thread t carries SV groups of 4 consecutive d of rows (e / 32), e = t + NT i.
-// Rows at or beyond kend are read from row kend - 1 (always valid) and replaced by zeros.
+// threads.  Thread t carries SV groups of 4 consecutive d of rows (e / 32), e = t + NT i, as
+// loaded (4 floats, or 4 BF16 values in two words, upcast only at the LDS store, which halves
+// the registers the BF16 staging holds).  Rows at or beyond kend are read from row kend - 1
+// (always valid) and replaced by zeros (zero bits are +0 in both formats).
+template <int DT>
+struct StageRaw { typedef float4 type; };
+template <>
+struct StageRaw<0> { typedef uint2 type; };
+
 template <int DT, int NT, int SBK>
 struct Stage {
     static constexpr int SV = SBK * (D / 4) / NT;
-    float4 v[SV];
+    typedef typename StageRaw<DT>::type raw_t;
+    raw_t v[SV];
+    __device__ __forceinline__ static raw_t fetch(const void* base, int64_t off) {
+        if constexpr (DT == 1) return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+        else return *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+    }
+    __device__ __forceinline__ static float4 up(const raw_t& t) {
+        if constexpr (DT == 1) return t;
+        else return make_float4(bf16_lo(t.x), bf16_hi(t.x), bf16_lo(t.y), bf16_hi(t.y));
+    }
     __device__ __forceinline__ void load(const void* base, int64_t kvbase, int kb, int kend, int tid) {
         if (kb + SBK <= kend) {
             // whole sub-block in range: row (tid >> 5) + (NT / 32) i, column 4 (tid & 31)
             const int64_t off = kvbase + (int64_t)(kb + (tid >> 5)) * D + (tid & 31) * 4;
 #pragma unroll
-            for (int i = 0; i < SV; ++i) {
-                float t[4];
-                load4<DT>(base, off + (int64_t)((NT / 32) * i) * D, t);
-                v[i] = make_float4(t[0], t[1], t[2], t[3]);
-            }
+            for (int i = 0; i < SV; ++i) v[i] = fetch(base, off + (int64_t)((NT / 32) * i) * D);
             return;
         }
 #pragma unroll
@@ -107,9 +120,8 @@ struct Stage {
             const int jj = e >> 5, d4 = (e & 31) * 4;
             const bool in = kb + jj < kend;
             const int row = in ? kb + jj : kend - 1;
-            float t[4];
-            load4<DT>(base, kvbase + (int64_t)row * D + d4, t);
-            v[i] = in ? make_float4(t[0], t[1], t[2], t[3]) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const raw_t t = fetch(base, kvbase + (int64_t)row * D + d4);
+            v[i] = in ? t : raw_t{};
         }
     }
     __device__ __forceinline__ void store_k(float* KV, int tid) const {
@@ -118,7 +130,8 @@ struct Stage {
             const int e = tid + NT * i;
             const int jj = e >> 5, q = e & 31;
             float* dst = KV + jj * KLD + q;
-            dst[0] = v[i].x; dst[32] = v[i].y; dst[64] = v[i].z; dst[96] = v[i].w;
+            const float4 x = up(v[i]);
+            dst[0] = x.x; dst[32] = x.y; dst[64] = x.z; dst[96] = x.w;
         }
     }
     __device__ __forceinline__ void store_v(float* KV, int tid) const {
@@ -126,15 +139,29 @@ struct Stage {
         for (int i = 0; i < SV; ++i) {
             const int e = tid + NT * i;
             const int jj = e >> 5, d4 = (e & 31) * 4;
-            *reinterpret_cast<float4*>(KV + jj * KLD + d4) = v[i];
+            *reinterpret_cast<float4*>(KV + jj * KLD + d4) = up(v[i]);
         }
     }
 };
 
-template <int DT, int NW, int SB>
+// Task split (SPLIT = true, small grids): a row block whose rows see more than R chunks is cut
+// into tasks of at most R consecutive chunks, so more workgroups share its keys.  A task of a
+// cut block stores each chunk's (m_c, l_c, o_c) per row -- the values the running merge would
+// fold next -- into the partials array, and attn_prefill_merge_kernel folds them in ascending
+// chunk order afterwards: the same two-rounding merge as in the single-task loop, so the same
+// bits.  Blocks with at most R chunks run whole, as without the split.
+struct PrefillSplit {
+    int R;          // chunks per task (0: no split)
+    int r_split;    // first row of the first cut block (rows >= r_split are folded by the merge)
+    int nch;        // chunk dimension of the partials array
+    float* ws;      // partials [B][Tq - r_split][Hq][nch][D + 2]
+};
+
+template <int DT, int NW, int SB, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
     const void* __restrict__ Q, const void* __restrict__ Kc, const void* __restrict__ Vc,
-    int B, int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O) {
+    int B, int Tq, int q_start, int Tmax, int Hq, int Hkv, float scale, float* __restrict__ O,
+    PrefillSplit sp) {
     constexpr int BQ = 16 * NW;                 // query rows per workgroup
     constexpr int KT = SB / 16;                 // key tiles per sub-block
     __shared__ __attribute__((aligned(16))) float KV[2][SB * KLD];
@@ -146,14 +173,32 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int pr = 4 * (r & 3) + (r >> 2);             // pi(r)
-    int qb, h, b;
+    int qb, h, b, c0 = 0, c1 = 0;
+    bool cut = false;                                   // this block's chunks go to several tasks
     {
         // workgroup id -> (row block, head, sequence): row blocks from the last (heaviest) down;
         // within one row block, consecutive ids take q heads h = (u % Hkv) G + u / Hkv, i.e. they
         // cycle over the kv heads
         const int nqb = (Tq + BQ - 1) / BQ, HB = Hq * B;
         const int L = blockIdx.x, u = L % HB, G = Hq / Hkv;
-        qb = nqb - 1 - L / HB;
+        if constexpr (SPLIT) {
+            // task j = L / HB: the blocks' tasks listed from the last block down, each block's
+            // chunk ranges [t R, (t + 1) R) in order
+            int j = L / HB;
+            qb = nqb - 1;
+            for (; qb > 0; --qb) {
+                const int n = (q_start + min(Tq, (qb + 1) * BQ) - 1) / CHUNK + 1;
+                const int nt = (n + sp.R - 1) / sp.R;
+                if (j < nt) break;
+                j -= nt;
+            }
+            const int n = (q_start + min(Tq, (qb + 1) * BQ) - 1) / CHUNK + 1;
+            cut = n > sp.R;
+            c0 = j * sp.R;
+            c1 = min(n, c0 + sp.R);
+        } else {
+            qb = nqb - 1 - L / HB;
+        }
         b = u / Hq;
         const int hh = u % Hq;
         h = (hh % Hkv) * G + hh / Hkv;
@@ -162,6 +207,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
     const int r0 = qb * BQ;
     const int nrows = min(BQ, Tq - r0);
     const int imax = q_start + r0 + nrows - 1;          // last valid absolute row of the block
+    if constexpr (!SPLIT) c1 = imax / CHUNK + 1;
     const int64_t kvbase = ((int64_t)b * Hkv + kvh) * Tmax * D;
     const int wrow0 = r0 + 16 * w;                      // first row (relative) of the wavefront
     const int i0 = q_start + wrow0;                     // its absolute position
@@ -185,10 +231,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
 #pragma unroll
     for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int clast = imax / CHUNK;
     Stage<DT, 64 * NW, SB> st;
     int buf = 0;
-    st.load(Kc, kvbase, 0, min(CHUNK, imax + 1), tid);
+    st.load(Kc, kvbase, c0 * CHUNK, min(c0 * CHUNK + CHUNK, imax + 1), tid);
     st.store_k(KV[0], tid);
     __syncthreads();
     float* tail = &Tail[w][r][0];
@@ -346,6 +391,20 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
             }
         }
         // ------------------------------------------------------ 4. merge
+        if (SPLIT && cut) {
+            // the chunk's partial for the merge kernel: (m_c, l_c, o_c[d]) of the lane's row
+            const int rel = wrow0 + r;
+            if (ne && rel < r0 + nrows) {
+                float* dst = sp.ws + ((((int64_t)b * (Tq - sp.r_split) + (rel - sp.r_split)) * Hq + h) * sp.nch + c) * (D + 2);
+                if (g == 0) { dst[0] = mc; dst[1] = lc[0]; }
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int t = 0; t < 8; t += 2)
+                        *reinterpret_cast<float2*>(dst + 2 + 32 * g + 8 * v + t) = make_float2(oc[t][v], oc[t + 1][v]);
+            }
+            return;
+        }
         if (ne) {
             if (c == 0) {
                 m = mc;
@@ -364,13 +423,14 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
             }
         }
     };
-    for (int c = 0; c <= clast; ++c) {
+    for (int c = c0; c < c1; ++c) {
         // the fast path needs the whole workgroup to agree: its first rows see the whole chunk
         // (every later row does too) and the chunk ends inside the block's range
         const bool wg_fast = (c + 1) * CHUNK <= q_start + r0 && (c + 1) * CHUNK <= imax + 1;
         if (wg_fast) chunk(c, std::integral_constant<bool, true>());
         else chunk(c, std::integral_constant<bool, false>());
     }
+    if (SPLIT && cut) return;                           // the merge kernel writes these rows
     // ------------------------------------------------------------------ output
     const int rel = wrow0 + r;
     if (rel < r0 + nrows) {
@@ -399,9 +459,9 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_kernel(
 // workgroups share a CU, so loads of one overlap the arithmetic of another.
 // attn_decode_merge_kernel: per (b, q head), folds the chunk partials in ascending order,
 // m' = max(m, m_c), a = exp_f(m - m'), b = exp_f(m_c - m'), l = l a + l_c b, o = o a + o_c b.
-// The running maximum is scanned by one thread and every chunk's (a, b) pair is then
-// evaluated in parallel -- the same values the sequential loop computes -- so the 128
-// threads (one per d) only run the fold itself.
+// The running maximum is a parallel prefix scan (max is exact, so any grouping gives the
+// sequential values) and every chunk's (a, b) pair is then evaluated in parallel -- the same
+// values the sequential loop computes -- so the 128 threads (one per d) only run the fold.
 constexpr int GMAX = 16;
 constexpr int KSL = 32;               // d per K stage
 constexpr int KSLD = KSL + 1;         // padded K stage row
@@ -715,17 +775,44 @@ __global__ __launch_bounds__(D) void attn_decode_merge_kernel(const int32_t* __r
     O[((int64_t)b * Hq + h) * D + d] = o / l;
 }
 
+// The fold of the split prefill: rows see few chunks (a row at position p has p / 256 + 1), so
+// each thread (row, head, d) runs the sequential merge itself -- running maximum in the same
+// comparison, m' = (m_c > m) ? m_c : m, a = exp_f(m - m'), b = exp_f(m_c - m'), l = l a + l_c b,
+// o = o a + o_c b, chunks ascending from (m_0, l_0, o_0) -- the arithmetic of the decode merge
+// and of the single-task loop.  Partials row y is query row r0 + y % (Tq - r0) of sequence
+// y / (Tq - r0).  One workgroup per (row, head).
+__global__ __launch_bounds__(D) void attn_prefill_merge_kernel(int Hq, int Tq, int q_start, int r0, int nchunks,
+                                                               const float* __restrict__ ws,
+                                                               float* __restrict__ O) {
+    const int h = blockIdx.x, y = blockIdx.y, d = threadIdx.x;
+    const int nsr = Tq - r0, row = r0 + y % nsr;
+    const int nc = (q_start + row) / CHUNK + 1;
+    const int D2 = D + 2;
+    const float* src = ws + ((int64_t)y * Hq + h) * nchunks * D2;
+    float m = src[0], l = src[1], o = src[2 + d];
+    for (int c = 1; c < nc; ++c) {
+        const float* pc = src + (int64_t)c * D2;
+        const float mc = pc[0], lc = pc[1], oc = pc[2 + d];
+        const float mn = (mc > m) ? mc : m;
+        const float al = exp_f(m - mn), be = exp_f(mc - mn);
+        l = (l * al) + (lc * be);
+        o = (o * al) + (oc * be);
+        m = mn;
+    }
+    O[(((int64_t)(y / nsr) * Tq + row) * Hq + h) * D + d] = o / l;
+}
+
 }  // namespace
 
-template <int NW, int SBK>
-hipError_t launch_prefill_nw(const AttnArgs& a, hipStream_t st) {
-    dim3 grid(((a.Tq + 16 * NW - 1) / (16 * NW)) * a.Hq * a.B);
+template <int NW, int SBK, bool SPLIT>
+hipError_t launch_prefill_nw(const AttnArgs& a, const PrefillSplit& sp, int ntasks, hipStream_t st) {
+    dim3 grid((SPLIT ? ntasks : (a.Tq + 16 * NW - 1) / (16 * NW)) * a.Hq * a.B);
     if (a.dtype == 1)
-        hipLaunchKernelGGL((attn_prefill_kernel<1, NW, SBK>), grid, dim3(64 * NW), 0, st, a.Q, a.Kc, a.Vc,
-                           a.B, a.Tq, a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
+        hipLaunchKernelGGL((attn_prefill_kernel<1, NW, SBK, SPLIT>), grid, dim3(64 * NW), 0, st, a.Q, a.Kc, a.Vc,
+                           a.B, a.Tq, a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O, sp);
     else
-        hipLaunchKernelGGL((attn_prefill_kernel<0, NW, SBK>), grid, dim3(64 * NW), 0, st, a.Q, a.Kc, a.Vc,
-                           a.B, a.Tq, a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O);
+        hipLaunchKernelGGL((attn_prefill_kernel<0, NW, SBK, SPLIT>), grid, dim3(64 * NW), 0, st, a.Q, a.Kc, a.Vc,
+                           a.B, a.Tq, a.q_start, a.Tmax, a.Hq, a.Hkv, a.scale, a.O, sp);
     return hipGetLastError();
 }
 
@@ -737,9 +824,47 @@ int attention_prefill_waves(int64_t B, int64_t Tq, int64_t Hq) {
     return wg128 >= 512 ? 8 : 4;
 }
 
-hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st) {
-    if (attention_prefill_waves(a.B, a.Tq, a.Hq) == 8) return launch_prefill_nw<8, 64>(a, st);
-    return launch_prefill_nw<4, 32>(a, st);
+// The split of a small prefill grid: with 64-row blocks giving fewer than two workgroups per CU,
+// blocks are cut into tasks of PREFILL_SPLIT_R chunks.  Returns the task count (0: no split).
+constexpr int PREFILL_SPLIT_R = 1;
+int64_t prefill_split_plan(int64_t B, int64_t Tq, int64_t q_start, int64_t Hq, int* R, int* r_split, int* nch) {
+    if (attention_prefill_waves(B, Tq, Hq) != 4) return 0;
+    const int64_t BQ = 64, nqb = (Tq + BQ - 1) / BQ;
+    if (nqb * Hq * B >= 512) return 0;
+    int64_t ntasks = 0, first = -1;
+    for (int64_t qb = 0; qb < nqb; ++qb) {
+        const int64_t n = (q_start + std::min(Tq, (qb + 1) * BQ) - 1) / CHUNK + 1;
+        ntasks += (n + PREFILL_SPLIT_R - 1) / PREFILL_SPLIT_R;
+        if (first < 0 && n > PREFILL_SPLIT_R) first = qb;
+    }
+    if (first < 0) return 0;                      // no block has more than R chunks
+    *R = PREFILL_SPLIT_R;
+    *r_split = (int)(first * BQ);
+    *nch = (int)((q_start + Tq + CHUNK - 1) / CHUNK);
+    return ntasks;
+}
+
+size_t prefill_split_ws_bytes(int64_t B, int64_t Tq, int64_t q_start, int64_t Hq) {
+    int R, r_split, nch;
+    if (!prefill_split_plan(B, Tq, q_start, Hq, &R, &r_split, &nch)) return 0;
+    return sizeof(float) * (size_t)(B * (Tq - r_split) * Hq * (int64_t)nch * (D + 2));
+}
+
+hipError_t launch_attention_prefill(const AttnArgs& a, float* ws, size_t ws_bytes, hipStream_t st) {
+    if (ws) {
+        PrefillSplit sp{0, 0, 0, ws};
+        const int64_t ntasks = prefill_split_plan(a.B, a.Tq, a.q_start, a.Hq, &sp.R, &sp.r_split, &sp.nch);
+        if (ntasks > 0 && ws_bytes >= prefill_split_ws_bytes(a.B, a.Tq, a.q_start, a.Hq)) {
+            hipError_t e = launch_prefill_nw<4, 32, true>(a, sp, (int)ntasks, st);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(attn_prefill_merge_kernel, dim3(a.Hq, a.B * (a.Tq - sp.r_split)), dim3(D), 0, st,
+                               a.Hq, a.Tq, a.q_start, sp.r_split, sp.nch, ws, a.O);
+            return hipGetLastError();
+        }
+    }
+    const PrefillSplit none{0, 0, 0, nullptr};
+    if (attention_prefill_waves(a.B, a.Tq, a.Hq) == 8) return launch_prefill_nw<8, 64, false>(a, none, 0, st);
+    return launch_prefill_nw<4, 32, false>(a, none, 0, st);
 }
 
 namespace {

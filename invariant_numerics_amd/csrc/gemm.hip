@@ -1047,9 +1047,17 @@ GemmRoute gemm_route(int64_t M, int64_t N) {
     if (M <= 64 && N >= 1024 && N <= 4096) return GR_GEMV64;
     const int64_t big = ((M + 127) / 128) * ((N + 255) / 256);
     const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
-    if (mid < (M <= 64 ? SMALL_BELOW / 2 : SMALL_BELOW)) return GR_SMALL32;
-    if (M <= 64 || big < 256) return GR_TILE64;
-    return GR_TILE128x256;
+    if (M <= 64) return mid < SMALL_BELOW / 2 ? GR_SMALL32 : GR_TILE64;
+    // 64 < M (measured on the decoder's weight shapes, cold weights): 32 x 32 tiles while the
+    // 64 x 64 grid is small and N moderate; the 128 x 256 tile (one workgroup per CU) when its
+    // tiles fill whole waves of 256 (the last one at least 90% full) or there are four waves or
+    // more; otherwise 64 x 128 tiles of eight wavefronts, or 64 x 64 ones for large N where
+    // M is just past a multiple of 64 or between 256 and 512 rows
+    if (mid < SMALL_BELOW && N <= 8192) return GR_SMALL32;
+    if (big >= 4 * 256 || (big >= 230 && (big % 256 == 0 || big % 256 >= 230))) return GR_TILE128x256;
+    const int64_t mtail = M % 64;
+    if (N > 8192 && ((mtail > 0 && mtail <= 16) || (M > 256 && M <= 512))) return GR_TILE64;
+    return GR_TILE64x128;
 }
 
 const char* gemm_route_name(GemmRoute r) {
@@ -1069,6 +1077,7 @@ const char* gemm_route_name(GemmRoute r) {
         case GR_GEMV64: return "gemm_gemv16_kernel<1,2,32,ROLE,4,4>";
         case GR_SMALL32: return "gemm_small_kernel<ROLE>";
         case GR_TILE64: return "gemm_mfma_kernel<64,64,2,2,ROLE>";
+        case GR_TILE64x128: return "gemm_mfma_kernel<64,128,2,4,ROLE>";
         case GR_TILE128x256: return "gemm_mfma_kernel<128,256,2,4,ROLE>";
         default: return "unknown";
     }
@@ -1093,6 +1102,7 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         case GR_GEMV64: return launch_gemv16<1, 2, 32, ROLE, 4>(a, st);
         case GR_SMALL32: return launch_small<ROLE>(a, st);
         case GR_TILE64: return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
+        case GR_TILE64x128: return launch_tiled<64, 128, 2, 4, ROLE>(a, st);
         case GR_TILE128x256: return launch_tiled<128, 256, 2, 4, ROLE>(a, st);
         default: return hipErrorInvalidValue;
     }

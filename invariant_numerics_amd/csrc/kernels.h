@@ -30,7 +30,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role = 0);
 enum GemmRoute : int {
     GR_SKINNY_M1_R4, GR_SKINNY_M1_R16, GR_SKINNY_M2_R4, GR_SKINNY_M2_R16, GR_SKINNY_M4_R16,
     GR_GEMV16_WN1, GR_GEMV16_WN1_W8, GR_GEMV16_WN2, GR_GEMV16_WN4, GR_GEMV32_WN1, GR_GEMV32_WN2, GR_GEMV32_WN4,
-    GR_GEMV64, GR_SMALL32, GR_TILE64, GR_TILE128x256
+    GR_GEMV64, GR_SMALL32, GR_TILE64, GR_TILE64x128, GR_TILE128x256
 };
 GemmRoute gemm_route(int64_t M, int64_t N);
 const char* gemm_route_name(GemmRoute r);   // kernel template with ROLE left symbolic
@@ -49,7 +49,10 @@ struct AttnArgs {
     float scale;
     float* O;
 };
-hipError_t launch_attention_prefill(const AttnArgs& a, hipStream_t st);
+// ws (may be null): partials of the split path for small grids, used when ws_bytes is at least
+// prefill_split_ws_bytes(); otherwise the single-task kernel runs.  Same bits either way.
+hipError_t launch_attention_prefill(const AttnArgs& a, float* ws, size_t ws_bytes, hipStream_t st);
+size_t prefill_split_ws_bytes(int64_t B, int64_t Tq, int64_t q_start, int64_t Hq);
 // 8 (128-row workgroups) or 4 (64-row workgroups): wavefronts per prefill workgroup
 int attention_prefill_waves(int64_t B, int64_t Tq, int64_t Hq);
 hipError_t launch_attention_decode(const AttnArgs& a, const int32_t* pos, float* ws,

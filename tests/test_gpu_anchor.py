@@ -50,7 +50,7 @@ def sample_cols(N, seed, n=192):
 
 # ------------------------------------------------------------------ GEMM tiles --
 
-@pytest.mark.parametrize("M,K,N2", [(1024, 520, 8192), (1000, 264, 8200)])
+@pytest.mark.parametrize("M,K,N2", [(1024, 520, 8192), (1000, 264, 8000)])
 def test_gated_gemm_large_tile_matches_oracle(orc, M, K, N2):
     """Gated W1||W3 projection on the 128 x 256 tile with the SwiGLU epilogue (the
     benchmark's prefill W1||W3 instantiation), element by element: full K slices plus a
@@ -67,7 +67,7 @@ def test_gated_gemm_large_tile_matches_oracle(orc, M, K, N2):
     assert_bitwise(got, want, "gated %dx%dx%d" % (M, K, N2))
 
 
-@pytest.mark.parametrize("M,K,N", [(1024, 264, 8192), (1030, 520, 8100)])
+@pytest.mark.parametrize("M,K,N", [(1024, 264, 8192), (1030, 520, 7100)])
 def test_residual_gemm_large_tile_matches_oracle(orc, M, K, N):
     """ROLE 0 projection with the residual epilogue on the 128 x 256 tile (the benchmark's
     prefill O and W2 instantiation), element by element."""

@@ -131,3 +131,43 @@ def test_unit_values_exactly_one():
     v = np.ones_like(k)
     O = host(inv().inv_attention_prefill(f32(q), f32(k), f32(v)))
     assert np.all(O == 1.0)
+
+
+@pytest.mark.parametrize("B,T,q0,Hq,Hkv,bf", [(1, 2048, 0, 8, 8, True), (2, 900, 0, 4, 2, False),
+                                              (1, 1000, 300, 8, 2, False), (3, 513, 40, 2, 1, True)])
+def test_split_prefill_equals_single_task_and_oracle(orc, B, T, q0, Hq, Hkv, bf):
+    """Small grids cut long row blocks into chunk tasks whose partials the merge folds: the
+    same bits as the single-task kernel (and the oracle), at ragged lengths and offsets."""
+    say("attn split", B, T, q0, Hq, Hkv, bf)
+    m = inv()
+    need = m.inv_attention_prefill_workspace_bytes(B, T, q0, Hq, D)
+    assert need > 0, "shape expected to take the split path"
+    q, k, v = rand_qkv(8300 + T + q0, B, q0 + T, Hq, Hkv, bf)
+    qs = q[:, q0:].copy()
+    split = host(m.inv_attention_prefill(dev(qs), dev(k), dev(v), q_start=q0, split=True))
+    single = host(m.inv_attention_prefill(dev(qs), dev(k), dev(v), q_start=q0, split=False))
+    assert_bitwise(split, single, "split vs single task")
+    if B * T * Hq <= 8000:
+        ref = orc.attention(q, k, v)[:, q0:]
+        assert_bitwise(split, ref, "split vs oracle")
+
+
+def test_split_prefill_workspace_rules():
+    """Large grids need no workspace; a too-small workspace is rejected, not silently used."""
+    say("attn split ws")
+    m = inv()
+    assert m.inv_attention_prefill_workspace_bytes(1, 16384, 0, 32, D) == 0
+    assert m.inv_attention_prefill_workspace_bytes(1, 200, 0, 8, D) == 0      # one chunk per row
+    need = m.inv_attention_prefill_workspace_bytes(1, 2048, 0, 8, D)
+    assert need > 0
+    import ctypes
+    q, k, v = rand_qkv(8400, 1, 2048, 8, 8, True)
+    Q, K, V = dev(q), dev(k), dev(v)
+    import torch
+    out = torch.empty((1, 2048, 8, D), dtype=torch.float32, device=Q.device)
+    ws = torch.empty(need - 16, dtype=torch.uint8, device=Q.device)
+    from invariant_numerics_amd import binding
+    rc = binding.LIB.inv_attention_prefill_ws(0, Q.data_ptr(), K.data_ptr(), V.data_ptr(), 1, 2048, 0, 2048, 8, 8, D,
+                                        ctypes.c_float(0.08838834764831845), out.data_ptr(), ws.data_ptr(),
+                                        need - 16, None)
+    assert rc == -5
