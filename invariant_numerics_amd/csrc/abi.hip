@@ -366,12 +366,22 @@ int inv_kernel_route(int op, int64_t a, int64_t b, char* name, size_t cap) {
         }
         default: return INV_ERR_DTYPE;
     }
-    // the template name with its ROLE argument filled in
-    const char* t = gemm_route_name(gemm_route(M, N));
-    const char* r = strstr(t, "ROLE");
-    if (r) snprintf(buf, sizeof(buf), "%.*s%s%s", (int)(r - t), t, role, r + 4);
-    else snprintf(buf, sizeof(buf), "%s", t);
-    snprintf(name, cap, "%s", buf);
+    // the template name with its ROLE argument filled in; a split-off tail adds its GEMV
+    auto fill = [&](char* out, size_t n, int64_t rows) {
+        const char* t = gemm_route_name(gemm_route(rows, N));
+        const char* r = strstr(t, "ROLE");
+        if (r) snprintf(out, n, "%.*s%s%s", (int)(r - t), t, role, r + 4);
+        else snprintf(out, n, "%s", t);
+    };
+    const int64_t tail = gemm_tail_rows(M, nullptr);
+    fill(buf, sizeof(buf), M - tail);
+    if (tail) {
+        char tb[64];
+        fill(tb, sizeof(tb), tail);
+        snprintf(name, cap, "%s+%s", buf, tb);
+    } else {
+        snprintf(name, cap, "%s", buf);
+    }
     return INV_OK;
 }
 

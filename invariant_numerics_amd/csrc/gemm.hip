@@ -1049,14 +1049,17 @@ GemmRoute gemm_route(int64_t M, int64_t N) {
     const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
     if (M <= 64) return mid < SMALL_BELOW / 2 ? GR_SMALL32 : GR_TILE64;
     // 64 < M (measured on the decoder's weight shapes, cold weights): 32 x 32 tiles while the
-    // 64 x 64 grid is small and N moderate; the 128 x 256 tile (one workgroup per CU) when its
-    // tiles fill whole waves of 256 (the last one at least 90% full) or there are four waves or
-    // more; otherwise 64 x 128 tiles of eight wavefronts, or 64 x 64 ones for large N where
-    // M is just past a multiple of 64 or between 256 and 512 rows
-    if (mid < SMALL_BELOW && N <= 8192) return GR_SMALL32;
+    // 64 x 64 grid has fewer than 256 tiles and N is moderate; the 128 x 256 tile (one workgroup
+    // per CU) when its tiles fill whole waves of 256 (the last one at least 90% full) or there
+    // are four waves or more; otherwise 64 x 128 tiles of eight wavefronts, or 64 x 64 ones when
+    // the 64 x 128 grid has fewer than 192 tiles, or for large N where M is just past a
+    // multiple of 64 or between 256 and 512 rows.  (Rows just past a multiple of 64 are
+    // usually split off to the skinny GEMV first: gemm_tail_rows.)
+    if (mid < SMALL_BELOW / 2 && N <= 8192) return GR_SMALL32;
     if (big >= 4 * 256 || (big >= 230 && (big % 256 == 0 || big % 256 >= 230))) return GR_TILE128x256;
     const int64_t mtail = M % 64;
-    if (N > 8192 && ((mtail > 0 && mtail <= 16) || (M > 256 && M <= 512))) return GR_TILE64;
+    const int64_t w8 = ((M + 63) / 64) * ((N + 127) / 128);
+    if (w8 < 192 || (N > 8192 && ((mtail > 0 && mtail <= 16) || (M > 256 && M <= 512)))) return GR_TILE64;
     return GR_TILE64x128;
 }
 
@@ -1124,7 +1127,28 @@ hipError_t launch_qkv_rope(const GemmArgs& a, const RopeArgs& ra, hipStream_t st
     }
 }
 
+// Rows past a multiple of 64 that would leave the last tile row nearly empty: M = 64 q + r
+// with r <= 4 and 64 q >= 128 runs as the tiled GEMM on the first 64 q rows and the skinny
+// GEMV on the last r (every output's order is per output, so the bits are the same).  Not for
+// a device-side row count.
+int64_t gemm_tail_rows(int64_t M, const int* Mdev) {
+    const int64_t r = M % 64;
+    return (!Mdev && M - r >= 128 && r >= 1 && r <= 4) ? r : 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role) {
+    const int64_t tail = gemm_tail_rows(a.M, a.Mdev);
+    if (tail) {
+        GemmArgs head = a, rest = a;
+        head.M = (int)(a.M - tail);
+        rest.M = (int)tail;
+        rest.X = a.X + (int64_t)head.M * a.ldx;
+        rest.Y = a.Y + (int64_t)head.M * a.ldy;
+        if (a.R) rest.R = a.R + (int64_t)head.M * a.ldr;
+        hipError_t e = launch_gemm(head, st, role);
+        if (e != hipSuccess) return e;
+        return launch_gemm(rest, st, role);
+    }
     if (role == 2) return launch_role<2>(a, st);
     return role == 1 ? launch_role<1>(a, st) : launch_role<0>(a, st);
 }

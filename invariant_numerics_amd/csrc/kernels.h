@@ -33,6 +33,8 @@ enum GemmRoute : int {
     GR_GEMV64, GR_SMALL32, GR_TILE64, GR_TILE64x128, GR_TILE128x256
 };
 GemmRoute gemm_route(int64_t M, int64_t N);
+// rows split off to the skinny GEMV after the tiled part (0: none)
+int64_t gemm_tail_rows(int64_t M, const int* Mdev);
 const char* gemm_route_name(GemmRoute r);   // kernel template with ROLE left symbolic
 // QKV projection of up to four rows (head dim 128) with RoPE and the KV append done by the
 // VALU GEMV's epilogue (role 3); the caller runs the projection and rope_kv_append otherwise

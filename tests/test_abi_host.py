@@ -125,9 +125,11 @@ def test_kernel_route_names(inv):
     assert r("gemm", 512, 14336) == "gemm_mfma_kernel<64,64,2,2,0>"
     assert r("gemm", 2048, 4096) == "gemm_mfma_kernel<128,256,2,4,0>"
     assert r("lmhead_gemm", 128, 128256) == "gemm_mfma_kernel<128,256,2,4,1>"
-    assert r("gemm", 257, 4096) == "gemm_small_kernel<0>"
+    assert r("gemm", 257, 4096) == "gemm_mfma_kernel<64,64,2,2,0>+gemm_skinny_kernel<1,0,4>"
+    assert r("gemm", 256, 4096) == "gemm_mfma_kernel<64,64,2,2,0>"
+    assert r("gemm", 260, 9000) == "gemm_mfma_kernel<64,128,2,4,0>+gemm_skinny_kernel<4,0,16>"
     assert r("gemm", 128, 4096) == "gemm_small_kernel<0>"
-    assert r("gemm", 257, 14336) == "gemm_mfma_kernel<64,64,2,2,0>"
+    assert r("gemm", 257, 14336) == "gemm_mfma_kernel<64,128,2,4,0>+gemm_skinny_kernel<1,0,4>"
     assert r("gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,0>"
     assert r("gemm", 16384, 6144) == "gemm_mfma_kernel<128,256,2,4,0>"
     assert r("gated_gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,2>"

@@ -21,7 +21,7 @@ def inv():
     (8, 8, 5), (8, 1000, 12300), (11, 520, 257), (16, 264, 12289), (13, 4104, 70), (9, 8200, 70),
     (17, 264, 129), (20, 8200, 2049), (32, 520, 12300), (33, 520, 2050), (64, 1032, 4096),
     (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
-    (190, 264, 8300), (260, 520, 9000),
+    (190, 264, 8300), (260, 520, 9000), (129, 264, 300), (193, 520, 8300),
 ])
 def test_gemm_matches_oracle_small(orc, M, K, N):
     say("gemm", M, K, N)
@@ -39,7 +39,7 @@ def test_gemm_residual_epilogue(orc):
     want = (R + orc.gemm(X, W)).astype(np.float32)   # float32 add, as in the oracle decoder
     got = host(inv().inv_fixed_order_gemm(f32(X), bf16(W), R=f32(R)))
     assert_bitwise(got, want, "residual")
-    for rows in (4, 10):
+    for rows in (4, 10, 131):                   # 131 = 128 + a 3-row tail on the skinny GEMV
         Xs = synth.normal(7204 + rows, (rows, 512))
         Rs = synth.normal(7205 + rows, (rows, 96))
         got = host(inv().inv_fixed_order_gemm(f32(Xs), bf16(W), R=f32(Rs)))
@@ -104,7 +104,7 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
 @pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (5, 1000, 64), (16, 4096, 130),
                                    (12, 520, 4200), (9, 264, 6500), (8, 4096, 14336), (6, 8456, 50), (17, 264, 129), (24, 520, 1030),
                                    (48, 264, 1100), (64, 768, 64), (65, 4096, 300),
-                                   (300, 1032, 257), (190, 264, 4200)])
+                                   (300, 1032, 257), (190, 264, 4200), (130, 264, 300)])
 def test_gated_gemm_equals_gemm_then_swiglu(orc, M, K, F):
     """inv_gated_gemm on gate/up rows interleaved equals inv_fixed_order_gemm followed by
     inv_swiglu on its even and odd columns, bit for bit, on the one-wavefront GEMV path
