@@ -797,7 +797,7 @@ __device__ __forceinline__ int qkv_row(int o, int rot) {
     return (o & ~(RD - 1)) + ((j & 1) ? pr + RD / 2 : pr);
 }
 
-template <int MB, int ROLE, int ROWS>
+template <int MB, int ROLE, int ROWS, int MX = 0>
 __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
@@ -812,8 +812,13 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     if (M <= 0) return;
     const int S = (K + KS - 1) / KS;
     const int tid = threadIdx.x;
-    const int sl = tid % SK_LANES;
-    const int nl = tid / SK_LANES;
+    // MX: the chains run on v_mfma_f32_4x4x1_16b_f32 -- block b of a wavefront is slice
+    // group + b, lane 4 b + j supplies weight row 4 w + j (w: wavefront) and activation row j
+    // (plus 4 g for the g-th group of four rows), and gets the four rows' accumulators of its
+    // weight row.  One instruction is one fma per (row, weight row, slice), the chain's step.
+    static_assert(MX == 0 || (MB % 4 == 0 && ROWS % 4 == 0), "matrix GEMV: 4-row groups");
+    const int sl = MX ? (tid & 63) >> 2 : tid % SK_LANES;
+    const int nl = MX ? ((tid >> 6) << 2) + (tid & 3) : tid / SK_LANES;
     const int n0 = blockIdx.x * ROWS;
     const int rot = ROLE == 3 ? (ra.Hq + ra.Hkv) * RD : 0;     // rotated outputs (ROLE 3)
 
@@ -875,6 +880,8 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const int fm = tid / ROWS, fr = tid % ROWS;   // output folded by this thread
     float T = 0.0f;
     float c[MB];
+    constexpr int NG = MX ? MB / 4 : 1;
+    f32x4v cm[NG];
     // one phase: its tile is in LDS; every thread advances its slice chain over it
     auto compute = [&](int st) {
         const int sg = (st / (KS / PH)) * SK_LANES;
@@ -882,12 +889,53 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
         if (p == 0) {
 #pragma unroll
             for (int m = 0; m < MB; ++m) c[m] = 0.0f;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) cm[g] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
         }
         const int s = sg + sl;
         const int kb = s * KS + p * PH;                       // first k of this phase
         const int nk = min(PH, K - kb);                       // elements of this phase (<= 0: none)
         const unsigned char* wseg = &Wl[(nl * SK_LANES + sl) * WSEG];
-        if (nk == PH) {
+        if constexpr (MX != 0) {
+            // A lane past its chain's end feeds 0 * 0: the accumulator, never -0 (it starts
+            // at +0 and an exact zero sum rounds to +0), is unchanged.
+            const int mi = tid & 3;
+            const bool full = (sg + SK_LANES - 1) * KS + (p + 1) * PH <= K;
+#pragma unroll
+            for (int j = 0; j < PH / 8; ++j) {
+                const uint4 w8 = *reinterpret_cast<const uint4*>(wseg + 16 * j);
+                float w[8] = {bf16_lo(w8.x), bf16_hi(w8.x), bf16_lo(w8.y), bf16_hi(w8.y),
+                              bf16_lo(w8.z), bf16_hi(w8.z), bf16_lo(w8.w), bf16_hi(w8.w)};
+                float x[NG][8];
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const float4 xa = *reinterpret_cast<const float4*>(&Xl[4 * g + mi][sl][8 * j]);
+                    const float4 xb = *reinterpret_cast<const float4*>(&Xl[4 * g + mi][sl][8 * j + 4]);
+                    x[g][0] = xa.x; x[g][1] = xa.y; x[g][2] = xa.z; x[g][3] = xa.w;
+                    x[g][4] = xb.x; x[g][5] = xb.y; x[g][6] = xb.z; x[g][7] = xb.w;
+                }
+                if (!full) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const bool ok = 8 * j + e < nk;
+                        w[e] = ok ? w[e] : 0.0f;
+#pragma unroll
+                        for (int g = 0; g < NG; ++g) x[g][e] = ok ? x[g][e] : 0.0f;
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g)
+                        cm[g] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[g][e], w[e], cm[g], 0, 0, 0);
+            }
+            if (p == KS / PH - 1) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) c[4 * g + i] = cm[g][i];
+            }
+        } else if (nk == PH) {
 #pragma unroll
             for (int j = 0; j < PH / 8; ++j) {
                 const uint4 w8 = *reinterpret_cast<const uint4*>(wseg + 16 * j);
@@ -1006,10 +1054,10 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int MB, int ROLE, int ROWS>
+template <int MB, int ROLE, int ROWS, int MX = 0>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra = RopeArgs{}) {
     dim3 grid((a.N + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, ROWS>), grid, dim3(ROWS * SK_LANES), 0, st,
+    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, ROWS, MX>), grid, dim3(ROWS * SK_LANES), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev, ra);
     return hipGetLastError();
 }
@@ -1018,8 +1066,9 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra =
 
 // Kernel choice for M rows and N weight rows (launch geometry only: the order of every
 // output's sum is the same on every route, which the tests check across M).
-//   M <= 4: the VALU GEMV (16-row workgroups, or 4-row ones for N < 16384 and M <= 2 so the
-//     small projections still spread evenly over the CUs);
+//   M <= 4: the slice-parallel GEMV (16-row workgroups, or 4-row ones for N < 16384 and M <= 2
+//     so the small projections still spread evenly over the CUs), its chains on the VALU for
+//     M <= 2 and on 4x4x1 matrix instructions for M = 3-4 (8-12% faster there, equal bits);
 //   5 <= M <= 16: the matrix-core GEMV with one 16-row tile (the VALU GEMV's per-row
 //     accumulators and LDS reads make it slower from 5 rows on); weight rows per workgroup:
 //     64 from N = 65536 (four wavefronts along the rows), 32 from 12288 (two along the rows,
@@ -1069,7 +1118,7 @@ const char* gemm_route_name(GemmRoute r) {
         case GR_SKINNY_M1_R16: return "gemm_skinny_kernel<1,ROLE,16>";
         case GR_SKINNY_M2_R4: return "gemm_skinny_kernel<2,ROLE,4>";
         case GR_SKINNY_M2_R16: return "gemm_skinny_kernel<2,ROLE,16>";
-        case GR_SKINNY_M4_R16: return "gemm_skinny_kernel<4,ROLE,16>";
+        case GR_SKINNY_M4_R16: return "gemm_skinny_kernel<4,ROLE,16,1>";
         case GR_GEMV16_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,1,4>";
         case GR_GEMV16_WN1_W8: return "gemm_gemv16_kernel<1,2,64,ROLE,1,8>";
         case GR_GEMV16_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,1,4>";
@@ -1094,7 +1143,7 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         case GR_SKINNY_M1_R16: return launch_skinny<1, ROLE, 16>(a, st);
         case GR_SKINNY_M2_R4: return launch_skinny<2, ROLE, 4>(a, st);
         case GR_SKINNY_M2_R16: return launch_skinny<2, ROLE, 16>(a, st);
-        case GR_SKINNY_M4_R16: return launch_skinny<4, ROLE, 16>(a, st);
+        case GR_SKINNY_M4_R16: return launch_skinny<4, ROLE, 16, 1>(a, st);
         case GR_GEMV16_WN1: return launch_gemv16<1, 2, 64, ROLE>(a, st);
         case GR_GEMV16_WN1_W8: return launch_gemv16<1, 2, 64, ROLE, 1, 8>(a, st);
         case GR_GEMV16_WN2: return launch_gemv16<2, 2, 64, ROLE>(a, st);
@@ -1122,7 +1171,7 @@ hipError_t launch_qkv_rope(const GemmArgs& a, const RopeArgs& ra, hipStream_t st
         case GR_SKINNY_M1_R16: return launch_skinny<1, 3, 16>(a, st, ra);
         case GR_SKINNY_M2_R4: return launch_skinny<2, 3, 4>(a, st, ra);
         case GR_SKINNY_M2_R16: return launch_skinny<2, 3, 16>(a, st, ra);
-        case GR_SKINNY_M4_R16: return launch_skinny<4, 3, 16>(a, st, ra);
+        case GR_SKINNY_M4_R16: return launch_skinny<4, 3, 16, 1>(a, st, ra);
         default: return hipErrorInvalidValue;
     }
 }

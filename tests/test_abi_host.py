@@ -113,7 +113,7 @@ def test_kernel_route_names(inv):
     r = inv.inv_kernel_route
     assert r("gemm", 1, 4096) == "gemm_skinny_kernel<1,0,4>"
     assert r("gemm", 1, 28672) == "gemm_skinny_kernel<1,0,16>"
-    assert r("gemm", 3, 4096) == "gemm_skinny_kernel<4,0,16>"
+    assert r("gemm", 3, 4096) == "gemm_skinny_kernel<4,0,16,1>"
     assert r("gemm", 16, 4096) == "gemm_gemv16_kernel<1,2,64,0,1,8>"
     assert r("gemm", 16, 6144) == "gemm_gemv16_kernel<1,2,64,0,1,4>"
     assert r("gemm", 32, 14336) == "gemm_gemv16_kernel<2,2,64,0,2,4>"
@@ -127,7 +127,7 @@ def test_kernel_route_names(inv):
     assert r("lmhead_gemm", 128, 128256) == "gemm_mfma_kernel<128,256,2,4,1>"
     assert r("gemm", 257, 4096) == "gemm_mfma_kernel<64,64,2,2,0>+gemm_skinny_kernel<1,0,4>"
     assert r("gemm", 256, 4096) == "gemm_mfma_kernel<64,64,2,2,0>"
-    assert r("gemm", 260, 9000) == "gemm_mfma_kernel<64,128,2,4,0>+gemm_skinny_kernel<4,0,16>"
+    assert r("gemm", 260, 9000) == "gemm_mfma_kernel<64,128,2,4,0>+gemm_skinny_kernel<4,0,16,1>"
     assert r("gemm", 128, 4096) == "gemm_small_kernel<0>"
     assert r("gemm", 257, 14336) == "gemm_mfma_kernel<64,128,2,4,0>+gemm_skinny_kernel<1,0,4>"
     assert r("gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,0>"

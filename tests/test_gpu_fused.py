@@ -18,7 +18,8 @@ def inv():
 
 
 @pytest.mark.parametrize("M,K,Hq,Hkv", [(1, 4096, 32, 8), (2, 4096, 32, 8), (3, 4096, 32, 8), (4, 512, 4, 2),
-                                        (1, 264, 2, 1), (5, 4096, 32, 8), (2, 8200, 4, 4)])
+                                        (1, 264, 2, 1), (5, 4096, 32, 8), (2, 8200, 4, 4),
+                                        (4, 8200, 4, 2), (3, 72, 2, 2)])
 def test_qkv_rope_kv_append_matches_oracle(orc, M, K, Hq, Hkv):
     D, Tmax, Bc = 128, 300, 5
     say("qkv rope", M, K, Hq, Hkv)

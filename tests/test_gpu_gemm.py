@@ -17,6 +17,7 @@ def inv():
 
 @pytest.mark.parametrize("M,K,N", [
     (1, 8, 5), (1, 264, 70), (2, 4096, 130), (3, 520, 257), (4, 8200, 33), (4, 72, 17), (2, 16, 1),
+    (3, 8, 5), (4, 16, 300), (3, 4104, 66),
     (5, 1000, 64), (16, 4096, 33),
     (8, 8, 5), (8, 1000, 12300), (11, 520, 257), (16, 264, 12289), (13, 4104, 70), (9, 8200, 70),
     (17, 264, 129), (20, 8200, 2049), (32, 520, 12300), (33, 520, 2050), (64, 1032, 4096),
@@ -101,7 +102,7 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
     assert_bitwise(full[rows][:, cols], want, "oracle sample")
 
 
-@pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (5, 1000, 64), (16, 4096, 130),
+@pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (3, 520, 70), (4, 8200, 37), (5, 1000, 64), (16, 4096, 130),
                                    (12, 520, 4200), (9, 264, 6500), (8, 4096, 14336), (6, 8456, 50), (17, 264, 129), (24, 520, 1030),
                                    (48, 264, 1100), (64, 768, 64), (65, 4096, 300),
                                    (300, 1032, 257), (190, 264, 4200), (130, 264, 300)])
