@@ -54,33 +54,42 @@ __device__ __forceinline__ void top2_merge(Top2& t, const Top2& o) {
 }
 
 // Row reduction in three kernels, so a few rows still spread over the whole chip:
-//   top2_kernel   grid (groups of 4 tiles = 4096 entries, rows): each workgroup's top-2 of
-//                 its entries (order free: a total order on (value desc, index asc));
-//   tiles_kernel  same grid: merges the row's partial top-2 pairs (again order free) to get
-//                 M = z_top1, then one wavefront per tile of its group sums exp_f(z - M) in the
-//                 pinned lane order and combines the 64 lanes pairwise -> S_u;
+//   top2_kernel   grid (groups of TOPG tiles, rows): each workgroup's top-2 of its entries,
+//                 all requested before the first comparison (order free: a total order on
+//                 (value desc, index asc));
+//   tiles_kernel  grid (groups of 4 tiles, rows): merges the row's partial top-2 pairs (again
+//                 order free) to get M = z_top1, then one wavefront per tile of its group sums
+//                 exp_f(z - M) in the pinned lane order and combines the 64 lanes pairwise ->
+//                 S_u; the first workgroup of a row stores the merged top-2 for the last kernel;
 //   final_kernel  one thread per row: S = S_0, S = S + S_u ascending; lp; margin; flags.
 // mode 0: rows 0..gridDim.y-1 as they are (output row = row); mode 1: F pass over the first
 // *count rows of the compacted list (output row = idx[row]).
-constexpr int GROUP = 4;                 // tiles per workgroup
+constexpr int GROUP = 4;                 // tiles per workgroup of the tiles kernel
 constexpr int LM_FUSED_MAX_B = 16;       // batch sizes whose FP32 logits share the primary GEMM
 
 __device__ __forceinline__ const float* zrow(const float* z, int V, int row) {
     return z + (int64_t)row * V;
 }
-constexpr int GV = GROUP * TV;           // vocabulary entries per workgroup
+constexpr int TOPG = 4;                  // tiles per workgroup of the top-2 kernel
+constexpr int TOPE = TOPG * TV / RED_THREADS;   // entries per thread of the top-2 kernel
 
 __global__ __launch_bounds__(RED_THREADS) void lmhead_top2_kernel(
     const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
     Top2* __restrict__ part) {
     __shared__ Top2 wtop[RED_THREADS / 64];
-    const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
+    const int u = blockIdx.x, row = blockIdx.y, ntop = gridDim.x;
     if (mode != 0 && row >= *count) return;
     const float* zr = zrow(z, V, row);
     const int tid = threadIdx.x, lane = tid % 64, w = tid / 64;
+    float zv[TOPE];
+#pragma unroll
+    for (int e = 0; e < TOPE; ++e) zv[e] = zr[min(u * TOPG * TV + e * RED_THREADS + tid, V - 1)];
     Top2 t = {-__builtin_inff(), 0x7fffffff, -__builtin_inff(), 0x7fffffff};
-    const int v0 = grp * GV, v1 = min(V, v0 + GV);
-    for (int v = v0 + tid; v < v1; v += RED_THREADS) top2_push(t, zr[v], v);
+#pragma unroll
+    for (int e = 0; e < TOPE; ++e) {
+        const int v = u * TOPG * TV + e * RED_THREADS + tid;
+        if (v < V) top2_push(t, zv[e], v);
+    }
     for (int off = 32; off >= 1; off >>= 1) {
         Top2 o;
         o.v1 = __shfl_xor(t.v1, off); o.i1 = __shfl_xor(t.i1, off);
@@ -92,38 +101,27 @@ __global__ __launch_bounds__(RED_THREADS) void lmhead_top2_kernel(
     if (tid == 0) {
         t = wtop[0];
         for (int k = 1; k < RED_THREADS / 64; ++k) top2_merge(t, wtop[k]);
-        part[(int64_t)row * ngrp + grp] = t;
+        part[(int64_t)row * ntop + u] = t;
     }
 }
 
-// The row's top-2 from its partials.  Values that compare with nothing (NaN logits) leave
-// the sentinel index in place; such an index is replaced by the scan's starting choice
-// (top1 = 0, top2 = the lowest index != top1), so no index >= V ever reaches a load.
-__device__ __forceinline__ Top2 merged_top2(const Top2* __restrict__ part, int row, int ngrp, int V) {
-    const Top2* pr = part + (int64_t)row * ngrp;
-    Top2 t = pr[0];
-    int k = 1;
-    for (; k + 8 <= ngrp; k += 8) {             // loads issued 8 at a time (the merge is order-free)
-        Top2 q[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) q[u] = pr[k + u];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) top2_merge(t, q[u]);
-    }
-    for (; k < ngrp; ++k) top2_merge(t, pr[k]);
-    if (t.i1 < 0 || t.i1 >= V) t.i1 = 0;
-    if (t.i2 < 0 || t.i2 >= V || t.i2 == t.i1) t.i2 = (t.i1 == 0) ? 1 : 0;
-    return t;
-}
-
-// The same top-2 computed by a whole wavefront: lanes read the partial pairs in parallel and
-// merge them in a shuffle tree (the merge is order free, so the result is the serial one's);
-// every lane returns it.
+// The row's top-2 from its partials, computed by a whole wavefront: each lane merges up to two
+// partial pairs per round (both requested before either merge), then the lanes merge in a
+// shuffle tree (the merge is order free, so the result is the serial one's); every lane
+// returns it.  Values that compare with nothing (NaN logits) leave the sentinel index in
+// place; such an index is replaced by the scan's starting choice (top1 = 0, top2 = the lowest
+// index != top1), so no index >= V ever reaches a load.
 __device__ __forceinline__ Top2 merged_top2_wave(const Top2* __restrict__ part, int row, int ngrp, int V,
                                                  int lane) {
     const Top2* pr = part + (int64_t)row * ngrp;
     Top2 t = {-__builtin_inff(), 0x7fffffff, -__builtin_inff(), 0x7fffffff};
-    for (int k = lane; k < ngrp; k += 64) top2_merge(t, pr[k]);
+    for (int k = lane; k < ngrp; k += 128) {
+        const bool two = k + 64 < ngrp;
+        const Top2 q0 = pr[k];
+        const Top2 q1 = pr[two ? k + 64 : k];
+        top2_merge(t, q0);
+        if (two) top2_merge(t, q1);
+    }
     for (int off = 32; off >= 1; off >>= 1) {
         Top2 o;
         o.v1 = __shfl_xor(t.v1, off); o.i1 = __shfl_xor(t.i1, off);
@@ -137,12 +135,13 @@ __device__ __forceinline__ Top2 merged_top2_wave(const Top2* __restrict__ part, 
 
 __global__ __launch_bounds__(RED_THREADS) void lmhead_tiles_kernel(
     const float* __restrict__ z, int V, int mode, const int32_t* __restrict__ count,
-    const Top2* __restrict__ part, float* __restrict__ tileS) {
-    const int grp = blockIdx.x, row = blockIdx.y, ngrp = gridDim.x;
+    const Top2* __restrict__ part, int ntop, Top2* __restrict__ rowtop, float* __restrict__ tileS) {
+    const int grp = blockIdx.x, row = blockIdx.y;
     if (mode != 0 && row >= *count) return;
     const float* zr = zrow(z, V, row);
     const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
-    const Top2 t = merged_top2_wave(part, row, ngrp, V, lane);
+    const Top2 t = merged_top2_wave(part, row, ntop, V, lane);
+    if (grp == 0 && threadIdx.x == 0) rowtop[row] = t;   // the row's top-2 for the final kernels
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
     const int u = grp * GROUP + w;                       // this wavefront's tile
@@ -179,12 +178,12 @@ struct RowOut {
     float lp, mg; int t1, t2;
 };
 
-// lp, margin and the top-2 of reduced row `row` (its logits, partial top-2 pairs and tile sums)
+// lp, margin and the top-2 of reduced row `row` (its logits, top-2 and tile sums)
 __device__ __forceinline__ RowOut row_result(const float* __restrict__ z, int V, int row, int tg,
-                                             const Top2* __restrict__ part, int ngrp,
+                                             const Top2* __restrict__ rowtop,
                                              const float* __restrict__ tileS) {
     const float* zr = zrow(z, V, row);
-    const Top2 t = merged_top2(part, row, ngrp, V);
+    const Top2 t = rowtop[row];
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
     const float S = fold_tiles(tileS + (int64_t)row * ntiles, ntiles);
@@ -201,14 +200,14 @@ __device__ __forceinline__ RowOut row_result(const float* __restrict__ z, int V,
 __global__ void lmhead_final_kernel(
     const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau, int mode,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-    const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
+    const Top2* __restrict__ rowtop, const float* __restrict__ tileS,
     float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
     int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= B) return;
     if (mode != 0 && row >= *count) return;
     const int orow = mode != 0 ? idx[row] : row;
-    const RowOut r = row_result(z, V, row, target[orow], part, ngrp, tileS);
+    const RowOut r = row_result(z, V, row, target[orow], rowtop, tileS);
     logprob[orow] = r.lp;
     margin[orow] = r.mg;
     top1[orow] = r.t1;
@@ -219,13 +218,13 @@ __global__ void lmhead_final_kernel(
 // Rows 0..B-1 are the primary pass and rows B..2B-1 the FP32 pass of the same hidden states:
 // output row b takes the FP32 result when the primary margin is below tau (strict; NaN never).
 // One workgroup of two wavefronts per output row: wavefront 0 finishes row b, wavefront 1 row
-// B + b.  Each merges its row's partial top-2 pairs in parallel, stages the tile sums in LDS
-// (all requested at once) and lets one lane fold them in ascending order.
+// B + b.  Each stages its row's tile sums in LDS (all requested at once) and lets one lane fold
+// them in ascending order.
 constexpr int SEL_MAXT = 1024;           // tiles per row held in LDS (V <= 1024 tiles)
 
 __global__ __launch_bounds__(128) void lmhead_final_select_kernel(
     const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target, float tau,
-    const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
+    const Top2* __restrict__ rowtop, const float* __restrict__ tileS,
     float* __restrict__ logprob, float* __restrict__ margin, int32_t* __restrict__ top1,
     int32_t* __restrict__ top2, uint8_t* __restrict__ recomputed) {
     __shared__ __attribute__((aligned(16))) float ts[2][SEL_MAXT];
@@ -233,13 +232,13 @@ __global__ __launch_bounds__(128) void lmhead_final_select_kernel(
     const int b = blockIdx.x, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int row = w == 0 ? b : B + b;
     const int tg = target[b];
-    const Top2 t = merged_top2_wave(part, row, ngrp, V, lane);
     const int ntiles = (V + TV - 1) / TV;
     const float* tr = tileS + (int64_t)row * ntiles;
     for (int u = lane; u < ntiles; u += 64) ts[w][u] = tr[u];
     for (int u = ntiles + lane; u < ((ntiles + 3) & ~3); u += 64) ts[w][u] = 0.0f;   // last float4's padding
     __syncthreads();
     if (lane == 0) {
+        const Top2 t = rowtop[row];
         const float* zr = zrow(z, V, row);
         const float M = zr[t.i1];
         const float z2 = zr[t.i2];
@@ -273,12 +272,12 @@ __global__ __launch_bounds__(128) void lmhead_final_select_kernel(
 
 // Logit gradient, step 1: per row M = z_top1 and S (the forward's fold), and the logprob.
 __global__ void lmhead_rowstats_kernel(const float* __restrict__ z, int V, int B, const int32_t* __restrict__ target,
-                                       const Top2* __restrict__ part, int ngrp, const float* __restrict__ tileS,
+                                       const Top2* __restrict__ rowtop, const float* __restrict__ tileS,
                                        float* __restrict__ stats, float* __restrict__ logprob) {
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= B) return;
     const float* zr = z + (int64_t)row * V;
-    const Top2 t = merged_top2(part, row, ngrp, V);
+    const Top2 t = rowtop[row];
     const float M = zr[t.i1];
     const int ntiles = (V + TV - 1) / TV;
     const float S = fold_tiles(tileS + (int64_t)row * ntiles, ntiles);
@@ -364,18 +363,19 @@ __global__ void gather_rows_kernel(const float* __restrict__ H, int K, int64_t l
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t a, z, idx, count, part, tiles, total;
+    size_t a, z, idx, count, part, rowtop, tiles, total;
 };
 WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
     WsLayout L;
-    const int64_t ngrp = (V + GV - 1) / GV, ntiles = (V + TV - 1) / TV;
+    const int64_t ntiles = (V + TV - 1) / TV;
     const int64_t zrows = B <= LM_FUSED_MAX_B ? 2 * B : B;     // P rows, then F rows when fused
     size_t off = 0;
     L.a = off; off = align_up(off + sizeof(float) * (size_t)zrows * K);
     L.z = off; off = align_up(off + sizeof(float) * (size_t)zrows * V);
     L.idx = off; off = align_up(off + sizeof(int32_t) * (size_t)B);
     L.count = off; off = align_up(off + sizeof(int32_t));
-    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)zrows * ngrp);
+    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)zrows * ((ntiles + TOPG - 1) / TOPG));
+    L.rowtop = off; off = align_up(off + sizeof(Top2) * (size_t)zrows);
     L.tiles = off; off = align_up(off + sizeof(float) * (size_t)zrows * ntiles);
     L.total = off;
     return L;
@@ -383,36 +383,37 @@ WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
 
 // top-2 partials and tile sums of `rows` logit rows (mode 0: all of them; mode 1: the first
 // *count, the compacted F rows)
-hipError_t launch_row_stats(const float* Z, int V, int rows, int mode, const int32_t* count, Top2* part,
+hipError_t launch_row_stats(const float* Z, int V, int rows, int mode, const int32_t* count, Top2* part, Top2* rowtop,
                             float* tiles, hipStream_t st) {
-    const int ngrp = (V + GV - 1) / GV;
-    dim3 grid(ngrp, rows);
-    hipLaunchKernelGGL(lmhead_top2_kernel, grid, dim3(RED_THREADS), 0, st, Z, V, mode, count, part);
+    const int ntiles = (V + TV - 1) / TV;
+    const int ntop = (ntiles + TOPG - 1) / TOPG;
+    hipLaunchKernelGGL(lmhead_top2_kernel, dim3(ntop, rows), dim3(RED_THREADS), 0, st, Z, V, mode, count, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lmhead_tiles_kernel, grid, dim3(RED_THREADS), 0, st, Z, V, mode, count, part, tiles);
+    hipLaunchKernelGGL(lmhead_tiles_kernel, dim3((ntiles + GROUP - 1) / GROUP, rows), dim3(RED_THREADS), 0, st, Z,
+                       V, mode, count, part, ntop, rowtop, tiles);
     return hipGetLastError();
 }
 
 hipError_t launch_reduce(const LmheadArgs& a, int mode, const float* Z, const int32_t* idx,
-                         const int32_t* count, Top2* part, float* tiles, hipStream_t st) {
-    const int ngrp = (a.V + GV - 1) / GV;
-    hipError_t e = launch_row_stats(Z, a.V, a.B, mode, count, part, tiles, st);
+                         const int32_t* count, Top2* part, Top2* rowtop, float* tiles, hipStream_t st) {
+    hipError_t e = launch_row_stats(Z, a.V, a.B, mode, count, part, rowtop, tiles, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_final_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, Z, a.V, a.B, a.target,
-                       a.tau, mode, idx, count, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
+                       a.tau, mode, idx, count, rowtop, tiles, a.logprob, a.margin, a.top1, a.top2,
                        a.recomputed);
     return hipGetLastError();
 }
 
 struct GradWs {
-    size_t part, tiles, stats, total;
+    size_t part, rowtop, tiles, stats, total;
 };
 GradWs grad_ws_layout(int64_t B, int64_t V) {
     GradWs L;
-    const int64_t ngrp = (V + GV - 1) / GV, ntiles = (V + TV - 1) / TV;
+    const int64_t ntiles = (V + TV - 1) / TV;
     size_t off = 0;
-    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)B * ngrp);
+    L.part = off; off = align_up(off + sizeof(Top2) * (size_t)B * ((ntiles + TOPG - 1) / TOPG));
+    L.rowtop = off; off = align_up(off + sizeof(Top2) * (size_t)B);
     L.tiles = off; off = align_up(off + sizeof(float) * (size_t)B * ntiles);
     L.stats = off; off = align_up(off + sizeof(float) * 2 * (size_t)B);
     L.total = off;
@@ -436,15 +437,15 @@ hipError_t launch_logit_grad(const LogitGradArgs& a, hipStream_t st) {
     const GradWs L = grad_ws_layout(a.B, a.V);
     char* ws = reinterpret_cast<char*>(a.ws);
     Top2* part = reinterpret_cast<Top2*>(ws + L.part);
+    Top2* rowtop = reinterpret_cast<Top2*>(ws + L.rowtop);
     float* tiles = reinterpret_cast<float*>(ws + L.tiles);
     float* stats = reinterpret_cast<float*>(ws + L.stats);
     hipError_t e;
     GemmArgs ga{a.Hs, a.B, a.K, a.ldh, a.W, a.V, (int64_t)a.K, nullptr, 0, a.G, (int64_t)a.V, nullptr};
     if ((e = launch_gemm(ga, st, 1)) != hipSuccess) return e;
-    const int ngrp = (a.V + GV - 1) / GV;
-    if ((e = launch_row_stats(a.G, a.V, a.B, 0, nullptr, part, tiles, st)) != hipSuccess) return e;
+    if ((e = launch_row_stats(a.G, a.V, a.B, 0, nullptr, part, rowtop, tiles, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(lmhead_rowstats_kernel, dim3((a.B + 63) / 64), dim3(64), 0, st, a.G, a.V, a.B, a.target,
-                       part, ngrp, tiles, stats, a.logprob);
+                       rowtop, tiles, stats, a.logprob);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int gx = (a.V + 1023) / 1024;
     hipLaunchKernelGGL(logit_grad_kernel, dim3(gx < 64 ? gx : 64, a.B), dim3(256), 0, st, a.G, a.V, a.target, a.coef,
@@ -460,6 +461,7 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
     int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
     Top2* part = reinterpret_cast<Top2*>(ws + L.part);
+    Top2* rowtop = reinterpret_cast<Top2*>(ws + L.rowtop);
     float* tiles = reinterpret_cast<float*>(ws + L.tiles);
     hipError_t e;
 
@@ -478,14 +480,13 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
 
     if (fused) {
         // both passes' rows in one reduce; the last kernel picks each row's pass
-        if ((e = launch_row_stats(Z, a.V, 2 * a.B, 0, nullptr, part, tiles, st)) != hipSuccess) return e;
-        const int ngrp = (a.V + GV - 1) / GV;
+        if ((e = launch_row_stats(Z, a.V, 2 * a.B, 0, nullptr, part, rowtop, tiles, st)) != hipSuccess) return e;
         hipLaunchKernelGGL(lmhead_final_select_kernel, dim3(a.B), dim3(128), 0, st, Z, a.V, a.B,
-                           a.target, a.tau, part, ngrp, tiles, a.logprob, a.margin, a.top1, a.top2,
+                           a.target, a.tau, rowtop, tiles, a.logprob, a.margin, a.top1, a.top2,
                            a.recomputed);
         return hipGetLastError();
     }
-    if ((e = launch_reduce(a, 0, Z, nullptr, nullptr, part, tiles, st)) != hipSuccess) return e;
+    if ((e = launch_reduce(a, 0, Z, nullptr, nullptr, part, rowtop, tiles, st)) != hipSuccess) return e;
     if (!recompute) return hipSuccess;
 
     hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, st, a.recomputed, a.B, idx, count);
@@ -496,7 +497,7 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     GemmArgs gf{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, count};
     if ((e = launch_gemm(gf, st, 1)) != hipSuccess) return e;
 
-    return launch_reduce(a, 1, Z, idx, count, part, tiles, st);
+    return launch_reduce(a, 1, Z, idx, count, part, rowtop, tiles, st);
 }
 
 }  // namespace invnum
