@@ -5,13 +5,16 @@ Seeded synthetic inputs from ``synth`` (the same arrays the parity tests use); e
 is the median of HIP-event-bracketed repetitions on the current stream, inputs resident in
 HBM.  Prints one JSON object per measurement:
   * C1: LM head, hidden 256, vocab 4096, 64 tokens as 64 / B calls of batch B;
-  * C2: causal attention, 8 heads x 2048 x 128, BF16 inputs: the whole prefill, and decode
-    calls at every 8th position;
+  * C2: causal attention, 8 heads x 2048 x 128, BF16 inputs: the whole prefill (four calls
+    back to back per timing, buffers allocated beforehand), and decode calls at every 8th
+    position;
   * C3: fixed-order GEMM at M in {1, 3, 16, 64, 257, 512} for the 4096 x 4096, 14336 x 4096
     and 4096 x 14336 weights, rotating over weight copies larger than the 256 MB last-level
-    cache so every call reads its weights from HBM;
-  * C4: LM head, hidden 4096, vocab 128256, B = 1 .. 256 (bytes count a second weight read
-    when any row is recomputed and B > 16; up to 16 rows the FP32 logits share the sweep);
+    cache so every call reads its weights from HBM; eight calls back to back per timing (the
+    launch gaps count, the host's time to issue a call does not);
+  * C4: LM head, hidden 4096, vocab 128256, B = 1 .. 256, four calls back to back per timing
+    with their buffers allocated beforehand (bytes count a second weight read when any row is
+    recomputed and B > 16; up to 16 rows the FP32 logits share the sweep);
   * C5 decode: graph-replayed decode steps of the 4-layer decoder at a 32k context for
     B = 1, 4, 16, 64 (seeded random KV caches; bytes = weights + the KV read once);
   * probes: the practical ceilings the kernels are compared with -- a plain 16-byte read
@@ -65,16 +68,23 @@ if "C1" in SECTIONS:
     d = synth.c1_inputs()
     H, W, T = f32(d["h"]), bf(d["w"]), torch.from_numpy(np.ascontiguousarray(d["target"], np.int32)).to(dev)
     for B in (1, 2, 4, 8):
+        ws1 = torch.empty(inv.inv_lmhead_workspace_bytes(B, 256, 4096), dtype=torch.uint8, device=dev)
+        r1 = inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1, ws=ws1)
         def run():
             for s in range(0, 64, B):
-                inv.inv_lmhead_logprob_top2(H[s:s + B], W, T[s:s + B], 0.1)
+                inv.inv_lmhead_logprob_top2(H[s:s + B], W, T[s:s + B], 0.1, ws=ws1, out=r1)
         t = timeit(run)
         out(config="C1", batch=B, calls=64 // B, us_per_call=round(t / (64 // B) * 1e6, 1), tokens_per_s=round(64 / t, 1))
 # ---- C2: attention 8 heads x 2048 x d128, bf16, causal
 if "C2" in SECTIONS:
     d = synth.c2_inputs()
     q, k, v = bf(d["q"]), bf(d["k"]), bf(d["v"])
-    t = timeit(lambda: inv.inv_attention_prefill(q, k, v))
+    op = torch.empty((1, 2048, 8, 128), dtype=torch.float32, device=dev)
+    wsp = torch.empty(max(1, inv.inv_attention_prefill_workspace_bytes(1, 2048, 0, 8, 128)), dtype=torch.uint8, device=dev)
+    def pre4():
+        for _ in range(4):
+            inv.inv_attention_prefill(q, k, v, out=op, ws=wsp)
+    t = timeit(pre4) / 4
     pairs = 8 * 2048 * 2049 // 2
     out(config="C2", op="prefill", ms=round(t * 1e3, 3), tflops=round(pairs * 512 / t / 1e12, 2), frac_fp32_peak=round(pairs * 512 / t / 157.3e12, 3))
     ws = torch.empty(inv.inv_attention_decode_workspace_bytes(1, 2048, 8, 128), dtype=torch.uint8, device=dev)
@@ -96,9 +106,11 @@ if "C3" in SECTIONS:
         for M in (1, 3, 16, 64, 257, 512):
             Y = torch.empty((M, n), dtype=torch.float32, device=dev)
             ctr = [0]
+            Xm = X[:M]
             def g():
-                inv.inv_fixed_order_gemm(X[:M], Ws[ctr[0] % len(Ws)], out=Y); ctr[0] += 1
-            t = timeit(g, reps=12)
+                for _ in range(8):
+                    inv.inv_fixed_order_gemm(Xm, Ws[ctr[0] % len(Ws)], out=Y); ctr[0] += 1
+            t = timeit(g, reps=12) / 8
             by = n * kk * 2 + 4 * M * kk + 4 * M * n
             out(config="C3", N=n, K=kk, M=M, us=round(t * 1e6, 1), tflops=round(2 * M * n * kk / t / 1e12, 2),
                 hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3), frac_fp32=round(2 * M * n * kk / t / 157.3e12, 3))
@@ -108,9 +120,13 @@ if "C4" in SECTIONS:
     d = synth.c4_inputs()
     H, W, T = f32(d["h"]), bf(d["w"]), torch.from_numpy(np.ascontiguousarray(d["target"], np.int32)).to(dev)
     for B in (1, 2, 4, 8, 16, 32, 64, 128, 256):
-        r = inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1)
+        ws = torch.empty(inv.inv_lmhead_workspace_bytes(B, 4096, 128256), dtype=torch.uint8, device=dev)
+        r = inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1, ws=ws)
         nrec = int(r["recomputed"].sum().item())
-        t = timeit(lambda: inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1), reps=6)
+        def four():
+            for _ in range(4):
+                inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1, ws=ws, out=r)
+        t = timeit(four, reps=6) / 4
         wb = 1050673152
         by = wb * (2 if (nrec and B > 16) else 1) + B * 4096 * 4
         out(config="C4", batch=B, recomputed=nrec, us=round(t * 1e6, 1), tokens_per_s=round(B / t, 1),
