@@ -115,11 +115,12 @@ def test_c5_prefill_projections_sampled(orc, name, N, K, kind):
     assert_bitwise(got[rows][:, cols], want, "%s sampled" % name)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 16, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16, 32])
 def test_c5_decode_projections_match_oracle(orc, M):
-    """The decode-step projections at the Llama-8B shapes (batch 1, 2, 3-4, 16 and 32 rows:
-    the VALU GEMV and the one- and two-tile matrix-core GEMVs), element by element: QKV, O and
-    W2 with the residual, W1||W3 with the gated epilogue."""
+    """The decode-step projections at the Llama-8B shapes (batch 1 and 2 rows: the slice GEMV's
+    VALU chains; 3 and 4: its 4x4x1 matrix chains; 16 and 32: the one- and two-tile matrix-core
+    GEMVs), element by element: QKV, O and W2 with the residual, W1||W3 with the gated
+    epilogue."""
     H, F, QKV = 4096, 14336, 6144
     X = synth.normal(12300 + M, (M, H))
     Xf = synth.normal(12301 + M, (M, F))
@@ -221,8 +222,9 @@ def lm(h, wd, tgt, tau):
 @pytest.mark.parametrize("B,tau", [(1, 0.0), (1, 0.1), (1, np.inf), (2, 0.1), (4, 0.1), (8, 0.1)])
 def test_lmhead_full_vocabulary_small_batch(orc, c4, B, tau):
     """The full 128256-entry vocabulary at decode batch sizes, element by element: one row
-    alone (VALU GEMV over 1 or 2 operand rows), 2 and 4 rows (4 and 8 operand rows), 8 rows
-    (the one-tile matrix-core GEMV over 16 operand rows)."""
+    alone (the slice GEMV's VALU chains over 1 or 2 operand rows), 2 rows (4 operand rows: its
+    4x4x1 matrix chains), 4 and 8 rows (8 and 16 operand rows: the one-tile matrix-core
+    GEMV)."""
     M = 2 * B if tau > 0 else B
     say("anchor lmhead", B, tau, route("gemm", M, 128256))
     got = lm(c4["h"][:B], c4["wd"], c4["target"][:B], tau)
