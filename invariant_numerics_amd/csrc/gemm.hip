@@ -778,7 +778,11 @@ hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st) {
 //   * compute: each thread runs its slice chain over the phase's 64 elements in order.
 //     The 16 lanes of an LDS pass hold 16 consecutive slices of one weight row: weight
 //     segments are 144 bytes apart and activation rows 272 bytes apart, so both 16-byte
-//     reads spread over all banks.
+//     reads spread over all banks.  Each weight row's 16 segments, and each activation row's
+//     16 slices, are followed by two unused ones, so rows sit 32 bytes apart in the bank
+//     order: the matrix-instruction form, whose lanes of one pass read four weight rows or
+//     four activation rows of two slices, then reads without bank conflicts too (3-5% faster
+//     at M = 4, unchanged at M = 1-2).
 // After each group the 16 new slice partials of every output are folded, in slice order,
 // into that output's running total by the thread that owns it.
 constexpr int SK_LANES = 16;  // slices per group
@@ -805,8 +809,8 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev, RopeArgs ra) {
     constexpr int NT = ROWS * SK_LANES;          // threads
     constexpr int XU = SK_LANES * (PH / 4) / NT; // activation float4 per thread, row and phase
-    __shared__ __attribute__((aligned(16))) unsigned char Wl[ROWS * SK_LANES * WSEG];
-    __shared__ __attribute__((aligned(16))) float Xl[MB][SK_LANES][XLD];
+    __shared__ __attribute__((aligned(16))) unsigned char Wl[ROWS * (SK_LANES + 2) * WSEG];
+    __shared__ __attribute__((aligned(16))) float Xl[MB][SK_LANES + 2][XLD];
     __shared__ float part[SK_LANES][MB][ROWS];
     if (Mdev) M = min(M, *Mdev);
     if (M <= 0) return;
@@ -862,7 +866,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
         for (int i = 0; i < 8; ++i) {
             const int q = tid + NT * i;
             const int seg = q >> 3, c8 = q & 7;
-            *reinterpret_cast<u32x4v*>(&Wl[seg * WSEG + c8 * 16]) = wp[i];
+            *reinterpret_cast<u32x4v*>(&Wl[((seg >> 4) * (SK_LANES + 2) + (seg & 15)) * WSEG + c8 * 16]) = wp[i];
         }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
@@ -895,7 +899,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
         const int s = sg + sl;
         const int kb = s * KS + p * PH;                       // first k of this phase
         const int nk = min(PH, K - kb);                       // elements of this phase (<= 0: none)
-        const unsigned char* wseg = &Wl[(nl * SK_LANES + sl) * WSEG];
+        const unsigned char* wseg = &Wl[(nl * (SK_LANES + 2) + sl) * WSEG];
         if constexpr (MX != 0) {
             // A lane past its chain's end feeds 0 * 0: the accumulator, never -0 (it starts
             // at +0 and an exact zero sum rounds to +0), is unchanged.
