@@ -1189,6 +1189,11 @@ int64_t gemm_tail_rows(int64_t M, const int* Mdev) {
     return (!Mdev && M - r >= 128 && r >= 1 && r <= 4) ? r : 0;
 }
 
+hipError_t launch_gemm_tiles64(const GemmArgs& a, hipStream_t st, int role) {
+    if (role == 2) return launch_tiled<64, 64, 2, 2, 2>(a, st);
+    return role == 1 ? launch_tiled<64, 64, 2, 2, 1>(a, st) : launch_tiled<64, 64, 2, 2, 0>(a, st);
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role) {
     const int64_t tail = gemm_tail_rows(a.M, a.Mdev);
     if (tail) {

@@ -26,6 +26,9 @@ struct GemmArgs {
 // role 0: activation projections; role 1: the LM head's vocabulary projection; role 2: gated
 // projection (W rows interleaved gate/up, Y[m][i] = silu(gate) * up, N even, R unused)
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role = 0);
+// the same sums on 64 x 64 tiles whatever M is (for a device-side row count far below M: only
+// the tile rows holding live rows do any work)
+hipError_t launch_gemm_tiles64(const GemmArgs& a, hipStream_t st, int role);
 // the kernel a GEMM of M activation rows and N weight rows runs on (every role routes alike)
 enum GemmRoute : int {
     GR_SKINNY_M1_R4, GR_SKINNY_M1_R16, GR_SKINNY_M2_R4, GR_SKINNY_M2_R16, GR_SKINNY_M4_R16,

@@ -320,7 +320,12 @@ __global__ void round_bf16_kernel(const float* __restrict__ H, int B, int K, int
     }
 }
 
-// Single workgroup: ascending list of rows flagged by the P pass, and their count.
+// Rows of the FP32 pass given to a GEMV of their own when the batch is small (see launch_lmhead).
+constexpr int LM_FHEAD = 32;
+constexpr int LM_FHEAD_MAX_B = 512;
+
+// Single workgroup: ascending list of rows flagged by the P pass, and their count; count[1] is
+// the count past the first LM_FHEAD rows (0 when there are no more).
 // Every thread keeps its own copy of the running base; the per-wavefront counts are
 // rewritten by each wavefront in every round, between two barriers.
 __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ flag, int B,
@@ -345,7 +350,10 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
         base += tot;
         __syncthreads();
     }
-    if (tid == 0) *count = base;
+    if (tid == 0) {
+        count[0] = base;
+        count[1] = base > LM_FHEAD ? base - LM_FHEAD : 0;
+    }
 }
 
 // Gather the flagged rows of h (fp32) into a dense [count, K] buffer.
@@ -373,7 +381,7 @@ WsLayout ws_layout(int64_t B, int64_t K, int64_t V) {
     L.a = off; off = align_up(off + sizeof(float) * (size_t)zrows * K);
     L.z = off; off = align_up(off + sizeof(float) * (size_t)zrows * V);
     L.idx = off; off = align_up(off + sizeof(int32_t) * (size_t)B);
-    L.count = off; off = align_up(off + sizeof(int32_t));
+    L.count = off; off = align_up(off + 2 * sizeof(int32_t));   // the count, and the count past LM_FHEAD
     L.part = off; off = align_up(off + sizeof(Top2) * (size_t)zrows * ((ntiles + TOPG - 1) / TOPG));
     L.rowtop = off; off = align_up(off + sizeof(Top2) * (size_t)zrows);
     L.tiles = off; off = align_up(off + sizeof(float) * (size_t)zrows * ntiles);
@@ -494,8 +502,24 @@ hipError_t launch_lmhead(const LmheadArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(gather_rows_kernel, dim3(a.B), dim3(256), 0, st, a.Hs, a.K, a.ldh, idx, count, A);
     if ((e = hipGetLastError()) != hipSuccess) return e;
 
-    GemmArgs gf{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, count};
-    if ((e = launch_gemm(gf, st, 1)) != hipSuccess) return e;
+    // The FP32 pass runs over the `count` compacted rows, a number known on the device only, so
+    // its launch covers B rows and the rows past the count exit.  A tile row with any live row
+    // runs whole, and with the usual handful of flagged rows in a batch of 33-512 that is the
+    // first tile row of a full-size GEMM (128 rows from B = 128 on).  So the first LM_FHEAD rows
+    // go to the GEMV of their own size, and the rest (count - LM_FHEAD live rows, count[1]) to
+    // 64 x 64 tiles, which exit at once when no row is left.  With tau = +inf every row is
+    // flagged and the pass runs as one GEMM of B rows.  Every row's sums are the same on every
+    // route.
+    if (a.B > LM_FHEAD && a.B <= LM_FHEAD_MAX_B && a.tau != __builtin_inff()) {
+        GemmArgs gh{A, LM_FHEAD, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, count};
+        if ((e = launch_gemm(gh, st, 1)) != hipSuccess) return e;
+        GemmArgs gr{A + (int64_t)LM_FHEAD * a.K, a.B - LM_FHEAD, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K,
+                    nullptr, 0, Z + (int64_t)LM_FHEAD * a.V, (int64_t)a.V, count + 1};
+        if ((e = launch_gemm_tiles64(gr, st, 1)) != hipSuccess) return e;
+    } else {
+        GemmArgs gf{A, a.B, a.K, (int64_t)a.K, a.W, a.V, (int64_t)a.K, nullptr, 0, Z, (int64_t)a.V, count};
+        if ((e = launch_gemm(gf, st, 1)) != hipSuccess) return e;
+    }
 
     return launch_reduce(a, 1, Z, idx, count, part, rowtop, tiles, st);
 }

@@ -64,6 +64,20 @@ def test_fused_and_separate_recompute_paths_agree(orc):
             check({k: np.concatenate([p[k] for p in parts]) for k in KEYS}, want, "B=%d tau=%s" % (B, tau))
 
 
+@pytest.mark.parametrize("B", [33, 100])
+def test_fp32_pass_head_and_rest(orc, B):
+    """Above 32 rows the FP32 pass runs its first 32 compacted rows on their own GEMV and the
+    rest on 64 x 64 tiles (live rows on the device): with every row flagged at a finite tau
+    (1e30) both parts carry rows, with tau = 0.1 usually only the first; tau = +inf runs the
+    pass as one GEMM."""
+    d = synth.c1_inputs(rows=B)
+    Wd = bf16(d["w"])
+    for tau, mode in ((1e30, 0), (np.inf, 2), (0.1, 0)):
+        say("lmhead fp32 head/rest", B, tau)
+        want = orc.lmhead(d["h"], d["w"], d["target"], tau=np.float32(tau), mode=mode)
+        check(run(d["h"], None, d["target"], tau=tau, Wd=Wd), want, "B=%d tau=%s" % (B, tau))
+
+
 def test_tau_limits_and_ties(orc):
     say("lmhead tau/ties")
     d = synth.c1_inputs(rows=16)
