@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # up to this many rows the LM head computes the FP32 (recompute) logits in the same sweep over
 # the vocabulary weights as the primary ones, so a recomputed row adds no weight read
-LM_SHARED_SWEEP_MAX_B = 16
+LM_SHARED_SWEEP_MAX_B = 32
 FP32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 matrix (MFMA) peak: 256 CU x 2.4 GHz x 256 flop/clk
 
 
@@ -432,7 +432,7 @@ def main():
                            "recompute pass), steps enqueued back to back and timed with HIP events on "
                            "the stream; host_ms_per_step is the host clock over the same loop; bytes = "
                            "BF16 weights + FP32 KV cache read once (+ a second vocabulary sweep when a "
-                           "row is recomputed and the batch exceeds 16 rows)")
+                           "row is recomputed and the batch exceeds 32 rows)")
         del dd
         # context for the decode fraction: a plain device copy (1 GiB read + 1 GiB written),
         # timed the same way

@@ -14,7 +14,7 @@ HBM.  Prints one JSON object per measurement:
     launch gaps count, the host's time to issue a call does not);
   * C4: LM head, hidden 4096, vocab 128256, B = 1 .. 256, four calls back to back per timing
     with their buffers allocated beforehand (bytes count a second weight read when any row is
-    recomputed and B > 16; up to 16 rows the FP32 logits share the sweep);
+    recomputed and B > 32; up to 32 rows the FP32 logits share the sweep);
   * C5 decode: graph-replayed decode steps of the 4-layer decoder at a 32k context for
     B = 1, 4, 16, 64 (seeded random KV caches; bytes = weights + the KV read once);
   * probes: the practical ceilings the kernels are compared with -- a plain 16-byte read
@@ -128,7 +128,7 @@ if "C4" in SECTIONS:
                 inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1, ws=ws, out=r)
         t = timeit(four, reps=6) / 4
         wb = 1050673152
-        by = wb * (2 if (nrec and B > 16) else 1) + B * 4096 * 4
+        by = wb * (2 if (nrec and B > 32) else 1) + B * 4096 * 4
         out(config="C4", batch=B, recomputed=nrec, us=round(t * 1e6, 1), tokens_per_s=round(B / t, 1),
             hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3),
             tflops=round(2 * 128256 * 4096 * (B + nrec) / t / 1e12, 2))
@@ -156,7 +156,7 @@ if "C5" in SECTIONS:
         nrec = int(r["recomputed"].sum().item())
         t = timeit(lambda: step(tok, pos, tgt), reps=10)
         kv = L5 * 2 * cfg["hkv"] * cfg["d"] * 4 * int((pos + 1).sum().item())
-        by = body_w + head_w * (2 if (nrec and B > 16) else 1) + kv
+        by = body_w + head_w * (2 if (nrec and B > 32) else 1) + kv
         out(config="C5", op="decode", context=T5, batch=B, recomputed=nrec, ms_per_step=round(t * 1e3, 3),
             tokens_per_s=round(B / t, 1), hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3))
 print("done", flush=True)

@@ -208,7 +208,7 @@ size_t inv_lmhead_workspace_bytes(int64_t B, int64_t K, int64_t V);
  *           lp = (z_target - M) - log_f(S).
  *   Rows with margin_P < tau (strict) are compacted on the device and redone with a = h
  *   (F pass); their outputs are F's and recomputed[b] = 1.  tau = +inf recomputes every
- *   row; tau = 0 recomputes none.  For B <= 16 the F-pass logits of every row are computed
+ *   row; tau = 0 recomputes none.  For B <= 32 the F-pass logits of every row are computed
  *   in the same sweep over W as the P ones (the weights are read once), and only the flagged
  *   rows' are used; the results are the same bits either way.
  * Hs: FP32 [B, K] (ldh); W: BF16 [V, K] (row stride K); target: INT32 [B] (device),
@@ -406,7 +406,7 @@ int inv_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, co
  *                              weight rows (K does not change the route);
  *   op INV_ROUTE_GATED_GEMM:   inv_gated_gemm with M = a, N2 = b;
  *   op INV_ROUTE_LMHEAD_GEMM:  the vocabulary projection inside inv_lmhead_logprob_top2
- *                              for B = a rows, V = b entries and tau > 0 (up to 16 rows
+ *                              for B = a rows, V = b entries and tau > 0 (up to 32 rows
  *                              the primary and FP32 operand rows share one projection of
  *                              2B rows; with tau <= 0 it is the route of a rows);
  *   op INV_ROUTE_ATTN_PREFILL: inv_attention_prefill with B * Hq = a and Tq = b.

@@ -65,7 +65,7 @@ __device__ __forceinline__ void top2_merge(Top2& t, const Top2& o) {
 // mode 0: rows 0..gridDim.y-1 as they are (output row = row); mode 1: F pass over the first
 // *count rows of the compacted list (output row = idx[row]).
 constexpr int GROUP = 4;                 // tiles per workgroup of the tiles kernel
-constexpr int LM_FUSED_MAX_B = 16;       // batch sizes whose FP32 logits share the primary GEMM
+constexpr int LM_FUSED_MAX_B = 32;       // batch sizes whose FP32 logits share the primary GEMM
 
 __device__ __forceinline__ const float* zrow(const float* z, int V, int row) {
     return z + (int64_t)row * V;

@@ -50,7 +50,7 @@ def test_shapes_match_oracle(orc, B, K, V):
 
 
 def test_fused_and_separate_recompute_paths_agree(orc):
-    """Up to 16 rows the FP32 logits share the primary sweep over W; above, flagged rows get
+    """Up to 32 rows the FP32 logits share the primary sweep over W; above, flagged rows get
     their own pass.  Both give the oracle's bits, for tau 0.1, +inf and 0."""
     d = synth.c1_inputs(rows=40)
     Wd = bf16(d["w"])
@@ -59,7 +59,7 @@ def test_fused_and_separate_recompute_paths_agree(orc):
         want = orc.lmhead(d["h"], d["w"], d["target"], tau=np.float32(tau), mode=mode)
         sep = run(d["h"], None, d["target"], tau=tau, Wd=Wd)
         check(sep, want, "B=40 tau=%s" % tau)
-        for B in (16, 5, 1):
+        for B in (20, 16, 5, 1):
             parts = [run(d["h"][s:s + B], None, d["target"][s:s + B], tau=tau, Wd=Wd) for s in range(0, 40, B)]
             check({k: np.concatenate([p[k] for p in parts]) for k in KEYS}, want, "B=%d tau=%s" % (B, tau))
 
