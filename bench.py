@@ -140,30 +140,31 @@ def across_batch(dec, model, cfg, dev, T):
         dec_rates[str(B)] = min(_rate(r[k], ref[k][:B]) for k in LM_KEYS)
     out["decode_32k"] = dec_rates
     out["decode_context"] = T - 1
-    # graph-replayed decode steps at larger batches on the same caches (timing only)
+    # graph-replayed decode steps at larger batches on the same caches (timing only): four
+    # steps at the same position per graph, as in the decode timing of the main check
     timing = {}
     H, F, V, L = cfg["hidden"], cfg["ffn"], cfg["vocab"], cfg["layers"]
     QKV = (cfg["hq"] + 2 * cfg["hkv"]) * cfg["d"]
     weights = L * 2 * (QKV * H + H * cfg["hq"] * cfg["d"] + 2 * F * H + H * F) + 2 * V * H
+    KS_ = 4
     for B in (16, 64):
-        gstep = dd.decode_graph(B)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(8)]
-        args_ = (tok[:B].contiguous(), pos[:B].contiguous(), tgt[:B].contiguous())
-        gstep(*args_)
-        nrec = 0
+        grun = dd.decode_graph_steps(KS_, B)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+        args_ = tuple(x[:B].contiguous().unsqueeze(0).repeat(KS_, 1) for x in (tok, pos, tgt))
+        grun(*args_)
         for a_, b_ in ev:
             a_.record()
-            r = gstep(*args_)
+            r = grun(*args_)
             b_.record()
         torch.cuda.synchronize()
-        nrec = int(r["recomputed"].sum().item())
-        sec = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev])) * 1e-3
+        nrec = int(r[-1]["recomputed"].sum().item())
+        sec = float(np.median([a_.elapsed_time(b_) for a_, b_ in ev])) * 1e-3 / KS_
         kv = L * 2 * cfg["hkv"] * T * cfg["d"] * 4 * B
         nbytes = weights + kv + (2 * V * H if (nrec and B > LM_SHARED_SWEEP_MAX_B) else 0)
         timing[str(B)] = dict(ms_per_step=round(sec * 1e3, 3), tokens_per_s=round(B / sec, 1),
                               algorithmic_bytes_per_step=float(nbytes),
                               hbm_frac=round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4))
-        del gstep
+        del grun
     out["decode_32k_graph_timing"] = timing
     del dd
     torch.cuda.synchronize()
@@ -423,14 +424,34 @@ def main():
         ds = np.array(step_s[1:]) if len(step_s) > 1 else np.array(step_s)
         db = np.array(step_bytes[1:]) if len(step_bytes) > 1 else np.array(step_bytes)
         gbs = float(db.sum() / ds.sum()) / 1e9
-        decode = dict(context=p0, batch=B, steps=int(len(ds)), ms_per_step=round(float(ds.mean()) * 1e3, 3),
-                      tokens_per_s=round(B / float(ds.mean()), 2),
-                      algorithmic_bytes_per_step=float(db.mean()),
-                      hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
-                      host_ms_per_step=round(host_s * 1e3, 3),
-                      note="whole decode step replayed from a HIP graph (all layers + LM head incl. "
-                           "recompute pass), steps enqueued back to back and timed with HIP events on "
-                           "the stream; host_ms_per_step is the host clock over the same loop; bytes = "
+        # the same steps as one graph of K steps: one replay runs them in order with one launch
+        # and one set of input copies; its outputs must be the single-step graph's, bit for bit
+        K = len(steps_t)
+        mrun = dd.decode_graph_steps(K, B)
+        tokK, posK, tgtK = torch.stack(tok_all), torch.stack(pos_all), torch.stack(tgt_all)
+        rK = mrun(tokK, posK, tgtK)
+        torch.cuda.synchronize()
+        bitwise["multi_step_graph_vs_single_step"] = float(min(rate(rK[i][k], res[i][k]) for i in range(K) for k in keys))
+        evm = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a_, b_ in evm:
+            a_.record()
+            mrun(tokK, posK, tgtK)
+            b_.record()
+        torch.cuda.synchronize()
+        msec = float(np.median([a_.elapsed_time(b_) for a_, b_ in evm])) * 1e-3 / K
+        mbytes = float(np.mean(step_bytes))
+        decode = dict(context=p0, batch=B, steps=K, ms_per_step=round(msec * 1e3, 3),
+                      tokens_per_s=round(B / msec, 2),
+                      algorithmic_bytes_per_step=mbytes,
+                      hbm_gbs=round(mbytes / msec / 1e9, 1), hbm_frac=round(mbytes / msec / 1e9 / HBM_PEAK_GBS, 4),
+                      single_step_graph=dict(steps=int(len(ds)), ms_per_step=round(float(ds.mean()) * 1e3, 3),
+                                             hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                                             host_ms_per_step=round(host_s * 1e3, 3)),
+                      note="K consecutive decode steps (all layers + LM head incl. recompute pass) captured "
+                           "as one HIP graph, replayed and timed with HIP events on the stream (median of 5 "
+                           "replays, divided by K; the input copies of the K steps included); "
+                           "single_step_graph: the same steps as K replays of a one-step graph, enqueued "
+                           "back to back, each with its own input copies (first step dropped); bytes = "
                            "BF16 weights + FP32 KV cache read once (+ a second vocabulary sweep when a "
                            "row is recomputed and the batch exceeds 32 rows)")
         del dd

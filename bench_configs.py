@@ -15,8 +15,9 @@ HBM.  Prints one JSON object per measurement:
   * C4: LM head, hidden 4096, vocab 128256, B = 1 .. 256, four calls back to back per timing
     with their buffers allocated beforehand (bytes count a second weight read when any row is
     recomputed and B > 32; up to 32 rows the FP32 logits share the sweep);
-  * C5 decode: graph-replayed decode steps of the 4-layer decoder at a 32k context for
-    B = 1, 4, 16, 64 (seeded random KV caches; bytes = weights + the KV read once);
+  * C5 decode: decode steps of the 4-layer decoder at a 32k context for B = 1, 4, 16, 64, four
+    consecutive steps captured as one HIP graph and replayed (seeded random KV caches; bytes =
+    weights + the KV read once);
   * probes: the practical ceilings the kernels are compared with -- a plain 16-byte read
     stream over 4 GiB (inv_read_stream_probe), torch's device copy, and the FP32 matrix
     instruction rates (inv_mfma_rate_probe) at 1, 2, 4 and 8 wavefronts per SIMD.
@@ -147,15 +148,16 @@ if "C5" in SECTIONS:
     QKV5 = (cfg["hq"] + 2 * cfg["hkv"]) * cfg["d"]
     body_w = L5 * 2 * (QKV5 * H5 + H5 * cfg["hq"] * cfg["d"] + 2 * F5 * H5 + H5 * F5)
     head_w = 2 * V5 * H5
+    K5 = 4
     for B in (1, 4, 16, 64):
-        step = dec5.decode_graph(B)
-        tok = torch.randint(0, V5, (B,), dtype=torch.int32, device=dev, generator=g5)
-        tgt = torch.randint(0, V5, (B,), dtype=torch.int32, device=dev, generator=g5)
-        pos = torch.tensor([T5 - 17 - 5 * b for b in range(B)], dtype=torch.int32, device=dev)
-        r = step(tok, pos, tgt)
-        nrec = int(r["recomputed"].sum().item())
-        t = timeit(lambda: step(tok, pos, tgt), reps=10)
-        kv = L5 * 2 * cfg["hkv"] * cfg["d"] * 4 * int((pos + 1).sum().item())
+        run = dec5.decode_graph_steps(K5, B)
+        tok = torch.randint(0, V5, (K5, B), dtype=torch.int32, device=dev, generator=g5)
+        tgt = torch.randint(0, V5, (K5, B), dtype=torch.int32, device=dev, generator=g5)
+        pos = torch.tensor([[T5 - 20 - 5 * b + k for b in range(B)] for k in range(K5)], dtype=torch.int32, device=dev)
+        r = run(tok, pos, tgt)
+        nrec = int(r[-1]["recomputed"].sum().item())
+        t = timeit(lambda: run(tok, pos, tgt), reps=10) / K5
+        kv = L5 * 2 * cfg["hkv"] * cfg["d"] * 4 * int((pos[-1] + 1).sum().item())
         by = body_w + head_w * (2 if (nrec and B > 32) else 1) + kv
         out(config="C5", op="decode", context=T5, batch=B, recomputed=nrec, ms_per_step=round(t * 1e3, 3),
             tokens_per_s=round(B / t, 1), hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3))

@@ -242,3 +242,35 @@ class Decoder:
 
         step.graph = graph
         return step
+
+    def decode_graph_steps(self, K, B=None):
+        """Capture K consecutive decode steps (batch B) in one HIP graph.  Returns
+        run(tok, pos, target) taking int32 [K, B] inputs (step k reads row k: the token, position
+        and target of every sequence at that step), which copies them into the graph's static
+        buffers, replays the K steps and returns their K output dicts (valid until the next
+        replay).  The steps are the single-step graph's kernels in sequence; one replay pays the
+        input copies and the graph launch once for K steps."""
+        B = self.batch if B is None else int(B)
+        K = int(K)
+        st_tok = torch.zeros((K, B), dtype=torch.int32, device=self.dev)
+        st_pos = torch.full((K, B), -1, dtype=torch.int32, device=self.dev)   # warm-up: no cache writes
+        st_tgt = torch.zeros((K, B), dtype=torch.int32, device=self.dev)
+        side = torch.cuda.Stream(device=self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            self.decode_step(st_tok[0], st_pos[0], st_tgt[0])
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize(self.dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            st_out = [self.decode_step(st_tok[k], st_pos[k], st_tgt[k]) for k in range(K)]
+
+        def run(tok, pos, target):
+            st_tok.copy_(tok)
+            st_pos.copy_(pos)
+            st_tgt.copy_(target)
+            graph.replay()
+            return st_out
+
+        run.graph = graph
+        return run

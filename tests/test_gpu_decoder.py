@@ -124,3 +124,38 @@ def test_small_decoder_graph_replays_equal_eager(small):
         _ = torch.randn(1000, device="cuda").sum().item()   # eager work between replays
         for k in KEYS:
             assert_bitwise(got[k], ref[t][k], "graph replay %d %s" % (t, k))
+
+
+def test_small_decoder_multi_step_graph_equals_eager(small):
+    """K consecutive decode steps captured as one graph and replayed (K = 5, windows of
+    positions across a 256-key chunk boundary, eager work between replays): every step of
+    every replay bitwise equal to eager decode at that position, and the KV cache the same."""
+    from invariant_numerics_amd.decoder import Decoder
+    import torch
+    say("small decoder multi-step graph")
+    T, K = 280, 5
+    toks = synth.tokens(9810, 2, T, synth.SMALL["vocab"])
+    td = i32(toks)
+    eager = Decoder(small, batch=2, tmax=320)
+    ref = []
+    for t in range(T - 1):
+        pos = torch.full((2,), t, dtype=torch.int32, device="cuda")
+        r = eager.decode_step(td[:, t].contiguous(), pos, td[:, t + 1].contiguous())
+        ref.append({k: host(v) for k, v in r.items()})
+    gdec = Decoder(small, batch=2, tmax=320)
+    gdec.prefill(td[:, :241].contiguous(), block=64)
+    run = gdec.decode_graph_steps(K)
+    for t0 in range(240, T - K, K):
+        tok = torch.stack([td[:, t] for t in range(t0, t0 + K)]).contiguous()
+        pos = torch.stack([torch.full((2,), t, dtype=torch.int32, device="cuda") for t in range(t0, t0 + K)])
+        tgt = torch.stack([td[:, t + 1] for t in range(t0, t0 + K)]).contiguous()
+        outs = run(tok, pos, tgt)
+        got = [{k: host(v) for k, v in o.items()} for o in outs]
+        _ = torch.randn(1000, device="cuda").sum().item()   # eager work between replays
+        for i in range(K):
+            for k in KEYS:
+                assert_bitwise(got[i][k], ref[t0 + i][k], "multi-step graph %d %s" % (t0 + i, k))
+    last = t0 + K
+    for li in range(len(eager.kc)):
+        assert_bitwise(host(gdec.kc[li][:, :, :last]), host(eager.kc[li][:, :, :last]), "k cache %d" % li)
+        assert_bitwise(host(gdec.vc[li][:, :, :last]), host(eager.vc[li][:, :, :last]), "v cache %d" % li)
