@@ -4,7 +4,8 @@ batch 1 to 64 (its prefill scoring is bench.py).
 Seeded synthetic inputs from ``synth`` (the same arrays the parity tests use); every timing
 is the median of HIP-event-bracketed repetitions on the current stream, inputs resident in
 HBM.  Prints one JSON object per measurement:
-  * C1: LM head, hidden 256, vocab 4096, 64 tokens as 64 / B calls of batch B;
+  * C1: LM head, hidden 256, vocab 4096, 64 tokens as 64 / B calls of batch B, issued call by
+    call from Python and, captured once as a HIP graph, replayed;
   * C2: causal attention, 8 heads x 2048 x 128, BF16 inputs: the whole prefill (four calls
     back to back per timing, buffers allocated beforehand), and decode calls at every 8th
     position;
@@ -75,7 +76,16 @@ if "C1" in SECTIONS:
             for s in range(0, 64, B):
                 inv.inv_lmhead_logprob_top2(H[s:s + B], W, T[s:s + B], 0.1, ws=ws1, out=r1)
         t = timeit(run)
-        out(config="C1", batch=B, calls=64 // B, us_per_call=round(t / (64 // B) * 1e6, 1), tokens_per_s=round(64 / t, 1))
+        # the same 64 / B calls captured once as a HIP graph and replayed: the device time,
+        # without the host's time to issue each call
+        run()
+        torch.cuda.synchronize()
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1):
+            run()
+        tg = timeit(g1.replay)
+        out(config="C1", batch=B, calls=64 // B, us_per_call=round(t / (64 // B) * 1e6, 1), tokens_per_s=round(64 / t, 1),
+            graph_us_per_call=round(tg / (64 // B) * 1e6, 1), graph_tokens_per_s=round(64 / tg, 1))
 # ---- C2: attention 8 heads x 2048 x d128, bf16, causal
 if "C2" in SECTIONS:
     d = synth.c2_inputs()
