@@ -1075,8 +1075,8 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra =
 //     M <= 2 and on 4x4x1 matrix instructions for M = 3-4 (8-12% faster there, equal bits);
 //   5 <= M <= 16: the matrix-core GEMV with one 16-row tile (the VALU GEMV's per-row
 //     accumulators and LDS reads make it slower from 5 rows on); weight rows per workgroup:
-//     64 from N = 65536 (four wavefronts along the rows), 32 from 12288 (two along the rows,
-//     two along K), else 16 with the slices split over four wavefronts, or over eight for
+//     64 from N = 65536 (four wavefronts along the rows, two along K: 4-10% faster on the
+//     128256-row vocabulary than one along K), 32 from 12288 (two along the rows, two along K), else 16 with the slices split over four wavefronts, or over eight for
 //     N = 2048..4096, where there are only N / 16 workgroups (12-18% faster at N = 4096 for
 //     K = 4096 and 14336, slower at N = 6144);
 //   17 <= M <= 32: the same with two row tiles (measured faster than the 32 x 32 tiles, or
@@ -1126,7 +1126,7 @@ const char* gemm_route_name(GemmRoute r) {
         case GR_GEMV16_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,1,4>";
         case GR_GEMV16_WN1_W8: return "gemm_gemv16_kernel<1,2,64,ROLE,1,8>";
         case GR_GEMV16_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,1,4>";
-        case GR_GEMV16_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,1,4>";
+        case GR_GEMV16_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,1,8>";
         case GR_GEMV32_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,2,4>";
         case GR_GEMV32_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,2,4>";
         case GR_GEMV32_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,2,4>";
@@ -1151,7 +1151,7 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         case GR_GEMV16_WN1: return launch_gemv16<1, 2, 64, ROLE>(a, st);
         case GR_GEMV16_WN1_W8: return launch_gemv16<1, 2, 64, ROLE, 1, 8>(a, st);
         case GR_GEMV16_WN2: return launch_gemv16<2, 2, 64, ROLE>(a, st);
-        case GR_GEMV16_WN4: return launch_gemv16<4, 2, 64, ROLE>(a, st);
+        case GR_GEMV16_WN4: return launch_gemv16<4, 2, 64, ROLE, 1, 8>(a, st);
         case GR_GEMV32_WN1: return launch_gemv16<1, 2, 64, ROLE, 2>(a, st);
         case GR_GEMV32_WN2: return launch_gemv16<2, 2, 64, ROLE, 2>(a, st);
         case GR_GEMV32_WN4: return launch_gemv16<4, 2, 64, ROLE, 2>(a, st);

@@ -135,7 +135,7 @@ def test_kernel_route_names(inv):
     assert r("gated_gemm", 1024, 8192) == "gemm_mfma_kernel<128,256,2,4,2>"
     assert r("gated_gemm", 1, 28672) == "gemm_skinny_kernel<1,2,16>"
     assert r("lmhead_gemm", 1, 128256) == "gemm_skinny_kernel<2,1,16>"
-    assert r("lmhead_gemm", 8, 128256) == "gemm_gemv16_kernel<4,2,64,1,1,4>"
+    assert r("lmhead_gemm", 8, 128256) == "gemm_gemv16_kernel<4,2,64,1,1,8>"
     assert r("lmhead_gemm", 32, 128256) == "gemm_mfma_kernel<64,64,2,2,1>"     # 64 rows, one sweep
     assert r("lmhead_gemm", 32767, 128256) == "gemm_mfma_kernel<128,256,2,4,1>"
     assert r("attention_prefill", 4 * 32, 512) == "attn_prefill_kernel<DT,8,64>"
