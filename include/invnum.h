@@ -396,6 +396,40 @@ int inv_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, co
                            float* Kc, float* Vc, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * inv_rmsnorm_gemm -- a projection of RMSNorm-ed rows, for one to four rows (decode):
+ *   bit for bit inv_rmsnorm(X, gamma, eps) followed by inv_fixed_order_gemm (gated = 0, with
+ *   the optional residual R) or inv_gated_gemm (gated = 1: W interleaved gate/up rows, N even,
+ *   Y [M, N/2], R must be NULL) on the normalised rows, without storing them: each workgroup of
+ *   the GEMV computes r = 1 / sqrt((dot_KS(x, x, K) / K) + eps) of every row itself, in the
+ *   RMSNorm's order, and stages (x_k * r) * up(g_k) as the operand.  One launch instead of two.
+ * X: FP32 [M, K] (ldx), the norm's input; gamma: BF16 [K], 16-byte aligned.  W, N, ldw, R,
+ * ldr, Y, ldy as inv_fixed_order_gemm / inv_gated_gemm.  K <= 16384.
+ * Errors: INV_ERR_NULL, INV_ERR_SHAPE, INV_ERR_ALIGN, INV_ERR_UNSUPPORTED (M outside 1..4, or
+ * K > 16384), INV_ERR_LAUNCH.
+ * Sources: Meituan page, "key practices" (batch-invariant RMSNorm and GEMM operators); FP32
+ * write-up section 5 (LayerCast).
+ * ------------------------------------------------------------------------------------ */
+int inv_rmsnorm_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma, float eps,
+                     const uint16_t* W, int64_t N, int64_t ldw, const float* R, int64_t ldr,
+                     float* Y, int64_t ldy, int gated, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * inv_rmsnorm_qkv_rope_kv_append -- inv_qkv_rope_kv_append of the RMSNorm-ed rows: bit for
+ * bit inv_rmsnorm(X, gamma, eps) and then inv_qkv_rope_kv_append on its output, in one GEMV
+ * launch whose workgroups compute the norm themselves (as inv_rmsnorm_gemm).  For one to four
+ * rows with D = 128 only (INV_ERR_UNSUPPORTED otherwise; K <= 16384); needs no workspace.
+ * Arguments as inv_qkv_rope_kv_append, plus gamma (BF16 [K], 16-byte aligned) and eps.
+ * Errors: INV_ERR_NULL, INV_ERR_SHAPE, INV_ERR_ALIGN, INV_ERR_UNSUPPORTED, INV_ERR_LAUNCH.
+ * Sources: Meituan page, "key practices" (batch-invariant operators; decode replays the same
+ * accumulation path as prefill).
+ * ------------------------------------------------------------------------------------ */
+int inv_rmsnorm_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                   float eps, const uint16_t* Wqkv, int64_t ldw, int64_t Hq, int64_t Hkv,
+                                   int64_t D, const int32_t* seq, const int32_t* pos, const float* cos_t,
+                                   const float* sin_t, int64_t Tmax, int64_t Bcache, float* Qout, float* Kc,
+                                   float* Vc, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * inv_kernel_route -- host-only query (enqueues nothing, touches no device): the name of
  * the kernel instantiation that a call with these sizes launches, written as a
  * NUL-terminated string into name[0 .. cap-1] (truncated to fit).  The choice is launch

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     inv_attention_prefill, inv_attention_prefill_workspace_bytes, inv_embed, inv_eval_numerics, inv_fixed_order_gemm, inv_gated_gemm,
     inv_get_constants, inv_kernel_route,
     inv_lmhead_logit_grad, inv_lmhead_logit_grad_workspace_bytes, inv_lmhead_logprob_top2, inv_lmhead_workspace_bytes, inv_mfma_f32_check, inv_mfma32_f32_check,
-    inv_mfma_bf16_check, inv_mfma_rate_probe, inv_read_stream_probe, inv_qkv_rope_kv_append, inv_rmsnorm, inv_rope_kv_append,
+    inv_mfma_bf16_check, inv_mfma_rate_probe, inv_read_stream_probe, inv_qkv_rope_kv_append, inv_rmsnorm, inv_rmsnorm_gemm,
+    inv_rmsnorm_qkv_rope_kv_append, inv_rope_kv_append,
     inv_round_activations, inv_status_string, inv_swiglu,
 )

@@ -79,6 +79,10 @@ def _load():
         "inv_attention_prefill_ws": (ctypes.c_int, [ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                                     ctypes.c_float, vp, vp, ctypes.c_size_t, vp]),
         "inv_kernel_route": (ctypes.c_int, [ctypes.c_int, i64, i64, ctypes.c_char_p, ctypes.c_size_t]),
+        "inv_rmsnorm_gemm": (ctypes.c_int, [vp, i64, i64, i64, vp, ctypes.c_float, vp, i64, i64, vp, i64, vp, i64,
+                                            ctypes.c_int, vp]),
+        "inv_rmsnorm_qkv_rope_kv_append": (ctypes.c_int, [vp, i64, i64, i64, vp, ctypes.c_float, vp, i64, i64, i64,
+                                                          i64, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -97,7 +101,8 @@ EXPORTS = ("inv_status_string", "inv_get_constants", "inv_fixed_order_gemm", "in
            "inv_mfma_bf16_check", "inv_kernel_route", "inv_attention_decode_noalloc",
            "inv_attention_decode_noalloc_max_bytes", "inv_qkv_rope_kv_append_workspace_bytes",
            "inv_qkv_rope_kv_append", "inv_read_stream_probe", "inv_mfma_rate_probe",
-           "inv_attention_prefill_workspace_bytes", "inv_attention_prefill_ws")
+           "inv_attention_prefill_workspace_bytes", "inv_attention_prefill_ws", "inv_rmsnorm_gemm",
+           "inv_rmsnorm_qkv_rope_kv_append")
 
 
 def _check(status, what):
@@ -214,6 +219,39 @@ def inv_rmsnorm(X, gamma, eps=1e-5, out=None):
     _check(LIB.inv_rmsnorm(_p(X), M, H, _row_ld(X), _p(gamma), float(eps), _p(out), _row_ld(out),
                            _stream(X)), "inv_rmsnorm")
     return out
+
+
+def inv_rmsnorm_gemm(X, gamma, W, eps=1e-5, R=None, out=None, gated=False):
+    """inv_rmsnorm(X, gamma, eps) then inv_fixed_order_gemm (or inv_gated_gemm when gated) on
+    the normalised rows, in one launch; X fp32 [M, K] with M <= 4, gamma bf16 [K]."""
+    _dev(X, gamma, W, R, out)
+    _f32(X)
+    _bf16(gamma)
+    _bf16(W)
+    M, K = X.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N // 2 if gated else N), dtype=torch.float32, device=X.device)
+    _check(LIB.inv_rmsnorm_gemm(_p(X), M, K, _row_ld(X), _p(gamma), float(eps), _p(W), N, _row_ld(W), _p(R),
+                                0 if R is None else _row_ld(R), _p(out), _row_ld(out), 1 if gated else 0,
+                                _stream(X)), "inv_rmsnorm_gemm")
+    return out
+
+
+def inv_rmsnorm_qkv_rope_kv_append(X, gamma, Wqkv, Hq, Hkv, D, seq, pos, cos_t, sin_t, Qout, Kc, Vc, eps=1e-5):
+    """inv_rmsnorm(X, gamma, eps) then inv_qkv_rope_kv_append on the normalised rows, in one
+    launch (one to four rows, D = 128)."""
+    _dev(X, gamma, Wqkv, seq, pos, cos_t, sin_t, Qout, Kc, Vc)
+    _f32(X)
+    _bf16(gamma)
+    _bf16(Wqkv)
+    M, K = X.shape
+    Bc, _, Tmax, _ = Kc.shape
+    _check(LIB.inv_rmsnorm_qkv_rope_kv_append(_p(X), M, K, _row_ld(X), _p(gamma), float(eps), _p(Wqkv),
+                                              _row_ld(Wqkv), Hq, Hkv, D, _p(seq), _p(pos), _p(cos_t), _p(sin_t),
+                                              Tmax, Bc, _p(Qout), _p(Kc), _p(Vc), _stream(X)),
+           "inv_rmsnorm_qkv_rope_kv_append")
+    return Qout
 
 
 def _ws(need, ws, dev):

@@ -115,6 +115,40 @@ int inv_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, co
                                      (int)Bcache, Qout, Kc, Vc, INV_F32, S(stream)));
 }
 
+int inv_rmsnorm_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma, float eps,
+                     const uint16_t* W, int64_t N, int64_t ldw, const float* R, int64_t ldr, float* Y, int64_t ldy,
+                     int gated, void* stream) {
+    if (!X || !gamma || !W || !Y) return INV_ERR_NULL;
+    if (gated != 0 && gated != 1) return INV_ERR_SHAPE;
+    if (N < 1 || K < 8 || K % 8 != 0 || M > I32MAX || N > I32MAX || K > I32MAX) return INV_ERR_SHAPE;
+    if (gated && (N < 2 || N % 2 != 0 || R)) return INV_ERR_SHAPE;
+    const int64_t ny = gated ? N / 2 : N;
+    if (M < 1 || ldx < K || ldw < K || ldy < ny || (R && ldr < N)) return INV_ERR_SHAPE;
+    if (!gemm_norm_fusable(M) || K > 16384) return INV_ERR_UNSUPPORTED;
+    if (!al16(X) || !al16(W) || !al16(gamma) || ldx % 4 || ldw % 8) return INV_ERR_ALIGN;
+    if ((reinterpret_cast<uintptr_t>(Y) & 3u) || (R && (reinterpret_cast<uintptr_t>(R) & 3u)))
+        return INV_ERR_ALIGN;
+    GemmArgs a{X, (int)M, (int)K, ldx, W, (int)N, ldw, R, ldr, Y, ldy, nullptr, gamma, eps};
+    return fin(launch_gemm(a, S(stream), gated ? 2 : 0));
+}
+
+int inv_rmsnorm_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                   float eps, const uint16_t* Wqkv, int64_t ldw, int64_t Hq, int64_t Hkv, int64_t D,
+                                   const int32_t* seq, const int32_t* pos, const float* cos_t, const float* sin_t,
+                                   int64_t Tmax, int64_t Bcache, float* Qout, float* Kc, float* Vc, void* stream) {
+    if (!X || !gamma || !Wqkv || !seq || !pos || !cos_t || !sin_t || !Qout || !Kc || !Vc) return INV_ERR_NULL;
+    if (M < 1 || K < 8 || K % 8 != 0 || Hq < 1 || Hkv < 1 || D < 2 || D % 2 != 0 || Tmax < 1 || Bcache < 1 ||
+        ldx < K || ldw < K || M > I32MAX || K > I32MAX || Tmax > I32MAX || Bcache > I32MAX ||
+        (Hq + 2 * Hkv) * D > I32MAX)
+        return INV_ERR_SHAPE;
+    if (!qkv_rope_fusable(M, D) || !gemm_norm_fusable(M) || K > 16384) return INV_ERR_UNSUPPORTED;
+    if (!al16(X) || !al16(Wqkv) || !al16(gamma) || ldx % 4 || ldw % 8) return INV_ERR_ALIGN;
+    const int64_t N = (Hq + 2 * Hkv) * D;
+    GemmArgs a{X, (int)M, (int)K, ldx, Wqkv, (int)N, ldw, nullptr, 0, nullptr, 0, nullptr, gamma, eps};
+    RopeArgs ra{(int)Hq, (int)Hkv, seq, pos, cos_t, sin_t, (int)Tmax, (int)Bcache, Qout, Kc, Vc};
+    return fin(launch_qkv_rope(a, ra, S(stream)));
+}
+
 static int check_attn(int dtype, const void* Q, const void* Kc, const void* Vc, const float* O,
                       int64_t B, int64_t Tq, int64_t q_start, int64_t Tmax, int64_t Hq, int64_t Hkv,
                       int64_t D) {

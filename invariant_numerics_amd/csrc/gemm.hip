@@ -801,17 +801,33 @@ __device__ __forceinline__ int qkv_row(int o, int rot) {
     return (o & ~(RD - 1)) + ((j & 1) ? pr + RD / 2 : pr);
 }
 
-template <int MB, int ROLE, int ROWS, int MX = 0>
+// NRM: the activation rows are RMSNorm inputs.  Before its first phase every workgroup
+// computes each row's r = 1 / sqrt(dot_KS(x, x) / K + eps) itself (the rows are staged 16
+// slices at a time in LDS, thread s runs slice s's chain x_k * x_k in k order, one thread per
+// row folds the slices in order) and the activation tiles are stored into LDS as
+// (x_k * r) * up(g_k) -- the arithmetic of rmsnorm_kernel, so the products see the bits the
+// separate RMSNorm would have stored, without its launch or its output.  The first weight
+// phases are requested before this prologue, so it runs under their latency.
+constexpr int NRM_SL = KS + 4;      // padded floats per slice of a staged norm row
+template <int MB, int ROLE, int ROWS, int MX = 0, int NRM = 0>
 __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
     const uint16_t* __restrict__ W, int N, int64_t ldw,
     const float* __restrict__ R, int64_t ldr,
-    float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev, RopeArgs ra) {
+    float* __restrict__ Y, int64_t ldy, const int* __restrict__ Mdev, RopeArgs ra,
+    const uint16_t* __restrict__ G, float eps) {
     constexpr int NT = ROWS * SK_LANES;          // threads
     constexpr int XU = SK_LANES * (PH / 4) / NT; // activation float4 per thread, row and phase
-    __shared__ __attribute__((aligned(16))) unsigned char Wl[ROWS * (SK_LANES + 2) * WSEG];
-    __shared__ __attribute__((aligned(16))) float Xl[MB][SK_LANES + 2][XLD];
+    constexpr int WL_BYTES = ROWS * (SK_LANES + 2) * WSEG;
+    constexpr int XL_BYTES = MB * (SK_LANES + 2) * XLD * 4;
+    constexpr int NRM_BYTES = NRM ? SK_LANES * NRM_SL * 4 : 0;
+    constexpr int SMEM = WL_BYTES + XL_BYTES > NRM_BYTES ? WL_BYTES + XL_BYTES : NRM_BYTES;
+    // the weight and activation tiles; the norm prologue's staged row shares their space
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+    unsigned char* const Wl = smem;
+    float (*const Xl)[SK_LANES + 2][XLD] = reinterpret_cast<float (*)[SK_LANES + 2][XLD]>(smem + WL_BYTES);
     __shared__ float part[SK_LANES][MB][ROWS];
+    __shared__ float nrm[NRM ? MB * (SK_LANES + 1) : 1];
     if (Mdev) M = min(M, *Mdev);
     if (M <= 0) return;
     const int S = (K + KS - 1) / KS;
@@ -835,9 +851,11 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
     // are native vectors (copies of the struct types were kept in scratch memory), and a
     // scheduling barrier keeps the loads ahead of the phase's compute.
     constexpr int DEPTH = MB * XU <= 4 ? 2 : 1;
+    constexpr int GU = NRM ? XU : 1;             // gain pairs per thread and phase (NRM)
     u32x4v wpre[DEPTH][8];
     f32x4v xpre[DEPTH][MB * XU];
-    auto load = [&](int stg, u32x4v (&wp)[8], f32x4v (&xp)[MB * XU]) {
+    uint2 gpre[DEPTH][GU];
+    auto load = [&](int stg, u32x4v (&wp)[8], f32x4v (&xp)[MB * XU], uint2 (&gp)[GU]) {
         const int sg = (stg / (KS / PH)) * SK_LANES;
         const int p = stg % (KS / PH);
 #pragma unroll
@@ -860,8 +878,17 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
                 xp[m * XU + j] = *reinterpret_cast<const f32x4v*>(X + (int64_t)min(m, M - 1) * ldx + min(k, K - 4));
             }
         }
+        if constexpr (NRM) {
+#pragma unroll
+            for (int j = 0; j < XU; ++j) {
+                const int u = tid + NT * j;
+                const int k = (sg + (u >> 4)) * KS + p * PH + 4 * (u & 15);
+                gp[j] = *reinterpret_cast<const uint2*>(G + min(k, K - 4));
+            }
+        }
     };
-    auto store = [&](const u32x4v (&wp)[8], const f32x4v (&xp)[MB * XU]) {
+    float rn[MB];                                // r of each row (NRM)
+    auto store = [&](const u32x4v (&wp)[8], const f32x4v (&xp)[MB * XU], const uint2 (&gp)[GU]) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int q = tid + NT * i;
@@ -873,7 +900,15 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
 #pragma unroll
             for (int j = 0; j < XU; ++j) {
                 const int u = tid + NT * j;
-                *reinterpret_cast<f32x4v*>(&Xl[m][u >> 4][(u & 15) * 4]) = xp[m * XU + j];
+                f32x4v v = xp[m * XU + j];
+                if constexpr (NRM) {
+                    const float r = rn[m];
+                    v.x = (v.x * r) * bf16_lo(gp[j].x);
+                    v.y = (v.y * r) * bf16_hi(gp[j].x);
+                    v.z = (v.z * r) * bf16_lo(gp[j].y);
+                    v.w = (v.w * r) * bf16_hi(gp[j].y);
+                }
+                *reinterpret_cast<f32x4v*>(&Xl[m][u >> 4][(u & 15) * 4]) = v;
             }
         }
     };
@@ -983,18 +1018,95 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
             }
         }
     };
+    // the norm's row loads (per thread NU float4 of a 16-slice group, in batches of NB)
+    constexpr int NU = SK_LANES * KS / 4 / NT;
+    constexpr int NB = NU < 8 ? NU : 8;
+    // with 256 threads and one row the first group is requested ahead of the weights (loads
+    // complete in order, so behind them it would wait for the whole first weight burst)
+    constexpr bool XFIRST = NRM && NU <= 4 && MB == 1;
+    f32x4v xv0[XFIRST ? NU : 1];
+    if constexpr (XFIRST) {
+        const int kn0 = min(SK_LANES * KS, K);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) xv0[u] = *reinterpret_cast<const f32x4v*>(X + min(4 * (tid + NT * u), kn0 - 4));
+    }
     // phase st lives in register buffer st % DEPTH from its load until its store
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
-        if (d < nstages) load(d, wpre[d], xpre[d]);
+        if (d < nstages) load(d, wpre[d], xpre[d], gpre[d]);
+    if constexpr (NRM) {
+        // r of each activation row, in the order of rmsnorm_kernel
+        float* xs = reinterpret_cast<float*>(smem);
+        for (int m = 0; m < M; ++m) {
+            const float* x = X + (int64_t)m * ldx;
+            float T = 0.0f;                          // thread 0: the row's running fold
+            for (int s0 = 0; s0 < S; s0 += SK_LANES) {
+                const int k0 = s0 * KS, kn = min(SK_LANES * KS, K - k0);
+                __syncthreads();       // the previous group's chains are done with xs
+#pragma unroll
+                for (int u0 = 0; u0 < NU; u0 += NB) {
+                    f32x4v v[NB];
+                    if (XFIRST && m == 0 && s0 == 0) {
+#pragma unroll
+                        for (int u = 0; u < NB; ++u) v[u] = xv0[XFIRST ? u0 + u : 0];
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < NB; ++u)
+                            v[u] = *reinterpret_cast<const f32x4v*>(x + k0 + min(4 * (tid + NT * (u0 + u)), kn - 4));
+                    }
+                    // stores at the clamped index too: a clamped load holds the elements of that
+                    // index, so a unit past the row rewrites them with their own values
+#pragma unroll
+                    for (int u = 0; u < NB; ++u) {
+                        const int i = min(4 * (tid + NT * (u0 + u)), kn - 4);
+                        *reinterpret_cast<f32x4v*>(&xs[(i / KS) * NRM_SL + i % KS]) = v[u];
+                    }
+                }
+                __syncthreads();
+                if (tid < SK_LANES && s0 + tid < S) {
+                    const int n = min(KS, K - (s0 + tid) * KS);   // a multiple of 8
+                    const float* sx = xs + tid * NRM_SL;
+                    float c = 0.0f;
+                    // 8 float4 read ahead of the chain's fused multiply-adds
+                    for (int kb = 0; kb < n; kb += 32) {
+                        f32x4v r4[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) r4[u] = *reinterpret_cast<const f32x4v*>(sx + min(kb + 4 * u, n - 4));
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            if (kb + 4 * u < n) {
+                                c = __builtin_fmaf(r4[u].x, r4[u].x, c);
+                                c = __builtin_fmaf(r4[u].y, r4[u].y, c);
+                                c = __builtin_fmaf(r4[u].z, r4[u].z, c);
+                                c = __builtin_fmaf(r4[u].w, r4[u].w, c);
+                            }
+                        }
+                    }
+                    nrm[m * (SK_LANES + 1) + tid] = c;
+                }
+                __syncthreads();
+                if (tid == 0) {
+                    for (int j = 0; j < SK_LANES && s0 + j < S; ++j) {
+                        const float c = nrm[m * (SK_LANES + 1) + j];
+                        T = (s0 + j == 0) ? c : T + c;
+                    }
+                    if (s0 + SK_LANES >= S)
+                        nrm[m * (SK_LANES + 1) + SK_LANES] = 1.0f / __builtin_sqrtf((T / (float)K) + eps);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MB; ++m) rn[m] = nrm[min(m, M - 1) * (SK_LANES + 1) + SK_LANES];
+    }
     for (int st = 0; st < nstages; st += DEPTH) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
             if (st + d < nstages) {
                 __syncthreads();       // everyone is done with the previous phase's LDS data
-                store(wpre[d], xpre[d]);
+                store(wpre[d], xpre[d], gpre[d]);
                 __syncthreads();
-                if (st + d + DEPTH < nstages) load(st + d + DEPTH, wpre[d], xpre[d]);
+                if (st + d + DEPTH < nstages) load(st + d + DEPTH, wpre[d], xpre[d], gpre[d]);
                 __builtin_amdgcn_sched_barrier(0);
                 compute(st + d);
             }
@@ -1008,9 +1120,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
             const int gn = n0 + fr;
             if (fm < M && gn < N) Y[(int64_t)fm * ldy + (gn >> 1)] = (T / (1.0f + exp_f(-T))) * u;
         }
-        return;
-    }
-    if constexpr (ROLE == 3) {
+    } else if constexpr (ROLE == 3) {
         // RoPE and KV append: a rotate-half pair (x_i, x_{i+64}) sits on threads fr, fr ^ 1;
         // y_i = x_i c - x_{i+64} s and y_{i+64} = x_i s + x_{i+64} c, each product rounded, as
         // the standalone RoPE kernel computes them.  q goes to Qout [M, Hq, 128], rotated k and
@@ -1038,9 +1148,7 @@ __global__ __launch_bounds__(ROWS * SK_LANES) void gemm_skinny_kernel(
                 }
             }
         }
-        return;
-    }
-    if (folder) {
+    } else if (folder) {
         const int gn = n0 + fr;
         if (fm < M && gn < N) {
             float y = T;
@@ -1061,8 +1169,15 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
 template <int MB, int ROLE, int ROWS, int MX = 0>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra = RopeArgs{}) {
     dim3 grid((a.N + ROWS - 1) / ROWS);
-    hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, ROWS, MX>), grid, dim3(ROWS * SK_LANES), 0, st,
-                       a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev, ra);
+    if (a.G) {
+        hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, ROWS, MX, 1>), grid, dim3(ROWS * SK_LANES), 0, st,
+                           a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev, ra, a.G,
+                           a.eps);
+    } else {
+        hipLaunchKernelGGL((gemm_skinny_kernel<MB, ROLE, ROWS, MX>), grid, dim3(ROWS * SK_LANES), 0, st,
+                           a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev, ra, nullptr,
+                           0.0f);
+    }
     return hipGetLastError();
 }
 
@@ -1166,6 +1281,8 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
 
 bool qkv_rope_fusable(int64_t M, int64_t D) { return M >= 1 && M <= 4 && D == RD; }
 
+bool gemm_norm_fusable(int64_t M) { return M >= 1 && M <= 4; }
+
 // the QKV projection of up to four rows with RoPE and the KV append in the VALU GEMV's epilogue
 // (same weight rows per workgroup as the plain projection of these sizes)
 hipError_t launch_qkv_rope(const GemmArgs& a, const RopeArgs& ra, hipStream_t st) {
@@ -1195,6 +1312,9 @@ hipError_t launch_gemm_tiles64(const GemmArgs& a, hipStream_t st, int role) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int role) {
+    // a normalised operand only on the slice-parallel GEMV, whose prologue computes the norm
+    if (a.G && (!gemm_norm_fusable(a.M) || gemm_route(a.M, a.N) > GR_SKINNY_M4_R16))
+        return hipErrorInvalidValue;
     const int64_t tail = gemm_tail_rows(a.M, a.Mdev);
     if (tail) {
         GemmArgs head = a, rest = a;

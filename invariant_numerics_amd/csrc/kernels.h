@@ -22,6 +22,10 @@ struct GemmArgs {
     const float* R; int64_t ldr;
     float* Y; int64_t ldy;
     const int* Mdev;  // optional: device-side row count (<= M); rows beyond it are skipped
+    // optional RMSNorm of the activation rows (gains G, BF16 [K]) applied as they are staged;
+    // only the slice-parallel GEMV routes (M <= 4) take it
+    const uint16_t* G = nullptr;
+    float eps = 0.0f;
 };
 // role 0: activation projections; role 1: the LM head's vocabulary projection; role 2: gated
 // projection (W rows interleaved gate/up, Y[m][i] = silu(gate) * up, N even, R unused)
@@ -42,6 +46,8 @@ const char* gemm_route_name(GemmRoute r);   // kernel template with ROLE left sy
 // QKV projection of up to four rows (head dim 128) with RoPE and the KV append done by the
 // VALU GEMV's epilogue (role 3); the caller runs the projection and rope_kv_append otherwise
 bool qkv_rope_fusable(int64_t M, int64_t D);
+// the RMSNorm of the activation rows runs in the GEMV's prologue for up to this many rows
+bool gemm_norm_fusable(int64_t M);
 hipError_t launch_qkv_rope(const GemmArgs& a, const RopeArgs& ra, hipStream_t st);
 
 hipError_t launch_rmsnorm(const float* X, int M, int H, int64_t ldx, const uint16_t* g, float eps,

@@ -103,23 +103,27 @@ class Decoder:
         x = inv.inv_embed(ids, self.emb)
         n = torch.empty_like(x)
         q = torch.empty((M, Hq, D), dtype=torch.float32, device=self.dev)
-        # up to four rows (decode): RoPE with the KV append runs in the QKV projection's epilogue
-        # (same bits, one launch fewer per layer)
-        fused = M <= 4 and self.gemm_events is None
+        # up to four rows (decode): each RMSNorm runs in the prologue of the projection that
+        # reads it, and RoPE with the KV append in the QKV projection's epilogue (same bits,
+        # three launches fewer per layer)
+        fused = M <= 4 and D == 128 and self.gemm_events is None
         for li, w in enumerate(self.layers):
-            inv.inv_rmsnorm(x, w["g1"], self.eps, out=n)
             if fused:
-                inv.inv_qkv_rope_kv_append(n, w["wqkv"], Hq, Hkv, D, seq, pos, self.cos, self.sin, q,
-                                           self.kc[li], self.vc[li])
+                inv.inv_rmsnorm_qkv_rope_kv_append(x, w["g1"], w["wqkv"], Hq, Hkv, D, seq, pos, self.cos,
+                                                   self.sin, q, self.kc[li], self.vc[li], eps=self.eps)
             else:
+                inv.inv_rmsnorm(x, w["g1"], self.eps, out=n)
                 qkv = self._gemm(n, w["wqkv"])
                 inv.inv_rope_kv_append(qkv, Hq, Hkv, D, seq, pos, self.cos, self.sin, q, self.kc[li], self.vc[li])
                 del qkv
             att = attend(q, li)
             self._gemm(att.view(M, Hq * D), w["wo"], R=x, out=x)
             del att
-            inv.inv_rmsnorm(x, w["g2"], self.eps, out=n)
-            h = self._gemm(n, w["w13"], gated=True)     # silu(gate) * up, [M, F]
+            if fused:
+                h = inv.inv_rmsnorm_gemm(x, w["g2"], w["w13"], eps=self.eps, gated=True)
+            else:
+                inv.inv_rmsnorm(x, w["g2"], self.eps, out=n)
+                h = self._gemm(n, w["w13"], gated=True)     # silu(gate) * up, [M, F]
             self._gemm(h, w["w2"], R=x, out=x)
             del h
         inv.inv_rmsnorm(x, self.gf, self.eps, out=n)
