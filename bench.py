@@ -240,15 +240,32 @@ def kernel_parity(orc, model, cfg, dev, T, block):
     rec("attn_decode_partial_kernel<1,4> + attn_decode_merge_kernel", got[0],
         orc.attention(qd[None], k, v, q_start=int(pos[0]))[0, 0])
     del kd, vd
-    # decode-step projections at one row (the VALU GEMV)
+    # decode-step projections at one row (the VALU GEMV): QKV and W1||W3 with the RMSNorm in
+    # their prologue (QKV with RoPE and the KV append), O plain, W2 below
     x1 = synth.normal(15208, (1, H))
-    for name in ("wqkv", "wo"):
-        w = lay[name]
-        nm = inv.inv_kernel_route("gemm", 1, w.shape[0])
-        rec(nm, inv.inv_fixed_order_gemm(dev_f32(x1), dev_bf16(w)).cpu().numpy(), orc.gemm(x1, w))
-    nm = inv.inv_kernel_route("gated_gemm", 1, 2 * F)
-    rec(nm, inv.inv_gated_gemm(dev_f32(x1), dev_bf16(wi)).cpu().numpy(),
-        orc.swiglu(orc.gemm(x1, w13[:F]), orc.gemm(x1, w13[F:])))
+    gam = synth.to_bf16_bits(np.float32(1.0) + synth.normal(15212, (H,), 0.1))
+    n1 = orc.rmsnorm(x1, gam)
+    w = lay["wqkv"]
+    nm = inv.inv_kernel_route("gemm", 1, w.shape[0]).replace("<1,0,", "<1,3,") + " + RMSNorm prologue, RoPE, KV append"
+    tm, p1 = 64, np.array([37], np.int32)
+    cos_t, sin_t = synth.rope_tables(tm, D, cfg["theta"])
+    qo = torch.zeros((1, Hq, D), device=dev)
+    kc = torch.zeros((1, Hkv, tm, D), device=dev)
+    vc = torch.zeros((1, Hkv, tm, D), device=dev)
+    inv.inv_rmsnorm_qkv_rope_kv_append(dev_f32(x1), dev_bf16(gam), dev_bf16(w), Hq, Hkv, D,
+                                       torch.zeros(1, dtype=torch.int32, device=dev), torch.from_numpy(p1).to(dev),
+                                       dev_f32(cos_t), dev_f32(sin_t), qo, kc, vc)
+    qkv = orc.gemm(n1, w)
+    rec(nm, qo.cpu().numpy(), orc.rope(qkv[:, :Hq * D].reshape(1, Hq, D), p1, cos_t, sin_t))
+    rec(nm, kc.cpu().numpy()[0, :, 37], orc.rope(qkv[:, Hq * D:(Hq + Hkv) * D].reshape(1, Hkv, D), p1, cos_t,
+                                                  sin_t)[0])
+    rec(nm, vc.cpu().numpy()[0, :, 37], qkv[:, (Hq + Hkv) * D:].reshape(Hkv, D))
+    w = lay["wo"]
+    nm = inv.inv_kernel_route("gemm", 1, w.shape[0])
+    rec(nm, inv.inv_fixed_order_gemm(dev_f32(x1), dev_bf16(w)).cpu().numpy(), orc.gemm(x1, w))
+    nm = inv.inv_kernel_route("gated_gemm", 1, 2 * F) + " + RMSNorm prologue"
+    rec(nm, inv.inv_rmsnorm_gemm(dev_f32(x1), dev_bf16(gam), dev_bf16(wi), gated=True).cpu().numpy(),
+        orc.swiglu(orc.gemm(n1, w13[:F]), orc.gemm(n1, w13[F:])))
     x1f = synth.normal(15209, (1, F))
     nm = inv.inv_kernel_route("gemm", 1, H) + " (K 14336)"
     rec(nm, inv.inv_fixed_order_gemm(dev_f32(x1f), dev_bf16(lay["w2"])).cpu().numpy(), orc.gemm(x1f, lay["w2"]))

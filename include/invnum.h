@@ -401,11 +401,13 @@ int inv_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, co
  *   the optional residual R) or inv_gated_gemm (gated = 1: W interleaved gate/up rows, N even,
  *   Y [M, N/2], R must be NULL) on the normalised rows, without storing them: each workgroup of
  *   the GEMV computes r = 1 / sqrt((dot_KS(x, x, K) / K) + eps) of every row itself, in the
- *   RMSNorm's order, and stages (x_k * r) * up(g_k) as the operand.  One launch instead of two.
+ *   RMSNorm's order, and stages (x_k * r) * up(g_k) as the operand.  One launch instead of two;
+ *   the rows' norms are computed one after another, so it pays for a single row.
  * X: FP32 [M, K] (ldx), the norm's input; gamma: BF16 [K], 16-byte aligned.  W, N, ldw, R,
- * ldr, Y, ldy as inv_fixed_order_gemm / inv_gated_gemm.  K <= 16384.
- * Errors: INV_ERR_NULL, INV_ERR_SHAPE, INV_ERR_ALIGN, INV_ERR_UNSUPPORTED (M outside 1..4, or
- * K > 16384), INV_ERR_LAUNCH.
+ * ldr, Y, ldy as inv_fixed_order_gemm / inv_gated_gemm; R may equal Y, but Y must not overlap X
+ * (every workgroup reads the whole rows of X while others store Y).  K <= 16384.
+ * Errors: INV_ERR_NULL, INV_ERR_SHAPE (also for Y overlapping X), INV_ERR_ALIGN,
+ * INV_ERR_UNSUPPORTED (M outside 1..4, or K > 16384), INV_ERR_LAUNCH.
  * Sources: Meituan page, "key practices" (batch-invariant RMSNorm and GEMM operators); FP32
  * write-up section 5 (LayerCast).
  * ------------------------------------------------------------------------------------ */
@@ -418,7 +420,8 @@ int inv_rmsnorm_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, const ui
  * bit inv_rmsnorm(X, gamma, eps) and then inv_qkv_rope_kv_append on its output, in one GEMV
  * launch whose workgroups compute the norm themselves (as inv_rmsnorm_gemm).  For one to four
  * rows with D = 128 only (INV_ERR_UNSUPPORTED otherwise; K <= 16384); needs no workspace.
- * Arguments as inv_qkv_rope_kv_append, plus gamma (BF16 [K], 16-byte aligned) and eps.
+ * Arguments as inv_qkv_rope_kv_append, plus gamma (BF16 [K], 16-byte aligned) and eps; X must
+ * not overlap Qout or the caches (INV_ERR_SHAPE).
  * Errors: INV_ERR_NULL, INV_ERR_SHAPE, INV_ERR_ALIGN, INV_ERR_UNSUPPORTED, INV_ERR_LAUNCH.
  * Sources: Meituan page, "key practices" (batch-invariant operators; decode replays the same
  * accumulation path as prefill).

@@ -115,6 +115,12 @@ int inv_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t ldx, co
                                      (int)Bcache, Qout, Kc, Vc, INV_F32, S(stream)));
 }
 
+// [a, a + an) and [b, b + bn) (bytes) overlap
+static bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + bn && pb < pa + an;
+}
+
 int inv_rmsnorm_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma, float eps,
                      const uint16_t* W, int64_t N, int64_t ldw, const float* R, int64_t ldr, float* Y, int64_t ldy,
                      int gated, void* stream) {
@@ -128,6 +134,9 @@ int inv_rmsnorm_gemm(const float* X, int64_t M, int64_t K, int64_t ldx, const ui
     if (!al16(X) || !al16(W) || !al16(gamma) || ldx % 4 || ldw % 8) return INV_ERR_ALIGN;
     if ((reinterpret_cast<uintptr_t>(Y) & 3u) || (R && (reinterpret_cast<uintptr_t>(R) & 3u)))
         return INV_ERR_ALIGN;
+    // every workgroup reads the whole rows of X while others already store Y
+    if (overlaps(X, sizeof(float) * (size_t)((M - 1) * ldx + K), Y, sizeof(float) * (size_t)((M - 1) * ldy + ny)))
+        return INV_ERR_SHAPE;
     GemmArgs a{X, (int)M, (int)K, ldx, W, (int)N, ldw, R, ldr, Y, ldy, nullptr, gamma, eps};
     return fin(launch_gemm(a, S(stream), gated ? 2 : 0));
 }
@@ -144,6 +153,12 @@ int inv_rmsnorm_qkv_rope_kv_append(const float* X, int64_t M, int64_t K, int64_t
     if (!qkv_rope_fusable(M, D) || !gemm_norm_fusable(M) || K > 16384) return INV_ERR_UNSUPPORTED;
     if (!al16(X) || !al16(Wqkv) || !al16(gamma) || ldx % 4 || ldw % 8) return INV_ERR_ALIGN;
     const int64_t N = (Hq + 2 * Hkv) * D;
+    // every workgroup reads the whole rows of X while others already store q, k and v
+    const size_t xb = sizeof(float) * (size_t)((M - 1) * ldx + K);
+    if (overlaps(X, xb, Qout, sizeof(float) * (size_t)(M * Hq * D)) ||
+        overlaps(X, xb, Kc, sizeof(float) * (size_t)(Bcache * Hkv * Tmax * D)) ||
+        overlaps(X, xb, Vc, sizeof(float) * (size_t)(Bcache * Hkv * Tmax * D)))
+        return INV_ERR_SHAPE;
     GemmArgs a{X, (int)M, (int)K, ldx, Wqkv, (int)N, ldw, nullptr, 0, nullptr, 0, nullptr, gamma, eps};
     RopeArgs ra{(int)Hq, (int)Hkv, seq, pos, cos_t, sin_t, (int)Tmax, (int)Bcache, Qout, Kc, Vc};
     return fin(launch_qkv_rope(a, ra, S(stream)));

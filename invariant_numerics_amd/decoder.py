@@ -103,14 +103,20 @@ class Decoder:
         x = inv.inv_embed(ids, self.emb)
         n = torch.empty_like(x)
         q = torch.empty((M, Hq, D), dtype=torch.float32, device=self.dev)
-        # up to four rows (decode): each RMSNorm runs in the prologue of the projection that
-        # reads it, and RoPE with the KV append in the QKV projection's epilogue (same bits,
-        # three launches fewer per layer)
+        # up to four rows (decode): RoPE with the KV append runs in the QKV projection's epilogue;
+        # for one row each RMSNorm also runs in the prologue of the projection that reads it
+        # (same bits, one and three launches fewer per layer; with more rows the prologue,
+        # which walks the rows in turn, costs more than the norm's launch)
         fused = M <= 4 and D == 128 and self.gemm_events is None
+        fnorm = fused and M == 1
         for li, w in enumerate(self.layers):
-            if fused:
+            if fnorm:
                 inv.inv_rmsnorm_qkv_rope_kv_append(x, w["g1"], w["wqkv"], Hq, Hkv, D, seq, pos, self.cos,
                                                    self.sin, q, self.kc[li], self.vc[li], eps=self.eps)
+            elif fused:
+                inv.inv_rmsnorm(x, w["g1"], self.eps, out=n)
+                inv.inv_qkv_rope_kv_append(n, w["wqkv"], Hq, Hkv, D, seq, pos, self.cos, self.sin, q,
+                                           self.kc[li], self.vc[li])
             else:
                 inv.inv_rmsnorm(x, w["g1"], self.eps, out=n)
                 qkv = self._gemm(n, w["wqkv"])
@@ -119,7 +125,7 @@ class Decoder:
             att = attend(q, li)
             self._gemm(att.view(M, Hq * D), w["wo"], R=x, out=x)
             del att
-            if fused:
+            if fnorm:
                 h = inv.inv_rmsnorm_gemm(x, w["g2"], w["w13"], eps=self.eps, gated=True)
             else:
                 inv.inv_rmsnorm(x, w["g2"], self.eps, out=n)

@@ -71,6 +71,33 @@ def test_gated_gemm_argument_validation(inv):
     assert g(MIS, 1, 64, 64, FAKE, 8, 64, FAKE, 4, None) == -3        # misaligned X
 
 
+def test_rmsnorm_fused_argument_validation(inv):
+    L = inv.LIB
+    g = L.inv_rmsnorm_gemm
+    OUT = FAKE + (1 << 20)                    # an output 1 MiB away from X
+    assert g(None, 1, 64, 64, FAKE, 1e-5, FAKE, 8, 64, None, 0, OUT, 8, 0, None) == -1
+    assert g(FAKE, 1, 64, 64, None, 1e-5, FAKE, 8, 64, None, 0, OUT, 8, 0, None) == -1    # no gains
+    assert g(FAKE, 1, 64, 64, FAKE, 1e-5, FAKE, 8, 64, None, 0, OUT, 8, 2, None) == -2    # gated not 0/1
+    assert g(FAKE, 1, 64, 64, FAKE, 1e-5, FAKE, 7, 64, None, 0, OUT, 8, 1, None) == -2    # gated, odd N
+    assert g(FAKE, 1, 64, 64, FAKE, 1e-5, FAKE, 8, 64, FAKE, 8, OUT, 8, 1, None) == -2    # gated with R
+    assert g(FAKE, 1, 60, 64, FAKE, 1e-5, FAKE, 8, 64, None, 0, OUT, 8, 0, None) == -2    # K % 8
+    assert g(FAKE, 5, 64, 64, FAKE, 1e-5, FAKE, 8, 64, None, 0, OUT, 8, 0, None) == -6    # M > 4
+    assert g(FAKE, 1, 16392, 16392, FAKE, 1e-5, FAKE, 8, 16392, None, 0, OUT, 8, 0, None) == -6  # K > 16384
+    assert g(FAKE, 1, 64, 64, MIS, 1e-5, FAKE, 8, 64, None, 0, OUT, 8, 0, None) == -3     # misaligned gains
+    assert g(FAKE, 2, 64, 64, FAKE, 1e-5, FAKE, 8, 64, None, 0, FAKE + 256, 8, 0, None) == -2  # Y overlaps X
+    q = L.inv_rmsnorm_qkv_rope_kv_append
+    args = [FAKE, 1, 64, 64, FAKE, 1e-5, FAKE, 64, 2, 1, 128, FAKE, FAKE, FAKE, FAKE, 16, 1, OUT, OUT + (1 << 16),
+            OUT + (1 << 17), None]
+    bad = list(args); bad[4] = None
+    assert q(*bad) == -1
+    bad = list(args); bad[1] = 5
+    assert q(*bad) == -6                                                                # M > 4
+    bad = list(args); bad[10] = 64
+    assert q(*bad) == -6                                                                # D != 128
+    bad = list(args); bad[17] = FAKE
+    assert q(*bad) == -2                                                                # Qout overlaps X
+
+
 def test_attention_argument_validation(inv):
     L = inv.LIB
     p = L.inv_attention_prefill
