@@ -506,6 +506,9 @@ hipError_t launch_small(const GemmArgs& a, hipStream_t st) {
 // lane group g reads it (k = 4 s + g for s = 0..CH/4-1: CH/2 contiguous bytes), the
 // activation tile as FP32 in the same order.  Measured: 64-wide chunks are best or equal on
 // every decoder shape (128-wide ones halve the workgroups a CU holds at N >= 12288).
+// With a grid of several rows (blockIdx.y) each grid row takes its own group of 16 MT
+// activation rows: more and lighter workgroups, so a CU holds several and one's staging and
+// barriers run under another's matrix work (every output's sum is unchanged).
 template <int WN, int PD, int CH, int ROLE, int MT, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
     const float* __restrict__ X, int M, int K, int64_t ldx,
@@ -527,6 +530,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
     __shared__ __attribute__((aligned(16))) float Xl[2][MR * WK * XSEG];
     __shared__ __attribute__((aligned(16))) float part[WK > 1 ? WK * WN * MT * 64 * 4 : 4];
     if (Mdev) M = min(M, *Mdev);
+    if (gridDim.y > 1) {
+        // row group blockIdx.y: activation rows 16 MT y .. 16 MT y + 16 MT - 1
+        const int my = blockIdx.y * 16 * MT;
+        X += (int64_t)my * ldx;
+        Y += (int64_t)my * ldy;
+        if (R) R += (int64_t)my * ldr;
+        M = min(M - my, 16 * MT);
+    }
     if (M <= 0) return;
     const int n0 = blockIdx.x * BN;
     const int S = (K + KS - 1) / KS;
@@ -758,9 +769,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_gemv16_kernel(
         }
 }
 
+// groups > 1: the rows are cut into groups of 16 MT, one grid row (blockIdx.y) per group
 template <int WN, int PD, int CH, int ROLE, int MT = 1, int NW = 4>
-hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st) {
-    dim3 grid((a.N + 16 * WN - 1) / (16 * WN));
+hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st, int groups = 1) {
+    dim3 grid((a.N + 16 * WN - 1) / (16 * WN), groups);
     hipLaunchKernelGGL((gemm_gemv16_kernel<WN, PD, CH, ROLE, MT, NW>), grid, dim3(64 * NW), 0, st,
                        a.X, a.M, a.K, a.ldx, a.W, a.N, a.ldw, a.R, a.ldr, a.Y, a.ldy, a.Mdev);
     return hipGetLastError();
@@ -1195,8 +1207,13 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra =
 //     N = 2048..4096, where there are only N / 16 workgroups (12-18% faster at N = 4096 for
 //     K = 4096 and 14336, slower at N = 6144);
 //   17 <= M <= 32: the same with two row tiles (measured faster than the 32 x 32 tiles, or
-//     equal, at every decoder shape); 33 <= M <= 64 with N of 1024 to 4096: four row tiles
-//     (1.4-1.6x faster there than the tiled kernels, slower at larger N);
+//     equal, at every decoder shape), except for 4096 < N < 12288, where the rows run as two
+//     grid rows of one 16-row tile (N = 6144: 46 -> 35 us at M = 24-32, cold weights);
+//   33 <= M <= 64 with N of 1024 to 4096: grid rows of 32 activation rows (two row tiles,
+//     32-wide chunks) from N = 3072, of 16 rows below; one workgroup with four row tiles took
+//     41 us at every such N and K = 4096 (its chunk loop, not the weight stream, set the time),
+//     row groups 35 us at N = 4096 (108 against 134 us at K = 14336) and 17-22 us at N =
+//     1024-2048;
 //   other M: 32 x 32 tiles while the 64 x 64 grid would have fewer than SMALL_BELOW (512)
 //     tiles, two per CU (256 for M <= 64) (M = 128 / 257 at N = 4096: 1.36 / 1.29x faster
 //     than 64 x 64, and the same for the down projection; equal or slower from 512 tiles on);
@@ -1211,8 +1228,12 @@ GemmRoute gemm_route(int64_t M, int64_t N) {
         if (N >= 12288) return GR_GEMV16_WN2;
         return (N >= 2048 && N <= 4096) ? GR_GEMV16_WN1_W8 : GR_GEMV16_WN1;
     }
-    if (M <= 32) return N >= 65536 ? GR_GEMV32_WN4 : (N >= 12288 ? GR_GEMV32_WN2 : GR_GEMV32_WN1);
-    if (M <= 64 && N >= 1024 && N <= 4096) return GR_GEMV64;
+    if (M <= 32) {
+        if (N >= 65536) return GR_GEMV32_WN4;
+        if (N >= 12288) return GR_GEMV32_WN2;
+        return N > 4096 ? GR_GEMV32_G16 : GR_GEMV32_WN1;
+    }
+    if (M <= 64 && N >= 1024 && N <= 4096) return N >= 3072 ? GR_GEMV64_G32 : GR_GEMV64_G16;
     const int64_t big = ((M + 127) / 128) * ((N + 255) / 256);
     const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
     if (M <= 64) return mid < SMALL_BELOW / 2 ? GR_SMALL32 : GR_TILE64;
@@ -1245,7 +1266,9 @@ const char* gemm_route_name(GemmRoute r) {
         case GR_GEMV32_WN1: return "gemm_gemv16_kernel<1,2,64,ROLE,2,4>";
         case GR_GEMV32_WN2: return "gemm_gemv16_kernel<2,2,64,ROLE,2,4>";
         case GR_GEMV32_WN4: return "gemm_gemv16_kernel<4,2,64,ROLE,2,4>";
-        case GR_GEMV64: return "gemm_gemv16_kernel<1,2,32,ROLE,4,4>";
+        case GR_GEMV32_G16: return "gemm_gemv16_kernel<1,2,64,ROLE,1,4> by 16-row groups";
+        case GR_GEMV64_G32: return "gemm_gemv16_kernel<1,2,32,ROLE,2,4> by 32-row groups";
+        case GR_GEMV64_G16: return "gemm_gemv16_kernel<1,2,64,ROLE,1,4> by 16-row groups";
         case GR_SMALL32: return "gemm_small_kernel<ROLE>";
         case GR_TILE64: return "gemm_mfma_kernel<64,64,2,2,ROLE>";
         case GR_TILE64x128: return "gemm_mfma_kernel<64,128,2,4,ROLE>";
@@ -1270,7 +1293,9 @@ hipError_t launch_role(const GemmArgs& a, hipStream_t st) {
         case GR_GEMV32_WN1: return launch_gemv16<1, 2, 64, ROLE, 2>(a, st);
         case GR_GEMV32_WN2: return launch_gemv16<2, 2, 64, ROLE, 2>(a, st);
         case GR_GEMV32_WN4: return launch_gemv16<4, 2, 64, ROLE, 2>(a, st);
-        case GR_GEMV64: return launch_gemv16<1, 2, 32, ROLE, 4>(a, st);
+        case GR_GEMV32_G16: return launch_gemv16<1, 2, 64, ROLE, 1>(a, st, (int)((a.M + 15) / 16));
+        case GR_GEMV64_G32: return launch_gemv16<1, 2, 32, ROLE, 2>(a, st, (int)((a.M + 31) / 32));
+        case GR_GEMV64_G16: return launch_gemv16<1, 2, 64, ROLE, 1>(a, st, (int)((a.M + 15) / 16));
         case GR_SMALL32: return launch_small<ROLE>(a, st);
         case GR_TILE64: return launch_tiled<64, 64, 2, 2, ROLE>(a, st);
         case GR_TILE64x128: return launch_tiled<64, 128, 2, 4, ROLE>(a, st);

@@ -37,7 +37,7 @@ hipError_t launch_gemm_tiles64(const GemmArgs& a, hipStream_t st, int role);
 enum GemmRoute : int {
     GR_SKINNY_M1_R4, GR_SKINNY_M1_R16, GR_SKINNY_M2_R4, GR_SKINNY_M2_R16, GR_SKINNY_M4_R16,
     GR_GEMV16_WN1, GR_GEMV16_WN1_W8, GR_GEMV16_WN2, GR_GEMV16_WN4, GR_GEMV32_WN1, GR_GEMV32_WN2, GR_GEMV32_WN4,
-    GR_GEMV64, GR_SMALL32, GR_TILE64, GR_TILE64x128, GR_TILE128x256
+    GR_GEMV32_G16, GR_GEMV64_G32, GR_GEMV64_G16, GR_SMALL32, GR_TILE64, GR_TILE64x128, GR_TILE128x256
 };
 GemmRoute gemm_route(int64_t M, int64_t N);
 // rows split off to the skinny GEMV after the tiled part (0: none)

@@ -23,6 +23,7 @@ def inv():
     (17, 264, 129), (20, 8200, 2049), (32, 520, 12300), (33, 520, 2050), (64, 1032, 4096),
     (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
     (190, 264, 8300), (260, 520, 9000), (129, 264, 300), (193, 520, 8300),
+    (24, 520, 6150), (17, 4104, 4100), (32, 264, 12287), (47, 264, 3072), (33, 8200, 1024),
 ])
 def test_gemm_matches_oracle_small(orc, M, K, N):
     say("gemm", M, K, N)
@@ -45,6 +46,22 @@ def test_gemm_residual_epilogue(orc):
         Rs = synth.normal(7205 + rows, (rows, 96))
         got = host(inv().inv_fixed_order_gemm(f32(Xs), bf16(W), R=f32(Rs)))
         assert_bitwise(got, (Rs + orc.gemm(Xs, W)).astype(np.float32), "residual %d rows" % rows)
+
+
+@pytest.mark.parametrize("M,K,N", [(50, 264, 4096), (64, 520, 3072), (40, 1032, 2048), (29, 264, 6144)])
+def test_gemm_row_groups_with_residual(orc, M, K, N):
+    """Routes that cut the activation rows into grid rows of 32 or 16 (33-64 rows at N =
+    1024-4096, 17-32 rows at N = 4097-12287), with the residual epilogue: every group's rows,
+    residual rows and output rows are its own."""
+    say("gemm row groups", M, K, N, inv().inv_kernel_route("gemm", M, N))
+    assert "row groups" in inv().inv_kernel_route("gemm", M, N)
+    X = synth.normal(7210 + M, (M, K))
+    W = synth.bf16_normal(7211 + N, (N, K))
+    R = synth.normal(7212 + M, (M, N))
+    want = (R + orc.gemm(X, W)).astype(np.float32)
+    Rd = f32(R)
+    inv().inv_fixed_order_gemm(f32(X), bf16(W), R=Rd, out=Rd)
+    assert_bitwise(host(Rd), want, "row groups + residual")
 
 
 def test_gemm_worked_example_k3_padded():
@@ -104,7 +121,8 @@ def test_gemm_full_size_batch_invariance(orc, n, k):
 
 @pytest.mark.parametrize("M,K,F", [(1, 4096, 14336), (2, 264, 37), (3, 520, 70), (4, 8200, 37), (5, 1000, 64), (16, 4096, 130),
                                    (12, 520, 4200), (9, 264, 6500), (8, 4096, 14336), (6, 8456, 50), (17, 264, 129), (24, 520, 1030),
-                                   (48, 264, 1100), (64, 768, 64), (65, 4096, 300),
+                                   (48, 264, 1100), (64, 768, 64), (65, 4096, 300), (20, 520, 3000),
+                                   (64, 264, 2048),
                                    (300, 1032, 257), (190, 264, 4200), (130, 264, 300)])
 def test_gated_gemm_equals_gemm_then_swiglu(orc, M, K, F):
     """inv_gated_gemm on gate/up rows interleaved equals inv_fixed_order_gemm followed by
