@@ -1209,11 +1209,12 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st, const RopeArgs& ra =
 //   17 <= M <= 32: the same with two row tiles (measured faster than the 32 x 32 tiles, or
 //     equal, at every decoder shape), except for 4096 < N < 12288, where the rows run as two
 //     grid rows of one 16-row tile (N = 6144: 46 -> 35 us at M = 24-32, cold weights);
-//   33 <= M <= 64 with N of 1024 to 4096: grid rows of 32 activation rows (two row tiles,
-//     32-wide chunks) from N = 3072, of 16 rows below; one workgroup with four row tiles took
-//     41 us at every such N and K = 4096 (its chunk loop, not the weight stream, set the time),
-//     row groups 35 us at N = 4096 (108 against 134 us at K = 14336) and 17-22 us at N =
-//     1024-2048;
+//   33 <= M <= 64 with N of 1024 to 8192: grid rows of 32 activation rows (two row tiles,
+//     32-wide chunks) above 48 rows from N = 3072, else of 16 rows (one tile); one workgroup
+//     with four row tiles took 41 us at every N of 1024-4096 and K = 4096 (its chunk loop, not
+//     the weight stream, set the time), row groups 35 us at N = 4096 (108 against 134 us at
+//     K = 14336) and 17-22 us at N = 1024-2048; at N = 6144 and 8192 they beat the 32 x 32
+//     tiles (79 -> 53-59 us, 82 -> 69 us), from N = 14336 the tiles are faster;
 //   other M: 32 x 32 tiles while the 64 x 64 grid would have fewer than SMALL_BELOW (512)
 //     tiles, two per CU (256 for M <= 64) (M = 128 / 257 at N = 4096: 1.36 / 1.29x faster
 //     than 64 x 64, and the same for the down projection; equal or slower from 512 tiles on);
@@ -1233,7 +1234,7 @@ GemmRoute gemm_route(int64_t M, int64_t N) {
         if (N >= 12288) return GR_GEMV32_WN2;
         return N > 4096 ? GR_GEMV32_G16 : GR_GEMV32_WN1;
     }
-    if (M <= 64 && N >= 1024 && N <= 4096) return N >= 3072 ? GR_GEMV64_G32 : GR_GEMV64_G16;
+    if (M <= 64 && N >= 1024 && N <= 8192) return (M > 48 && N >= 3072) ? GR_GEMV64_G32 : GR_GEMV64_G16;
     const int64_t big = ((M + 127) / 128) * ((N + 255) / 256);
     const int64_t mid = ((M + 63) / 64) * ((N + 63) / 64);
     if (M <= 64) return mid < SMALL_BELOW / 2 ? GR_SMALL32 : GR_TILE64;

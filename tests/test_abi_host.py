@@ -148,7 +148,10 @@ def test_kernel_route_names(inv):
     assert r("gemm", 40, 2048) == "gemm_gemv16_kernel<1,2,64,0,1,4> by 16-row groups"
     assert r("gemm", 24, 6144) == "gemm_gemv16_kernel<1,2,64,0,1,4> by 16-row groups"
     assert r("gemm", 24, 4096) == "gemm_gemv16_kernel<1,2,64,0,2,4>"
-    assert r("gemm", 64, 8192) == "gemm_small_kernel<0>"
+    assert r("gemm", 48, 4096) == "gemm_gemv16_kernel<1,2,64,0,1,4> by 16-row groups"
+    assert r("gemm", 40, 6144) == "gemm_gemv16_kernel<1,2,64,0,1,4> by 16-row groups"
+    assert r("gemm", 64, 8192) == "gemm_gemv16_kernel<1,2,32,0,2,4> by 32-row groups"
+    assert not r("gemm", 64, 14336).startswith("gemm_gemv16")
     assert r("gemm", 64, 16384) == "gemm_mfma_kernel<64,64,2,2,0>"
     assert r("gemm", 512, 4096) == "gemm_mfma_kernel<64,128,2,4,0>"
     assert r("gemm", 1024, 14336) == "gemm_mfma_kernel<64,128,2,4,0>"

@@ -24,6 +24,7 @@ def inv():
     (40, 4096, 200), (64, 768, 64), (65, 256, 300), (130, 1032, 257), (200, 4096, 129),
     (190, 264, 8300), (260, 520, 9000), (129, 264, 300), (193, 520, 8300),
     (24, 520, 6150), (17, 4104, 4100), (32, 264, 12287), (47, 264, 3072), (33, 8200, 1024),
+    (40, 264, 6144), (64, 264, 8192), (49, 520, 3072),
 ])
 def test_gemm_matches_oracle_small(orc, M, K, N):
     say("gemm", M, K, N)
@@ -48,7 +49,8 @@ def test_gemm_residual_epilogue(orc):
         assert_bitwise(got, (Rs + orc.gemm(Xs, W)).astype(np.float32), "residual %d rows" % rows)
 
 
-@pytest.mark.parametrize("M,K,N", [(50, 264, 4096), (64, 520, 3072), (40, 1032, 2048), (29, 264, 6144)])
+@pytest.mark.parametrize("M,K,N", [(50, 264, 4096), (64, 520, 3072), (40, 1032, 2048), (29, 264, 6144),
+                                   (64, 264, 6144)])
 def test_gemm_row_groups_with_residual(orc, M, K, N):
     """Routes that cut the activation rows into grid rows of 32 or 16 (33-64 rows at N =
     1024-4096, 17-32 rows at N = 4097-12287), with the residual epilogue: every group's rows,
