@@ -3,7 +3,8 @@ batch 1 to 64 (its prefill scoring is bench.py).
 
 Seeded synthetic inputs from ``synth`` (the same arrays the parity tests use); every timing
 is the median of HIP-event-bracketed repetitions on the current stream, inputs resident in
-HBM.  Prints one JSON object per measurement:
+HBM.  Prints one JSON object per measurement, and per configuration the bitwise match rates of
+GPU outputs across batch sizes (C1, C3, C4) and between prefill and decode (C2):
   * C1: LM head, hidden 256, vocab 4096, 64 tokens as 64 / B calls of batch B, issued call by
     call from Python and, captured once as a HIP graph, replayed;
   * C2: causal attention, 8 heads x 2048 x 128, BF16 inputs: the whole prefill (four calls
@@ -39,6 +40,13 @@ def timeit(fn, reps=10, warm=2):
         a.record(); fn(); b.record(); torch.cuda.synchronize(); ts.append(a.elapsed_time(b) * 1e-3)
     return float(np.median(ts))
 def out(**k): print(json.dumps(k), flush=True)
+def match(a, b):
+    """Bitwise match rate: equal 32-bit words / compared words (float32 outputs compared as bits)."""
+    a, b = a.contiguous(), b.contiguous()
+    if a.dtype == torch.float32:
+        a, b = a.view(torch.int32), b.view(torch.int32)
+    return round(float((a == b).sum().item()) / a.numel(), 6)
+LMK = ("logprob", "margin", "top1", "top2", "recomputed")
 def bf(a): return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
 def f32(a): return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 HBM = 8000.0
@@ -69,6 +77,7 @@ if "probes" in SECTIONS:
 if "C1" in SECTIONS:
     d = synth.c1_inputs()
     H, W, T = f32(d["h"]), bf(d["w"]), torch.from_numpy(np.ascontiguousarray(d["target"], np.int32)).to(dev)
+    c1out = {}
     for B in (1, 2, 4, 8):
         ws1 = torch.empty(inv.inv_lmhead_workspace_bytes(B, 256, 4096), dtype=torch.uint8, device=dev)
         r1 = inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1, ws=ws1)
@@ -76,6 +85,12 @@ if "C1" in SECTIONS:
             for s in range(0, 64, B):
                 inv.inv_lmhead_logprob_top2(H[s:s + B], W, T[s:s + B], 0.1, ws=ws1, out=r1)
         t = timeit(run)
+        # the 64 rows as computed at this batch size, for the across-batch match rate
+        c1rows = {k: [] for k in LMK}
+        for s in range(0, 64, B):
+            rr = inv.inv_lmhead_logprob_top2(H[s:s + B], W, T[s:s + B], 0.1, ws=ws1)
+            for k in LMK: c1rows[k].append(rr[k].clone())
+        c1out[B] = {k: torch.cat(v) for k, v in c1rows.items()}
         # the same 64 / B calls captured once as a HIP graph and replayed: the device time,
         # without the host's time to issue each call
         run()
@@ -86,6 +101,8 @@ if "C1" in SECTIONS:
         tg = timeit(g1.replay)
         out(config="C1", batch=B, calls=64 // B, us_per_call=round(t / (64 // B) * 1e6, 1), tokens_per_s=round(64 / t, 1),
             graph_us_per_call=round(tg / (64 // B) * 1e6, 1), graph_tokens_per_s=round(64 / tg, 1))
+    out(config="C1", bitwise_across_batch_vs_b1={B: min(match(c1out[B][k], c1out[1][k]) for k in LMK) for B in c1out},
+        words_per_batch=64 * len(LMK))
 # ---- C2: attention 8 heads x 2048 x d128, bf16, causal
 if "C2" in SECTIONS:
     d = synth.c2_inputs()
@@ -106,6 +123,14 @@ if "C2" in SECTIONS:
             inv.inv_attention_decode(q[:, tt], k, v, posd[tt:tt + 1], out=o1, ws=ws)
     t = timeit(dec, reps=3, warm=1)
     out(config="C2", op="decode", us_per_call=round(t / 256 * 1e6, 2), note="256 calls at positions 0, 8, ..., 2040")
+    # every position's decode row against the prefill row, and the prefill of the first 1024
+    # rows (a different grid) against the same rows of the full prefill
+    dall = torch.empty((2048, 8, 128), dtype=torch.float32, device=dev)
+    for tt in range(2048):
+        inv.inv_attention_decode(q[:, tt], k, v, posd[tt:tt + 1], out=dall[tt:tt + 1], ws=ws)
+    half = inv.inv_attention_prefill(q[:, :1024].contiguous(), k, v)
+    out(config="C2", bitwise_prefill_vs_decode=match(dall, op[0]), positions=2048,
+        bitwise_prefill_1024_rows_vs_2048=match(half[0], op[0, :1024]))
 # ---- C3: GEMM, weights cold (rotating copies > the 256 MB last-level cache)
 if "C3" in SECTIONS:
     for (n, kk) in ((4096, 4096), (14336, 4096), (4096, 14336)):
@@ -114,6 +139,7 @@ if "C3" in SECTIONS:
         X = f32(dd["x"]); W0 = bf(dd["w"])
         ncp = max(2, int(600e6 // (n * kk * 2)) + 1)
         Ws = [W0] + [W0.clone() for _ in range(ncp - 1)]
+        c3out = {}
         for M in (1, 3, 16, 64, 257, 512):
             Y = torch.empty((M, n), dtype=torch.float32, device=dev)
             ctr = [0]
@@ -125,14 +151,21 @@ if "C3" in SECTIONS:
             by = n * kk * 2 + 4 * M * kk + 4 * M * n
             out(config="C3", N=n, K=kk, M=M, us=round(t * 1e6, 1), tflops=round(2 * M * n * kk / t / 1e12, 2),
                 hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3), frac_fp32=round(2 * M * n * kk / t / 157.3e12, 3))
+            c3out[M] = Y.clone()
+        perm = torch.from_numpy(synth.permutation(7400, 512).astype(np.int64)).to(dev)
+        shuf = inv.inv_fixed_order_gemm(X[perm].contiguous(), W0)
+        out(config="C3", N=n, K=kk, bitwise_rows_vs_m512={M: match(c3out[M], c3out[512][:M]) for M in c3out},
+            bitwise_shuffled_rows=match(shuf, c3out[512][perm]))
         del Ws
 # ---- C4: LM head hidden 4096, vocab 128256, B = 1 .. 256
 if "C4" in SECTIONS:
     d = synth.c4_inputs()
     H, W, T = f32(d["h"]), bf(d["w"]), torch.from_numpy(np.ascontiguousarray(d["target"], np.int32)).to(dev)
+    c4out = {}
     for B in (1, 2, 4, 8, 16, 32, 64, 128, 256):
         ws = torch.empty(inv.inv_lmhead_workspace_bytes(B, 4096, 128256), dtype=torch.uint8, device=dev)
         r = inv.inv_lmhead_logprob_top2(H[:B], W, T[:B], 0.1, ws=ws)
+        c4out[B] = {k: r[k].clone() for k in LMK}
         nrec = int(r["recomputed"].sum().item())
         def four():
             for _ in range(4):
@@ -143,6 +176,7 @@ if "C4" in SECTIONS:
         out(config="C4", batch=B, recomputed=nrec, us=round(t * 1e6, 1), tokens_per_s=round(B / t, 1),
             hbm_gbs=round(by / t / 1e9, 1), frac_hbm=round(by / t / 1e9 / HBM, 3),
             tflops=round(2 * 128256 * 4096 * (B + nrec) / t / 1e12, 2))
+    out(config="C4", bitwise_rows_vs_b256={B: min(match(c4out[B][k], c4out[256][k][:B]) for k in LMK) for B in c4out})
 # ---- C5: decode steps of the 4-layer decoder at a 32k context, batch 1 .. 64 (graph replay;
 # KV caches filled with seeded random values, every row at its own position near 32k)
 if "C5" in SECTIONS:
