@@ -308,7 +308,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(rows are independent, so N GPUs would each score their own sequences). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
