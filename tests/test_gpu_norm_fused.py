@@ -31,7 +31,8 @@ def _gamma(seed, K):
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (1, 4096, 28672), (2, 4096, 6144), (2, 4096, 16400),
                                    (3, 4096, 4096), (4, 4096, 1040), (1, 8200, 520), (4, 8200, 16400),
-                                   (2, 14336, 256), (3, 264, 40), (1, 72, 24), (4, 72, 16)])
+                                   (2, 14336, 256), (3, 264, 40), (1, 72, 24), (4, 72, 16), (1, 8, 5),
+                                   (2, 16, 33), (4, 16384, 20)])
 def test_rmsnorm_gemm_matches_oracle(orc, M, K, N):
     """Routes: N below 16384 with one or two rows runs 4-row workgroups, else 16-row ones;
     three and four rows run the 4x4x1 matrix chains."""
